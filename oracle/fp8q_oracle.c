@@ -1,0 +1,308 @@
+/*
+ * fp8q oracle -- TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.
+ *
+ * A deliberately plain, slow CPU implementation of what the FP8
+ * weight-quantized linear path computes.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load this library; the
+ * product (the HIP library and its Python binding) never calls it and shares
+ * no code with it.
+ *
+ * Build flags matter for bit-exactness: -O2 -fno-fast-math -ffp-contract=off,
+ * so that every fp32 division is an IEEE-754 correctly rounded division and
+ * no multiply-add is fused.  OpenMP is used only across independent outputs
+ * (rows, or output elements whose own k-order is fixed), so the number of
+ * threads never changes a result.
+ *
+ * Sources (web pages on FP8 quantization of Llama 3):
+ *   [P2] "FP8量化与长上下文实测：Llama 3 70B部署优化指南"
+ *        §1.1 -- E4M3: 4 exponent bits, 3 mantissa bits, largest value about
+ *                448, smallest non-zero about 2^-9.
+ *        §1.2 -- weights scaled per channel, activations per tensor.
+ *        §3.1 -- conversion: per-channel absmax / 448, scale clamped below at
+ *                1e-12, weight divided by the scale and cast to
+ *                float8_e4m3fn; scale kept beside the weight.
+ *   [P1] "Llama 3 精读" FP8 + 128K deployment write-up
+ *        §2.1 -- E4M3 range is symmetric, [-448, 448].
+ *        §3.1 step 3 -- the FP8 MatMul modes fp8_w_bf16_a (FP8 weight, BF16
+ *                activation) and fp8_w_fp8_a (FP8 weight and activation).
+ *
+ * Readings where the pages are silent or contradict each other (each one is
+ * listed, with its reason, in the design notes of the repository):
+ *   - scale arithmetic is fp32 (the scale is stored as a float),
+ *   - the quotient is an IEEE fp32 division, then a separate RNE cast to E4M3
+ *     (two roundings, in that order),
+ *   - values at or beyond 448 in magnitude saturate to +-448,
+ *   - the sign of zero is kept (negatives that round to zero give code 0x80),
+ *   - the activation scale uses the same formula as the weight scale, taken
+ *     over the whole tensor.
+ *
+ * Parity pins for every function live in tests/test_oracle_*.py.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+
+#define ORACLE_ABI 1
+
+int oracle_abi_version(void) { return ORACLE_ABI; }
+
+/* ------------------------------------------------------------------------ */
+/* E4M3 (OCP "e4m3fn") decode, from the bit fields.                          */
+/* [P2 §1.1] 4 exponent bits and 3 mantissa bits; max about 448, smallest    */
+/* non-zero about 2^-9.  With 4+3 bits, a maximum of 448 = 1.75 * 2^8 forces  */
+/* exponent bias 7 and an all-ones exponent that is still finite (only the    */
+/* mantissa 111 pattern of it is NaN); 2^-9 = 2^(1-7) * 2^-3 is then the      */
+/* smallest subnormal.  There are no infinities.                              */
+/* ------------------------------------------------------------------------ */
+double oracle_e4m3_value(unsigned code)
+{
+    unsigned s = (code >> 7) & 1u;
+    unsigned e = (code >> 3) & 15u;
+    unsigned m = code & 7u;
+    double mag;
+    if (e == 15u && m == 7u)
+        return NAN;
+    if (e == 0u)
+        mag = ldexp((double)m, -9);                 /* m/8 * 2^(1-7) */
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -mag : mag;
+}
+
+void oracle_e4m3_table(double *out256)
+{
+    for (unsigned c = 0; c < 256u; ++c)
+        out256[c] = oracle_e4m3_value(c);
+}
+
+/* The 127 non-negative finite magnitudes, codes 0x00..0x7E, in code order. */
+static double g_mag[127];
+static int g_mag_ready = 0;
+
+static void mag_init(void)
+{
+    if (g_mag_ready)
+        return;
+    for (unsigned c = 0; c < 127u; ++c)
+        g_mag[c] = oracle_e4m3_value(c);
+    g_mag_ready = 1;
+}
+
+__attribute__((constructor)) static void oracle_init(void) { mag_init(); }
+
+/* ------------------------------------------------------------------------ */
+/* Cast fp32 -> E4M3 code, round to nearest, ties to even, saturating.       */
+/* [P2 §3.1] cast to float8_e4m3fn (round to nearest even);                  */
+/* [P1 §2.1] representable range is [-448, 448]: anything beyond saturates.  */
+/* Method: search the table of representable magnitudes for the nearest one; */
+/* on an exact tie pick the code whose mantissa LSB is 0 (an even code).     */
+/* The sign is attached afterwards, so -0 and negative values that round to  */
+/* zero give 0x80.                                                           */
+/* ------------------------------------------------------------------------ */
+static unsigned pick_nearest(double a, unsigned lo_code)
+{
+    /* g_mag[lo_code] <= a < g_mag[lo_code + 1] */
+    double dlo = a - g_mag[lo_code];
+    double dhi = g_mag[lo_code + 1] - a;
+    if (dlo < dhi)
+        return lo_code;
+    if (dhi < dlo)
+        return lo_code + 1;
+    return (lo_code & 1u) ? lo_code + 1 : lo_code;   /* tie: even code */
+}
+
+unsigned oracle_cast_e4m3(float t)
+{
+    if (isnan(t))
+        return 0x7Fu;                    /* out of domain; canonical NaN */
+    unsigned sign = signbit(t) ? 0x80u : 0u;
+    double a = fabs((double)t);
+    if (a >= 448.0)
+        return sign | 0x7Eu;             /* saturate */
+    /* binary search for the largest code with g_mag[code] <= a */
+    unsigned lo = 0, hi = 126;           /* g_mag[0] = 0 <= a < g_mag[126] = 448 */
+    while (hi - lo > 1u) {
+        unsigned mid = (lo + hi) / 2u;
+        if (g_mag[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return sign | pick_nearest(a, lo);
+}
+
+/* The same cast found by a different route: a linear scan for the arg-min  */
+/* distance over all 127 magnitudes.  Used only to cross-check the search.  */
+unsigned oracle_cast_e4m3_scan(float t)
+{
+    if (isnan(t))
+        return 0x7Fu;
+    unsigned sign = signbit(t) ? 0x80u : 0u;
+    double a = fabs((double)t);
+    if (a >= 448.0)
+        return sign | 0x7Eu;
+    unsigned best = 0;
+    double bestd = INFINITY;
+    for (unsigned c = 0; c < 127u; ++c) {
+        double d = fabs(g_mag[c] - a);
+        if (d < bestd || (d == bestd && (c & 1u) == 0u)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return sign | best;
+}
+
+void oracle_cast_e4m3_array(const float *t, int64_t count, uint8_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = (uint8_t)oracle_cast_e4m3(t[i]);
+}
+
+/* Cast every fp32 bit pattern in [first, first + count) and store the codes. */
+void oracle_cast_e4m3_bits(uint32_t first, int64_t count, uint8_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        uint32_t b = first + (uint32_t)i;
+        float t;
+        memcpy(&t, &b, 4);
+        out[i] = (uint8_t)oracle_cast_e4m3(t);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* BF16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.   */
+/* ------------------------------------------------------------------------ */
+static float bf16_value(uint16_t h)
+{
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scale from an absolute maximum.                                           */
+/* [P2 §3.1] scale = absmax / 448, then clamped below at 1e-12.              */
+/* fp32 IEEE division; the clamp constant is the fp32 value nearest 1e-12.   */
+/* ------------------------------------------------------------------------ */
+float oracle_scale_from_amax(float amax)
+{
+    float s = amax / 448.0f;
+    const float floor_ = 1e-12f;
+    if (s < floor_)
+        s = floor_;
+    return s;
+}
+
+/* One quantized element: fp32 quotient first, then the E4M3 cast. */
+static uint8_t quantize_one(float w, float s)
+{
+    float t = w / s;                     /* IEEE fp32 division */
+    return (uint8_t)oracle_cast_e4m3(t);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-output-channel weight quantization.                                   */
+/* [P2 §3.1] for each row n of the [out, in] weight: absmax over the row,    */
+/* scale = absmax/448 clamped at 1e-12, codes = cast(w / scale).             */
+/* [P2 §1.2] weights use per-channel scales.                                 */
+/* Returns 1 if any input was NaN or infinite (such input is out of domain), */
+/* else 0.                                                                   */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                           uint8_t *q, int64_t ld_q, float *scale)
+{
+    int nonfinite = 0;
+#pragma omp parallel for schedule(static) reduction(| : nonfinite)
+    for (int64_t r = 0; r < n; ++r) {
+        const uint16_t *row = w + r * ld_w;
+        float amax = 0.0f;
+        for (int64_t c = 0; c < k; ++c) {
+            float a = fabsf(bf16_value(row[c]));
+            if (!isfinite(a))
+                nonfinite = 1;
+            if (a > amax)
+                amax = a;
+        }
+        float s = oracle_scale_from_amax(amax);
+        scale[r] = s;
+        for (int64_t c = 0; c < k; ++c)
+            q[r * ld_q + c] = quantize_one(bf16_value(row[c]), s);
+    }
+    return nonfinite;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic per-tensor activation quantization.                               */
+/* [P2 §1.2] activations use a single per-tensor scale; the scale formula is */
+/* the one of [P2 §3.1] taken over all elements of the tensor, recomputed    */
+/* on every call.                                                            */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                        uint8_t *q, int64_t ld_q, float *scale_out)
+{
+    int nonfinite = 0;
+    float amax = 0.0f;
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t c = 0; c < k; ++c) {
+            float a = fabsf(bf16_value(x[r * ld_x + c]));
+            if (!isfinite(a))
+                nonfinite = 1;
+            if (a > amax)
+                amax = a;
+        }
+    float s = oracle_scale_from_amax(amax);
+    *scale_out = s;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t c = 0; c < k; ++c)
+            q[r * ld_q + c] = quantize_one(bf16_value(x[r * ld_x + c]), s);
+    return nonfinite;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The scaled linear layer, in fp64.                                         */
+/* [P1 §3.1 step 3] two of the FP8 MatMul modes:                             */
+/*   mode 0, fp8_w_bf16_a:  Y[m,n] = s_w[n] * sum_k X[m,k] * dec(Wq[n,k])     */
+/*   mode 1, fp8_w_fp8_a:   Y[m,n] = s_x * s_w[n] * sum_k dec(Xq[m,k]) *      */
+/*                                   dec(Wq[n,k])                            */
+/* The weight follows the [out, in] layout of a linear layer, so Y = X W^T.   */
+/* Every term is widened to double and summed in increasing k.  For mode 1    */
+/* every product is a multiple of 2^-18 below 2^17, so the double sum is      */
+/* exact for any K below 2^18.                                               */
+/* `rows` selects which rows of X to evaluate (NULL means all m rows); the    */
+/* result has shape [nrows, n] in y.                                         */
+/* ------------------------------------------------------------------------ */
+void oracle_linear(int mode, const void *x, int64_t m, int64_t k, int64_t ld_x,
+                   float x_scale, const uint8_t *wq, int64_t n, int64_t ld_w,
+                   const float *w_scale, const int64_t *rows, int64_t nrows,
+                   double *y)
+{
+    double tab[256];
+    oracle_e4m3_table(tab);
+    if (rows == NULL)
+        nrows = m;
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int64_t i = 0; i < nrows; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t r = rows ? rows[i] : i;
+            const uint8_t *wrow = wq + j * ld_w;
+            double acc = 0.0;
+            if (mode == 0) {
+                const uint16_t *xrow = (const uint16_t *)x + r * ld_x;
+                for (int64_t c = 0; c < k; ++c)
+                    acc += (double)bf16_value(xrow[c]) * tab[wrow[c]];
+                y[i * n + j] = acc * (double)w_scale[j];
+            } else {
+                const uint8_t *xrow = (const uint8_t *)x + r * ld_x;
+                for (int64_t c = 0; c < k; ++c)
+                    acc += tab[xrow[c]] * tab[wrow[c]];
+                y[i * n + j] = acc * ((double)x_scale * (double)w_scale[j]);
+            }
+        }
+    }
+}
