@@ -1,0 +1,403 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 weight-quantized linear path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+Prints ONE JSON line.  The headline workload is Llama-3-8B q_proj decode:
+W [4096, 4096] E4M3 with per-channel scales, bf16 X with M in {1, 8, 32, 64},
+fp8_w_bf16_a (W8A16).  One step = one linear call per M (4 calls), each on a
+different copy of the quantized weight from a rotating pool larger than the
+256 MB Infinity Cache, so every step streams its weights from HBM.  The steps
+are captured in HIP graphs (as a decode loop would run them) and timed with
+HIP events on the launch stream.  `value` is the algorithmic weight-stream
+throughput: (N*K codes + 4N scale bytes + 2MK activation bytes + 2MN output
+bytes) summed over the step's calls, divided by the step time.
+
+Unless --quick, the same line carries measurements of the other rows of the
+path on their own workloads ("rows"): weight quantization, activation
+quantization, the W8A8 prefill GEMM (Llama-3-8B gate+up and Llama-3-70B
+down_proj) and the Llama-3-70B decoder layer's seven linears at M = 12.
+
+`cpu_baseline` is the CPU oracle (tests' checker) timed on this host on one
+full decode step.  Inputs are seeded synthetic data (workloads.py).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published
+MALL_BYTES = 256 << 20         # Infinity Cache
+DECODE_MS = (1, 8, 32, 64)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=12)
+    ap.add_argument("--quick", action="store_true", help="headline only (no extra rows)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pool-mb", type=int, default=1024,
+                    help="size of the rotating pool of quantized weight copies")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(json.dumps({"error": "this benchmark runs on exactly one GPU; the FP8 linear "
+                              "path is measured on one MI355X (see DESIGN.md for how it would shard)",
+                              "n_gpus": args.gpus}), flush=True)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+
+    import numpy as np
+    import torch
+
+    import fp8_weight_quantized_amd as fq
+    import workloads
+    from fp8_weight_quantized_amd import _lib
+
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda:0")
+    L = _lib.lib()
+    log("library", fq.library_path(), "device", torch.cuda.get_device_name(dev))
+
+    def up_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def ptr(t):
+        return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(None)
+
+    # ------------------------------------------------------------------ decode
+    wl = workloads.WORKLOADS["q_proj_decode"]
+    lin = wl.linears[0]
+    N, K = lin.n, lin.k
+    t0 = time.time()
+    w_bits = workloads.weight(wl, lin)
+    xs_bits = {m: workloads.activation(wl, m, K) for m in DECODE_MS}
+    log(f"generated q_proj inputs in {time.time() - t0:.1f}s")
+    wq0, w_scale = fq.quantize_weight(up_bf16(w_bits))
+    copies_n = max(8, (args.pool_mb << 20) // (N * K))
+    copies_n = (copies_n + len(DECODE_MS) - 1) // len(DECODE_MS) * len(DECODE_MS)
+    pool = torch.empty((copies_n, N, K), dtype=torch.uint8, device=dev)
+    pool[:] = wq0.unsqueeze(0)
+    xs = {m: up_bf16(xs_bits[m]) for m in DECODE_MS}
+    ys = {m: torch.empty((m, N), dtype=torch.bfloat16, device=dev) for m in DECODE_MS}
+    wsn = {m: L.fp8q_linear_workspace_size(0, m, N, K) for m in DECODE_MS}
+    wsp = {m: (torch.empty(wsn[m], dtype=torch.uint8, device=dev) if wsn[m] else None) for m in DECODE_MS}
+    step_bytes = sum(N * K + 4 * N + 2 * m * K + 2 * m * N for m in DECODE_MS)
+    rot = copies_n // len(DECODE_MS)          # steps per full rotation of the pool
+
+    def decode_step(i: int, stream: int):
+        for j, m in enumerate(DECODE_MS):
+            c = (len(DECODE_MS) * i + j) % copies_n
+            st = L.fp8q_linear(0, ptr(xs[m]), m, K, K, None, ptr(pool[c]), N, K, ptr(w_scale),
+                               ptr(ys[m]), N, ptr(wsp[m]), wsn[m], stream)
+            if st != 0:
+                raise RuntimeError(_lib.last_error())
+
+    def capture(nsteps: int):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream(device=dev)
+        s.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+            h = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(nsteps):
+                decode_step(i, h)
+        torch.cuda.current_stream(dev).wait_stream(s)
+        return g
+
+    cur = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(args.warmup):                       # eager warm-up steps
+        decode_step(i, cur)
+    n_full, rem = divmod(args.steps, rot)
+    g_full = capture(rot) if n_full else None
+    g_rem = capture(rem) if rem else None
+    for g in (g_full, g_rem):                          # first replay uploads the graph
+        if g is not None:
+            g.replay()
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(n_full):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"decode step {ms_per_step * 1e3:.2f} us, {value:.1f} GB/s")
+
+    # per-M breakdown (each call alone, graph of one rotation)
+    per_m = {}
+    for j, m in enumerate(DECODE_MS):
+        def one_m(i, stream, m=m):
+            c = i % copies_n
+            st = L.fp8q_linear(0, ptr(xs[m]), m, K, K, None, ptr(pool[c]), N, K, ptr(w_scale),
+                               ptr(ys[m]), N, ptr(wsp[m]), wsn[m], stream)
+            if st != 0:
+                raise RuntimeError(_lib.last_error())
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream(device=dev)
+        s.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+            h = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(copies_n):
+                one_m(i, h)
+        torch.cuda.current_stream(dev).wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        end.record()
+        end.synchronize()
+        us = start.elapsed_time(end) * 1e3 / copies_n
+        b = N * K + 4 * N + 2 * m * K + 2 * m * N
+        per_m[str(m)] = {"us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                         "kernel": fq.describe_linear(0, m, N, K)}
+    log("per-M", per_m)
+
+    result = {
+        "metric": "FP8 linear TFLOPS (prefill M) and weight-stream GB/s (decode M); % of roofline",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 weights x bf16 activations, fp32 accumulate, bf16 out",
+        "data": "synthetic: seeded heavy-tail N(0,0.1)+3% +-U(2,4) weights, N(0,1) activations",
+        "config": {
+            "workload": "Llama-3-8B q_proj decode, fp8_w_bf16_a (W8A16)",
+            "N": N, "K": K, "M": list(DECODE_MS),
+            "weight_copies_rotated": copies_n,
+            "weight_pool_MB": round(copies_n * N * K / 1e6, 1),
+            "timing": "HIP graphs of whole steps, HIP events on the launch stream",
+        },
+        "per_m": per_m,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_w8a16 (+ k_splitk_reduce where K is split)",
+            "achieved": round(value, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+
+    # --------------------------------------------------------------- other rows
+    if not args.quick:
+        result["rows"] = other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev)
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = nbytes
+
+    # ------------------------------------------------------------ CPU baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, lin, w_bits, xs_bits, step_bytes)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def time_eager(torch, fn, iters: int, warm: int = 2) -> float:
+    """Average ms per call of fn() over `iters` calls, HIP events on the current stream."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
+    rows = {}
+    iters = max(3, min(args.steps, 20))
+    stream = lambda: torch.cuda.current_stream(dev).cuda_stream  # noqa: E731
+
+    # prefill: activation quantization + W8A8 GEMM
+    for key in ("mlp_prefill", "down_prefill_70b"):
+        wl = workloads.WORKLOADS[key]
+        lin = wl.linears[0]
+        m = wl.ms[0]
+        t0 = time.time()
+        w_bits = workloads.weight(wl, lin)
+        x_bits = workloads.activation(wl, m, lin.k)
+        log(f"generated {key} inputs in {time.time() - t0:.1f}s")
+        w = up_bf16(w_bits)
+        x = up_bf16(x_bits)
+        del w_bits, x_bits
+        wq, ws = fq.quantize_weight(w)
+        xq, xsc = fq.quantize_act(x)
+        y = torch.empty((m, lin.n), dtype=torch.bfloat16, device=dev)
+        n, k = lin.n, lin.k
+
+        def gemm():
+            st = L.fp8q_linear(1, ptr(xq), m, k, xq.stride(0), ptr(xsc), ptr(wq), n, wq.stride(0),
+                               ptr(ws), ptr(y), n, None, 0, stream())
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+        ms = time_eager(torch, gemm, iters)
+        flops = 2.0 * m * n * k
+        tf = flops / (ms * 1e-3) / 1e12
+        rows[f"a6a7_w8a8_{key}"] = {
+            "shape": f"M={m} N={n} K={k}", "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+            "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4), "kernel": fq.describe_linear(1, m, n, k)}
+        log(key, rows[f"a6a7_w8a8_{key}"])
+
+        aws_n = L.fp8q_quantize_act_workspace_size(m, k)
+        aws = torch.empty(aws_n, dtype=torch.uint8, device=dev)
+
+        def actq():
+            st = L.fp8q_quantize_act(ptr(x), m, k, k, ptr(xq), xq.stride(0), ptr(xsc), ptr(aws),
+                                     aws_n, None, stream())
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+        ms = time_eager(torch, actq, iters)
+        b = 3.0 * m * k + 4
+        rows[f"a3a4_quantize_act_{key}"] = {
+            "shape": f"M={m} K={k}", "us": round(ms * 1e3, 2),
+            "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "two kernels (absmax, cast); X is re-read by the cast"}
+        log(key, rows[f"a3a4_quantize_act_{key}"])
+        del w, x, wq, ws, xq, y
+        torch.cuda.empty_cache()
+
+    # 70B decoder layer at decode M = 12 (W8A16), plus weight quantization of gate_proj
+    wl = workloads.WORKLOADS["layer_decode_70b"]
+    m = wl.ms[0]
+    t0 = time.time()
+    layer = []
+    for lin in wl.linears:
+        w = up_bf16(workloads.weight(wl, lin))
+        if lin.name == "gate_proj":
+            q = torch.empty((lin.n, lin.k), dtype=torch.uint8, device=dev)
+            s = torch.empty(lin.n, dtype=torch.float32, device=dev)
+
+            def wquant(w=w, q=q, s=s, lin=lin):
+                st = L.fp8q_quantize_weight(ptr(w), lin.n, lin.k, lin.k, ptr(q), lin.k, ptr(s), None, stream())
+                if st != 0:
+                    raise RuntimeError(fq._lib.last_error())
+            ms = time_eager(torch, wquant, iters)
+            b = 3.0 * lin.n * lin.k + 4 * lin.n
+            rows["a1a2_quantize_weight_gate_proj_70b"] = {
+                "shape": f"N={lin.n} K={lin.k}", "us": round(ms * 1e3, 2),
+                "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(rows["a1a2_quantize_weight_gate_proj_70b"])
+        wq, ws = fq.quantize_weight(w)
+        del w
+        x = up_bf16(workloads.activation(wl, m, lin.k))
+        y = torch.empty((m, lin.n), dtype=torch.bfloat16, device=dev)
+        nws = L.fp8q_linear_workspace_size(0, m, lin.n, lin.k)
+        wsb = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+        layer.append((lin, wq, ws, x, y, wsb, nws))
+    log(f"prepared 70B layer in {time.time() - t0:.1f}s")
+    torch.cuda.empty_cache()
+
+    def layer_step(h):
+        for lin, wq, ws, x, y, wsb, nws in layer:
+            st = L.fp8q_linear(0, ptr(x), m, lin.k, lin.k, None, ptr(wq), lin.n, wq.stride(0), ptr(ws),
+                               ptr(y), lin.n, ptr(wsb), nws, h)
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+        layer_step(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    ms = time_eager(torch, g.replay, iters)
+    b = sum(lin.n * lin.k + 4 * lin.n + 2 * m * lin.k + 2 * m * lin.n for lin, *_ in layer)
+    per = {}
+    for lin, wq, ws, x, y, wsb, nws in layer:
+        def one(lin=lin, wq=wq, ws=ws, x=x, y=y, wsb=wsb, nws=nws):
+            st = L.fp8q_linear(0, ptr(x), m, lin.k, lin.k, None, ptr(wq), lin.n, wq.stride(0), ptr(ws),
+                               ptr(y), lin.n, ptr(wsb), nws, stream())
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+        mso = time_eager(torch, one, iters)
+        bb = lin.n * lin.k + 4 * lin.n + 2 * m * lin.k + 2 * m * lin.n
+        per[lin.name] = {"us": round(mso * 1e3, 2), "GB/s": round(bb / (mso * 1e-3) / 1e9, 1)}
+    rows["a5_layer_decode_70b"] = {
+        "shape": "7 linears, M=12", "weight_MB": round(b / 1e6, 1), "us": round(ms * 1e3, 2),
+        "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "timing": "one HIP graph per layer step", "per_linear_eager": per}
+    log(rows["a5_layer_decode_70b"])
+    del layer
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(wl, lin, w_bits, xs_bits, step_bytes) -> dict:
+    """The CPU oracle (unchanged, fp64) on one full decode step: the four
+    q_proj calls M = 1, 8, 32, 64 on the oracle-quantized weight."""
+    import oracle
+    oracle.build()
+    wq, ws, _ = oracle.quantize_weight(w_bits)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:                         # repeat whole steps for about 10 s of CPU work
+        for m in DECODE_MS:
+            oracle.linear(0, xs_bits[m], wq, ws)
+        reps += 1
+        if time.perf_counter() - t0 >= 10.0:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "seconds_per_step": round(dt, 3), "steps_timed": reps,
+            "sample": f"{reps} full decode steps (q_proj W[4096,4096], M=1,8,32,64), fp64 oracle "
+                      "GEMM; weight quantization excluded as on the GPU side"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,162 @@
+"""fp8q: FP8 (E4M3) weight-quantized linear layers on AMD MI355X (gfx950).
+
+A thin binding over the C ABI of libfp8q.so (include/fp8q.h): it checks
+tensor metadata, allocates outputs and scratch with torch (device memory
+only) and passes raw pointers and the current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no CPU path.
+
+    wq, w_scale = quantize_weight(w_bf16)             # per output channel
+    xq, x_scale = quantize_act(x_bf16)                # per tensor, dynamic
+    y = linear(x_bf16, wq, w_scale)                   # fp8_w_bf16_a (decode)
+    y = linear(xq, wq, w_scale, x_scale=x_scale)      # fp8_w_fp8_a  (prefill)
+
+Codes are returned as uint8 tensors holding raw e4m3fn bit patterns (view
+them with .view(torch.float8_e4m3fn)).  Code matrices are allocated with a
+row stride rounded up to 16 bytes, as the GEMM requires.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import FP8Q_W8A8, FP8Q_W8A16, Fp8qError, check
+
+__all__ = [
+    "quantize_weight", "quantize_act", "linear", "cast_f32_to_e4m3", "describe_linear",
+    "FP8Q_W8A16", "FP8Q_W8A8", "Fp8qError", "library_path",
+]
+
+
+def library_path() -> str:
+    _lib.lib()
+    return _lib.LIB_PATH
+
+
+def _round_up(v: int, a: int) -> int:
+    return (v + a - 1) // a * a
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else None)
+
+
+def _matrix(t: torch.Tensor, name: str, dtypes) -> tuple[int, int, int]:
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+    ld = t.stride(0) if rows > 1 else max(cols, t.stride(0))
+    return rows, cols, ld
+
+
+def _codes(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def _new_codes(rows: int, cols: int, dev: torch.device) -> torch.Tensor:
+    ld = _round_up(max(cols, 1), 16)
+    return torch.empty((rows, ld), dtype=torch.uint8, device=dev)[:, :cols]
+
+
+def quantize_weight(w: torch.Tensor, nonfinite_flag: torch.Tensor | None = None):
+    """Per-output-channel E4M3 quantization of a bf16 [N, K] weight.
+
+    Returns (codes uint8 [N, K], scale float32 [N]).  `nonfinite_flag`, an
+    int32 GPU tensor, is set to 1 if any weight is NaN or infinite.
+    """
+    n, k, ld = _matrix(w, "w", (torch.bfloat16,))
+    dev = w.device
+    q = _new_codes(n, k, dev)
+    scale = torch.empty(n, dtype=torch.float32, device=dev)
+    check(_lib.lib().fp8q_quantize_weight(
+        _ptr(w), n, k, ld, _ptr(q), q.stride(0) if n else _round_up(k, 16), _ptr(scale),
+        _ptr(nonfinite_flag), _stream(dev)))
+    return q, scale
+
+
+def quantize_act(x: torch.Tensor, nonfinite_flag: torch.Tensor | None = None):
+    """Dynamic per-tensor E4M3 quantization of bf16 activations [M, K].
+
+    Returns (codes uint8 [M, K], scale float32 [1]) -- the scale stays on the GPU.
+    """
+    m, k, ld = _matrix(x, "x", (torch.bfloat16,))
+    dev = x.device
+    q = _new_codes(m, k, dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    L = _lib.lib()
+    nws = L.fp8q_quantize_act_workspace_size(m, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    check(L.fp8q_quantize_act(
+        _ptr(x), m, k, ld, _ptr(q), q.stride(0) if m else _round_up(k, 16), _ptr(scale),
+        _ptr(ws), nws, _ptr(nonfinite_flag), _stream(dev)))
+    return q, scale
+
+
+def linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+           x_scale: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X . dequant(Wq)^T in bf16.
+
+    x bf16 [M, K] with x_scale None  -> fp8_w_bf16_a (W8A16, decode).
+    x E4M3 codes [M, K] with x_scale -> fp8_w_fp8_a  (W8A8, prefill).
+    """
+    wq = _codes(wq)
+    x = _codes(x)
+    if x.dtype == torch.bfloat16:
+        mode = FP8Q_W8A16
+        if x_scale is not None:
+            raise ValueError("a bf16 activation takes no x_scale (fp8_w_bf16_a)")
+    elif x.dtype == torch.uint8:
+        mode = FP8Q_W8A8
+        if x_scale is None:
+            raise ValueError("E4M3 activations need x_scale (fp8_w_fp8_a)")
+    else:
+        raise TypeError(f"x must be bf16 or E4M3 codes, got {x.dtype}")
+    m, k, ldx = _matrix(x, "x", (torch.bfloat16, torch.uint8))
+    n, k2, ldw = _matrix(wq, "wq", (torch.uint8,))
+    if k2 != k:
+        raise ValueError(f"inner dimensions differ: x has K={k}, wq has K={k2}")
+    if w_scale.dtype != torch.float32 or w_scale.numel() != n or not w_scale.is_cuda:
+        raise ValueError("w_scale must be a float32 GPU tensor with N elements")
+    w_scale = w_scale.reshape(-1)
+    if not w_scale.is_contiguous():
+        raise ValueError("w_scale must be contiguous")
+    if x_scale is not None and (x_scale.dtype != torch.float32 or x_scale.numel() != 1 or not x_scale.is_cuda):
+        raise ValueError("x_scale must be a float32 GPU tensor with one element")
+    dev = x.device
+    if out is None:
+        out = torch.empty((m, _round_up(max(n, 1), 8)), dtype=torch.bfloat16, device=dev)[:, :n]
+    om, on, ldy = _matrix(out, "out", (torch.bfloat16,))
+    if (om, on) != (m, n):
+        raise ValueError(f"out must be [{m}, {n}]")
+    L = _lib.lib()
+    nws = L.fp8q_linear_workspace_size(mode, m, n, k)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    check(L.fp8q_linear(mode, _ptr(x), m, k, ldx, _ptr(x_scale), _ptr(wq), n, ldw,
+                        _ptr(w_scale), _ptr(out), ldy, _ptr(ws), nws, _stream(dev)))
+    return out
+
+
+def cast_f32_to_e4m3(x: torch.Tensor) -> torch.Tensor:
+    """RNE, saturating fp32 -> E4M3 codes, elementwise (any shape, contiguous)."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    check(_lib.lib().fp8q_cast_f32_to_e4m3(_ptr(x), x.numel(), _ptr(out), _stream(x.device)))
+    return out
+
+
+def describe_linear(mode: int, m: int, n: int, k: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    check(_lib.lib().fp8q_linear_describe(mode, m, n, k, buf, 256))
+    return buf.value.decode()

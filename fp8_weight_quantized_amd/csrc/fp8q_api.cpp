@@ -1,0 +1,360 @@
+// C ABI of the fp8q library: argument validation, device checks and kernel
+// dispatch.  Nothing here allocates device memory or synchronizes; every
+// kernel is enqueued on the caller's stream.  The operations are documented
+// in include/fp8q.h.
+#include "fp8q.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "kernels/launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp8q_status fail(fp8q_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fp8q_status ok()
+{
+    g_err[0] = '\0';
+    return FP8Q_OK;
+}
+
+fp8q_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(FP8Q_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- per-device property cache ---------------------------------------------
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+    bool known = false;
+    bool gfx950 = false;
+    char arch[64] = "";
+};
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+fp8q_status stream_device(hipStream_t stream, int *dev)
+{
+    hipDevice_t d = 0;
+    hipError_t e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FP8Q_ERR_HIP, "cannot query the device of the stream: %s", hipGetErrorString(e));
+    }
+    *dev = (int)d;
+    if (*dev < 0 || *dev >= kMaxDevices)
+        return fail(FP8Q_ERR_UNSUPPORTED, "device ordinal %d out of range", *dev);
+    return FP8Q_OK;
+}
+
+fp8q_status check_device(int dev)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceInfo &info = g_dev[dev];
+    if (!info.known) {
+        hipDeviceProp_t prop;
+        hipError_t e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return hip_fail(e, "hipGetDeviceProperties");
+        }
+        std::snprintf(info.arch, sizeof(info.arch), "%s", prop.gcnArchName);
+        info.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        info.known = true;
+    }
+    if (!info.gfx950)
+        return fail(FP8Q_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 only", dev,
+                    info.arch);
+    return FP8Q_OK;
+}
+
+// The device of `stream`, checked to be a gfx950.
+fp8q_status prepare(hipStream_t stream, int *dev)
+{
+    fp8q_status s = stream_device(stream, dev);
+    if (s != FP8Q_OK)
+        return s;
+    return check_device(*dev);
+}
+
+// A pointer the kernels will dereference: non-null, aligned, device memory
+// on the stream's device.
+fp8q_status check_ptr(const void *p, const char *name, int dev, size_t align)
+{
+    if (p == nullptr)
+        return fail(FP8Q_ERR_INVALID_ARG, "%s is NULL", name);
+    if (align > 1 && (reinterpret_cast<uintptr_t>(p) % align) != 0)
+        return fail(FP8Q_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FP8Q_ERR_INVALID_ARG, "%s is not device memory (%s)", name, hipGetErrorString(e));
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged && !attr.isManaged)
+        return fail(FP8Q_ERR_INVALID_ARG, "%s is not device memory (memory type %d)", name,
+                    (int)attr.type);
+    if (attr.device != dev)
+        return fail(FP8Q_ERR_INVALID_ARG, "%s lives on device %d but the stream is on device %d",
+                    name, attr.device, dev);
+    return FP8Q_OK;
+}
+
+// Byte extent of a row-major [rows, cols] matrix with row stride ld.
+size_t extent(int64_t rows, int64_t cols, int64_t ld, size_t elem)
+{
+    if (rows <= 0 || cols <= 0)
+        return 0;
+    return (size_t)((rows - 1) * ld + cols) * elem;
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (na == 0 || nb == 0)
+        return false;
+    uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+fp8q_status check_ld(int64_t ld, int64_t cols, int64_t multiple, const char *name)
+{
+    if (ld < cols)
+        return fail(FP8Q_ERR_INVALID_ARG, "%s = %lld is smaller than the row length %lld", name,
+                    (long long)ld, (long long)cols);
+    if (ld % multiple != 0)
+        return fail(FP8Q_ERR_INVALID_ARG, "%s = %lld is not a multiple of %lld", name,
+                    (long long)ld, (long long)multiple);
+    return FP8Q_OK;
+}
+
+#define FP8Q_TRY(expr)                   \
+    do {                                 \
+        fp8q_status _s = (expr);         \
+        if (_s != FP8Q_OK)               \
+            return _s;                   \
+    } while (0)
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
+
+const char *fp8q_status_string(fp8q_status s)
+{
+    switch (s) {
+    case FP8Q_OK: return "FP8Q_OK";
+    case FP8Q_ERR_INVALID_ARG: return "FP8Q_ERR_INVALID_ARG: invalid argument";
+    case FP8Q_ERR_UNSUPPORTED: return "FP8Q_ERR_UNSUPPORTED: device is not gfx950";
+    case FP8Q_ERR_HIP: return "FP8Q_ERR_HIP: HIP runtime or launch error";
+    case FP8Q_ERR_WORKSPACE: return "FP8Q_ERR_WORKSPACE: workspace missing or too small";
+    }
+    return "FP8Q: unknown status";
+}
+
+const char *fp8q_last_error(void) { return g_err; }
+
+fp8q_status fp8q_quantize_weight(const uint16_t *w_bf16, int64_t n, int64_t k, int64_t ld_w,
+                                 uint8_t *w_fp8, int64_t ld_q, float *w_scale,
+                                 int32_t *nonfinite_flag, hipStream_t stream)
+{
+    if (n < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "need n >= 0 and k >= 1 (n=%lld, k=%lld)", (long long)n,
+                    (long long)k);
+    FP8Q_TRY(check_ld(ld_w, k, 1, "ld_w"));
+    FP8Q_TRY(check_ld(ld_q, k, 1, "ld_q"));
+    if (n == 0)
+        return ok();
+    int dev = 0;
+    FP8Q_TRY(prepare(stream, &dev));
+    FP8Q_TRY(check_ptr(w_bf16, "w_bf16", dev, 2));
+    FP8Q_TRY(check_ptr(w_fp8, "w_fp8", dev, 1));
+    FP8Q_TRY(check_ptr(w_scale, "w_scale", dev, 4));
+    if (nonfinite_flag != nullptr)
+        FP8Q_TRY(check_ptr(nonfinite_flag, "nonfinite_flag", dev, 4));
+    const size_t ew = extent(n, k, ld_w, 2), eq = extent(n, k, ld_q, 1), es = (size_t)n * 4;
+    if (overlap(w_fp8, eq, w_bf16, ew) || overlap(w_scale, es, w_bf16, ew) ||
+        overlap(w_scale, es, w_fp8, eq))
+        return fail(FP8Q_ERR_INVALID_ARG, "outputs overlap each other or the input");
+    hipError_t e = fp8q::launch::quantize_weight(w_bf16, n, k, ld_w, w_fp8, ld_q, w_scale,
+                                                 nonfinite_flag, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "weight quantization launch");
+    return ok();
+}
+
+size_t fp8q_quantize_act_workspace_size(int64_t m, int64_t k)
+{
+    if (m < 0 || k < 1)
+        return 0;
+    return round_up((size_t)fp8q::launch::act_blocks(m, k) * sizeof(uint32_t), 256);
+}
+
+fp8q_status fp8q_quantize_act(const uint16_t *x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                              uint8_t *x_fp8, int64_t ld_q, float *x_scale,
+                              void *workspace, size_t workspace_bytes,
+                              int32_t *nonfinite_flag, hipStream_t stream)
+{
+    if (m < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "need m >= 0 and k >= 1 (m=%lld, k=%lld)", (long long)m,
+                    (long long)k);
+    FP8Q_TRY(check_ld(ld_x, k, 1, "ld_x"));
+    FP8Q_TRY(check_ld(ld_q, k, 1, "ld_q"));
+    const size_t need = fp8q_quantize_act_workspace_size(m, k);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(FP8Q_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                    workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+    int dev = 0;
+    FP8Q_TRY(prepare(stream, &dev));
+    if (m > 0) {
+        FP8Q_TRY(check_ptr(x_bf16, "x_bf16", dev, 2));
+        FP8Q_TRY(check_ptr(x_fp8, "x_fp8", dev, 1));
+    }
+    FP8Q_TRY(check_ptr(x_scale, "x_scale", dev, 4));
+    FP8Q_TRY(check_ptr(workspace, "workspace", dev, 16));
+    if (nonfinite_flag != nullptr)
+        FP8Q_TRY(check_ptr(nonfinite_flag, "nonfinite_flag", dev, 4));
+    const size_t ex = extent(m, k, ld_x, 2), eq = extent(m, k, ld_q, 1);
+    if (overlap(x_fp8, eq, x_bf16, ex) || overlap(x_scale, 4, x_bf16, ex) ||
+        overlap(x_scale, 4, x_fp8, eq) || overlap(workspace, need, x_bf16, ex) ||
+        overlap(workspace, need, x_fp8, eq) || overlap(workspace, need, x_scale, 4))
+        return fail(FP8Q_ERR_INVALID_ARG, "outputs, workspace and input overlap");
+    hipError_t e = fp8q::launch::quantize_act(x_bf16, m, k, ld_x, x_fp8, ld_q, x_scale,
+                                              static_cast<uint32_t *>(workspace), nonfinite_flag,
+                                              stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "activation quantization launch");
+    return ok();
+}
+
+size_t fp8q_linear_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k)
+{
+    if (m <= 0 || n <= 0 || k < 1)
+        return 0;
+    if (mode == FP8Q_W8A16)
+        return round_up(fp8q::launch::plan_w8a16(m, n, k).workspace, 256);
+    if (mode == FP8Q_W8A8)
+        return round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
+    return 0;
+}
+
+fp8q_status fp8q_linear(fp8q_mode mode,
+                        const void *x, int64_t m, int64_t k, int64_t ld_x, const float *x_scale,
+                        const uint8_t *w_fp8, int64_t n, int64_t ld_w, const float *w_scale,
+                        uint16_t *y_bf16, int64_t ld_y,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (mode != FP8Q_W8A16 && mode != FP8Q_W8A8)
+        return fail(FP8Q_ERR_INVALID_ARG, "unknown mode %d", (int)mode);
+    if (m < 0 || n < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "need m >= 0, n >= 0, k >= 1 (m=%lld, n=%lld, k=%lld)",
+                    (long long)m, (long long)n, (long long)k);
+    if (mode == FP8Q_W8A16 && x_scale != nullptr)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_bf16_a takes no activation scale (x_scale must be NULL)");
+    if (mode == FP8Q_W8A8 && x_scale == nullptr)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_fp8_a needs the activation scale (x_scale is NULL)");
+    const size_t xelem = mode == FP8Q_W8A16 ? 2 : 1;
+    FP8Q_TRY(check_ld(ld_x, k, mode == FP8Q_W8A16 ? 8 : 16, "ld_x"));
+    FP8Q_TRY(check_ld(ld_w, k, 16, "ld_w"));
+    FP8Q_TRY(check_ld(ld_y, n, 8, "ld_y"));
+    if (m == 0 || n == 0)
+        return ok();
+    const size_t need = fp8q_linear_workspace_size(mode, m, n, k);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(FP8Q_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                    workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+    int dev = 0;
+    FP8Q_TRY(prepare(stream, &dev));
+    FP8Q_TRY(check_ptr(x, "x", dev, 16));
+    FP8Q_TRY(check_ptr(w_fp8, "w_fp8", dev, 16));
+    FP8Q_TRY(check_ptr(w_scale, "w_scale", dev, 4));
+    FP8Q_TRY(check_ptr(y_bf16, "y_bf16", dev, 16));
+    if (x_scale != nullptr)
+        FP8Q_TRY(check_ptr(x_scale, "x_scale", dev, 4));
+    if (need > 0)
+        FP8Q_TRY(check_ptr(workspace, "workspace", dev, 16));
+    const size_t ex = extent(m, k, ld_x, xelem), ew = extent(n, k, ld_w, 1),
+                 ey = extent(m, n, ld_y, 2);
+    if (overlap(y_bf16, ey, x, ex) || overlap(y_bf16, ey, w_fp8, ew) ||
+        overlap(y_bf16, ey, w_scale, (size_t)n * 4) ||
+        (x_scale != nullptr && overlap(y_bf16, ey, x_scale, 4)) ||
+        (need > 0 && (overlap(workspace, need, y_bf16, ey) || overlap(workspace, need, x, ex) ||
+                      overlap(workspace, need, w_fp8, ew))))
+        return fail(FP8Q_ERR_INVALID_ARG, "the output or workspace overlaps an input");
+
+    hipError_t e;
+    if (mode == FP8Q_W8A16) {
+        const auto plan = fp8q::launch::plan_w8a16(m, n, k);
+        e = fp8q::launch::w8a16(plan, static_cast<const uint16_t *>(x), m, k, ld_x, w_fp8, n,
+                                ld_w, w_scale, y_bf16, ld_y, static_cast<float *>(workspace),
+                                stream);
+    } else {
+        const auto plan = fp8q::launch::plan_w8a8(m, n, k);
+        e = fp8q::launch::w8a8(plan, static_cast<const uint8_t *>(x), m, k, ld_x, x_scale, w_fp8,
+                               n, ld_w, w_scale, y_bf16, ld_y, stream);
+    }
+    if (e != hipSuccess)
+        return hip_fail(e, "linear launch");
+    return ok();
+}
+
+fp8q_status fp8q_cast_f32_to_e4m3(const float *x, int64_t count, uint8_t *out, hipStream_t stream)
+{
+    if (count < 0)
+        return fail(FP8Q_ERR_INVALID_ARG, "count < 0");
+    if (count == 0)
+        return ok();
+    int dev = 0;
+    FP8Q_TRY(prepare(stream, &dev));
+    FP8Q_TRY(check_ptr(x, "x", dev, 16));
+    FP8Q_TRY(check_ptr(out, "out", dev, 16));
+    if (overlap(x, (size_t)count * 4, out, (size_t)count))
+        return fail(FP8Q_ERR_INVALID_ARG, "out overlaps x");
+    hipError_t e = fp8q::launch::cast_f32(x, count, out, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "cast launch");
+    return ok();
+}
+
+fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k, char *buf,
+                                 size_t len)
+{
+    if (buf == nullptr || len == 0)
+        return fail(FP8Q_ERR_INVALID_ARG, "buf is NULL or empty");
+    if (m < 0 || n < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "bad sizes");
+    if (mode == FP8Q_W8A16) {
+        const auto p = fp8q::launch::plan_w8a16(m, n, k);
+        std::snprintf(buf, len,
+                      "k_w8a16<af=%d,mb=%d> rows=%d grid=(%lld,%lld) block=%d kchunk=%lld",
+                      p.af, p.mb, p.rows, (long long)p.grid_n, (long long)p.grid_m,
+                      64 * p.waves, (long long)p.kchunk);
+    } else if (mode == FP8Q_W8A8) {
+        const auto p = fp8q::launch::plan_w8a8(m, n, k);
+        std::snprintf(buf, len, "k_w8a8 tile=256x256x64 grid=%lld (%lldx%lld) block=512",
+                      (long long)(p.tiles_m * p.tiles_n), (long long)p.tiles_m,
+                      (long long)p.tiles_n);
+    } else {
+        return fail(FP8Q_ERR_INVALID_ARG, "unknown mode %d", (int)mode);
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// Device helpers shared by the fp8q kernels (gfx950 / CDNA4 only).
+//
+// E4M3 here is the OCP "e4m3fn" encoding the deployment guide
+// ("FP8量化与长上下文实测：Llama 3 70B部署优化指南", §1.1) describes: 4 exponent
+// bits with bias 7, 3 mantissa bits, largest finite value 448, smallest
+// subnormal 2^-9, no infinities.  gfx950 converts to and from this encoding
+// in hardware (v_cvt_pk_fp8_f32, v_cvt_scalef32_pk_bf16_fp8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+namespace dev {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Largest finite E4M3 magnitude (the range is [-448, 448]).
+constexpr float kE4M3Max = 448.0f;
+// Lower clamp of a scale, as an fp32 constant (the fp32 value nearest 1e-12).
+constexpr float kScaleFloor = 1e-12f;
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// |bf16| as an unsigned key: for non-NaN values the order of the keys is the
+// order of the magnitudes; NaN keys sort above +Inf (0x7F80).
+__device__ __forceinline__ uint32_t abs_key_max2(uint32_t pair)
+{
+    uint32_t lo = pair & 0x7FFFu;
+    uint32_t hi = (pair >> 16) & 0x7FFFu;
+    return lo > hi ? lo : hi;
+}
+
+// Scale from an absolute maximum given as a |bf16| key:
+// s = max(fl32(amax / 448), 1e-12f), with an IEEE division.
+__device__ __forceinline__ float scale_from_key(uint32_t key)
+{
+    float amax = __uint_as_float(key << 16);
+    float s = amax / kE4M3Max;
+    return s < kScaleFloor ? kScaleFloor : s;
+}
+
+// Four fp32 values -> four E4M3 codes packed little-endian in a dword.
+// Round to nearest even; |t| >= 448 saturates to +-448 (the clamp runs first
+// because the hardware conversion is not saturating by itself).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
+{
+    a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+    b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+    c = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
+    d = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+    return (uint32_t)v;
+}
+
+// Eight bf16 values (a uint4) divided by s, cast to eight E4M3 codes (a uint2).
+__device__ __forceinline__ uint2 quantize8(uint4 v, float s)
+{
+    uint2 r;
+    r.x = e4m3x4(bf16_lo(v.x) / s, bf16_hi(v.x) / s, bf16_lo(v.y) / s, bf16_hi(v.y) / s);
+    r.y = e4m3x4(bf16_lo(v.z) / s, bf16_hi(v.z) / s, bf16_lo(v.w) / s, bf16_hi(v.w) / s);
+    return r;
+}
+
+// Four E4M3 codes (a dword) -> four bf16 values (two dwords).  Exact: every
+// E4M3 value is representable in bf16.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t codes)
+{
+    v2bf lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)codes, 1.0f, false);
+    v2bf hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)codes, 1.0f, true);
+    uint2 r;
+    r.x = __builtin_bit_cast(uint32_t, lo);
+    r.y = __builtin_bit_cast(uint32_t, hi);
+    return r;
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Wave-wide unsigned max (64 lanes).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t o = __shfl_xor(v, off, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Block-wide unsigned max; every thread gets the result.  `red` is LDS of
+// at least blockDim.x / 64 words.  Contains __syncthreads: call uniformly.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red)
+{
+    v = wave_max_u32(v);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    if (lane == 0)
+        red[wave] = v;
+    __syncthreads();
+    uint32_t r = 0;
+    const int nw = (blockDim.x + kWave - 1) / kWave;
+    for (int i = 0; i < nw; ++i)
+        r = red[i] > r ? red[i] : r;
+    __syncthreads();
+    return r;
+}
+
+}  // namespace dev
+}  // namespace fp8q

@@ -1,0 +1,57 @@
+// Internal launchers of the fp8q kernels (host side).  Each returns the HIP
+// error of its launches; argument validation happens before, in the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+// Upper bound on the blocks of the activation passes (also the number of
+// partial maxima kept in the workspace).
+constexpr int kActMaxBlocks = 1024;
+
+namespace launch {
+
+hipError_t quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                           uint8_t *q, int64_t ld_q, float *scale, int32_t *flag,
+                           hipStream_t stream);
+
+int act_blocks(int64_t m, int64_t k);
+hipError_t quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                        uint8_t *q, int64_t ld_q, float *x_scale, uint32_t *partial,
+                        int32_t *flag, hipStream_t stream);
+
+hipError_t cast_f32(const float *x, int64_t count, uint8_t *out, hipStream_t stream);
+
+// ---- W8A16 (fp8_w_bf16_a) skinny GEMM --------------------------------------
+struct W8A16Plan {
+    int mb;            // 16-column activation groups per block (1..4)
+    int rows;          // weight rows per block (4, 8, 16 or 32)
+    int af;            // 16-row MFMA fragments per wave (1, or 2 when rows == 32)
+    int waves;         // waves per block; they split K
+    int64_t kchunk;    // K range per wave, a multiple of 64
+    int64_t grid_n;    // blocks along N
+    int64_t grid_m;    // blocks along M (16 * mb activation rows each)
+    int64_t splits;    // K splits across blocks (always 1: one launch, no partials)
+    int64_t np;        // unused (no partials)
+    size_t workspace;  // scratch bytes (0)
+};
+W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k);
+hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                 const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
+                 uint16_t *y, int64_t ld_y, float *partial, hipStream_t stream);
+
+// ---- W8A8 (fp8_w_fp8_a) GEMM on FP8 MFMA -----------------------------------
+struct W8A8Plan {
+    int64_t tiles_m, tiles_n;
+    size_t workspace;
+};
+W8A8Plan plan_w8a8(int64_t m, int64_t n, int64_t k);
+hipError_t w8a8(const W8A8Plan &p, const uint8_t *x, int64_t m, int64_t k, int64_t ld_x,
+                const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
+                const float *w_scale, uint16_t *y, int64_t ld_y, hipStream_t stream);
+
+}  // namespace launch
+}  // namespace fp8q

@@ -1,0 +1,346 @@
+// Quantization kernels: per-output-channel weight quantization, dynamic
+// per-tensor activation quantization (two passes) and the bare fp32 -> E4M3
+// cast.  The method is the conversion of the deployment guide
+// ("FP8量化与长上下文实测：Llama 3 70B部署优化指南", §3.1): absmax / 448 with the
+// scale clamped at 1e-12, an fp32 division, and an RNE cast to E4M3 that
+// saturates at +-448; weights get one scale per output row, activations one
+// scale per tensor (§1.2).
+//
+// All three are HBM-bound streaming kernels: bf16 in (2 B/element), codes out
+// (1 B/element).  Loads are 16 B per lane, stores 8 B per lane, fully
+// coalesced; the reductions use wave shuffles and a few words of LDS.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8q {
+namespace {
+
+using namespace dev;
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Weights: one workgroup per output row.  CH > 0: the row is held in
+// registers (at most CH 16-byte chunks per thread) between the absmax and the
+// cast, so every weight byte is read from HBM once.  CH == 0: rows longer
+// than 16 * 256 * 8 elements are streamed twice (the second pass mostly hits
+// in L2 / Infinity Cache).
+// ---------------------------------------------------------------------------
+template <int CH>
+__global__ __launch_bounds__(kThreads) void k_quant_weight(
+    const uint16_t *__restrict__ w, int64_t k, int64_t ld_w,
+    uint8_t *__restrict__ q, int64_t ld_q, float *__restrict__ scale,
+    int32_t *__restrict__ flag)
+{
+    __shared__ uint32_t red[kThreads / kWave];
+    const int64_t row = blockIdx.x;
+    const uint16_t *wr = w + row * ld_w;
+    uint8_t *qr = q + row * ld_q;
+    const int64_t nfull = k >> 3;          // full 8-element (16-byte) chunks
+    const int tail = (int)(k & 7);
+    const int tid = threadIdx.x;
+
+    uint32_t key = 0;
+    uint4 buf[CH > 0 ? CH : 1];
+    if constexpr (CH > 0) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int64_t idx = tid + (int64_t)c * kThreads;
+            if (idx < nfull) {
+                buf[c] = *reinterpret_cast<const uint4 *>(wr + idx * 8);
+                uint32_t m01 = max(abs_key_max2(buf[c].x), abs_key_max2(buf[c].y));
+                uint32_t m23 = max(abs_key_max2(buf[c].z), abs_key_max2(buf[c].w));
+                key = max(key, max(m01, m23));
+            }
+        }
+    } else {
+        for (int64_t idx = tid; idx < nfull; idx += kThreads) {
+            uint4 v = *reinterpret_cast<const uint4 *>(wr + idx * 8);
+            key = max(key, max(max(abs_key_max2(v.x), abs_key_max2(v.y)),
+                               max(abs_key_max2(v.z), abs_key_max2(v.w))));
+        }
+    }
+    if (tid < tail)
+        key = max(key, (uint32_t)(wr[nfull * 8 + tid] & 0x7FFFu));
+
+    key = block_max_u32(key, red);
+    const float s = scale_from_key(key);
+    if (tid == 0) {
+        scale[row] = s;
+        if (flag != nullptr && key >= 0x7F80u)
+            *flag = 1;
+    }
+
+    if constexpr (CH > 0) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int64_t idx = tid + (int64_t)c * kThreads;
+            if (idx < nfull)
+                *reinterpret_cast<uint2 *>(qr + idx * 8) = quantize8(buf[c], s);
+        }
+    } else {
+        for (int64_t idx = tid; idx < nfull; idx += kThreads) {
+            uint4 v = *reinterpret_cast<const uint4 *>(wr + idx * 8);
+            *reinterpret_cast<uint2 *>(qr + idx * 8) = quantize8(v, s);
+        }
+    }
+    if (tid < tail) {
+        const float t = __uint_as_float((uint32_t)wr[nfull * 8 + tid] << 16) / s;
+        qr[nfull * 8 + tid] = (uint8_t)(e4m3x4(t, 0.f, 0.f, 0.f) & 0xFFu);
+    }
+}
+
+// Rows that are not 16-byte aligned (a leading dimension that is not a
+// multiple of 8, or an offset pointer): the same computation element by
+// element, reading the row twice.
+__global__ __launch_bounds__(kThreads) void k_quant_weight_scalar(
+    const uint16_t *__restrict__ w, int64_t k, int64_t ld_w,
+    uint8_t *__restrict__ q, int64_t ld_q, float *__restrict__ scale,
+    int32_t *__restrict__ flag)
+{
+    __shared__ uint32_t red[kThreads / kWave];
+    const int64_t row = blockIdx.x;
+    const uint16_t *wr = w + row * ld_w;
+    uint8_t *qr = q + row * ld_q;
+    uint32_t key = 0;
+    for (int64_t e = threadIdx.x; e < k; e += kThreads)
+        key = max(key, (uint32_t)(wr[e] & 0x7FFFu));
+    key = block_max_u32(key, red);
+    const float s = scale_from_key(key);
+    if (threadIdx.x == 0) {
+        scale[row] = s;
+        if (flag != nullptr && key >= 0x7F80u)
+            *flag = 1;
+    }
+    for (int64_t e = threadIdx.x; e < k; e += kThreads) {
+        const float t = __uint_as_float((uint32_t)wr[e] << 16) / s;
+        qr[e] = (uint8_t)(e4m3x4(t, 0.f, 0.f, 0.f) & 0xFFu);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Activations, pass 1: each workgroup writes the |x| key maximum of its share
+// of the tensor to partial[blockIdx.x].  No atomics, no initialisation.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t key_max8(uint4 v)
+{
+    return max(max(abs_key_max2(v.x), abs_key_max2(v.y)), max(abs_key_max2(v.z), abs_key_max2(v.w)));
+}
+
+// Layouts of an activation tensor, from fastest to most general.
+enum ActLayout : int {
+    kFlat = 0,      // ld == k, k % 8 == 0, 16-byte aligned: one stream of 16-byte chunks
+    kRows = 1,      // rows 16-byte aligned: 16-byte chunks per row, element tail
+    kScalar = 2     // anything else: element by element
+};
+
+__global__ __launch_bounds__(kThreads) void k_act_amax(
+    const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
+    uint32_t *__restrict__ partial, int layout)
+{
+    __shared__ uint32_t red[kThreads / kWave];
+    uint32_t key = 0;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (layout == kScalar) {
+        const int64_t total = m * k;
+        for (; i < total; i += stride) {
+            const int64_t row = i / k;
+            key = max(key, (uint32_t)(x[row * ld_x + (i - row * k)] & 0x7FFFu));
+        }
+    } else if (layout == kFlat) {
+        // contiguous tensor: a flat stream of 16-byte chunks, 4 in flight per thread
+        const uint4 *p = reinterpret_cast<const uint4 *>(x);
+        const int64_t total = m * (k >> 3);
+        for (; i + 3 * stride < total; i += 4 * stride) {
+            uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+            key = max(key, max(max(key_max8(a), key_max8(b)), max(key_max8(c), key_max8(d))));
+        }
+        for (; i < total; i += stride)
+            key = max(key, key_max8(p[i]));
+    } else {
+        const int64_t cpr = (k + 7) >> 3;          // chunks per row, last one may be partial
+        const int64_t total = m * cpr;
+        for (; i < total; i += stride) {
+            const int64_t row = i / cpr;
+            const int64_t j = (i - row * cpr) * 8;
+            const uint16_t *p = x + row * ld_x + j;
+            if (j + 8 <= k) {
+                key = max(key, key_max8(*reinterpret_cast<const uint4 *>(p)));
+            } else {
+                for (int64_t e = 0; e < k - j; ++e)
+                    key = max(key, (uint32_t)(p[e] & 0x7FFFu));
+            }
+        }
+    }
+    key = block_max_u32(key, red);
+    if (threadIdx.x == 0)
+        partial[blockIdx.x] = key;
+}
+
+// ---------------------------------------------------------------------------
+// Activations, pass 2: every workgroup folds the partial maxima (a few KB,
+// L2-resident) into the tensor's scale, then casts its share.  Workgroup 0
+// publishes the scale and the non-finite flag.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_act_cast(
+    const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
+    uint8_t *__restrict__ q, int64_t ld_q,
+    const uint32_t *__restrict__ partial, int npart,
+    float *__restrict__ x_scale, int32_t *__restrict__ flag, int layout)
+{
+    __shared__ uint32_t red[kThreads / kWave];
+    uint32_t key = 0;
+    for (int j = threadIdx.x; j < npart; j += kThreads)
+        key = max(key, partial[j]);
+    key = block_max_u32(key, red);
+    const float s = scale_from_key(key);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *x_scale = s;
+        if (flag != nullptr && key >= 0x7F80u)
+            *flag = 1;
+    }
+
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (layout == kScalar) {
+        const int64_t total = m * k;
+        for (; i < total; i += stride) {
+            const int64_t row = i / k;
+            const int64_t c = i - row * k;
+            const float t = __uint_as_float((uint32_t)x[row * ld_x + c] << 16) / s;
+            q[row * ld_q + c] = (uint8_t)(e4m3x4(t, 0.f, 0.f, 0.f) & 0xFFu);
+        }
+    } else if (layout == kFlat) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(x);
+        uint2 *o = reinterpret_cast<uint2 *>(q);
+        const int64_t total = m * (k >> 3);
+        for (; i + 3 * stride < total; i += 4 * stride) {
+            uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+            o[i] = quantize8(a, s);
+            o[i + stride] = quantize8(b, s);
+            o[i + 2 * stride] = quantize8(c, s);
+            o[i + 3 * stride] = quantize8(d, s);
+        }
+        for (; i < total; i += stride)
+            o[i] = quantize8(p[i], s);
+    } else {
+        const int64_t cpr = (k + 7) >> 3;
+        const int64_t total = m * cpr;
+        for (; i < total; i += stride) {
+            const int64_t row = i / cpr;
+            const int64_t j = (i - row * cpr) * 8;
+            const uint16_t *p = x + row * ld_x + j;
+            uint8_t *o = q + row * ld_q + j;
+            if (j + 8 <= k) {
+                *reinterpret_cast<uint2 *>(o) = quantize8(*reinterpret_cast<const uint4 *>(p), s);
+            } else {
+                for (int64_t e = 0; e < k - j; ++e) {
+                    const float t = __uint_as_float((uint32_t)p[e] << 16) / s;
+                    o[e] = (uint8_t)(e4m3x4(t, 0.f, 0.f, 0.f) & 0xFFu);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Bare cast: fp32 -> E4M3 codes, four per lane per step.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_cast_f32(
+    const float *__restrict__ x, int64_t count, uint8_t *__restrict__ out)
+{
+    const int64_t n4 = count >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const float4 *p = reinterpret_cast<const float4 *>(x);
+    uint32_t *o = reinterpret_cast<uint32_t *>(out);
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+        float4 v = p[i];
+        o[i] = e4m3x4(v.x, v.y, v.z, v.w);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (count & 3)) {
+        const int64_t e = n4 * 4 + threadIdx.x;
+        out[e] = (uint8_t)(e4m3x4(x[e], 0.f, 0.f, 0.f) & 0xFFu);
+    }
+}
+
+int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers (host).
+// ---------------------------------------------------------------------------
+namespace launch {
+
+static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipError_t quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                           uint8_t *q, int64_t ld_q, float *scale, int32_t *flag,
+                           hipStream_t stream)
+{
+    if (n == 0)
+        return hipSuccess;
+    const int64_t per_thread = div_up(k >> 3, kThreads);
+    const dim3 grid((unsigned)n), block(kThreads);
+    const bool vec = aligned(w, 16) && ld_w % 8 == 0 && aligned(q, 8) && ld_q % 8 == 0;
+    if (!vec)
+        hipLaunchKernelGGL(k_quant_weight_scalar, grid, block, 0, stream, w, k, ld_w, q, ld_q, scale, flag);
+    else if (per_thread <= 1)
+        hipLaunchKernelGGL(k_quant_weight<1>, grid, block, 0, stream, w, k, ld_w, q, ld_q, scale, flag);
+    else if (per_thread <= 2)
+        hipLaunchKernelGGL(k_quant_weight<2>, grid, block, 0, stream, w, k, ld_w, q, ld_q, scale, flag);
+    else if (per_thread <= 4)
+        hipLaunchKernelGGL(k_quant_weight<4>, grid, block, 0, stream, w, k, ld_w, q, ld_q, scale, flag);
+    else if (per_thread <= 8)
+        hipLaunchKernelGGL(k_quant_weight<8>, grid, block, 0, stream, w, k, ld_w, q, ld_q, scale, flag);
+    else if (per_thread <= 16)
+        hipLaunchKernelGGL(k_quant_weight<16>, grid, block, 0, stream, w, k, ld_w, q, ld_q, scale, flag);
+    else
+        hipLaunchKernelGGL(k_quant_weight<0>, grid, block, 0, stream, w, k, ld_w, q, ld_q, scale, flag);
+    return hipGetLastError();
+}
+
+int act_blocks(int64_t m, int64_t k)
+{
+    const int64_t chunks = m * div_up(k, 8);
+    int64_t g = div_up(chunks, (int64_t)kThreads * 8);
+    if (g < 1)
+        g = 1;
+    if (g > kActMaxBlocks)
+        g = kActMaxBlocks;
+    return (int)g;
+}
+
+hipError_t quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                        uint8_t *q, int64_t ld_q, float *x_scale, uint32_t *partial,
+                        int32_t *flag, hipStream_t stream)
+{
+    const int g = act_blocks(m, k);
+    const bool rows_ok = aligned(x, 16) && ld_x % 8 == 0 && aligned(q, 8) && ld_q % 8 == 0;
+    const int layout = !rows_ok ? kScalar : (ld_x == k && ld_q == k && k % 8 == 0) ? kFlat : kRows;
+    hipLaunchKernelGGL(k_act_amax, dim3(g), dim3(kThreads), 0, stream, x, m, k, ld_x, partial,
+                       layout);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_act_cast, dim3(g), dim3(kThreads), 0, stream, x, m, k, ld_x, q, ld_q,
+                       (const uint32_t *)partial, g, x_scale, flag, layout);
+    return hipGetLastError();
+}
+
+hipError_t cast_f32(const float *x, int64_t count, uint8_t *out, hipStream_t stream)
+{
+    if (count == 0)
+        return hipSuccess;
+    int64_t g = div_up(div_up(count, 4), (int64_t)kThreads * 4);
+    if (g < 1)
+        g = 1;
+    if (g > 4096)
+        g = 4096;
+    hipLaunchKernelGGL(k_cast_f32, dim3((unsigned)g), dim3(kThreads), 0, stream, x, count, out);
+    return hipGetLastError();
+}
+
+}  // namespace launch
+}  // namespace fp8q

@@ -1,0 +1,168 @@
+/*
+ * fp8q -- FP8 (E4M3) weight-quantized linear layers on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Every pointer argument is a DEVICE
+ * pointer on the device that owns `stream` unless the comment says otherwise;
+ * every call only enqueues work on `stream` and returns.  The library never
+ * allocates, frees or synchronizes device memory: the caller owns every
+ * buffer, including the scratch workspaces whose sizes the *_workspace_size
+ * queries return.
+ *
+ * Layouts are row-major with a contiguous last dimension and a leading
+ * dimension (row stride, in elements) `ld_*`.  A weight has the [out, in]
+ * layout of a linear layer: row n holds output channel n.  The linear layer
+ * computes Y = X . W^T.
+ *
+ * Sources (web pages on FP8 quantization of Llama 3):
+ *   "FP8量化与长上下文实测：Llama 3 70B部署优化指南" (called "the deployment
+ *   guide" below) §1.1 gives the E4M3 format, §1.2 the granularity (weights
+ *   per channel, activations per tensor) and §3.1 the conversion recipe;
+ *   "Llama 3 精读" FP8 + 128K write-up (called "the write-up") §3.1 step 3
+ *   names the FP8 MatMul modes.
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued;
+ * on any error nothing is launched and a status other than FP8Q_OK is
+ * returned.  fp8q_last_error() gives a thread-local description of the most
+ * recent error.  NaN or infinite inputs are outside the method's domain: they
+ * are reported through an optional device flag (set to 1, never cleared by
+ * the library), and the codes they produce are unspecified.
+ *
+ * Threading.  Calls are thread-safe; the only shared state is a per-device
+ * cache of device properties.  Two calls that share a workspace must be
+ * ordered on one stream.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_ABI_VERSION 1
+
+typedef enum {
+    FP8Q_OK = 0,
+    FP8Q_ERR_INVALID_ARG = 1,   /* null pointer, bad size/stride/alignment, host pointer,
+                                   aliasing, wrong mode/scale combination */
+    FP8Q_ERR_UNSUPPORTED = 2,   /* the stream's device is not a gfx950 GPU */
+    FP8Q_ERR_HIP = 3,           /* a HIP runtime call or a kernel launch failed */
+    FP8Q_ERR_WORKSPACE = 4      /* workspace missing or smaller than the query returned */
+} fp8q_status;
+
+/* The FP8 MatMul modes of the write-up (§3.1 step 3). */
+typedef enum {
+    FP8Q_W8A16 = 0,             /* "fp8_w_bf16_a": E4M3 weight, bf16 activation (decode) */
+    FP8Q_W8A8 = 1               /* "fp8_w_fp8_a":  E4M3 weight and activation (prefill)  */
+} fp8q_mode;
+
+/* FP8Q_ABI_VERSION of the built library. */
+int fp8q_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *fp8q_status_string(fp8q_status s);
+
+/* Thread-local description of the last non-OK status returned on this thread
+ * (an empty string if there was none).  Valid until the next call on the
+ * same thread. */
+const char *fp8q_last_error(void);
+
+/*
+ * Per-output-channel weight quantization (deployment guide §3.1, §1.2).
+ *
+ * For each row n of W (bf16 bit patterns, [n, k], row stride ld_w):
+ *   amax      = max_k |W[n,k]|
+ *   s         = max(fl32(amax / 448), 1e-12f)                 -> w_scale[n]  (fp32)
+ *   w_fp8[n,k] = E4M3_RNE_saturating(fl32(W[n,k] / s))        (IEEE fp32 division,
+ *                                                              then one RNE cast)
+ * E4M3 is the OCP "e4m3fn" format of §1.1 (bias 7, max 448, no infinities);
+ * the codes are raw bit patterns (viewable as torch.float8_e4m3fn).
+ *
+ *   w_bf16  [n, k] bf16, ld_w >= k
+ *   w_fp8   [n, k] uint8 out, ld_q >= k
+ *   (rows that are 16-byte aligned -- aligned pointers, ld_w % 8 == 0 and
+ *   ld_q % 8 == 0 -- take the vectorized path; any other layout is handled
+ *   element by element)
+ *   w_scale [n] fp32 out
+ *   nonfinite_flag  optional int32 (may be NULL): set to 1 if any input is NaN/Inf
+ * n == 0 is a no-op; k must be >= 1.  Results are bit-exact and deterministic.
+ */
+fp8q_status fp8q_quantize_weight(const uint16_t *w_bf16, int64_t n, int64_t k, int64_t ld_w,
+                                 uint8_t *w_fp8, int64_t ld_q, float *w_scale,
+                                 int32_t *nonfinite_flag, hipStream_t stream);
+
+/*
+ * Dynamic per-tensor activation quantization (deployment guide §1.2: one scale
+ * for the whole activation tensor; the scale formula is the one of §3.1,
+ * recomputed on every call).
+ *   amax = max_{m,k} |X[m,k]|,  s = max(fl32(amax / 448), 1e-12f) -> *x_scale
+ *   x_fp8[m,k] = E4M3_RNE_saturating(fl32(X[m,k] / s))
+ *
+ *   x_bf16  [m, k] bf16, ld_x >= k
+ *   x_fp8   [m, k] uint8 out, ld_q >= k
+ *   (16-byte aligned rows take the vectorized path, as for the weights)
+ *   x_scale one fp32 out (device)
+ *   workspace  device scratch of at least fp8q_quantize_act_workspace_size(m, k)
+ *              bytes, 16-byte aligned; its contents need no initialisation
+ *   nonfinite_flag  optional, as above
+ * Two kernels run on `stream` (a global absmax, then the cast).  m == 0 writes
+ * the scale of an empty tensor (1e-12f); k must be >= 1.  Bit-exact.
+ */
+size_t fp8q_quantize_act_workspace_size(int64_t m, int64_t k);
+fp8q_status fp8q_quantize_act(const uint16_t *x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                              uint8_t *x_fp8, int64_t ld_q, float *x_scale,
+                              void *workspace, size_t workspace_bytes,
+                              int32_t *nonfinite_flag, hipStream_t stream);
+
+/*
+ * The scaled linear layer, Y = X . dequant(W)^T, in the write-up's modes
+ * (§3.1 step 3), with the per-channel weight scale and per-tensor activation
+ * scale of the deployment guide §1.2:
+ *   FP8Q_W8A16: Y[m,n] = bf16_RNE( w_scale[n] * sum_k X[m,k] * dec(W[n,k]) )
+ *               x = bf16 [m, k] (ld_x % 8 == 0); x_scale must be NULL.
+ *   FP8Q_W8A8:  Y[m,n] = bf16_RNE( x_scale * w_scale[n] * sum_k dec(X[m,k]) * dec(W[n,k]) )
+ *               x = E4M3 codes [m, k] (ld_x % 16 == 0); x_scale = device fp32[1].
+ * Products are exact and sums are accumulated in fp32; the result is within
+ * 5e-3 relative Frobenius error of the exact value (see the tests).
+ *
+ *   w_fp8   [n, k] E4M3 codes, ld_w >= k, ld_w % 16 == 0, 16-byte aligned
+ *   w_scale [n] fp32
+ *   y_bf16  [m, n] bf16 out, ld_y >= n, ld_y % 8 == 0, 16-byte aligned; must not
+ *           overlap any input
+ *   workspace  device scratch of at least fp8q_linear_workspace_size(mode, m, n, k)
+ *              bytes (may be 0, then workspace may be NULL); needs no initialisation
+ * m == 0 or n == 0 is a no-op; k must be >= 1.  Deterministic: the same inputs
+ * give the same bits on every call.
+ */
+size_t fp8q_linear_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k);
+fp8q_status fp8q_linear(fp8q_mode mode,
+                        const void *x, int64_t m, int64_t k, int64_t ld_x, const float *x_scale,
+                        const uint8_t *w_fp8, int64_t n, int64_t ld_w, const float *w_scale,
+                        uint16_t *y_bf16, int64_t ld_y,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The element cast used by both quantizers, exposed on its own: fp32 -> E4M3
+ * code, round to nearest even, saturating to +-448 (deployment guide §1.1,
+ * §3.1; the write-up §2.1 gives the [-448, 448] range).  The sign of zero is
+ * kept.  NaN input gives an unspecified code.
+ *   x   [count] fp32, 16-byte aligned;  out [count] uint8, 16-byte aligned.
+ */
+fp8q_status fp8q_cast_f32_to_e4m3(const float *x, int64_t count, uint8_t *out, hipStream_t stream);
+
+/*
+ * Describe the kernel configuration fp8q_linear would launch for these sizes
+ * (kernel name, grid, split factor) into buf (host memory, NUL-terminated,
+ * truncated to len).  Host-only; launches nothing.
+ */
+fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
+                                 char *buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

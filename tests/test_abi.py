@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fp8q.h declares, and rejects invalid arguments on the host before
+anything touches a device (the checks that come first in each entry point).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fp8_weight_quantized_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from fp8_weight_quantized_amd import build
+        build.build(verbose=False)
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8q_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    from fp8_weight_quantized_amd import _lib
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures must mirror the header"
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_strings(L):
+    assert L.fp8q_abi_version() == 1
+    for s in range(5):
+        assert L.fp8q_status_string(s).startswith(b"FP8Q")
+    assert L.fp8q_status_string(99) == b"FP8Q: unknown status"
+
+
+def test_workspace_queries(L):
+    # activation pass-1 partials: one word per block, rounded to 256 bytes
+    assert L.fp8q_quantize_act_workspace_size(8192, 4096) == 4096
+    assert L.fp8q_quantize_act_workspace_size(1, 8) == 256
+    assert L.fp8q_quantize_act_workspace_size(0, 8) == 256
+    assert L.fp8q_quantize_act_workspace_size(4, 0) == 0
+    # both linear modes run as one launch without scratch
+    assert L.fp8q_linear_workspace_size(1, 8192, 28672, 4096) == 0
+    assert L.fp8q_linear_workspace_size(0, 1, 4096, 4096) == 0
+    assert L.fp8q_linear_workspace_size(0, 12, 28672, 8192) == 0
+    assert L.fp8q_linear_workspace_size(0, 0, 4096, 4096) == 0
+
+
+def test_describe(L):
+    buf = ctypes.create_string_buffer(256)
+    assert L.fp8q_linear_describe(0, 1, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16")
+    assert L.fp8q_linear_describe(1, 8192, 28672, 4096, buf, 256) == 0
+    assert b"32x112" in buf.value
+    assert L.fp8q_linear_describe(7, 1, 1, 1, buf, 256) == 1
+
+
+NULL = None
+
+
+def test_linear_host_validation(L):
+    # (mode, m, k, ld_x, x_scale, n, ld_w, ld_y, ws_bytes) -> expected status
+    fake = ctypes.c_void_p(0x1000)
+    cases = [
+        ((5, 1, 64, 64, NULL, 16, 64, 16), 1),          # unknown mode
+        ((0, 1, 0, 64, NULL, 16, 64, 16), 1),           # k < 1
+        ((0, -1, 64, 64, NULL, 16, 64, 16), 1),         # m < 0
+        ((0, 1, 64, 32, NULL, 16, 64, 16), 1),          # ld_x < k
+        ((0, 1, 64, 68, NULL, 16, 64, 16), 1),          # ld_x not a multiple of 8 (bf16)
+        ((1, 1, 64, 72, fake, 16, 64, 16), 1),          # ld_x not a multiple of 16 (fp8)
+        ((0, 1, 64, 64, NULL, 16, 72, 16), 1),          # ld_w not a multiple of 16
+        ((0, 1, 64, 64, NULL, 16, 64, 12), 1),          # ld_y not a multiple of 8
+        ((0, 1, 64, 64, fake, 16, 64, 16), 1),          # x_scale given in W8A16
+        ((1, 1, 64, 64, NULL, 16, 64, 16), 1),          # x_scale missing in W8A8
+        ((0, 0, 64, 64, NULL, 16, 64, 16), 0),          # empty M: no-op
+        ((1, 4, 64, 64, fake, 0, 64, 16), 0),           # empty N: no-op
+    ]
+    for (mode, m, k, ldx, xs, n, ldw, ldy), want in cases:
+        got = L.fp8q_linear(mode, NULL, m, k, ldx, xs, NULL, n, ldw, NULL, NULL, ldy, NULL, 0, NULL)
+        assert got == want, ((mode, m, k, ldx, n, ldw, ldy), got, L.fp8q_last_error())
+        if want:
+            assert L.fp8q_last_error()
+
+
+def test_quantize_host_validation(L):
+    assert L.fp8q_quantize_weight(NULL, 4, 0, 8, NULL, 8, NULL, NULL, NULL) == 1
+    assert L.fp8q_quantize_weight(NULL, 4, 8, 4, NULL, 8, NULL, NULL, NULL) == 1
+    assert L.fp8q_quantize_weight(NULL, 0, 8, 8, NULL, 8, NULL, NULL, NULL) == 0
+    assert L.fp8q_quantize_act(NULL, 4, 8, 8, NULL, 8, NULL, NULL, 0, NULL, NULL) == 4
+    assert L.fp8q_quantize_act(NULL, 4, 8, 8, NULL, 8, NULL, ctypes.c_void_p(0x1000), 8, NULL, NULL) == 4
+    assert L.fp8q_quantize_act(NULL, -1, 8, 8, NULL, 8, NULL, NULL, 0, NULL, NULL) == 1
+    assert L.fp8q_cast_f32_to_e4m3(NULL, -1, NULL, NULL) == 1
+    assert L.fp8q_cast_f32_to_e4m3(NULL, 0, NULL, NULL) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from fp8_weight_quantized_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

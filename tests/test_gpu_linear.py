@@ -1,0 +1,233 @@
+"""GPU parity of the scaled linear layer against the fp64 oracle.
+
+Both FP8 MatMul modes of Llama 3 精读 §3.1 step 3 -- fp8_w_bf16_a (W8A16,
+decode) and fp8_w_fp8_a (W8A8, prefill) -- are checked with the same codes
+and scales on both sides (the codes come from the oracle, so this file tests
+the GEMM alone), to rel. Frobenius <= 5e-3 and per-element <= 1e-2 max|ref|.
+Exact cases (one-hot activations) pin every E4M3 code's decode and the MFMA
+lane layouts bit for bit.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from helpers import assert_gemm_close, dev_bf16, dev_u8, host_bf16_as_f64, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fq():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import fp8_weight_quantized_amd as fq
+    fq.library_path()
+    return fq
+
+
+def pad16(a: np.ndarray):
+    """Upload codes with a 16-byte-multiple row stride (what the GEMM requires)."""
+    rows, cols = a.shape
+    ld = (cols + 15) // 16 * 16
+    t = torch.zeros((rows, ld), dtype=torch.uint8, device="cuda")
+    t[:, :cols] = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return t[:, :cols]
+
+
+def pad8_bf16(bits: np.ndarray):
+    rows, cols = bits.shape
+    ld = (cols + 7) // 8 * 8
+    t = torch.zeros((rows, ld), dtype=torch.bfloat16, device="cuda")
+    t[:, :cols] = dev_bf16(bits)
+    return t[:, :cols]
+
+
+def run_w8a16(fq, x_bits, wq, ws):
+    y = fq.linear(pad8_bf16(x_bits), pad16(wq), torch.from_numpy(ws).cuda())
+    torch.cuda.synchronize()
+    return host_bf16_as_f64(y)
+
+
+def run_w8a8(fq, xq, xs, wq, ws):
+    y = fq.linear(pad16(xq), pad16(wq), torch.from_numpy(ws).cuda(),
+                  x_scale=torch.tensor([xs], dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    return host_bf16_as_f64(y)
+
+
+def all_codes_weight(n: int, k: int) -> np.ndarray:
+    w = ((np.arange(n)[:, None] + np.arange(k)[None, :]) % 256).astype(np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x00           # no NaN codes
+    return w
+
+
+@pytest.mark.parametrize("m,n", [(16, 256), (1, 256), (64, 272), (12, 256)])
+def test_w8a16_exact_every_code(fq, orc, m, n):
+    """X = identity rows: Y[i, j] = dec(W[j, i]) exactly, for all 254 finite codes."""
+    k = 64
+    wq = all_codes_weight(n, k)
+    x = np.zeros((m, k), np.uint16)
+    x[np.arange(m), np.arange(m) % k] = 0x3F80          # 1.0
+    ws = np.ones(n, np.float32)
+    say("w8a16 exact", m, n, k)
+    y = run_w8a16(fq, x, wq, ws)
+    ref = orc.linear(0, x, wq, ws)
+    assert (y == ref).all(), np.argwhere(y != ref)[:5]
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 256, 64), (300, 260, 128), (33, 512, 64)])
+def test_w8a8_exact_every_code(fq, orc, m, n, k):
+    wq = all_codes_weight(n, k)
+    xq = np.zeros((m, k), np.uint8)
+    xq[np.arange(m), np.arange(m) % k] = 0x38          # 1.0
+    ws = np.ones(n, np.float32)
+    say("w8a8 exact", m, n, k)
+    y = run_w8a8(fq, xq, 1.0, wq, ws)
+    ref = orc.linear(1, xq, wq, ws, np.float32(1.0))
+    assert (y == ref).all(), np.argwhere(y != ref)[:5]
+
+
+def test_tiny(fq, orc):
+    wl = workloads.WORKLOADS["tiny"]
+    lin = wl.linears[0]
+    w = workloads.weight(wl, lin)
+    x = workloads.activation(wl, 16, lin.k)
+    wq, ws, _ = orc.quantize_weight(w)
+    say("tiny w8a16")
+    y = run_w8a16(fq, x, wq, ws)
+    assert_gemm_close(y, orc.linear(0, x, wq, ws), "tiny")
+
+
+RAGGED = [(3, 100, 1000), (17, 130, 520), (65, 64, 64), (100, 96, 4104), (1, 16, 8),
+          (5, 1, 40), (2, 4096, 4096), (64, 1024, 8192), (33, 77, 13), (129, 200, 96)]
+
+
+@pytest.mark.parametrize("m,n,k", RAGGED)
+def test_w8a16_ragged(fq, orc, m, n, k):
+    w = workloads.heavy_tail_weight(n, k, m + n)
+    x = workloads.normal_act(m, k, k)
+    wq, ws, _ = orc.quantize_weight(w)
+    say("w8a16 ragged", m, n, k, fq.describe_linear(0, m, n, k))
+    y = run_w8a16(fq, x, wq, ws)
+    assert_gemm_close(y, orc.linear(0, x, wq, ws), f"w8a16 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", RAGGED + [(300, 520, 1000), (256, 256, 4096), (513, 257, 200)])
+def test_w8a8_ragged(fq, orc, m, n, k):
+    w = workloads.heavy_tail_weight(n, k, m + n)
+    x = workloads.outlier_act(m, k, k)
+    wq, ws, _ = orc.quantize_weight(w)
+    xq, xs, _ = orc.quantize_act(x)
+    say("w8a8 ragged", m, n, k, fq.describe_linear(1, m, n, k))
+    y = run_w8a8(fq, xq, xs, wq, ws)
+    assert_gemm_close(y, orc.linear(1, xq, wq, ws, xs), f"w8a8 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m", [1, 8, 32, 64])
+def test_q_proj_decode_full(fq, orc, m):
+    wl = workloads.WORKLOADS["q_proj_decode"]
+    lin = wl.linears[0]
+    wq, ws, _ = orc.quantize_weight(workloads.weight(wl, lin))
+    x = workloads.activation(wl, m, lin.k)
+    say("q_proj decode", m, fq.describe_linear(0, m, lin.n, lin.k))
+    y = run_w8a16(fq, x, wq, ws)
+    assert_gemm_close(y, orc.linear(0, x, wq, ws), f"q_proj M={m}")
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_layer_decode_70b_full(fq, orc, idx):
+    wl = workloads.WORKLOADS["layer_decode_70b"]
+    lin = wl.linears[idx]
+    wq, ws, _ = orc.quantize_weight(workloads.weight(wl, lin))
+    x = workloads.activation(wl, 12, lin.k)
+    say("70b layer decode", lin.name, fq.describe_linear(0, 12, lin.n, lin.k))
+    y = run_w8a16(fq, x, wq, ws)
+    assert_gemm_close(y, orc.linear(0, x, wq, ws), lin.name)
+
+
+@pytest.mark.parametrize("key", ["mlp_prefill", "down_prefill_70b"])
+def test_prefill_full_size_sampled(fq, orc, key):
+    """Full-size W8A8 GEMM as the benchmark launches it; 24 seeded rows x all N
+    columns compared with the fp64 oracle."""
+    wl = workloads.WORKLOADS[key]
+    lin = wl.linears[0]
+    m = wl.ms[0]
+    wq, ws, _ = orc.quantize_weight(workloads.weight(wl, lin))
+    xq, xs, _ = orc.quantize_act(workloads.activation(wl, m, lin.k))
+    say("prefill", key, fq.describe_linear(1, m, lin.n, lin.k))
+    y = fq.linear(pad16(xq), pad16(wq), torch.from_numpy(ws).cuda(),
+                  x_scale=torch.tensor([xs], dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(7).choice(m, 24, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, m - 1]]))
+    ysel = host_bf16_as_f64(y[torch.from_numpy(rows).cuda()])
+    ref = orc.linear(1, xq, wq, ws, xs, rows=rows)
+    assert_gemm_close(ysel, ref, key)
+
+
+def test_pipeline_w8a8_from_gpu_quantizers(fq, orc):
+    """quantize_weight + quantize_act + linear, all on the GPU, against the oracle."""
+    m, n, k = 384, 512, 1024
+    w = workloads.heavy_tail_weight(n, k, 11)
+    x = workloads.swiglu_act(m, k, 12)
+    say("pipeline w8a8")
+    wq, ws = fq.quantize_weight(dev_bf16(w))
+    xq, xs = fq.quantize_act(dev_bf16(x))
+    y = host_bf16_as_f64(fq.linear(xq, wq, ws, x_scale=xs))
+    owq, ows, _ = orc.quantize_weight(w)
+    oxq, oxs, _ = orc.quantize_act(x)
+    assert_gemm_close(y, orc.linear(1, oxq, owq, ows, oxs), "pipeline")
+
+
+def test_deterministic(fq, orc):
+    w = workloads.heavy_tail_weight(1024, 8192, 3)
+    wq, ws = fq.quantize_weight(dev_bf16(w))
+    x = dev_bf16(workloads.normal_act(12, 8192, 4))
+    say("determinism w8a16 split-K")
+    y1 = fq.linear(x, wq, ws)
+    y2 = fq.linear(x, wq, ws)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    xq, xs = fq.quantize_act(dev_bf16(workloads.normal_act(512, 8192, 5)))
+    say("determinism w8a8")
+    z1 = fq.linear(xq, wq, ws, x_scale=xs)
+    z2 = fq.linear(xq, wq, ws, x_scale=xs)
+    assert torch.equal(z1.view(torch.int16), z2.view(torch.int16))
+
+
+def test_host_pointer_and_device_checks(fq):
+    """Boundary errors the library turns into statuses before launching."""
+    from fp8_weight_quantized_amd import _lib
+    L = _lib.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    host = torch.zeros((16, 64), dtype=torch.uint8).pin_memory()
+    dev_w = torch.zeros((16, 64), dtype=torch.uint8, device="cuda")
+    ws = torch.ones(16, dtype=torch.float32, device="cuda")
+    y = torch.empty((4, 16), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    # pinned host memory passed where device memory is required
+    st = L.fp8q_linear(0, x.data_ptr(), 4, 64, 64, None, host.data_ptr(), 16, 64,
+                       ws.data_ptr(), y.data_ptr(), 16, None, 0, stream)
+    assert st == 1, L.fp8q_last_error()
+    # plain host (pageable) memory
+    buf = np.zeros(4096, np.uint8)
+    st = L.fp8q_linear(0, x.data_ptr(), 4, 64, 64, None, buf.ctypes.data, 16, 64,
+                       ws.data_ptr(), y.data_ptr(), 16, None, 0, stream)
+    assert st == 1, L.fp8q_last_error()
+    # null weight pointer
+    st = L.fp8q_linear(0, x.data_ptr(), 4, 64, 64, None, None, 16, 64,
+                       ws.data_ptr(), y.data_ptr(), 16, None, 0, stream)
+    assert st == 1
+    # misaligned pointer
+    st = L.fp8q_linear(0, x.data_ptr(), 4, 64, 64, None, dev_w.data_ptr() + 8, 16, 64,
+                       ws.data_ptr(), y.data_ptr(), 16, None, 0, stream)
+    assert st == 1
+    # output overlapping the activation
+    st = L.fp8q_linear(0, x.data_ptr(), 4, 64, 64, None, dev_w.data_ptr(), 16, 64,
+                       ws.data_ptr(), x.data_ptr(), 16, None, 0, stream)
+    assert st == 1
+    # a valid call still works afterwards
+    st = L.fp8q_linear(0, x.data_ptr(), 4, 64, 64, None, dev_w.data_ptr(), 16, 64,
+                       ws.data_ptr(), y.data_ptr(), 16, None, 0, stream)
+    assert st == 0, L.fp8q_last_error()
+    torch.cuda.synchronize()
+    assert (y.float() == 0).all()

@@ -68,7 +68,7 @@ def test_matches_torch_on_every_fp32_pattern(orc):
     chunk = 1 << 26
     for first in range(0, 1 << 32, chunk):
         got = orc.cast_e4m3_bits(first, chunk)
-        vals = np.arange(first, first + chunk, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        vals = (np.arange(chunk, dtype=np.uint32) + np.uint32(first)).view(np.float32)
         ref = _torch_cast(torch, vals)
         ok = (got == ref) | np.isnan(vals)
         if not ok.all():
