@@ -207,7 +207,7 @@ def main() -> int:
         "per_m": per_m,
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_w8a16 (+ k_splitk_reduce where K is split)",
+            "kernel": "k_w8a16",
             "achieved": round(value, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -22,6 +22,8 @@
 //     accumulation.  The k order inside an MFMA is free as long as both
 //     operands use the same one, which lets one 16-byte weight load feed two
 //     MFMAs and one 32-byte activation load match it.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -32,7 +34,7 @@ using namespace dev;
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxWaves = 16;
+constexpr int kThreads = 256;    // 4 waves split K
 
 __device__ __forceinline__ v8bf as_v8bf(v4u v) { return __builtin_bit_cast(v8bf, v); }
 
@@ -67,7 +69,22 @@ __device__ __forceinline__ v4u load_x8_tail(const uint16_t *rowp, int64_t kx, in
     return v4u{xd[0], xd[1], xd[2], xd[3]};
 }
 
-__device__ __forceinline__ v4u mask(v4u v, bool keep) { return keep ? v : v4u{0u, 0u, 0u, 0u}; }
+// s_waitcnt immediate for "at most n vector-memory loads outstanding" (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // Widen a lane's 16 weight codes into the A operands of two MFMA k-steps.
 __device__ __forceinline__ void widen(v4u wv, v8bf &a0, v8bf &a1)
@@ -78,18 +95,41 @@ __device__ __forceinline__ void widen(v4u wv, v8bf &a0, v8bf &a1)
     a1 = as_v8bf(v4u{p2.x, p2.y, p3.x, p3.y});
 }
 
+// One 64-k step of a wave: widen the weight codes and issue the MFMAs.
+// Rows past N (weights) or past M (activations) were clamped to a valid row
+// when loading; they only feed output rows/columns that are never stored, so
+// no masking is needed here.
+template <int AF, int MB>
+__device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[MB][2],
+                                          v4f (&acc)[AF][MB])
+{
+#pragma unroll
+    for (int a = 0; a < AF; ++a) {
+        v8bf a0, a1;
+        widen(wv[a], a0, a1);
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+            acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_v8bf(xv[j][0]), acc[a][j], 0, 0, 0);
+            acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_v8bf(xv[j][1]), acc[a][j], 0, 0, 0);
+        }
+    }
+}
+
 // AF: A fragments (16-row groups) per wave, so a block owns up to 16*AF rows;
 // `rows` (<= 16*AF) is how many of them are real weight rows.
 // MB: 16-column groups of activations (M <= 16*MB per block along grid.y).
-// UNR: 64-k steps whose loads are issued together.
-template <int AF, int MB, int UNR>
-__global__ __launch_bounds__(1024) void k_w8a16(
+// P:  pipeline depth -- 64-k steps whose loads are in flight while a step's
+//     MFMAs run.  The pipelined span of a wave is a multiple of P steps; the
+//     remaining steps (and a partial step at the end of K) run one by one.
+template <int AF, int MB, int P>
+__global__ __launch_bounds__(kThreads) void k_w8a16(
     const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
     int rows, int64_t kchunk)
 {
-    __shared__ v4f red[kMaxWaves][AF * MB][kWave];
+    constexpr int L = AF + 2 * MB;    // loads per step
+    __shared__ v4f red[kThreads / kWave][AF * MB][kWave];
 
     const int nwaves = blockDim.x / kWave;
     const int wave = threadIdx.x / kWave;
@@ -98,102 +138,99 @@ __global__ __launch_bounds__(1024) void k_w8a16(
     const int g = lane >> 4;          // which 16 k-values of a 64-k step this lane holds
     const int64_t n0 = (int64_t)blockIdx.x * rows;
     const int64_t m0 = (int64_t)blockIdx.y * 16 * MB;
-    const int64_t kb = (int64_t)wave * kchunk;
+    const int64_t kb = min(k, (int64_t)wave * kchunk);
     const int64_t ke = min(k, kb + kchunk);
 
     const uint8_t *wp[AF];
-    bool wvalid[AF];
 #pragma unroll
     for (int a = 0; a < AF; ++a) {
         const int lr = 16 * a + r;
-        wvalid[a] = lr < rows && n0 + lr < n;
-        wp[a] = w + (wvalid[a] ? n0 + lr : n0) * ld_w;
+        const bool ok = lr < rows && n0 + lr < n;
+        wp[a] = w + (ok ? n0 + lr : n0) * ld_w + 16 * g;
     }
     const uint16_t *xp[MB];
-    bool xvalid[MB];
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
         const int64_t xr = m0 + 16 * j + r;
-        xvalid[j] = xr < m;
-        xp[j] = x + (xvalid[j] ? xr : m0) * ld_x;
+        xp[j] = x + (xr < m ? xr : m0) * ld_x + 16 * g;
     }
 
-    v4f acc[AF][MB];
+    v4f acc[2][AF][MB];
 #pragma unroll
-    for (int a = 0; a < AF; ++a)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < MB; ++j)
-            acc[a][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int a = 0; a < AF; ++a)
+#pragma unroll
+            for (int j = 0; j < MB; ++j)
+                acc[h][a][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    const int64_t nfull = (ke - kb) / 64;          // whole 64-k steps
+    const int64_t npipe = nfull - nfull % P;       // pipelined span
     int64_t kk = kb;
-    for (; kk + 64 * UNR <= ke; kk += 64 * UNR) {
-        v4u wv[UNR][AF];
-        v4u xv[UNR][MB][2];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int64_t kw = kk + 64 * u + 16 * g;
+    if (npipe > 0) {
+        v4u wb[P][AF];
+        v4u xb[P][MB][2];
+        auto issue = [&](int u, int64_t k0) {
 #pragma unroll
             for (int a = 0; a < AF; ++a)
-                wv[u][a] = ldg_nt(wp[a] + kw);
+                wb[u][a] = ldg_nt(wp[a] + k0);
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
-                xv[u][j][0] = ldg(xp[j] + kw);
-                xv[u][j][1] = ldg(xp[j] + kw + 8);
+                xb[u][j][0] = ldg(xp[j] + k0);
+                xb[u][j][1] = ldg(xp[j] + k0 + 8);
             }
+        };
+        const int64_t kend = kb + 64 * npipe;
+#pragma unroll
+        for (int u = 0; u < P; ++u)
+            issue(u, kb + 64 * u);
+        __builtin_amdgcn_sched_barrier(0);
+        for (; kk + 64 * P < kend; kk += 64 * P) {
+            static_for<0, P>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                // loads retire in order: with (P-1) steps' loads still in
+                // flight, step u's loads have landed
+                wait_vmcnt<(P - 1) * L>();
+                __builtin_amdgcn_sched_barrier(0);
+                step_mfma<AF, MB>(wb[u], xb[u], acc[u & 1]);
+                issue(u, kk + 64 * (P + u));
+                __builtin_amdgcn_sched_barrier(0);
+            });
         }
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            v8bf b0[MB], b1[MB];
-#pragma unroll
-            for (int j = 0; j < MB; ++j) {
-                b0[j] = as_v8bf(mask(xv[u][j][0], xvalid[j]));
-                b1[j] = as_v8bf(mask(xv[u][j][1], xvalid[j]));
-            }
-#pragma unroll
-            for (int a = 0; a < AF; ++a) {
-                v8bf a0, a1;
-                widen(mask(wv[u][a], wvalid[a]), a0, a1);
-#pragma unroll
-                for (int j = 0; j < MB; ++j) {
-                    acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[j], acc[a][j], 0, 0, 0);
-                    acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[j], acc[a][j], 0, 0, 0);
-                }
-            }
-        }
+        // last pipelined round: no more loads to issue
+        static_for<0, P>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            wait_vmcnt<(P - 1 - u) * L>();
+            __builtin_amdgcn_sched_barrier(0);
+            step_mfma<AF, MB>(wb[u], xb[u], acc[u & 1]);
+        });
+        kk = kend;
     }
-    // remainder steps, masked at k
+    // remaining steps one at a time; the last one may be partial (masked at k)
     for (; kk < ke; kk += 64) {
         const int64_t kw = kk + 16 * g;
-        const bool full = kw + 16 <= k;
-        v8bf b0[MB], b1[MB];
+        v4u wv[AF];
+        v4u xv[MB][2];
+        if (kk + 64 <= k) {
 #pragma unroll
-        for (int j = 0; j < MB; ++j) {
-            v4u x0 = v4u{0u, 0u, 0u, 0u}, x1 = x0;
-            if (full) {
-                x0 = ldg(xp[j] + kw);
-                x1 = ldg(xp[j] + kw + 8);
-            } else if (kw < k) {
-                x0 = load_x8_tail(xp[j], kw, k);
-                x1 = load_x8_tail(xp[j], kw + 8, k);
-            }
-            b0[j] = as_v8bf(mask(x0, xvalid[j]));
-            b1[j] = as_v8bf(mask(x1, xvalid[j]));
-        }
-#pragma unroll
-        for (int a = 0; a < AF; ++a) {
-            v4u wv = v4u{0u, 0u, 0u, 0u};
-            if (full)
-                wv = ldg(wp[a] + kw);
-            else if (kw < k)
-                wv = load_w16_tail(wp[a], kw, k);
-            v8bf a0, a1;
-            widen(mask(wv, wvalid[a]), a0, a1);
+            for (int a = 0; a < AF; ++a)
+                wv[a] = ldg(wp[a] + kk);
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
-                acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[j], acc[a][j], 0, 0, 0);
-                acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[j], acc[a][j], 0, 0, 0);
+                xv[j][0] = ldg(xp[j] + kk);
+                xv[j][1] = ldg(xp[j] + kk + 8);
+            }
+        } else {
+#pragma unroll
+            for (int a = 0; a < AF; ++a)
+                wv[a] = kw < k ? load_w16_tail(wp[a] - 16 * g, kw, k) : v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                xv[j][0] = kw < k ? load_x8_tail(xp[j] - 16 * g, kw, k) : v4u{0u, 0u, 0u, 0u};
+                xv[j][1] = kw + 8 < k ? load_x8_tail(xp[j] - 16 * g, kw + 8, k) : v4u{0u, 0u, 0u, 0u};
             }
         }
+        step_mfma<AF, MB>(wv, xv, acc[0]);
     }
 
     // ---- sum the waves' partial tiles in wave order, then scale and store --
@@ -201,7 +238,7 @@ __global__ __launch_bounds__(1024) void k_w8a16(
     for (int a = 0; a < AF; ++a)
 #pragma unroll
         for (int j = 0; j < MB; ++j)
-            red[wave][a * MB + j][lane] = acc[a][j];
+            red[wave][a * MB + j][lane] = acc[0][a][j] + acc[1][a][j];
     __syncthreads();
 
     // one thread per (fragment, lane) slot: 4 outputs of one row of Y
@@ -215,19 +252,19 @@ __global__ __launch_bounds__(1024) void k_w8a16(
         const int64_t nb = n0 + nl;
         if (mr >= m || nl >= rows || nb >= n)
             continue;
-        v4f s = red[0][f][sl];
+        v4f sum = red[0][f][sl];
         for (int wv = 1; wv < nwaves; ++wv)
-            s += red[wv][f][sl];
+            sum += red[wv][f][sl];
         uint16_t *yp = y + mr * ld_y + nb;
         const int valid = (int)min<int64_t>(min<int64_t>(4, rows - nl), n - nb);
         if (valid == 4) {
             uint2 o;
-            o.x = pack_bf16x2(s[0] * w_scale[nb], s[1] * w_scale[nb + 1]);
-            o.y = pack_bf16x2(s[2] * w_scale[nb + 2], s[3] * w_scale[nb + 3]);
+            o.x = pack_bf16x2(sum[0] * w_scale[nb], sum[1] * w_scale[nb + 1]);
+            o.y = pack_bf16x2(sum[2] * w_scale[nb + 2], sum[3] * w_scale[nb + 3]);
             *reinterpret_cast<uint2 *>(yp) = o;
         } else {
             for (int v = 0; v < valid; ++v)
-                yp[v] = (uint16_t)f32_to_bf16_rne(s[v] * w_scale[nb + v]);
+                yp[v] = (uint16_t)f32_to_bf16_rne(sum[v] * w_scale[nb + v]);
         }
     }
 }
@@ -235,6 +272,10 @@ __global__ __launch_bounds__(1024) void k_w8a16(
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
+
+// Pipeline depth (64-k steps in flight per wave) for a tile shape: about 24-36
+// outstanding 16-byte loads per lane, within the register budget.
+constexpr int w8a16_depth(int af, int mb) { return (af + 2 * mb) <= 4 ? 8 : ((af + 2 * mb) <= 6 ? 4 : 2); }
 
 namespace launch {
 
@@ -248,19 +289,17 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
     int rows = 32;
     while (rows > 4 && div_up(n, rows) * p.grid_m < 256)
         rows /= 2;
-    if (rows == 32 && p.mb > 2)
-        rows = 16;                       // keep the LDS reduction buffer <= 64 KB
+    if (rows == 32 && p.mb > 1)
+        rows = 16;                       // keep the register pipeline within budget
     p.rows = rows;
     p.af = rows > 16 ? 2 : 1;
     p.grid_n = div_up(n, rows);
-    // waves split K, each taking a multiple of 64 and at least 256 k values
-    int64_t waves = div_up(k, 256);
-    if (waves > kMaxWaves)
-        waves = kMaxWaves;
-    if (waves < 1)
-        waves = 1;
-    p.kchunk = div_up(div_up(k, waves), 64) * 64;
-    p.waves = (int)div_up(k, p.kchunk);
+    // the 4 waves split K; a wave's range is a multiple of the pipelined span
+    // (64 * depth) when K is large enough, else of 64
+    p.waves = kThreads / kWave;
+    const int64_t per = div_up(k, p.waves);
+    const int64_t span = 64 * w8a16_depth(p.af, p.mb);
+    p.kchunk = per >= span ? div_up(per, span) * span : div_up(per, 64) * 64;
     p.splits = 1;
     p.np = n;
     p.workspace = 0;
@@ -272,9 +311,9 @@ static void launch_t(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k
                      const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
                      uint16_t *y, int64_t ld_y, hipStream_t stream)
 {
-    constexpr int UNR = (AF * 1 + MB * 2) <= 4 ? 4 : 2;
+    constexpr int P = w8a16_depth(AF, MB);
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
-    hipLaunchKernelGGL((k_w8a16<AF, MB, UNR>), grid, dim3(64 * p.waves), 0, stream, x, m, k,
+    hipLaunchKernelGGL((k_w8a16<AF, MB, P>), grid, dim3(kThreads), 0, stream, x, m, k,
                        ld_x, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk);
 }
 
@@ -284,10 +323,7 @@ hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, in
 {
     (void)partial;
     if (p.af == 2) {
-        switch (p.mb) {
-        case 1: launch_t<2, 1>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream); break;
-        default: launch_t<2, 2>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream); break;
-        }
+        launch_t<2, 1>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream);
     } else {
         switch (p.mb) {
         case 1: launch_t<1, 1>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream); break;
