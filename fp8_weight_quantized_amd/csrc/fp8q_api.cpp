@@ -274,6 +274,10 @@ fp8q_status fp8q_linear(fp8q_mode mode,
     FP8Q_TRY(check_ld(ld_x, k, mode == FP8Q_W8A16 ? 8 : 16, "ld_x"));
     FP8Q_TRY(check_ld(ld_w, k, 16, "ld_w"));
     FP8Q_TRY(check_ld(ld_y, n, 8, "ld_y"));
+    if (mode == FP8Q_W8A8 &&
+        (!fp8q::launch::w8a8_supports_ld(ld_x) || !fp8q::launch::w8a8_supports_ld(ld_w)))
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_fp8_a needs ld_x and ld_w below 2^23 (got %lld, %lld)",
+                    (long long)ld_x, (long long)ld_w);
     if (m == 0 || n == 0)
         return ok();
     const size_t need = fp8q_linear_workspace_size(mode, m, n, k);

@@ -11,12 +11,23 @@
 // Design (gfx950, 256 CUs in 8 XCDs, 160 KB LDS per CU):
 //   * 256 x 256 output tile per workgroup of 8 waves (2 x 4); each wave owns a
 //     128 x 64 sub-tile = 4 x 2 blocks of v_mfma_scale_f32_32x32x64_f8f6f4
-//     (E4M3 x E4M3, unit E8M0 scales), 128 fp32 accumulators per lane;
-//   * K advances 64 bytes per stage; X and W stage tiles are loaded with
-//     16-byte global loads into registers, then written to LDS rows padded to
-//     80 bytes (so the 16-byte fragment reads of 8 or 16 consecutive rows hit
-//     distinct banks), double buffered: the global loads of stage s+1 are in
-//     flight while stage s feeds the MFMAs, with one barrier per stage;
+//     (E4M3 x E4M3, unit E8M0 scales), 128 fp32 accumulators per lane, two
+//     waves per SIMD so one wave's LDS reads overlap the other's MFMAs;
+//   * the weights are the MFMA's A operand and the activations its B
+//     operand, so the accumulator D holds Y^T: each lane ends up with runs of
+//     4 consecutive output columns, stored as 8-byte bf16 packets;
+//   * K advances 64 bytes per stage through a 4-slot LDS ring filled by
+//     direct global->LDS loads (global_load_lds_dwordx4) issued three stages
+//     ahead, with one barrier per stage.  The direct loads are issued from
+//     inline assembly: the compiler cannot tell the ring slots apart, and if
+//     it sees the loads it waits for every one of them before each LDS read,
+//     which serializes the pipeline.  The kernel's own s_waitcnt (each wave
+//     waits for its loads of the stage it is about to read) and barrier
+//     provide the ordering instead;
+//   * a direct load writes a wave's 64 lanes to 1 KB of consecutive LDS, so
+//     the bank-conflict-avoiding layout is an XOR swizzle of the 16-byte
+//     chunks of each row, applied by choosing which global chunk each lane
+//     fetches;
 //   * the k order inside an MFMA is free as long as X and W use the same
 //     one, so a lane simply takes 32 contiguous bytes of its row;
 //   * tile order: consecutive workgroups are dealt round-robin to the 8 XCDs,
@@ -34,27 +45,39 @@ using namespace dev;
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;               // bytes (= k values) per stage
+constexpr int kStages = 4;           // LDS ring; loads run kStages-1 stages ahead
 constexpr int kThreads = 512;        // 8 waves
+constexpr int kWaves = kThreads / kWave;
 constexpr int kWavesM = 2;
 constexpr int kWavesN = 4;
-constexpr int WM = BM / kWavesM;     // 128
-constexpr int WN = BN / kWavesN;     // 64
+constexpr int WM = BM / kWavesM;     // 128 activation rows per wave
+constexpr int WN = BN / kWavesN;     // 64 weight rows per wave
 constexpr int TM = WM / 32;          // 4 MFMA blocks along M per wave
 constexpr int TN = WN / 32;          // 2 MFMA blocks along N per wave
-constexpr int kRowBytes = BK + 16;   // padded LDS row
-constexpr int kTileBytes = BM * kRowBytes;        // one operand, one stage (20 KB)
+constexpr int kTileBytes = BM * BK;               // one operand, one stage (16 KB)
 constexpr int kStageBytes = 2 * kTileBytes;       // X + W
-constexpr int kLdsBytes = 2 * kStageBytes;        // double buffered (80 KB)
-constexpr int kChunksPerRow = BK / 16;            // 16-byte chunks per stage row
-constexpr int kLoadsPerThread = BM * kChunksPerRow / kThreads;   // 2 per operand
+constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KB
+constexpr int kRowsPerInst = kWave * 16 / BK;     // rows one wave load instruction fills (16)
+constexpr int kInst = BM / kRowsPerInst / kWaves; // load instructions per operand per wave (2)
+constexpr int kOps = 2 * kInst;                   // vector-memory operations per full stage
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
 static_assert(BM == BN, "one loader layout serves both operands");
-static_assert(kLoadsPerThread * kThreads == BM * kChunksPerRow, "loader covers the tile");
+static_assert(kInst * kRowsPerInst * kWaves == BM, "loader covers the tile");
 
-// 16 codes of a row at k index kc, zero past k (only on a K tail).
-__device__ __forceinline__ uint4 load16_tail(const uint8_t *rowp, int64_t kc, int64_t k)
+// LDS layout of a stage tile: rows of BK = 64 bytes; the four 16-byte chunks
+// of row r are stored at chunk positions c ^ swz(r).  gfx950 serves a
+// ds_read_b128 16 lanes (256 bytes, all 64 banks) per clock, so the 16
+// consecutive rows a fragment read touches per clock must land on 16
+// distinct 16-byte slots of the 256-byte bank space: rows r..r+3 already sit
+// in different 64-byte quarters, and XOR-ing the chunk with (r >> 2) & 3
+// separates r, r+4, r+8, r+12 (measured: no bank conflicts, against 4 extra
+// cycles per read for the unswizzled or (r >> 1)-based layouts).
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+// 16 bytes of a row starting at k index kc, zero-filled at and past k.
+__device__ __forceinline__ uint4 tail16(const uint8_t *rowp, int64_t kc, int64_t k)
 {
     uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -65,57 +88,100 @@ __device__ __forceinline__ uint4 load16_tail(const uint8_t *rowp, int64_t kc, in
     return make_uint4(d[0], d[1], d[2], d[3]);
 }
 
-struct TileLoader {
-    const uint8_t *row[kLoadsPerThread];
-    bool valid[kLoadsPerThread];
-    int lds_off[kLoadsPerThread];
-    int col[kLoadsPerThread];
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at
+// LDS address lds + 16 * l.  `base` is wave-uniform (an SGPR pair), `off`
+// the lane's 32-bit byte offset from it, `lds` a wave-uniform LDS address.
+// The instruction takes its LDS address from M0, which the asm sets; nothing
+// else in this kernel uses M0 (gfx950 LDS instructions do not), which keeps
+// the clobber harmless -- the compiler warns about clobbering a reserved
+// register, so the warning is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
-    __device__ void init(const uint8_t *base, int64_t row0, int64_t rows, int64_t ld, int tid)
+// One operand's per-lane share of a stage load.  The wave fills 1 KB blocks
+// (16 rows x 64 bytes) of the stage tile; lane l writes LDS slot l of a block,
+// i.e. row l / 4 at chunk position l % 4, so it fetches logical chunk
+// (l % 4) ^ swz(row).  Addresses are a wave-uniform base (the tile's first
+// row) plus a 32-bit per-lane offset, to keep the register footprint small;
+// a tile spans fewer than 2^31 bytes (256 rows x ld, checked by the host).
+struct StageLoader {
+    const uint8_t *base;          // row0 of the operand (uniform)
+    uint32_t off[kInst];          // (row - row0) * ld + chunk offset; rows past the end clamp to row0
+    uint32_t lds_off[kInst];      // wave-uniform LDS offset of the 1 KB block
+    bool ok[kInst];               // row exists (only the register path needs it)
+
+    __device__ void init(const uint8_t *mat, int64_t row0, int64_t rows, int64_t ld, int wave, int lane)
     {
+        base = mat + row0 * ld;
 #pragma unroll
-        for (int i = 0; i < kLoadsPerThread; ++i) {
-            const int c = tid + i * kThreads;
-            const int r = c / kChunksPerRow;
-            col[i] = (c % kChunksPerRow) * 16;
-            const int64_t gr = row0 + r;
-            valid[i] = gr < rows;
-            row[i] = base + (valid[i] ? gr : 0) * ld;
-            lds_off[i] = r * kRowBytes + col[i];
+        for (int i = 0; i < kInst; ++i) {
+            const int blk = wave * kInst + i;
+            const int r = blk * kRowsPerInst + lane / 4;
+            ok[i] = row0 + r < rows;
+            off[i] = (uint32_t)((ok[i] ? (int64_t)r * ld : 0) + ((lane % 4) ^ swz(r)) * 16);
+            lds_off[i] = (uint32_t)(blk * kRowsPerInst * BK);
         }
     }
 
-    __device__ void load(uint4 *regs, int64_t k0, int64_t k, bool full_k) const
+    // A stage wholly inside K: exactly kInst direct loads, which the caller's
+    // wait counts rely on.  Rows past the end read their clamped row and only
+    // feed outputs that are never stored.
+    __device__ void load_full(uint32_t tile_lds, int64_t k0) const
     {
+        const uint8_t *stage = base + k0;
 #pragma unroll
-        for (int i = 0; i < kLoadsPerThread; ++i) {
-            const int64_t kc = k0 + col[i];
-            if (!valid[i])
-                regs[i] = make_uint4(0u, 0u, 0u, 0u);
-            else if (full_k || kc + 16 <= k)
-                regs[i] = *reinterpret_cast<const uint4 *>(row[i] + kc);
-            else if (kc < k)
-                regs[i] = load16_tail(row[i], kc, k);
-            else
-                regs[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int i = 0; i < kInst; ++i)
+            dma16(stage, off[i], tile_lds + lds_off[i]);
     }
 
-    __device__ void store(uint8_t *lds, const uint4 *regs) const
+    // The stage that crosses k goes through registers with zero fill (bytes
+    // past k, and rows past the end, read 0).
+    __device__ void load_tail(uint8_t *tile, int64_t k0, int64_t k, int wave, int lane) const
     {
 #pragma unroll
-        for (int i = 0; i < kLoadsPerThread; ++i)
-            *reinterpret_cast<uint4 *>(lds + lds_off[i]) = regs[i];
+        for (int i = 0; i < kInst; ++i) {
+            const int r = (wave * kInst + i) * kRowsPerInst + lane / 4;
+            const uint32_t kofs = ((lane % 4) ^ swz(r)) * 16;
+            const int64_t kc = k0 + kofs;                    // this lane's logical chunk start
+            const uint8_t *rowp = base + (off[i] - kofs);
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (ok[i] && kc < k)
+                v = kc + 16 <= k ? *reinterpret_cast<const uint4 *>(rowp + kc) : tail16(rowp, kc, k);
+            *reinterpret_cast<uint4 *>(tile + lds_off[i] + lane * 16) = v;
+        }
     }
 };
 
-__device__ __forceinline__ v8i lds_frag(const uint8_t *tile, int row, int half)
+// The 32 bytes lane (r, half) feeds an MFMA: logical chunks 2*half, 2*half+1 of row r.
+__device__ __forceinline__ v8i lds_frag(const uint8_t *tile, int r, int half)
 {
-    const uint8_t *p = tile + row * kRowBytes + half * 32;
-    uint4 a = *reinterpret_cast<const uint4 *>(p);
-    uint4 b = *reinterpret_cast<const uint4 *>(p + 16);
+    const uint8_t *rp = tile + r * BK;
+    const int s = swz(r);
+    const uint4 a = *reinterpret_cast<const uint4 *>(rp + ((2 * half) ^ s) * 16);
+    const uint4 b = *reinterpret_cast<const uint4 *>(rp + ((2 * half + 1) ^ s) * 16);
     return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
+
+// s_waitcnt immediate for "at most n vector-memory operations and no LDS
+// operations outstanding" (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4 left at max, lgkmcnt 11:8 = 0).
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// Workgroup barrier without a memory fence.  __syncthreads() would wait for
+// every outstanding global load (vmcnt(0)) -- including the prefetches of
+// later stages -- so the pipeline uses an explicit s_waitcnt for the data it
+// needs and this bare barrier; the "memory" clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     const uint8_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
@@ -142,82 +208,118 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    // the wave index is uniform across the wave; saying so keeps the LDS
+    // addresses of the direct loads in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
     const int wm = wave / kWavesN;
     const int wn = wave % kWavesN;
     const int lr = lane & 31;        // row of the MFMA operand this lane feeds
     const int lh = lane >> 5;        // which 32-byte half of the 64-byte k step
 
-    TileLoader lx, lw;
-    lx.init(x, m0, m, ld_x, tid);
-    lw.init(w, n0, n, ld_w, tid);
+    StageLoader lx, lw;
+    lx.init(x, m0, m, ld_x, wave, lane);
+    lw.init(w, n0, n, ld_w, wave, lane);
+    const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
 
-    v16f acc[TM][TN];
+    // acc[i][j] = D^T block: rows n (i-th 32-row block of the wave's W rows),
+    // columns m (j-th 32-row block of the wave's X rows)
+    v16f acc[TN][TM];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TM; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 acc[i][j][v] = 0.f;
 
-    const int64_t ksteps = (k + BK - 1) / BK;
-    uint4 rx[kLoadsPerThread], rw[kLoadsPerThread];
-    lx.load(rx, 0, k, BK <= k);
-    lw.load(rw, 0, k, BK <= k);
-    lx.store(lds, rx);
-    lw.store(lds + kTileBytes, rw);
-    __syncthreads();
-
-    for (int64_t ks = 0; ks < ksteps; ++ks) {
-        const int cur = (int)(ks & 1);
-        const bool more = ks + 1 < ksteps;
-        if (more) {
-            const int64_t k0 = (ks + 1) * BK;
-            const bool full = k0 + BK <= k;
-            lx.load(rx, k0, k, full);
-            lw.load(rw, k0, k, full);
-        }
-        const uint8_t *tx = lds + cur * kStageBytes;
+    auto compute = [&](int64_t st) {
+        const uint8_t *tx = lds + (int)(st % kStages) * kStageBytes;
         const uint8_t *tw = tx + kTileBytes;
-        v8i bf[TN];
+        v8i xf[TM];
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            bf[j] = lds_frag(tw, wn * WN + j * 32 + lr, lh);
+        for (int j = 0; j < TM; ++j)
+            xf[j] = lds_frag(tx, wm * WM + j * 32 + lr, lh);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const v8i af = lds_frag(tx, wm * WM + i * 32 + lr, lh);
+        for (int i = 0; i < TN; ++i) {
+            const v8i wf = lds_frag(tw, wn * WN + i * 32 + lr, lh);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TM; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af, bf[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+                    wf, xf[j], acc[i][j], 0, 0, 0, 127, 0, 127);
         }
-        if (more) {
-            uint8_t *nx = lds + (cur ^ 1) * kStageBytes;
-            lx.store(nx, rx);
-            lw.store(nx + kTileBytes, rw);
-        }
-        __syncthreads();
+    };
+    auto issue_full = [&](int64_t st) {
+        const uint32_t t = lds_base + (uint32_t)((st % kStages) * kStageBytes);
+        lx.load_full(t, st * BK);
+        lw.load_full(t + kTileBytes, st * BK);
+    };
+
+    // Full stages run through the ring, loaded kStages-1 stages ahead; a
+    // partial last stage (k not a multiple of BK) is peeled off after the loop.
+    const int64_t nfull = k / BK;
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st)
+        if (st < nfull)
+            issue_full(st);
+
+    for (int64_t ks = 0; ks < nfull; ++ks) {
+        // This wave's loads for stage ks have landed once no more than the
+        // loads of the later stages already issued (up to kStages-2 of them,
+        // exactly kOps each) are outstanding.  The barrier then makes every
+        // wave's part of the stage visible, and guarantees that all waves are
+        // done with stage ks-1, whose slot the next issue overwrites.
+        const int64_t later = min<int64_t>(kStages - 2, nfull - 1 - ks);
+        if (later >= 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(2 * kOps));
+        else if (later == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kOps));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+        barrier_no_fence();
+        if (ks + kStages - 1 < nfull)
+            issue_full(ks + kStages - 1);
+        compute(ks);
+    }
+    if (k % BK != 0) {
+        // All direct loads have landed (the last loop iteration waited for
+        // vmcnt(0)).  The partial stage's slot was last read by stage
+        // nfull - kStages, finished by every wave before an earlier barrier;
+        // this barrier also covers the reads of the last full stage.
+        barrier_no_fence();
+        uint8_t *t = lds + (int)(nfull % kStages) * kStageBytes;
+        lx.load_tail(t, nfull * BK, k, wave, lane);
+        lw.load_tail(t + kTileBytes, nfull * BK, k, wave, lane);
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+        barrier_no_fence();
+        compute(nfull);
     }
 
-    // ---- epilogue: D[i][j] at lane (col j = lane % 32), rows
-    //      8 * (v / 4) + 4 * (lane / 32) + v % 4 of each 32 x 32 block --------
+    // ---- epilogue.  In a 32 x 32 block, lane (col = lane % 32, h = lane / 32)
+    // holds D rows 8 * (v / 4) + 4 * h + v % 4, v = 0..15.  D = Y^T here, so
+    // the lane holds Y[m = col][n = ... + 4 consecutive], stored as 8 bytes.
     const float xs = *x_scale;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int64_t col = n0 + wn * WN + j * 32 + lr;
-        if (col >= n)
+    for (int j = 0; j < TM; ++j) {
+        const int64_t mr = m0 + wm * WM + j * 32 + lr;
+        if (mr >= m)
             continue;
-        const float s = xs * w_scale[col];
+        uint16_t *yrow = y + mr * ld_y;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int64_t rbase = m0 + wm * WM + i * 32 + 4 * lh;
+        for (int i = 0; i < TN; ++i) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t rr = rbase + 8 * (v / 4) + (v % 4);
-                if (rr < m)
-                    y[rr * ld_y + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * s);
+            for (int q = 0; q < 4; ++q) {
+                const int64_t nb = n0 + wn * WN + i * 32 + 8 * q + 4 * lh;
+                const v16f &a = acc[i][j];
+                if (nb + 4 <= n) {
+                    uint2 o;
+                    o.x = pack_bf16x2(a[4 * q + 0] * (xs * w_scale[nb + 0]), a[4 * q + 1] * (xs * w_scale[nb + 1]));
+                    o.y = pack_bf16x2(a[4 * q + 2] * (xs * w_scale[nb + 2]), a[4 * q + 3] * (xs * w_scale[nb + 3]));
+                    *reinterpret_cast<uint2 *>(yrow + nb) = o;
+                } else {
+                    for (int v = 0; v < 4 && nb + v < n; ++v)
+                        yrow[nb + v] = (uint16_t)f32_to_bf16_rne(a[4 * q + v] * (xs * w_scale[nb + v]));
+                }
             }
         }
     }
@@ -226,6 +328,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
 }  // namespace
 
 namespace launch {
+
+// Per-lane load offsets are 32-bit: a 256-row tile must span < 2^31 bytes.
+bool w8a8_supports_ld(int64_t ld) { return ld > 0 && ld * BM < ((int64_t)1 << 31); }
 
 W8A8Plan plan_w8a8(int64_t m, int64_t n, int64_t k)
 {

@@ -124,7 +124,8 @@ fp8q_status fp8q_quantize_act(const uint16_t *x_bf16, int64_t m, int64_t k, int6
  *   FP8Q_W8A16: Y[m,n] = bf16_RNE( w_scale[n] * sum_k X[m,k] * dec(W[n,k]) )
  *               x = bf16 [m, k] (ld_x % 8 == 0); x_scale must be NULL.
  *   FP8Q_W8A8:  Y[m,n] = bf16_RNE( x_scale * w_scale[n] * sum_k dec(X[m,k]) * dec(W[n,k]) )
- *               x = E4M3 codes [m, k] (ld_x % 16 == 0); x_scale = device fp32[1].
+ *               x = E4M3 codes [m, k] (ld_x % 16 == 0); x_scale = device fp32[1];
+ *               ld_x and ld_w must be below 2^23 in this mode.
  * Products are exact and sums are accumulated in fp32; the result is within
  * 5e-3 relative Frobenius error of the exact value (see the tests).
  *
