@@ -105,7 +105,7 @@ def main() -> int:
     xs = {m: up_bf16(xs_bits[m]) for m in DECODE_MS}
     ys = {m: torch.empty((m, N), dtype=torch.bfloat16, device=dev) for m in DECODE_MS}
     wsn = {m: L.fp8q_linear_workspace_size(0, m, N, K) for m in DECODE_MS}
-    wsp = {m: (torch.empty(wsn[m], dtype=torch.uint8, device=dev) if wsn[m] else None) for m in DECODE_MS}
+    wsp = {m: (torch.zeros(wsn[m], dtype=torch.uint8, device=dev) if wsn[m] else None) for m in DECODE_MS}
     step_bytes = sum(N * K + 4 * N + 2 * m * K + 2 * m * N for m in DECODE_MS)
     rot = copies_n // len(DECODE_MS)          # steps per full rotation of the pool
 
@@ -180,8 +180,9 @@ def main() -> int:
         end.synchronize()
         us = start.elapsed_time(end) * 1e3 / copies_n
         b = N * K + 4 * N + 2 * m * K + 2 * m * N
+        desc = fq.describe_linear(0, m, N, K)
         per_m[str(m)] = {"us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
-                         "kernel": fq.describe_linear(0, m, N, K)}
+                         "bytes": b, "kernel": desc, "kernel_symbol": desc[:desc.index(">") + 1]}
     log("per-M", per_m)
 
     result = {
@@ -195,7 +196,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 weights x bf16 activations, fp32 accumulate, bf16 out",
+        "dtype": "bf16",
         "data": "synthetic: seeded heavy-tail N(0,0.1)+3% +-U(2,4) weights, N(0,1) activations",
         "config": {
             "workload": "Llama-3-8B q_proj decode, fp8_w_bf16_a (W8A16)",
@@ -203,17 +204,11 @@ def main() -> int:
             "weight_copies_rotated": copies_n,
             "weight_pool_MB": round(copies_n * N * K / 1e6, 1),
             "timing": "HIP graphs of whole steps, HIP events on the launch stream",
+            "arithmetic": "E4M3 weight codes widened exactly to bf16 in registers, bf16 MFMA, "
+                          "fp32 accumulation, fp32 per-channel scale, bf16 output",
         },
         "per_m": per_m,
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "k_w8a16",
-            "achieved": round(value, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(value / HBM_PEAK_GBS, 4),
-            "traffic": None,
-        },
+        "roofline": roofline_decode(per_m, N, K),
     }
 
     # --------------------------------------------------------------- other rows
@@ -221,12 +216,15 @@ def main() -> int:
         result["rows"] = other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev)
 
     if args.copy_calibration:
+        # a plain elementwise copy of known size (1 GiB read + 1 GiB written) whose
+        # FETCH_SIZE / WRITE_SIZE readings scale the counters of the kernels above
         nbytes = 1 << 30
-        a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        a = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.mul(a, 1, out=b)
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = nbytes
+        del a, b
 
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
@@ -234,6 +232,61 @@ def main() -> int:
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+KERNEL_SOURCES = ("fp8_weight_quantized_amd/csrc/kernels/w8a16.hip",
+                  "fp8_weight_quantized_amd/csrc/kernels/device_common.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_w8a16_q_proj_decode_hbm_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(m: int):
+    """HBM bytes per launch of the decode kernel at this M, from the committed
+    FETCH_SIZE / WRITE_SIZE summary, or None when there is none or the kernel
+    source has changed since the counters were taken."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    fields = {}
+    for ln in lines:
+        if ":" in ln and not ln.startswith(("#", " ", "|")):
+            key, val = ln.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    val = fields.get(f"traffic_bytes_per_launch_m{m}")
+    return float(val) if val else None
+
+
+def roofline_decode(per_m: dict, n: int, k: int) -> dict:
+    """Roofline of the step's dominant kernel: the decode instantiation with the
+    longest launches.  achieved = its algorithmic bytes per launch (N*K codes +
+    4N scale bytes + 2MK activation + 2MN output bytes) / its average launch
+    time, timed with HIP events around a graph of launches on their stream."""
+    m = max(per_m, key=lambda key: per_m[key]["us"])
+    rec = per_m[m]
+    achieved = rec["GB/s"]
+    return {
+        "bound": "hbm",
+        "kernel": f"{rec['kernel_symbol']} (M={m}, N={n}, K={k})",
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(int(m)),
+        "algorithmic_bytes_per_launch": rec["bytes"],
+        "us_per_launch": rec["us"],
+        "kernel_source_sha256": kernel_source_hash(),
+    }
 
 
 def time_eager(torch, fn, iters: int, warm: int = 2) -> float:
@@ -331,7 +384,7 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
         x = up_bf16(workloads.activation(wl, m, lin.k))
         y = torch.empty((m, lin.n), dtype=torch.bfloat16, device=dev)
         nws = L.fp8q_linear_workspace_size(0, m, lin.n, lin.k)
-        wsb = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+        wsb = torch.zeros(nws, dtype=torch.uint8, device=dev) if nws else None
         layer.append((lin, wq, ws, x, y, wsb, nws))
     log(f"prepared 70B layer in {time.time() - t0:.1f}s")
     torch.cuda.empty_cache()

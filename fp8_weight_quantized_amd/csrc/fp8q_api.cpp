@@ -278,6 +278,8 @@ fp8q_status fp8q_linear(fp8q_mode mode,
         (!fp8q::launch::w8a8_supports_ld(ld_x) || !fp8q::launch::w8a8_supports_ld(ld_w)))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_fp8_a needs ld_x and ld_w below 2^23 (got %lld, %lld)",
                     (long long)ld_x, (long long)ld_w);
+    if (mode == FP8Q_W8A16 && (m + 63) / 64 > 65535)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_bf16_a takes at most 65535 * 64 activation rows");
     if (m == 0 || n == 0)
         return ok();
     const size_t need = fp8q_linear_workspace_size(mode, m, n, k);
@@ -307,8 +309,7 @@ fp8q_status fp8q_linear(fp8q_mode mode,
     if (mode == FP8Q_W8A16) {
         const auto plan = fp8q::launch::plan_w8a16(m, n, k);
         e = fp8q::launch::w8a16(plan, static_cast<const uint16_t *>(x), m, k, ld_x, w_fp8, n,
-                                ld_w, w_scale, y_bf16, ld_y, static_cast<float *>(workspace),
-                                stream);
+                                ld_w, w_scale, y_bf16, ld_y, workspace, stream);
     } else {
         const auto plan = fp8q::launch::plan_w8a8(m, n, k);
         e = fp8q::launch::w8a8(plan, static_cast<const uint8_t *>(x), m, k, ld_x, x_scale, w_fp8,
@@ -346,10 +347,17 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
         return fail(FP8Q_ERR_INVALID_ARG, "bad sizes");
     if (mode == FP8Q_W8A16) {
         const auto p = fp8q::launch::plan_w8a16(m, n, k);
-        std::snprintf(buf, len,
-                      "k_w8a16<af=%d,mb=%d> rows=%d grid=(%lld,%lld) block=%d kchunk=%lld",
-                      p.af, p.mb, p.rows, (long long)p.grid_n, (long long)p.grid_m,
-                      64 * p.waves, (long long)p.kchunk);
+        if (p.kind == fp8q::launch::W8A16Plan::kRows)
+            std::snprintf(buf, len,
+                          "k_w8a16_rows<%d, %d, %d, %d> rows=%d grid=(%lld,%lld) block=%d kchunk=%lld",
+                          p.af, p.mb, p.depth, p.waves, p.rows, (long long)p.grid_n,
+                          (long long)p.grid_m, 64 * p.waves, (long long)p.kchunk);
+        else
+            std::snprintf(buf, len,
+                          "k_w8a16_tile<%d, %d, %d> grid=(%lld,%lld) block=256 splits=%lld kper=%lld%s",
+                          p.mb, p.xd, p.steps, (long long)p.grid_n, (long long)p.grid_m,
+                          (long long)p.splits, (long long)p.kper,
+                          p.splits > 1 ? " + k_w8a16_reduce" : "");
     } else if (mode == FP8Q_W8A8) {
         const auto p = fp8q::launch::plan_w8a8(m, n, k);
         std::snprintf(buf, len, "k_w8a8 tile=256x256x64 grid=%lld (%lldx%lld) block=512",

@@ -27,21 +27,30 @@ hipError_t cast_f32(const float *x, int64_t count, uint8_t *out, hipStream_t str
 
 // ---- W8A16 (fp8_w_bf16_a) skinny GEMM --------------------------------------
 struct W8A16Plan {
-    int mb;            // 16-column activation groups per block (1..4)
-    int rows;          // weight rows per block (4, 8, 16 or 32)
-    int af;            // 16-row MFMA fragments per wave (1, or 2 when rows == 32)
-    int waves;         // waves per block; they split K
-    int64_t kchunk;    // K range per wave, a multiple of 64
-    int64_t grid_n;    // blocks along N
-    int64_t grid_m;    // blocks along M (16 * mb activation rows each)
-    int64_t splits;    // K splits across blocks (always 1: one launch, no partials)
-    int64_t np;        // unused (no partials)
-    size_t workspace;  // scratch bytes (0)
+    enum Kind { kRows = 0, kTile = 1 };
+    int kind;
+    int mb;            // 16-row activation groups per workgroup (1..4)
+    int64_t grid_m;    // workgroups along M (16 * mb activation rows each)
+    int64_t grid_n;    // workgroups along N (times the K splits for the tile kernel)
+    // k_w8a16_rows
+    int rows;          // weight rows per workgroup (4, 8, 16 or 32)
+    int af;            // 16-row MFMA fragments per wave (2 when rows == 32)
+    int waves;         // waves per workgroup; they split K
+    int depth;         // 64-k steps of loads in flight per wave
+    int64_t kchunk;    // K range per wave
+    // k_w8a16_tile (+ k_w8a16_reduce when splits > 1)
+    int xd;            // activation rows each of the 4 waves stages per chunk
+    int steps;         // 64-k steps per staged chunk
+    int64_t tiles_n;   // tiles of 64 weight rows
+    int64_t splits;    // K splits across workgroups
+    int64_t kper;      // K range per split, a multiple of the chunk
+    int64_t ldp;       // row stride of the fp32 partial tiles (n rounded up to 4)
+    size_t workspace;  // scratch bytes: the partial tiles [splits][m][ldp] (0 if no split)
 };
 W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k);
 hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
                  const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                 uint16_t *y, int64_t ld_y, float *partial, hipStream_t stream);
+                 uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream);
 
 // ---- W8A8 (fp8_w_fp8_a) GEMM on FP8 MFMA -----------------------------------
 struct W8A8Plan {

@@ -7,21 +7,31 @@
 // batch 1 FP8 and BF16 are within 10% of each other because bandwidth is the
 // limit).  Every weight byte is read exactly once.
 //
-// Design (gfx950):
-//   * one launch, no second pass: a workgroup owns R weight rows (R = 4, 8,
-//     16 or 32, chosen so that N/R workgroups cover the 256 CUs) and the
-//     whole K range; its waves split K between them and their fp32 partial
-//     tiles are summed through LDS in wave order (deterministic);
-//   * a lane streams 16 contiguous weight bytes per 64-k step with one
-//     16-byte load straight into registers (non-temporal: weights are read
-//     once, activations stay in L2); rows past N or past R are clamped to a
-//     valid row and zeroed after the load, so every load is a plain
-//     unconditional dwordx4;
-//   * the codes are widened to bf16 in registers (exact) and fed to
-//     v_mfma_f32_16x16x32_bf16 as the A operand, the activations as B, fp32
-//     accumulation.  The k order inside an MFMA is free as long as both
-//     operands use the same one, which lets one 16-byte weight load feed two
-//     MFMAs and one 32-byte activation load match it.
+// Both kernels widen the E4M3 codes to bf16 in registers (exact) and feed
+// v_mfma_f32_16x16x32_bf16 with them as the A operand and the activations as
+// B, fp32 accumulation.  The k order inside an MFMA is free as long as both
+// operands use the same one, which lets one 16-byte weight load feed two
+// MFMAs.  A lane streams 16 contiguous weight bytes per 64-k step with one
+// non-temporal 16-byte load straight into registers; rows past N are clamped
+// to a valid row and their outputs dropped, so every load is a plain
+// unconditional dwordx4.  Nothing crosses workgroups inside a kernel: on
+// MI355X the agent-scope release/acquire that would need (an L2 write-back
+// and invalidate per workgroup) measured at 3-70 us per launch.
+//
+// k_w8a16_rows -- few activation rows on a small N.  A workgroup owns 4-32
+//   weight rows and the whole K range; its waves split K and their fp32
+//   partial tiles are summed through LDS in wave order.  Each wave loads its
+//   own activation fragments straight into registers.
+// k_w8a16_tile -- more activation rows, or an N large enough to fill the GPU
+//   with 64-row tiles.  The 4 waves own 16 rows each and walk the same K
+//   range, so the activations are staged once per workgroup through LDS (in
+//   contiguous 1 KB row segments, double-buffered) and shared.  The
+//   activation fragments the MFMA layout wants cover 16 rows x half a cache
+//   line per load; fetched from L2 by every wave that way they cost about as
+//   much as the weight stream itself at M = 12 and 3x more at M = 64.  When
+//   N / 64 tiles cannot fill the GPU, K is split across workgroups: each
+//   split writes an fp32 partial tile, and k_w8a16_reduce adds the splits in
+//   split order (deterministic), scales and stores.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -34,7 +44,6 @@ using namespace dev;
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;    // 4 waves split K
 
 __device__ __forceinline__ v8bf as_v8bf(v4u v) { return __builtin_bit_cast(v8bf, v); }
 
@@ -121,18 +130,18 @@ __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[M
 // P:  pipeline depth -- 64-k steps whose loads are in flight while a step's
 //     MFMAs run.  The pipelined span of a wave is a multiple of P steps; the
 //     remaining steps (and a partial step at the end of K) run one by one.
-template <int AF, int MB, int P>
-__global__ __launch_bounds__(kThreads) void k_w8a16(
+// NW: waves per workgroup; wave w owns K range [w*kchunk, (w+1)*kchunk).
+template <int AF, int MB, int P, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
     const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
     int rows, int64_t kchunk)
 {
     constexpr int L = AF + 2 * MB;    // loads per step
-    __shared__ v4f red[kThreads / kWave][AF * MB][kWave];
+    __shared__ v4f red[NW][AF * MB][kWave];
 
-    const int nwaves = blockDim.x / kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int r = lane & 15;          // row of the A (weight) / B (activation) operand
     const int g = lane >> 4;          // which 16 k-values of a 64-k step this lane holds
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void k_w8a16(
         if (mr >= m || nl >= rows || nb >= n)
             continue;
         v4f sum = red[0][f][sl];
-        for (int wv = 1; wv < nwaves; ++wv)
+        for (int wv = 1; wv < NW; ++wv)
             sum += red[wv][f][sl];
         uint16_t *yp = y + mr * ld_y + nb;
         const int valid = (int)min<int64_t>(min<int64_t>(4, rows - nl), n - nb);
@@ -269,15 +278,245 @@ __global__ __launch_bounds__(kThreads) void k_w8a16(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// k_w8a16_tile
+// ---------------------------------------------------------------------------
+
+constexpr int kTileThreads = 256;              // 4 waves
+constexpr int kTileWaves = kTileThreads / kWave;
+constexpr int kTileN = 16 * kTileWaves;        // weight rows per workgroup
+
+// Workgroup barrier after this wave's LDS writes have landed.  Written out
+// because __syncthreads() also waits for every outstanding global load,
+// which would drain the weight pipeline at each chunk boundary.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Scale 4 consecutive outputs of row mr and store them as bf16 (8 bytes when
+// all 4 columns exist; the pointer is then 8-byte aligned).
+__device__ __forceinline__ void store_y4(uint16_t *__restrict__ y, int64_t ld_y,
+                                         const float *__restrict__ w_scale, int64_t mr,
+                                         int64_t nb, int64_t n, v4f s)
+{
+    uint16_t *yp = y + mr * ld_y + nb;
+    if (nb + 4 <= n) {
+        uint2 o;
+        o.x = pack_bf16x2(s[0] * w_scale[nb], s[1] * w_scale[nb + 1]);
+        o.y = pack_bf16x2(s[2] * w_scale[nb + 2], s[3] * w_scale[nb + 3]);
+        *reinterpret_cast<uint2 *>(yp) = o;
+    } else {
+        for (int v = 0; v < (int)(n - nb); ++v)
+            yp[v] = (uint16_t)f32_to_bf16_rne(s[v] * w_scale[nb + v]);
+    }
+}
+
+// MB: 16-row groups of activations per workgroup (M <= 16*MB along grid.y).
+// XD: activation rows each wave stages per chunk (4*XD rows are staged; rows
+//     past M are clamped to row M-1; LDS rows past 4*XD are never written and
+//     only feed output columns that are never stored).
+// T:  64-k steps per chunk; a chunk's weights are loaded one chunk ahead.
+// Grid: x = tiles of 64 weight rows times K splits (split index fastest),
+// y = groups of 16*MB activation rows.
+template <int MB, int XD, int T>
+__global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
+    const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
+    const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
+    const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
+    int64_t kper, int splits, float *__restrict__ partial, int64_t ldp)
+{
+    constexpr int XR = 16 * MB;                // LDS rows per buffer
+    constexpr int CK = 64 * T;                 // k per chunk
+    constexpr int RB = 2 * CK;                 // LDS bytes of one staged row
+    constexpr int XH = T / 8;                  // 1 KB loads per staged row
+    constexpr int XL = XD * XH;                // activation loads per wave per chunk
+    static_assert(kTileWaves * XD <= XR, "staged rows exceed the buffer");
+    static_assert(T % 8 == 0, "a chunk is a whole number of 1 KB row segments");
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2 * XR * RB];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int r = lane & 15;          // row of the A (weight) / B (activation) operand
+    const int g = lane >> 4;          // which 16 k-values of a 64-k step this lane holds
+    const int split = (int)(blockIdx.x % (unsigned)splits);
+    const int64_t tile_n = blockIdx.x / (unsigned)splits;
+    const int64_t n0 = tile_n * kTileN + 16 * wave;    // this wave's first weight row
+    const int64_t m0 = (int64_t)blockIdx.y * XR;
+    const int64_t kb = (int64_t)split * kper;
+    const int64_t ke = min(k, kb + kper);
+    const int64_t nchunks = (ke - kb) / CK;
+
+    const uint8_t *wrow = w + min(n0 + r, n - 1) * ld_w + 16 * g;
+    const uint8_t *wp = wrow + kb;
+
+    // LDS byte offset of 16-byte unit u of staged row rho.  The units of a row
+    // are XOR-permuted by the row's low 4 bits, so the 16 rows one B-operand
+    // read touches (same u) land in 16 different 4-bank groups.
+    auto xs_off = [](int rho, int u) { return rho * RB + 16 * (u ^ (rho & 15)); };
+
+    v4f acc[2][MB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+            acc[h][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    if (nchunks > 0) {
+        // this wave stages activation rows wave, wave + 4, ...; lane l holds
+        // 16-byte unit l of each 1 KB segment of the row's chunk
+        const uint16_t *xsrc[XD];
+#pragma unroll
+        for (int i = 0; i < XD; ++i)
+            xsrc[i] = x + min(m0 + wave + kTileWaves * i, m - 1) * ld_x + kb + 8 * lane;
+        v4u xr[XD][XH];
+        v4u wr[T];
+        auto load_x = [&](int64_t c) {
+#pragma unroll
+            for (int i = 0; i < XD; ++i)
+#pragma unroll
+                for (int h = 0; h < XH; ++h)
+                    xr[i][h] = ldg(xsrc[i] + c * CK + 512 * h);
+        };
+        auto store_x = [&](int buf) {
+            uint8_t *base = xs + buf * (XR * RB);
+#pragma unroll
+            for (int i = 0; i < XD; ++i)
+#pragma unroll
+                for (int h = 0; h < XH; ++h)
+                    *reinterpret_cast<v4u *>(base + xs_off(wave + kTileWaves * i, 64 * h + lane)) = xr[i][h];
+        };
+        auto compute = [&](int u, int buf, v4f(&a)[MB]) {
+            v8bf a0, a1;
+            widen(wr[u], a0, a1);
+            const uint8_t *base = xs + buf * (XR * RB);
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                const v4u b0 = *reinterpret_cast<const v4u *>(base + xs_off(16 * j + r, 8 * u + 2 * g));
+                const v4u b1 = *reinterpret_cast<const v4u *>(base + xs_off(16 * j + r, 8 * u + 2 * g + 1));
+                a[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_v8bf(b0), a[j], 0, 0, 0);
+                a[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_v8bf(b1), a[j], 0, 0, 0);
+            }
+        };
+
+        // prologue: chunk 0's activations, then its weights
+        load_x(0);
+        static_for<0, T>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            wr[u] = ldg_nt(wp + 64 * u);
+        });
+        wait_vmcnt<T>();                      // the activation loads (issued first) landed
+        __builtin_amdgcn_sched_barrier(0);
+        store_x(0);
+        lds_barrier();
+
+        int64_t c = 0;
+        for (; c + 1 < nchunks; ++c) {
+            const int buf = (int)(c & 1);
+            load_x(c + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, T>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                // loads retire in order; issued after this step's weights:
+                // T-1 weight loads and the XL activation loads of chunk c+1
+                wait_vmcnt<T - 1 + XL>();
+                __builtin_amdgcn_sched_barrier(0);
+                compute(u, buf, acc[u & 1]);
+                wr[u] = ldg_nt(wp + (c + 1) * CK + 64 * u);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // chunk c+1's activations: only its T weight loads were issued after them
+            wait_vmcnt<T>();
+            __builtin_amdgcn_sched_barrier(0);
+            store_x(buf ^ 1);     // that buffer was last read in chunk c-1, before the
+            lds_barrier();        // previous barrier
+        }
+        // last chunk: nothing more to load
+        static_for<0, T>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            wait_vmcnt<T - 1 - u>();
+            __builtin_amdgcn_sched_barrier(0);
+            compute(u, (int)(c & 1), acc[u & 1]);
+        });
+    }
+
+    // K left after the whole chunks (less than one chunk, only in the last
+    // split): one 64-k step at a time straight from global memory, the last
+    // step masked at k
+    for (int64_t kk = kb + nchunks * CK; kk < ke; kk += 64) {
+        const int64_t kw = kk + 16 * g;
+        v4u wv;
+        v4u xv[MB][2];
+        if (kk + 64 <= k) {
+            wv = ldg(wrow + kk);
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                const uint16_t *xrow = x + min(m0 + 16 * j + r, m - 1) * ld_x + kw;
+                xv[j][0] = ldg(xrow);
+                xv[j][1] = ldg(xrow + 8);
+            }
+        } else {
+            wv = kw < k ? load_w16_tail(wrow - 16 * g, kw, k) : v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                const uint16_t *xrow = x + min(m0 + 16 * j + r, m - 1) * ld_x;
+                xv[j][0] = kw < k ? load_x8_tail(xrow, kw, k) : v4u{0u, 0u, 0u, 0u};
+                xv[j][1] = kw + 8 < k ? load_x8_tail(xrow, kw + 8, k) : v4u{0u, 0u, 0u, 0u};
+            }
+        }
+        v8bf a0, a1;
+        widen(wv, a0, a1);
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_v8bf(xv[j][0]), acc[0][j], 0, 0, 0);
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_v8bf(xv[j][1]), acc[0][j], 0, 0, 0);
+        }
+    }
+
+    // lane (r, g) holds D rows 4g..4g+3 (weight rows n0+4g..) of column r
+    // (activation row m0 + 16j + r)
+    const int64_t nb = n0 + 4 * g;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+        const int64_t mr = m0 + 16 * j + r;
+        if (mr >= m || nb >= n)
+            continue;
+        const v4f s = acc[0][j] + acc[1][j];
+        if (splits == 1)
+            store_y4(y, ld_y, w_scale, mr, nb, n, s);
+        else      // partial[split][m][ldp]; ldp >= n rounded up to 4, so the 16 bytes fit
+            *reinterpret_cast<v4f *>(partial + ((int64_t)split * m + mr) * ldp + nb) = s;
+    }
+}
+
+// Sum of the K splits' partial tiles in split order, scaled and stored as
+// bf16: one thread per 4 consecutive outputs of a row.
+__global__ __launch_bounds__(256) void k_w8a16_reduce(
+    const float *__restrict__ partial, int64_t m, int64_t n, int64_t ldp, int splits,
+    const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y)
+{
+    const int64_t q = ldp / 4;
+    const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (slot >= m * q)
+        return;
+    const int64_t mr = slot / q;
+    const int64_t nb = 4 * (slot % q);
+    v4f s = *reinterpret_cast<const v4f *>(partial + mr * ldp + nb);
+    for (int sp = 1; sp < splits; ++sp)
+        s += *reinterpret_cast<const v4f *>(partial + ((int64_t)sp * m + mr) * ldp + nb);
+    store_y4(y, ld_y, w_scale, mr, nb, n, s);
+}
+
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-// Pipeline depth (64-k steps in flight per wave) for a tile shape: about 24-36
-// outstanding 16-byte loads per lane, within the register budget.
-constexpr int w8a16_depth(int af, int mb) { return (af + 2 * mb) <= 4 ? 8 : ((af + 2 * mb) <= 6 ? 4 : 2); }
-
 namespace launch {
+
+// Register-pipeline depth of the rows kernel: about 24-36 16-byte loads in
+// flight per lane.
+static int rows_depth(int af, int mb) { return (af + 2 * mb) <= 4 ? 8 : ((af + 2 * mb) <= 6 ? 4 : 2); }
 
 W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
 {
@@ -285,54 +524,116 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
     const int64_t mgroups = div_up(m, 16);
     p.mb = (int)(mgroups >= 4 ? 4 : (mgroups < 1 ? 1 : mgroups));
     p.grid_m = div_up(m, 16 * p.mb);
-    // rows per block: the most rows (up to 32) that still leave >= 256 blocks
-    int rows = 32;
-    while (rows > 4 && div_up(n, rows) * p.grid_m < 256)
-        rows /= 2;
-    if (rows == 32 && p.mb > 1)
-        rows = 16;                       // keep the register pipeline within budget
-    p.rows = rows;
-    p.af = rows > 16 ? 2 : 1;
-    p.grid_n = div_up(n, rows);
-    // the 4 waves split K; a wave's range is a multiple of the pipelined span
-    // (64 * depth) when K is large enough, else of 64
-    p.waves = kThreads / kWave;
-    const int64_t per = div_up(k, p.waves);
-    const int64_t span = 64 * w8a16_depth(p.af, p.mb);
-    p.kchunk = per >= span ? div_up(per, span) * span : div_up(per, 64) * 64;
+    p.tiles_n = div_up(n, kTileN);
     p.splits = 1;
-    p.np = n;
     p.workspace = 0;
+    // The rows kernel wins for up to 16 activation rows on a mid-sized weight
+    // (N <= 16K, K < 16K); a weight large in N or K, a small N, or more
+    // activation rows go to the tile kernel (measured on MI355X across the
+    // Llama-3 8B/70B decode shapes).
+    const int64_t tiles = p.tiles_n * p.grid_m;
+    const bool tile = p.mb > 1 || tiles >= 256 || tiles <= 32 || k >= 16384;
+    if (!tile) {
+        p.kind = W8A16Plan::kRows;
+        // rows per block: the most rows (up to 32) that still leave >= 256 blocks
+        int rows = 32;
+        while (rows > 4 && div_up(n, rows) * p.grid_m < 256)
+            rows /= 2;
+        p.rows = rows;
+        p.af = rows > 16 ? 2 : 1;
+        p.grid_n = div_up(n, rows);
+        p.waves = 4;
+        p.depth = rows_depth(p.af, p.mb);
+        // the waves split K; a wave's range is a multiple of the pipelined span
+        // (64 * depth) when K is large enough, else of 64
+        const int64_t per = div_up(k, p.waves);
+        const int64_t span = 64 * p.depth;
+        p.kchunk = per >= span ? div_up(per, span) * span : div_up(per, 64) * 64;
+        return p;
+    }
+    p.kind = W8A16Plan::kTile;
+    if (p.mb == 1) {
+        // stage only the activation rows that exist: 4, 8 or 16 of the 16
+        p.xd = m <= 4 ? 1 : (m <= 8 ? 2 : 4);
+        p.steps = (k >= 16384 || tiles >= 256) ? 16 : 8;
+    } else {
+        p.xd = 4 * p.mb;
+        p.steps = 8;
+    }
+    // split K (in whole chunks) towards 256 workgroups, keeping at least two
+    // chunks per split so each workgroup's pipeline gets past its prologue
+    const int64_t chunk = 64 * p.steps;
+    int64_t s = 256 / tiles;
+    const int64_t s_max = k / (2 * chunk);
+    s = s > s_max ? s_max : s;
+    s = s < 1 ? 1 : s;
+    p.kper = div_up(div_up(k, s), chunk) * chunk;
+    p.splits = div_up(k, p.kper);
+    p.ldp = div_up(n, 4) * 4;
+    if (p.splits > 1)
+        p.workspace = (size_t)p.splits * m * p.ldp * sizeof(float);
+    p.grid_n = p.tiles_n * p.splits;
     return p;
 }
 
-template <int AF, int MB>
-static void launch_t(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
-                     const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                     uint16_t *y, int64_t ld_y, hipStream_t stream)
+template <int AF, int MB, int P, int NW>
+static void launch_rows(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                        const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
+                        uint16_t *y, int64_t ld_y, hipStream_t stream)
 {
-    constexpr int P = w8a16_depth(AF, MB);
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
-    hipLaunchKernelGGL((k_w8a16<AF, MB, P>), grid, dim3(kThreads), 0, stream, x, m, k,
+    hipLaunchKernelGGL((k_w8a16_rows<AF, MB, P, NW>), grid, dim3(NW * kWave), 0, stream, x, m, k,
                        ld_x, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk);
+}
+
+template <int MB, int XD, int T>
+static void launch_tile(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                        const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
+                        uint16_t *y, int64_t ld_y, float *partial, hipStream_t stream)
+{
+    const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
+    hipLaunchKernelGGL((k_w8a16_tile<MB, XD, T>), grid, dim3(kTileThreads), 0, stream, x, m, k,
+                       ld_x, w, n, ld_w, w_scale, y, ld_y, p.kper, (int)p.splits, partial, p.ldp);
+    if (p.splits > 1) {
+        const int64_t slots = m * (p.ldp / 4);
+        hipLaunchKernelGGL(k_w8a16_reduce, dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
+                           partial, m, n, p.ldp, (int)p.splits, w_scale, y, ld_y);
+    }
 }
 
 hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
                  const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                 uint16_t *y, int64_t ld_y, float *partial, hipStream_t stream)
+                 uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream)
 {
-    (void)partial;
-    if (p.af == 2) {
-        launch_t<2, 1>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream);
-    } else {
-        switch (p.mb) {
-        case 1: launch_t<1, 1>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream); break;
-        case 2: launch_t<1, 2>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream); break;
-        case 3: launch_t<1, 3>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream); break;
-        default: launch_t<1, 4>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream); break;
+    float *partial = static_cast<float *>(workspace);
+    if (p.kind == W8A16Plan::kRows) {
+#define FP8Q_ROWS_CASE(AF, MB, P, NW)                                                         \
+        if (p.af == AF && p.mb == MB && p.depth == P && p.waves == NW) {                      \
+            launch_rows<AF, MB, P, NW>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream); \
+            return hipGetLastError();                                                         \
         }
+        FP8Q_ROWS_CASE(2, 1, 8, 4)
+        FP8Q_ROWS_CASE(1, 1, 8, 4)
+#undef FP8Q_ROWS_CASE
+    } else {
+#define FP8Q_TILE_CASE(MB, XD, T)                                                             \
+        if (p.mb == MB && p.xd == XD && p.steps == T) {                                       \
+            launch_tile<MB, XD, T>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, partial,   \
+                                   stream);                                                   \
+            return hipGetLastError();                                                         \
+        }
+        FP8Q_TILE_CASE(1, 1, 8)
+        FP8Q_TILE_CASE(1, 2, 8)
+        FP8Q_TILE_CASE(1, 4, 8)
+        FP8Q_TILE_CASE(1, 1, 16)
+        FP8Q_TILE_CASE(1, 2, 16)
+        FP8Q_TILE_CASE(1, 4, 16)
+        FP8Q_TILE_CASE(2, 8, 8)
+        FP8Q_TILE_CASE(3, 12, 8)
+        FP8Q_TILE_CASE(4, 16, 8)
+#undef FP8Q_TILE_CASE
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 }  // namespace launch

@@ -134,9 +134,14 @@ fp8q_status fp8q_quantize_act(const uint16_t *x_bf16, int64_t m, int64_t k, int6
  *   y_bf16  [m, n] bf16 out, ld_y >= n, ld_y % 8 == 0, 16-byte aligned; must not
  *           overlap any input
  *   workspace  device scratch of at least fp8q_linear_workspace_size(mode, m, n, k)
- *              bytes (may be 0, then workspace may be NULL); needs no initialisation
+ *              bytes, 16-byte aligned (the size may be 0, then workspace may be
+ *              NULL); needs no initialisation.  W8A16 uses it when it splits K
+ *              across workgroups (N / 64 row tiles too few to fill the GPU): it
+ *              then holds fp32 partial sums that a second kernel on `stream`
+ *              adds up.
  * m == 0 or n == 0 is a no-op; k must be >= 1.  Deterministic: the same inputs
- * give the same bits on every call.
+ * give the same bits on every call (K-split partial sums are added in split
+ * order).
  */
 size_t fp8q_linear_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k);
 fp8q_status fp8q_linear(fp8q_mode mode,

@@ -49,17 +49,35 @@ def test_workspace_queries(L):
     assert L.fp8q_quantize_act_workspace_size(1, 8) == 256
     assert L.fp8q_quantize_act_workspace_size(0, 8) == 256
     assert L.fp8q_quantize_act_workspace_size(4, 0) == 0
-    # both linear modes run as one launch without scratch
+    # W8A8 needs no scratch
     assert L.fp8q_linear_workspace_size(1, 8192, 28672, 4096) == 0
+    # W8A16, up to 16 activation rows on a mid-sized weight: the rows kernel,
+    # one launch, no scratch
     assert L.fp8q_linear_workspace_size(0, 1, 4096, 4096) == 0
+    assert L.fp8q_linear_workspace_size(0, 12, 8192, 8192) == 0
+    # 64-row tiles: no K split when 448 tiles cover the GPU or K is under two chunks
     assert L.fp8q_linear_workspace_size(0, 12, 28672, 8192) == 0
+    assert L.fp8q_linear_workspace_size(0, 4, 64, 500) == 0
+    # otherwise K splits towards 256 workgroups (at least two chunks each),
+    # with fp32 partial tiles [splits][m][n rounded up to 4]
+    #   M=64, N=K=4096: 64 tiles -> 4 splits of 1024
+    assert L.fp8q_linear_workspace_size(0, 64, 4096, 4096) == 4 * 64 * 4096 * 4
+    #   M=12, N=1022 (16 tiles), K=8192: 8 splits of 1024; rows padded to 1024
+    assert L.fp8q_linear_workspace_size(0, 12, 1022, 8192) == 8 * 12 * 1024 * 4
+    #   M=12, N=8192, K=28672 (16-step chunks of 1024): 2 splits
+    assert L.fp8q_linear_workspace_size(0, 12, 8192, 28672) == 2 * 12 * 8192 * 4
+    #   M=40, N=100, K=3000: 2 tiles, at most 2 splits of whole 512-k chunks
+    assert L.fp8q_linear_workspace_size(0, 40, 100, 3000) == 2 * 40 * 100 * 4
     assert L.fp8q_linear_workspace_size(0, 0, 4096, 4096) == 0
 
 
 def test_describe(L):
     buf = ctypes.create_string_buffer(256)
     assert L.fp8q_linear_describe(0, 1, 4096, 4096, buf, 256) == 0
-    assert buf.value.startswith(b"k_w8a16")
+    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
+    assert L.fp8q_linear_describe(0, 64, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_tile<4, 16, 8>")
+    assert b"splits=4" in buf.value and b"k_w8a16_reduce" in buf.value
     assert L.fp8q_linear_describe(1, 8192, 28672, 4096, buf, 256) == 0
     assert b"32x112" in buf.value
     assert L.fp8q_linear_describe(7, 1, 1, 1, buf, 256) == 1

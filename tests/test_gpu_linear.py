@@ -61,15 +61,18 @@ def all_codes_weight(n: int, k: int) -> np.ndarray:
     return w
 
 
-@pytest.mark.parametrize("m,n", [(16, 256), (1, 256), (64, 272), (12, 256)])
-def test_w8a16_exact_every_code(fq, orc, m, n):
-    """X = identity rows: Y[i, j] = dec(W[j, i]) exactly, for all 254 finite codes."""
-    k = 64
+@pytest.mark.parametrize("m,n,k", [(16, 256, 64), (1, 256, 64), (64, 272, 64), (12, 256, 64),
+                                   (1, 272, 576), (7, 300, 1100), (16, 256, 2048), (40, 320, 1536),
+                                   (64, 272, 1600), (5, 4096, 1100), (1, 2304, 640)])
+def test_w8a16_exact_every_code(fq, orc, m, n, k):
+    """X = one-hot rows: Y[i, j] = dec(W[j, p_i]) exactly, for all 254 finite codes.
+    The one-hot positions p_i are spread over K, so with K > 512 they land in
+    different staged chunks, steps and K splits."""
     wq = all_codes_weight(n, k)
     x = np.zeros((m, k), np.uint16)
-    x[np.arange(m), np.arange(m) % k] = 0x3F80          # 1.0
+    x[np.arange(m), (np.arange(m) * 37 + 5) % k] = 0x3F80          # 1.0
     ws = np.ones(n, np.float32)
-    say("w8a16 exact", m, n, k)
+    say("w8a16 exact", m, n, k, fq.describe_linear(0, m, n, k))
     y = run_w8a16(fq, x, wq, ws)
     ref = orc.linear(0, x, wq, ws)
     assert (y == ref).all(), np.argwhere(y != ref)[:5]
@@ -99,7 +102,8 @@ def test_tiny(fq, orc):
 
 
 RAGGED = [(3, 100, 1000), (17, 130, 520), (65, 64, 64), (100, 96, 4104), (1, 16, 8),
-          (5, 1, 40), (2, 4096, 4096), (64, 1024, 8192), (33, 77, 13), (129, 200, 96)]
+          (5, 1, 40), (2, 4096, 4096), (64, 1024, 8192), (33, 77, 13), (129, 200, 96),
+          (7, 300, 2048), (13, 63, 1536), (40, 522, 3000), (6, 1, 700)]
 
 
 @pytest.mark.parametrize("m,n,k", RAGGED)
@@ -177,6 +181,35 @@ def test_pipeline_w8a8_from_gpu_quantizers(fq, orc):
     owq, ows, _ = orc.quantize_weight(w)
     oxq, oxs, _ = orc.quantize_act(x)
     assert_gemm_close(y, orc.linear(1, oxq, owq, ows, oxs), "pipeline")
+
+
+@pytest.mark.parametrize("shapes", [[(40, 200, 5000), (20, 100, 2100)],
+                                    [(64, 1024, 4096), (33, 130, 3000), (64, 1024, 4096)]])
+def test_w8a16_split_workspace_reuse(fq, orc, shapes):
+    """K-split calls sharing one workspace that starts full of NaN bit patterns:
+    every partial a call reads, the same call wrote."""
+    from fp8_weight_quantized_amd import _lib
+    L = _lib.lib()
+    need = max(L.fp8q_linear_workspace_size(0, m, n, k) for m, n, k in shapes)
+    assert need > 0
+    ws_buf = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for i, (m, n, k) in enumerate(shapes):
+        w = workloads.heavy_tail_weight(n, k, 50 + i)
+        x = workloads.normal_act(m, k, 60 + i)
+        wq, wsc, _ = orc.quantize_weight(w)
+        xd, wd = pad8_bf16(x), pad16(wq)
+        wsd = torch.from_numpy(wsc).cuda()
+        y = torch.empty((m, (n + 7) // 8 * 8), dtype=torch.bfloat16, device="cuda")[:, :n]
+        say("w8a16 workspace reuse", m, n, k, fq.describe_linear(0, m, n, k))
+        assert "splits=1 " not in fq.describe_linear(0, m, n, k)
+        for rep in range(2):
+            st = L.fp8q_linear(0, xd.data_ptr(), m, k, xd.stride(0), None, wd.data_ptr(), n,
+                               wd.stride(0), wsd.data_ptr(), y.data_ptr(), y.stride(0),
+                               ws_buf.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+            assert st == 0, _lib.last_error()
+            torch.cuda.synchronize()
+            assert_gemm_close(host_bf16_as_f64(y), orc.linear(0, x, wq, wsc),
+                              f"reuse {m}x{n}x{k} call {rep}")
 
 
 def test_deterministic(fq, orc):
