@@ -360,7 +360,7 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
                           p.splits > 1 ? " + k_w8a16_reduce" : "");
     } else if (mode == FP8Q_W8A8) {
         const auto p = fp8q::launch::plan_w8a8(m, n, k);
-        std::snprintf(buf, len, "k_w8a8 tile=256x256x64 grid=%lld (%lldx%lld) block=512",
+        std::snprintf(buf, len, "k_w8a8 tile=256x256x128 grid=%lld (%lldx%lld) block=512",
                       (long long)(p.tiles_m * p.tiles_n), (long long)p.tiles_m,
                       (long long)p.tiles_n);
     } else {

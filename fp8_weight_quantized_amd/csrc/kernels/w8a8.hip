@@ -10,26 +10,30 @@
 //
 // Design (gfx950, 256 CUs in 8 XCDs, 160 KB LDS per CU):
 //   * 256 x 256 output tile per workgroup of 8 waves (2 x 4); each wave owns a
-//     128 x 64 sub-tile = 4 x 2 blocks of v_mfma_scale_f32_32x32x64_f8f6f4
-//     (E4M3 x E4M3, unit E8M0 scales), 128 fp32 accumulators per lane, two
-//     waves per SIMD so one wave's LDS reads overlap the other's MFMAs;
+//     128 x 64 sub-tile = 4 x 2 blocks of v_mfma_f32_32x32x64_f8f6f4 (E4M3 x
+//     E4M3; the scaled builtin with zero scale operands selects the unscaled
+//     instruction, about 2% faster here than unit E8M0 scales), 128 fp32
+//     accumulators per lane, two waves per SIMD so one wave's LDS reads
+//     overlap the other's MFMAs;
 //   * the weights are the MFMA's A operand and the activations its B
 //     operand, so the accumulator D holds Y^T: each lane ends up with runs of
 //     4 consecutive output columns, stored as 8-byte bf16 packets;
-//   * K advances 64 bytes per stage through a 4-slot LDS ring filled by
-//     direct global->LDS loads (global_load_lds_dwordx4) issued three stages
-//     ahead, with one barrier per stage.  The direct loads are issued from
+//   * K advances 128 bytes per stage (two MFMA k-steps) through a 2-slot,
+//     128 KB LDS ring filled by direct global->LDS loads
+//     (global_load_lds_dwordx4) issued one stage ahead, with one barrier per
+//     stage.  128-byte stages halve the barriers and waits per MFMA against
+//     64-byte stages with a 4-slot ring (7% faster here).  The direct loads are issued from
 //     inline assembly: the compiler cannot tell the ring slots apart, and if
 //     it sees the loads it waits for every one of them before each LDS read,
 //     which serializes the pipeline.  The kernel's own s_waitcnt (each wave
 //     waits for its loads of the stage it is about to read) and barrier
 //     provide the ordering instead;
-//   * a direct load writes a wave's 64 lanes to 1 KB of consecutive LDS, so
-//     the bank-conflict-avoiding layout is an XOR swizzle of the 16-byte
-//     chunks of each row, applied by choosing which global chunk each lane
-//     fetches;
+//   * a direct load writes a wave's 64 lanes to 1 KB of consecutive LDS (8
+//     rows of 128 bytes), so the bank-conflict-avoiding layout is an XOR
+//     swizzle of the 16-byte chunks of each row, applied by choosing which
+//     global chunk each lane fetches;
 //   * the k order inside an MFMA is free as long as X and W use the same
-//     one, so a lane simply takes 32 contiguous bytes of its row;
+//     one, so a lane simply takes 32 contiguous bytes of its row per k-step;
 //   * tile order: consecutive workgroups are dealt round-robin to the 8 XCDs,
 //     so the tile index is remapped to give each XCD a contiguous band of
 //     tiles, grouped 8 tile-rows high so that concurrent tiles share X and W
@@ -44,8 +48,8 @@ using namespace dev;
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;               // bytes (= k values) per stage
-constexpr int kStages = 4;           // LDS ring; loads run kStages-1 stages ahead
+constexpr int BK = 128;              // bytes (= k values) per stage
+constexpr int kStages = 2;           // LDS ring; loads run kStages-1 stages ahead
 constexpr int kThreads = 512;        // 8 waves
 constexpr int kWaves = kThreads / kWave;
 constexpr int kWavesM = 2;
@@ -57,24 +61,24 @@ constexpr int TN = WN / 32;          // 2 MFMA blocks along N per wave
 constexpr int kTileBytes = BM * BK;               // one operand, one stage (16 KB)
 constexpr int kStageBytes = 2 * kTileBytes;       // X + W
 constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KB
-constexpr int kRowsPerInst = kWave * 16 / BK;     // rows one wave load instruction fills (16)
-constexpr int kInst = BM / kRowsPerInst / kWaves; // load instructions per operand per wave (2)
+constexpr int kRowsPerInst = kWave * 16 / BK;     // rows one wave load instruction fills (8)
+constexpr int kInst = BM / kRowsPerInst / kWaves; // load instructions per operand per wave (4)
 constexpr int kOps = 2 * kInst;                   // vector-memory operations per full stage
+constexpr int kChunks = BK / 16;                  // 16-byte chunks per tile row
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
 static_assert(BM == BN, "one loader layout serves both operands");
 static_assert(kInst * kRowsPerInst * kWaves == BM, "loader covers the tile");
 
-// LDS layout of a stage tile: rows of BK = 64 bytes; the four 16-byte chunks
-// of row r are stored at chunk positions c ^ swz(r).  gfx950 serves a
-// ds_read_b128 16 lanes (256 bytes, all 64 banks) per clock, so the 16
-// consecutive rows a fragment read touches per clock must land on 16
-// distinct 16-byte slots of the 256-byte bank space: rows r..r+3 already sit
-// in different 64-byte quarters, and XOR-ing the chunk with (r >> 2) & 3
-// separates r, r+4, r+8, r+12 (measured: no bank conflicts, against 4 extra
-// cycles per read for the unswizzled or (r >> 1)-based layouts).
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// LDS layout of a stage tile: rows of BK = 128 bytes; the eight 16-byte
+// chunks of row r are stored at chunk positions c ^ swz(r).  gfx950 serves a
+// ds_read_b128 16 lanes (256 bytes, all 64 banks) per clock, and a fragment
+// read has 16 consecutive rows read the same logical chunk: rows r and r+1
+// sit in different 128-byte halves of the bank space, and XOR-ing the chunk
+// with (r >> 1) & 7 spreads the 8 rows of equal parity over the 8 chunk
+// positions, so the 16 reads hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // 16 bytes of a row starting at k index kc, zero-filled at and past k.
 __device__ __forceinline__ uint4 tail16(const uint8_t *rowp, int64_t kc, int64_t k)
@@ -125,9 +129,9 @@ struct StageLoader {
 #pragma unroll
         for (int i = 0; i < kInst; ++i) {
             const int blk = wave * kInst + i;
-            const int r = blk * kRowsPerInst + lane / 4;
+            const int r = blk * kRowsPerInst + lane / kChunks;
             ok[i] = row0 + r < rows;
-            off[i] = (uint32_t)((ok[i] ? (int64_t)r * ld : 0) + ((lane % 4) ^ swz(r)) * 16);
+            off[i] = (uint32_t)((ok[i] ? (int64_t)r * ld : 0) + ((lane % kChunks) ^ swz(r)) * 16);
             lds_off[i] = (uint32_t)(blk * kRowsPerInst * BK);
         }
     }
@@ -149,8 +153,8 @@ struct StageLoader {
     {
 #pragma unroll
         for (int i = 0; i < kInst; ++i) {
-            const int r = (wave * kInst + i) * kRowsPerInst + lane / 4;
-            const uint32_t kofs = ((lane % 4) ^ swz(r)) * 16;
+            const int r = (wave * kInst + i) * kRowsPerInst + lane / kChunks;
+            const uint32_t kofs = ((lane % kChunks) ^ swz(r)) * 16;
             const int64_t kc = k0 + kofs;                    // this lane's logical chunk start
             const uint8_t *rowp = base + (off[i] - kofs);
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -162,12 +166,12 @@ struct StageLoader {
 };
 
 // The 32 bytes lane (r, half) feeds an MFMA: logical chunks 2*half, 2*half+1 of row r.
-__device__ __forceinline__ v8i lds_frag(const uint8_t *tile, int r, int half)
+__device__ __forceinline__ v8i lds_frag(const uint8_t *tile, int r, int half, int sub)
 {
     const uint8_t *rp = tile + r * BK;
     const int s = swz(r);
-    const uint4 a = *reinterpret_cast<const uint4 *>(rp + ((2 * half) ^ s) * 16);
-    const uint4 b = *reinterpret_cast<const uint4 *>(rp + ((2 * half + 1) ^ s) * 16);
+    const uint4 a = *reinterpret_cast<const uint4 *>(rp + ((4 * sub + 2 * half) ^ s) * 16);
+    const uint4 b = *reinterpret_cast<const uint4 *>(rp + ((4 * sub + 2 * half + 1) ^ s) * 16);
     return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
@@ -236,17 +240,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     auto compute = [&](int64_t st) {
         const uint8_t *tx = lds + (int)(st % kStages) * kStageBytes;
         const uint8_t *tw = tx + kTileBytes;
-        v8i xf[TM];
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
-            xf[j] = lds_frag(tx, wm * WM + j * 32 + lr, lh);
-#pragma unroll
-        for (int i = 0; i < TN; ++i) {
-            const v8i wf = lds_frag(tw, wn * WN + i * 32 + lr, lh);
+        for (int sub = 0; sub < BK / 64; ++sub) {
+            v8i xf[TM];
 #pragma unroll
             for (int j = 0; j < TM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    wf, xf[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+                xf[j] = lds_frag(tx, wm * WM + j * 32 + lr, lh, sub);
+#pragma unroll
+            for (int i = 0; i < TN; ++i) {
+                const v8i wf = lds_frag(tw, wn * WN + i * 32 + lr, lh, sub);
+#pragma unroll
+                for (int j = 0; j < TM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        wf, xf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+            }
         }
     };
     auto issue_full = [&](int64_t st) {
