@@ -349,9 +349,12 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
         const auto p = fp8q::launch::plan_w8a16(m, n, k);
         if (p.kind == fp8q::launch::W8A16Plan::kRows)
             std::snprintf(buf, len,
-                          "k_w8a16_rows<%d, %d, %d, %d> rows=%d grid=(%lld,%lld) block=%d kchunk=%lld",
+                          "k_w8a16_rows<%d, %d, %d, %d> rows=%d grid=(%lld,%lld,%lld) block=%d "
+                          "kchunk=%lld splits=%lld%s",
                           p.af, p.mb, p.depth, p.waves, p.rows, (long long)p.grid_n,
-                          (long long)p.grid_m, 64 * p.waves, (long long)p.kchunk);
+                          (long long)p.grid_m, (long long)p.splits, 64 * p.waves,
+                          (long long)p.kchunk, (long long)p.splits,
+                          p.splits > 1 ? " + k_w8a16_reduce" : "");
         else
             std::snprintf(buf, len,
                           "k_w8a16_tile<%d, %d, %d> grid=(%lld,%lld) block=256 splits=%lld kper=%lld%s",

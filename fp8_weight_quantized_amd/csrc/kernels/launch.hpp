@@ -38,12 +38,13 @@ struct W8A16Plan {
     int waves;         // waves per workgroup; they split K
     int depth;         // 64-k steps of loads in flight per wave
     int64_t kchunk;    // K range per wave
-    // k_w8a16_tile (+ k_w8a16_reduce when splits > 1)
+    // k_w8a16_tile
     int xd;            // activation rows each of the 4 waves stages per chunk
     int steps;         // 64-k steps per staged chunk
     int64_t tiles_n;   // tiles of 64 weight rows
+    // both kernels (+ k_w8a16_reduce when splits > 1)
     int64_t splits;    // K splits across workgroups
-    int64_t kper;      // K range per split, a multiple of the chunk
+    int64_t kper;      // K range per split (a multiple of 64)
     int64_t ldp;       // row stride of the fp32 partial tiles (n rounded up to 4)
     size_t workspace;  // scratch bytes: the partial tiles [splits][m][ldp] (0 if no split)
 };

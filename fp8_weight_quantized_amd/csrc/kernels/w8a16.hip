@@ -136,7 +136,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
     const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
-    int rows, int64_t kchunk)
+    int rows, int64_t kchunk, int64_t kper, float *__restrict__ partial, int64_t ldp)
 {
     constexpr int L = AF + 2 * MB;    // loads per step
     __shared__ v4f red[NW][AF * MB][kWave];
@@ -147,8 +147,13 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
     const int g = lane >> 4;          // which 16 k-values of a 64-k step this lane holds
     const int64_t n0 = (int64_t)blockIdx.x * rows;
     const int64_t m0 = (int64_t)blockIdx.y * 16 * MB;
-    const int64_t kb = min(k, (int64_t)wave * kchunk);
-    const int64_t ke = min(k, kb + kchunk);
+    // grid.z splits K into ranges of kper (a multiple of 64); within the
+    // range the waves take kchunk each
+    const int split = (int)blockIdx.z;
+    const int64_t k_lo = (int64_t)split * kper;
+    const int64_t k_hi = min(k, k_lo + kper);
+    const int64_t kb = min(k_hi, k_lo + (int64_t)wave * kchunk);
+    const int64_t ke = min(k_hi, kb + kchunk);
 
     const uint8_t *wp[AF];
 #pragma unroll
@@ -264,6 +269,12 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
         v4f sum = red[0][f][sl];
         for (int wv = 1; wv < NW; ++wv)
             sum += red[wv][f][sl];
+        if (gridDim.z > 1) {
+            // K split across workgroups: partial[split][m][ldp] (ldp >= n
+            // rounded up to 4, so the 16 bytes fit); k_w8a16_reduce finishes
+            *reinterpret_cast<v4f *>(partial + ((int64_t)split * m + mr) * ldp + nb) = sum;
+            continue;
+        }
         uint16_t *yp = y + mr * ld_y + nb;
         const int valid = (int)min<int64_t>(min<int64_t>(4, rows - nl), n - nb);
         if (valid == 4) {
@@ -532,7 +543,32 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
     // activation rows go to the tile kernel (measured on MI355X across the
     // Llama-3 8B/70B decode shapes).
     const int64_t tiles = p.tiles_n * p.grid_m;
-    const bool tile = p.mb > 1 || tiles >= 256 || tiles <= 32 || k >= 16384;
+    const bool small_n_long_k = p.mb == 1 && tiles <= 32 && k >= 4096 && k < 16384;
+    const bool tile = !small_n_long_k && (p.mb > 1 || tiles >= 256 || tiles <= 32 || k >= 16384);
+    p.splits = 1;
+    p.ldp = div_up(n, 4) * 4;
+    if (small_n_long_k) {
+        // a small N on a long K (e.g. the k/v projections): 16-row
+        // workgroups, K split across workgroups towards 256 of them, each
+        // wave keeping at least 512 k (one pipelined span)
+        p.kind = W8A16Plan::kRows;
+        p.rows = 16;
+        p.af = 1;
+        p.grid_n = div_up(n, 16);
+        p.waves = 4;
+        p.depth = rows_depth(p.af, p.mb);
+        const int64_t span = 64 * p.depth * p.waves;        // one span per wave
+        int64_t s = 256 / (p.grid_n * p.grid_m);
+        const int64_t s_max = k / span;
+        s = s > s_max ? s_max : s;
+        s = s < 1 ? 1 : s;
+        p.kper = div_up(div_up(k, s), span) * span;
+        p.splits = div_up(k, p.kper);
+        p.kchunk = p.kper / p.waves;
+        if (p.splits > 1)
+            p.workspace = (size_t)p.splits * m * p.ldp * sizeof(float);
+        return p;
+    }
     if (!tile) {
         p.kind = W8A16Plan::kRows;
         // rows per block: the most rows (up to 32) that still leave >= 256 blocks
@@ -549,12 +585,13 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
         const int64_t per = div_up(k, p.waves);
         const int64_t span = 64 * p.depth;
         p.kchunk = per >= span ? div_up(per, span) * span : div_up(per, 64) * 64;
+        p.kper = p.kchunk * p.waves;
         return p;
     }
     p.kind = W8A16Plan::kTile;
     if (p.mb == 1) {
         // stage only the activation rows that exist: 4, 8 or 16 of the 16
-        p.xd = m <= 4 ? 1 : (m <= 8 ? 2 : 4);
+        p.xd = (int)div_up(m, kTileWaves);   // stage only the rows that exist
         p.steps = (k >= 16384 || tiles >= 256) ? 16 : 8;
     } else {
         p.xd = 4 * p.mb;
@@ -569,7 +606,6 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
     s = s < 1 ? 1 : s;
     p.kper = div_up(div_up(k, s), chunk) * chunk;
     p.splits = div_up(k, p.kper);
-    p.ldp = div_up(n, 4) * 4;
     if (p.splits > 1)
         p.workspace = (size_t)p.splits * m * p.ldp * sizeof(float);
     p.grid_n = p.tiles_n * p.splits;
@@ -579,11 +615,17 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
 template <int AF, int MB, int P, int NW>
 static void launch_rows(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
                         const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                        uint16_t *y, int64_t ld_y, hipStream_t stream)
+                        uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream)
 {
-    const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
+    float *partial = static_cast<float *>(workspace);
+    const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m, (unsigned)p.splits);
     hipLaunchKernelGGL((k_w8a16_rows<AF, MB, P, NW>), grid, dim3(NW * kWave), 0, stream, x, m, k,
-                       ld_x, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk);
+                       ld_x, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk, p.kper, partial, p.ldp);
+    if (p.splits > 1) {
+        const int64_t slots = m * (p.ldp / 4);
+        hipLaunchKernelGGL(k_w8a16_reduce, dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
+                           partial, m, n, p.ldp, (int)p.splits, w_scale, y, ld_y);
+    }
 }
 
 template <int MB, int XD, int T>
@@ -609,7 +651,8 @@ hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, in
     if (p.kind == W8A16Plan::kRows) {
 #define FP8Q_ROWS_CASE(AF, MB, P, NW)                                                         \
         if (p.af == AF && p.mb == MB && p.depth == P && p.waves == NW) {                      \
-            launch_rows<AF, MB, P, NW>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, stream); \
+            launch_rows<AF, MB, P, NW>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, workspace, \
+                                       stream);                                           \
             return hipGetLastError();                                                         \
         }
         FP8Q_ROWS_CASE(2, 1, 8, 4)
@@ -624,9 +667,11 @@ hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, in
         }
         FP8Q_TILE_CASE(1, 1, 8)
         FP8Q_TILE_CASE(1, 2, 8)
+        FP8Q_TILE_CASE(1, 3, 8)
         FP8Q_TILE_CASE(1, 4, 8)
         FP8Q_TILE_CASE(1, 1, 16)
         FP8Q_TILE_CASE(1, 2, 16)
+        FP8Q_TILE_CASE(1, 3, 16)
         FP8Q_TILE_CASE(1, 4, 16)
         FP8Q_TILE_CASE(2, 8, 8)
         FP8Q_TILE_CASE(3, 12, 8)

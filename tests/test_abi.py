@@ -62,8 +62,10 @@ def test_workspace_queries(L):
     # with fp32 partial tiles [splits][m][n rounded up to 4]
     #   M=64, N=K=4096: 64 tiles -> 4 splits of 1024
     assert L.fp8q_linear_workspace_size(0, 64, 4096, 4096) == 4 * 64 * 4096 * 4
-    #   M=12, N=1022 (16 tiles), K=8192: 8 splits of 1024; rows padded to 1024
-    assert L.fp8q_linear_workspace_size(0, 12, 1022, 8192) == 8 * 12 * 1024 * 4
+    #   a small N on a long K (k/v projections): 16-row workgroups, K split in
+    #   ranges of 2048 (4 waves x 512): N=1022, K=8192 -> 64 x 4 workgroups,
+    #   partial rows padded to 1024
+    assert L.fp8q_linear_workspace_size(0, 12, 1022, 8192) == 4 * 12 * 1024 * 4
     #   M=12, N=8192, K=28672 (16-step chunks of 1024): 2 splits
     assert L.fp8q_linear_workspace_size(0, 12, 8192, 28672) == 2 * 12 * 8192 * 4
     #   M=40, N=100, K=3000: 2 tiles, at most 2 splits of whole 512-k chunks

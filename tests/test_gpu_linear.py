@@ -63,14 +63,17 @@ def all_codes_weight(n: int, k: int) -> np.ndarray:
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 64), (1, 256, 64), (64, 272, 64), (12, 256, 64),
                                    (1, 272, 576), (7, 300, 1100), (16, 256, 2048), (40, 320, 1536),
-                                   (64, 272, 1600), (5, 4096, 1100), (1, 2304, 640)])
+                                   (64, 272, 1600), (5, 4096, 1100), (1, 2304, 640),
+                                   (16, 512, 4160), (2, 300, 8200)])
 def test_w8a16_exact_every_code(fq, orc, m, n, k):
     """X = one-hot rows: Y[i, j] = dec(W[j, p_i]) exactly, for all 254 finite codes.
-    The one-hot positions p_i are spread over K, so with K > 512 they land in
-    different staged chunks, steps and K splits."""
+    The one-hot positions p_i are spread evenly over K (first to last), so
+    with K > 512 they land in different staged chunks, steps, K splits and
+    the ragged end of K."""
     wq = all_codes_weight(n, k)
     x = np.zeros((m, k), np.uint16)
-    x[np.arange(m), (np.arange(m) * 37 + 5) % k] = 0x3F80          # 1.0
+    pos = (np.arange(m) * (k - 1)) // max(m - 1, 1)
+    x[np.arange(m), pos] = 0x3F80          # 1.0
     ws = np.ones(n, np.float32)
     say("w8a16 exact", m, n, k, fq.describe_linear(0, m, n, k))
     y = run_w8a16(fq, x, wq, ws)
@@ -103,7 +106,8 @@ def test_tiny(fq, orc):
 
 RAGGED = [(3, 100, 1000), (17, 130, 520), (65, 64, 64), (100, 96, 4104), (1, 16, 8),
           (5, 1, 40), (2, 4096, 4096), (64, 1024, 8192), (33, 77, 13), (129, 200, 96),
-          (7, 300, 2048), (13, 63, 1536), (40, 522, 3000), (6, 1, 700)]
+          (7, 300, 2048), (13, 63, 1536), (40, 522, 3000), (6, 1, 700),
+          (5, 300, 5000), (12, 1022, 8192), (1, 100, 4096), (16, 64, 12288)]
 
 
 @pytest.mark.parametrize("m,n,k", RAGGED)
