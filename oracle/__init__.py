@@ -36,6 +36,7 @@ _lib = None
 
 MODE_W8A16 = 0
 MODE_W8A8 = 1
+MODE_W8A16_F16 = 2
 
 
 def build(force: bool = False) -> str:
@@ -58,6 +59,8 @@ def _load():
             lib.oracle_abi_version.restype = ctypes.c_int
             lib.oracle_e4m3_value.restype = ctypes.c_double
             lib.oracle_e4m3_value.argtypes = [ctypes.c_uint]
+            lib.oracle_f16_value.restype = ctypes.c_double
+            lib.oracle_f16_value.argtypes = [ctypes.c_uint]
             lib.oracle_e4m3_table.argtypes = [P]
             lib.oracle_cast_e4m3.restype = ctypes.c_uint
             lib.oracle_cast_e4m3.argtypes = [ctypes.c_float]
@@ -156,17 +159,23 @@ def quantize_act(x_bf16: np.ndarray):
 
 
 # ---------------------------------------------------------------- linear ----
+def f16_value(bits: int) -> float:
+    """IEEE binary16 value of a 16-bit pattern, decoded from its bit fields."""
+    return _load().oracle_f16_value(int(bits) & 0xFFFF)
+
+
 def linear(mode: int, x: np.ndarray, wq: np.ndarray, w_scale: np.ndarray,
            x_scale: float | None = None, rows: np.ndarray | None = None) -> np.ndarray:
     """fp64 Y = X . dequant(Wq)^T for the selected rows of X.
 
     mode 0 (fp8_w_bf16_a): x is bf16 bits uint16 [M, K], x_scale must be None.
     mode 1 (fp8_w_fp8_a):  x is E4M3 codes uint8 [M, K], x_scale is the fp32 scale.
+    mode 2 (fp8_w_fp16_a): x is fp16 bits uint16 [M, K], x_scale must be None.
     """
-    if mode == MODE_W8A16:
+    if mode in (MODE_W8A16, MODE_W8A16_F16):
         _need(x, np.uint16, "x")
         if x_scale is not None:
-            raise ValueError("fp8_w_bf16_a takes no activation scale")
+            raise ValueError("the 16-bit activation modes take no activation scale")
         xs = 0.0
     elif mode == MODE_W8A8:
         _need(x, np.uint8, "x")

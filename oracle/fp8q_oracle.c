@@ -265,11 +265,33 @@ int oracle_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
 }
 
 /* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16 (fp16) decode, from the bit fields: 1 sign bit, 5      */
+/* exponent bits with bias 15, 10 mantissa bits; exponent 0 is subnormal    */
+/* (m * 2^-24), exponent 31 is infinity (m = 0) or NaN.                      */
+/* ------------------------------------------------------------------------ */
+double oracle_f16_value(unsigned bits)
+{
+    unsigned s = (bits >> 15) & 1u;
+    unsigned e = (bits >> 10) & 31u;
+    unsigned m = bits & 1023u;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -24);
+    else
+        v = ldexp(1.0 + (double)m / 1024.0, (int)e - 15);
+    return s ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
 /* The scaled linear layer, in fp64.                                         */
-/* [P1 §3.1 step 3] two of the FP8 MatMul modes:                             */
-/*   mode 0, fp8_w_bf16_a:  Y[m,n] = s_w[n] * sum_k X[m,k] * dec(Wq[n,k])     */
+/* [P1 §3.1 step 3] the three FP8 MatMul modes:                              */
+/*   mode 0, fp8_w_bf16_a:  Y[m,n] = s_w[n] * sum_k X[m,k] * dec(Wq[n,k]),   */
+/*                          X bf16                                            */
 /*   mode 1, fp8_w_fp8_a:   Y[m,n] = s_x * s_w[n] * sum_k dec(Xq[m,k]) *      */
 /*                                   dec(Wq[n,k])                            */
+/*   mode 2, fp8_w_fp16_a:  mode 0 with X in fp16                            */
 /* The weight follows the [out, in] layout of a linear layer, so Y = X W^T.   */
 /* Every term is widened to double and summed in increasing k.  For mode 1    */
 /* every product is a multiple of 2^-18 below 2^17, so the double sum is      */
@@ -296,6 +318,11 @@ void oracle_linear(int mode, const void *x, int64_t m, int64_t k, int64_t ld_x,
                 const uint16_t *xrow = (const uint16_t *)x + r * ld_x;
                 for (int64_t c = 0; c < k; ++c)
                     acc += (double)bf16_value(xrow[c]) * tab[wrow[c]];
+                y[i * n + j] = acc * (double)w_scale[j];
+            } else if (mode == 2) {
+                const uint16_t *xrow = (const uint16_t *)x + r * ld_x;
+                for (int64_t c = 0; c < k; ++c)
+                    acc += oracle_f16_value(xrow[c]) * tab[wrow[c]];
                 y[i * n + j] = acc * (double)w_scale[j];
             } else {
                 const uint8_t *xrow = (const uint8_t *)x + r * ld_x;

@@ -75,3 +75,20 @@ def test_matches_torch_decoder(table):
     assert (ref[~nan] == table[~nan]).all()
     # signed zero
     assert math.copysign(1.0, ref[0x80]) == math.copysign(1.0, table[0x80])
+
+
+def test_f16_decode_every_pattern(orc):
+    """IEEE binary16 decode (the fp8_w_fp16_a activations) against numpy's
+    float16 on all 65536 bit patterns, plus the landmarks of the format."""
+    import numpy as np
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([orc.f16_value(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert orc.f16_value(0x3C00) == 1.0
+    assert orc.f16_value(0x7BFF) == 65504.0
+    assert orc.f16_value(0x0001) == 2.0 ** -24
+    assert orc.f16_value(0x0400) == 2.0 ** -14
+    assert orc.f16_value(0x8000) == 0.0 and np.signbit(orc.f16_value(0x8000))

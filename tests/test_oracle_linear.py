@@ -1,8 +1,8 @@
 """Pins for the oracle's scaled linear layer (fp64).
 
-The two FP8 MatMul modes of Llama 3 精读 §3.1 step 3 -- fp8_w_bf16_a and
-fp8_w_fp8_a -- with the per-channel weight scale and per-tensor activation
-scale of FP8量化与长上下文实测 §1.2.  The weight keeps the [out, in] layout of
+The three FP8 MatMul modes of Llama 3 精读 §3.1 step 3 -- fp8_w_bf16_a,
+fp8_w_fp8_a and fp8_w_fp16_a -- with the per-channel weight scale and
+per-tensor activation scale of FP8量化与长上下文实测 §1.2.  The weight keeps the [out, in] layout of
 a linear layer, so Y = X W^T.
 
 Pins: exact rational brute force (fractions.Fraction, decoding codes with
@@ -32,6 +32,8 @@ def exact_linear(mode, x, wq, w_scale, x_scale=None):
     wd = torch_decode(wq)
     if mode == 0:
         xd = workloads.bf16_bits_to_f32(x).astype(np.float64)
+    elif mode == 2:
+        xd = np.ascontiguousarray(x, dtype=np.uint16).view(np.float16).astype(np.float64)
     else:
         xd = torch_decode(x)
     y = [[None] * n for _ in range(m)]
@@ -81,6 +83,40 @@ def test_w8a16_brute_force(orc, m, n, k, seed):
         for j in range(n):
             mag = float(np.dot(xd[i], wd[j])) * float(ws[j])
             assert abs(Fraction(got[i, j]) - ref[i][j]) <= Fraction(k + 2) * Fraction(2.0 ** -53) * Fraction(mag) + Fraction(0)
+
+
+def f16_bits(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(3, 5, 7, 0), (2, 6, 8, 4), (5, 3, 2, 5), (1, 4, 9, 6)])
+def test_w8a16_f16_brute_force(orc, m, n, k, seed):
+    """fp8_w_fp16_a: activations decoded by numpy's float16, not the oracle."""
+    rng = np.random.default_rng(seed)
+    x = f16_bits(rng.standard_normal((m, k)) * 3.0)
+    x[0, 0] = 0x0001                       # a subnormal (2^-24)
+    wq = random_codes(rng, (n, k))
+    ws = rng.random(n).astype(np.float32) + np.float32(0.01)
+    got = orc.linear(2, x, wq, ws)
+    ref = exact_linear(2, x, wq, ws)
+    xd = np.abs(x.view(np.float16).astype(np.float64))
+    wd = np.abs(torch_decode(wq))
+    for i in range(m):
+        for j in range(n):
+            mag = float(np.dot(xd[i], wd[j])) * float(ws[j])
+            assert abs(Fraction(got[i, j]) - ref[i][j]) <= Fraction(k + 2) * Fraction(2.0 ** -53) * Fraction(mag)
+
+
+def test_modes_read_activation_bits_differently(orc):
+    """The same 16-bit pattern 0x3C00 is 1.0 in fp16 and 2^-7 in bf16: a
+    one-hot X picks one weight column, scaled accordingly."""
+    wq = random_codes(np.random.default_rng(9), (5, 6))
+    ws = np.ones(5, np.float32)
+    x = np.zeros((1, 6), np.uint16)
+    x[0, 4] = 0x3C00
+    col = torch_decode(wq)[:, 4]
+    assert np.array_equal(orc.linear(2, x, wq, ws)[0], col)
+    assert np.array_equal(orc.linear(0, x, wq, ws)[0], col * 2.0 ** -7)
 
 
 def test_row_sums_closed_form(orc):
