@@ -213,7 +213,41 @@ def main() -> int:
 
     # --------------------------------------------------------------- other rows
     if not args.quick:
-        result["rows"] = other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev)
+        rows = {}
+        # fp8_w_fp16_a on the same decode step: fp16 copies of the activations
+        xs16 = {m: xs[m].to(torch.float16) for m in DECODE_MS}
+        ys16 = {m: torch.empty((m, N), dtype=torch.float16, device=dev) for m in DECODE_MS}
+
+        def decode_step_f16(i: int, stream: int):
+            for j, m in enumerate(DECODE_MS):
+                c = (len(DECODE_MS) * i + j) % copies_n
+                st = L.fp8q_linear(2, ptr(xs16[m]), m, K, K, None, ptr(pool[c]), N, K, ptr(w_scale),
+                                   ptr(ys16[m]), N, ptr(wsp[m]), wsn[m], stream)
+                if st != 0:
+                    raise RuntimeError(_lib.last_error())
+        g16 = torch.cuda.CUDAGraph()
+        s16 = torch.cuda.Stream(device=dev)
+        s16.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.graph(g16, stream=s16, capture_error_mode="relaxed"):
+            h = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(rot):
+                decode_step_f16(i, h)
+        torch.cuda.current_stream(dev).wait_stream(s16)
+        g16.replay()
+        torch.cuda.synchronize()
+        start.record()
+        g16.replay()
+        end.record()
+        end.synchronize()
+        us16 = start.elapsed_time(end) * 1e3 / rot
+        rows["f1_w8a16_f16_q_proj_decode"] = {
+            "shape": "N=K=4096, M=1,8,32,64 per step", "us_per_step": round(us16, 3),
+            "GB/s": round(step_bytes / (us16 * 1e-6) / 1e9, 1),
+            "frac_hbm": round(step_bytes / (us16 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "mode": "fp8_w_fp16_a (fp16 activations and output)"}
+        log(rows["f1_w8a16_f16_q_proj_decode"])
+        rows.update(other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev))
+        result["rows"] = rows
 
     if args.copy_calibration:
         # a plain elementwise copy of known size (1 GiB read + 1 GiB written) whose

@@ -21,7 +21,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import FP8Q_W8A8, FP8Q_W8A16, Fp8qError, check
+from ._lib import FP8Q_W8A8, FP8Q_W8A16, FP8Q_W8A16_F16, Fp8qError, check
 
 __all__ = [
     "quantize_weight", "quantize_act", "linear", "cast_f32_to_e4m3", "describe_linear",
@@ -105,24 +105,25 @@ def quantize_act(x: torch.Tensor, nonfinite_flag: torch.Tensor | None = None):
 
 def linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
            x_scale: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = X . dequant(Wq)^T in bf16.
+    """Y = X . dequant(Wq)^T.
 
-    x bf16 [M, K] with x_scale None  -> fp8_w_bf16_a (W8A16, decode).
-    x E4M3 codes [M, K] with x_scale -> fp8_w_fp8_a  (W8A8, prefill).
+    x bf16 [M, K] with x_scale None  -> fp8_w_bf16_a (W8A16), bf16 Y.
+    x fp16 [M, K] with x_scale None  -> fp8_w_fp16_a (W8A16, fp16), fp16 Y.
+    x E4M3 codes [M, K] with x_scale -> fp8_w_fp8_a  (W8A8), bf16 Y.
     """
     wq = _codes(wq)
     x = _codes(x)
-    if x.dtype == torch.bfloat16:
-        mode = FP8Q_W8A16
+    if x.dtype in (torch.bfloat16, torch.float16):
+        mode = FP8Q_W8A16 if x.dtype == torch.bfloat16 else FP8Q_W8A16_F16
         if x_scale is not None:
-            raise ValueError("a bf16 activation takes no x_scale (fp8_w_bf16_a)")
+            raise ValueError("a 16-bit activation takes no x_scale (fp8_w_bf16_a / fp8_w_fp16_a)")
     elif x.dtype == torch.uint8:
         mode = FP8Q_W8A8
         if x_scale is None:
             raise ValueError("E4M3 activations need x_scale (fp8_w_fp8_a)")
     else:
-        raise TypeError(f"x must be bf16 or E4M3 codes, got {x.dtype}")
-    m, k, ldx = _matrix(x, "x", (torch.bfloat16, torch.uint8))
+        raise TypeError(f"x must be bf16, fp16 or E4M3 codes, got {x.dtype}")
+    m, k, ldx = _matrix(x, "x", (torch.bfloat16, torch.float16, torch.uint8))
     n, k2, ldw = _matrix(wq, "wq", (torch.uint8,))
     if k2 != k:
         raise ValueError(f"inner dimensions differ: x has K={k}, wq has K={k2}")
@@ -134,9 +135,10 @@ def linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
     if x_scale is not None and (x_scale.dtype != torch.float32 or x_scale.numel() != 1 or not x_scale.is_cuda):
         raise ValueError("x_scale must be a float32 GPU tensor with one element")
     dev = x.device
+    ydt = torch.float16 if mode == FP8Q_W8A16_F16 else torch.bfloat16
     if out is None:
-        out = torch.empty((m, _round_up(max(n, 1), 8)), dtype=torch.bfloat16, device=dev)[:, :n]
-    om, on, ldy = _matrix(out, "out", (torch.bfloat16,))
+        out = torch.empty((m, _round_up(max(n, 1), 8)), dtype=ydt, device=dev)[:, :n]
+    om, on, ldy = _matrix(out, "out", (ydt,))
     if (om, on) != (m, n):
         raise ValueError(f"out must be [{m}, {n}]")
     L = _lib.lib()

@@ -24,6 +24,7 @@ FP8Q_ERR_WORKSPACE = 4
 
 FP8Q_W8A16 = 0
 FP8Q_W8A8 = 1
+FP8Q_W8A16_F16 = 2
 
 _lock = threading.Lock()
 _lib = None

@@ -248,7 +248,7 @@ size_t fp8q_linear_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t 
 {
     if (m <= 0 || n <= 0 || k < 1)
         return 0;
-    if (mode == FP8Q_W8A16)
+    if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16)
         return round_up(fp8q::launch::plan_w8a16(m, n, k).workspace, 256);
     if (mode == FP8Q_W8A8)
         return round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
@@ -261,25 +261,27 @@ fp8q_status fp8q_linear(fp8q_mode mode,
                         uint16_t *y_bf16, int64_t ld_y,
                         void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    if (mode != FP8Q_W8A16 && mode != FP8Q_W8A8)
+    if (mode != FP8Q_W8A16 && mode != FP8Q_W8A8 && mode != FP8Q_W8A16_F16)
         return fail(FP8Q_ERR_INVALID_ARG, "unknown mode %d", (int)mode);
+    const bool a16 = mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16;   // 16-bit activations
     if (m < 0 || n < 0 || k < 1)
         return fail(FP8Q_ERR_INVALID_ARG, "need m >= 0, n >= 0, k >= 1 (m=%lld, n=%lld, k=%lld)",
                     (long long)m, (long long)n, (long long)k);
-    if (mode == FP8Q_W8A16 && x_scale != nullptr)
-        return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_bf16_a takes no activation scale (x_scale must be NULL)");
+    if (a16 && x_scale != nullptr)
+        return fail(FP8Q_ERR_INVALID_ARG,
+                    "fp8_w_bf16_a and fp8_w_fp16_a take no activation scale (x_scale must be NULL)");
     if (mode == FP8Q_W8A8 && x_scale == nullptr)
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_fp8_a needs the activation scale (x_scale is NULL)");
-    const size_t xelem = mode == FP8Q_W8A16 ? 2 : 1;
-    FP8Q_TRY(check_ld(ld_x, k, mode == FP8Q_W8A16 ? 8 : 16, "ld_x"));
+    const size_t xelem = a16 ? 2 : 1;
+    FP8Q_TRY(check_ld(ld_x, k, a16 ? 8 : 16, "ld_x"));
     FP8Q_TRY(check_ld(ld_w, k, 16, "ld_w"));
     FP8Q_TRY(check_ld(ld_y, n, 8, "ld_y"));
     if (mode == FP8Q_W8A8 &&
         (!fp8q::launch::w8a8_supports_ld(ld_x) || !fp8q::launch::w8a8_supports_ld(ld_w)))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_fp8_a needs ld_x and ld_w below 2^23 (got %lld, %lld)",
                     (long long)ld_x, (long long)ld_w);
-    if (mode == FP8Q_W8A16 && (m + 63) / 64 > 65535)
-        return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_bf16_a takes at most 65535 * 64 activation rows");
+    if (a16 && (m + 63) / 64 > 65535)
+        return fail(FP8Q_ERR_INVALID_ARG, "the 16-bit activation modes take at most 65535 * 64 rows");
     if (m == 0 || n == 0)
         return ok();
     const size_t need = fp8q_linear_workspace_size(mode, m, n, k);
@@ -306,9 +308,10 @@ fp8q_status fp8q_linear(fp8q_mode mode,
         return fail(FP8Q_ERR_INVALID_ARG, "the output or workspace overlaps an input");
 
     hipError_t e;
-    if (mode == FP8Q_W8A16) {
+    if (a16) {
         const auto plan = fp8q::launch::plan_w8a16(m, n, k);
-        e = fp8q::launch::w8a16(plan, static_cast<const uint16_t *>(x), m, k, ld_x, w_fp8, n,
+        e = fp8q::launch::w8a16(plan, mode == FP8Q_W8A16_F16, static_cast<const uint16_t *>(x), m,
+                                k, ld_x, w_fp8, n,
                                 ld_w, w_scale, y_bf16, ld_y, workspace, stream);
     } else {
         const auto plan = fp8q::launch::plan_w8a8(m, n, k);
@@ -345,7 +348,7 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
         return fail(FP8Q_ERR_INVALID_ARG, "buf is NULL or empty");
     if (m < 0 || n < 0 || k < 1)
         return fail(FP8Q_ERR_INVALID_ARG, "bad sizes");
-    if (mode == FP8Q_W8A16) {
+    if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16) {
         const auto p = fp8q::launch::plan_w8a16(m, n, k);
         if (p.kind == fp8q::launch::W8A16Plan::kRows)
             std::snprintf(buf, len,

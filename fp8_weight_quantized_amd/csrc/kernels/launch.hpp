@@ -49,8 +49,9 @@ struct W8A16Plan {
     size_t workspace;  // scratch bytes: the partial tiles [splits][m][ldp] (0 if no split)
 };
 W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k);
-hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
-                 const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
+// f16_act: the activations and the output are fp16 (fp8_w_fp16_a), else bf16.
+hipError_t w8a16(const W8A16Plan &p, bool f16_act, const uint16_t *x, int64_t m, int64_t k,
+                 int64_t ld_x, const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
                  uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream);
 
 // ---- W8A8 (fp8_w_fp8_a) GEMM on FP8 MFMA -----------------------------------

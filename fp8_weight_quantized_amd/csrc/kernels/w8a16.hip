@@ -45,8 +45,6 @@ using namespace dev;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 
-__device__ __forceinline__ v8bf as_v8bf(v4u v) { return __builtin_bit_cast(v8bf, v); }
-
 __device__ __forceinline__ v4u ldg_nt(const uint8_t *p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
@@ -95,31 +93,79 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// The 16-bit activation types of the write-up's modes (§3.1 step 3):
+// fp8_w_bf16_a and fp8_w_fp16_a.  Each gives the MFMA operand type, the
+// exact widening of four E4M3 codes to it, the 16x16x32 MFMA and the RNE
+// conversion of an fp32 output to the same 16-bit type.
+enum { kActBF16 = 0, kActF16 = 1 };
+template <int AT> struct Act;
+
+template <> struct Act<kActBF16> {
+    typedef v8bf frag;
+    static __device__ __forceinline__ frag cast(v4u v) { return __builtin_bit_cast(v8bf, v); }
+    static __device__ __forceinline__ uint2 widen4(uint32_t codes) { return e4m3x4_to_bf16(codes); }
+    static __device__ __forceinline__ v4f mfma(frag a, frag b, v4f c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+    static __device__ __forceinline__ uint16_t one(float v) { return (uint16_t)f32_to_bf16_rne(v); }
+};
+
+template <> struct Act<kActF16> {
+    typedef v8h frag;
+    static __device__ __forceinline__ frag cast(v4u v) { return __builtin_bit_cast(v8h, v); }
+    // Four E4M3 codes -> four fp16 values (exact: E4M3 spans 2^-9 .. 448).
+    static __device__ __forceinline__ uint2 widen4(uint32_t codes)
+    {
+        const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)codes, 1.0f, false);
+        const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)codes, 1.0f, true);
+        uint2 r;
+        r.x = __builtin_bit_cast(uint32_t, lo);
+        r.y = __builtin_bit_cast(uint32_t, hi);
+        return r;
+    }
+    static __device__ __forceinline__ v4f mfma(frag a, frag b, v4f c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    // fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default mode)
+    static __device__ __forceinline__ uint16_t one(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi)
+    {
+        return (uint32_t)one(lo) | ((uint32_t)one(hi) << 16);
+    }
+};
+
 // Widen a lane's 16 weight codes into the A operands of two MFMA k-steps.
-__device__ __forceinline__ void widen(v4u wv, v8bf &a0, v8bf &a1)
+template <int AT>
+__device__ __forceinline__ void widen(v4u wv, typename Act<AT>::frag &a0, typename Act<AT>::frag &a1)
 {
-    uint2 p0 = e4m3x4_to_bf16(wv.x), p1 = e4m3x4_to_bf16(wv.y);
-    uint2 p2 = e4m3x4_to_bf16(wv.z), p3 = e4m3x4_to_bf16(wv.w);
-    a0 = as_v8bf(v4u{p0.x, p0.y, p1.x, p1.y});
-    a1 = as_v8bf(v4u{p2.x, p2.y, p3.x, p3.y});
+    uint2 p0 = Act<AT>::widen4(wv.x), p1 = Act<AT>::widen4(wv.y);
+    uint2 p2 = Act<AT>::widen4(wv.z), p3 = Act<AT>::widen4(wv.w);
+    a0 = Act<AT>::cast(v4u{p0.x, p0.y, p1.x, p1.y});
+    a1 = Act<AT>::cast(v4u{p2.x, p2.y, p3.x, p3.y});
 }
 
 // One 64-k step of a wave: widen the weight codes and issue the MFMAs.
 // Rows past N (weights) or past M (activations) were clamped to a valid row
 // when loading; they only feed output rows/columns that are never stored, so
 // no masking is needed here.
-template <int AF, int MB>
+template <int AF, int MB, int AT>
 __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[MB][2],
                                           v4f (&acc)[AF][MB])
 {
 #pragma unroll
     for (int a = 0; a < AF; ++a) {
-        v8bf a0, a1;
-        widen(wv[a], a0, a1);
+        typename Act<AT>::frag a0, a1;
+        widen<AT>(wv[a], a0, a1);
 #pragma unroll
         for (int j = 0; j < MB; ++j) {
-            acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_v8bf(xv[j][0]), acc[a][j], 0, 0, 0);
-            acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_v8bf(xv[j][1]), acc[a][j], 0, 0, 0);
+            acc[a][j] = Act<AT>::mfma(a0, Act<AT>::cast(xv[j][0]), acc[a][j]);
+            acc[a][j] = Act<AT>::mfma(a1, Act<AT>::cast(xv[j][1]), acc[a][j]);
         }
     }
 }
@@ -131,7 +177,7 @@ __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[M
 //     MFMAs run.  The pipelined span of a wave is a multiple of P steps; the
 //     remaining steps (and a partial step at the end of K) run one by one.
 // NW: waves per workgroup; wave w owns K range [w*kchunk, (w+1)*kchunk).
-template <int AF, int MB, int P, int NW>
+template <int AF, int MB, int P, int NW, int AT>
 __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
     const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
@@ -206,7 +252,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
                 // flight, step u's loads have landed
                 wait_vmcnt<(P - 1) * L>();
                 __builtin_amdgcn_sched_barrier(0);
-                step_mfma<AF, MB>(wb[u], xb[u], acc[u & 1]);
+                step_mfma<AF, MB, AT>(wb[u], xb[u], acc[u & 1]);
                 issue(u, kk + 64 * (P + u));
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -216,7 +262,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
             constexpr int u = decltype(uc)::value;
             wait_vmcnt<(P - 1 - u) * L>();
             __builtin_amdgcn_sched_barrier(0);
-            step_mfma<AF, MB>(wb[u], xb[u], acc[u & 1]);
+            step_mfma<AF, MB, AT>(wb[u], xb[u], acc[u & 1]);
         });
         kk = kend;
     }
@@ -244,7 +290,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
                 xv[j][1] = kw + 8 < k ? load_x8_tail(xp[j] - 16 * g, kw + 8, k) : v4u{0u, 0u, 0u, 0u};
             }
         }
-        step_mfma<AF, MB>(wv, xv, acc[0]);
+        step_mfma<AF, MB, AT>(wv, xv, acc[0]);
     }
 
     // ---- sum the waves' partial tiles in wave order, then scale and store --
@@ -279,12 +325,12 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
         const int valid = (int)min<int64_t>(min<int64_t>(4, rows - nl), n - nb);
         if (valid == 4) {
             uint2 o;
-            o.x = pack_bf16x2(sum[0] * w_scale[nb], sum[1] * w_scale[nb + 1]);
-            o.y = pack_bf16x2(sum[2] * w_scale[nb + 2], sum[3] * w_scale[nb + 3]);
+            o.x = Act<AT>::pack2(sum[0] * w_scale[nb], sum[1] * w_scale[nb + 1]);
+            o.y = Act<AT>::pack2(sum[2] * w_scale[nb + 2], sum[3] * w_scale[nb + 3]);
             *reinterpret_cast<uint2 *>(yp) = o;
         } else {
             for (int v = 0; v < valid; ++v)
-                yp[v] = (uint16_t)f32_to_bf16_rne(sum[v] * w_scale[nb + v]);
+                yp[v] = Act<AT>::one(sum[v] * w_scale[nb + v]);
         }
     }
 }
@@ -308,6 +354,7 @@ __device__ __forceinline__ void lds_barrier()
 
 // Scale 4 consecutive outputs of row mr and store them as bf16 (8 bytes when
 // all 4 columns exist; the pointer is then 8-byte aligned).
+template <int AT>
 __device__ __forceinline__ void store_y4(uint16_t *__restrict__ y, int64_t ld_y,
                                          const float *__restrict__ w_scale, int64_t mr,
                                          int64_t nb, int64_t n, v4f s)
@@ -315,12 +362,12 @@ __device__ __forceinline__ void store_y4(uint16_t *__restrict__ y, int64_t ld_y,
     uint16_t *yp = y + mr * ld_y + nb;
     if (nb + 4 <= n) {
         uint2 o;
-        o.x = pack_bf16x2(s[0] * w_scale[nb], s[1] * w_scale[nb + 1]);
-        o.y = pack_bf16x2(s[2] * w_scale[nb + 2], s[3] * w_scale[nb + 3]);
+        o.x = Act<AT>::pack2(s[0] * w_scale[nb], s[1] * w_scale[nb + 1]);
+        o.y = Act<AT>::pack2(s[2] * w_scale[nb + 2], s[3] * w_scale[nb + 3]);
         *reinterpret_cast<uint2 *>(yp) = o;
     } else {
         for (int v = 0; v < (int)(n - nb); ++v)
-            yp[v] = (uint16_t)f32_to_bf16_rne(s[v] * w_scale[nb + v]);
+            yp[v] = Act<AT>::one(s[v] * w_scale[nb + v]);
     }
 }
 
@@ -331,7 +378,7 @@ __device__ __forceinline__ void store_y4(uint16_t *__restrict__ y, int64_t ld_y,
 // T:  64-k steps per chunk; a chunk's weights are loaded one chunk ahead.
 // Grid: x = tiles of 64 weight rows times K splits (split index fastest),
 // y = groups of 16*MB activation rows.
-template <int MB, int XD, int T>
+template <int MB, int XD, int T, int AT>
 __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
     const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
@@ -399,15 +446,15 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
                     *reinterpret_cast<v4u *>(base + xs_off(wave + kTileWaves * i, 64 * h + lane)) = xr[i][h];
         };
         auto compute = [&](int u, int buf, v4f(&a)[MB]) {
-            v8bf a0, a1;
-            widen(wr[u], a0, a1);
+            typename Act<AT>::frag a0, a1;
+            widen<AT>(wr[u], a0, a1);
             const uint8_t *base = xs + buf * (XR * RB);
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
                 const v4u b0 = *reinterpret_cast<const v4u *>(base + xs_off(16 * j + r, 8 * u + 2 * g));
                 const v4u b1 = *reinterpret_cast<const v4u *>(base + xs_off(16 * j + r, 8 * u + 2 * g + 1));
-                a[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_v8bf(b0), a[j], 0, 0, 0);
-                a[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_v8bf(b1), a[j], 0, 0, 0);
+                a[j] = Act<AT>::mfma(a0, Act<AT>::cast(b0), a[j]);
+                a[j] = Act<AT>::mfma(a1, Act<AT>::cast(b1), a[j]);
             }
         };
 
@@ -476,12 +523,12 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
                 xv[j][1] = kw + 8 < k ? load_x8_tail(xrow, kw + 8, k) : v4u{0u, 0u, 0u, 0u};
             }
         }
-        v8bf a0, a1;
-        widen(wv, a0, a1);
+        typename Act<AT>::frag a0, a1;
+        widen<AT>(wv, a0, a1);
 #pragma unroll
         for (int j = 0; j < MB; ++j) {
-            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_v8bf(xv[j][0]), acc[0][j], 0, 0, 0);
-            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_v8bf(xv[j][1]), acc[0][j], 0, 0, 0);
+            acc[0][j] = Act<AT>::mfma(a0, Act<AT>::cast(xv[j][0]), acc[0][j]);
+            acc[0][j] = Act<AT>::mfma(a1, Act<AT>::cast(xv[j][1]), acc[0][j]);
         }
     }
 
@@ -495,7 +542,7 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
             continue;
         const v4f s = acc[0][j] + acc[1][j];
         if (splits == 1)
-            store_y4(y, ld_y, w_scale, mr, nb, n, s);
+            store_y4<AT>(y, ld_y, w_scale, mr, nb, n, s);
         else      // partial[split][m][ldp]; ldp >= n rounded up to 4, so the 16 bytes fit
             *reinterpret_cast<v4f *>(partial + ((int64_t)split * m + mr) * ldp + nb) = s;
     }
@@ -503,6 +550,7 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 
 // Sum of the K splits' partial tiles in split order, scaled and stored as
 // bf16: one thread per 4 consecutive outputs of a row.
+template <int AT>
 __global__ __launch_bounds__(256) void k_w8a16_reduce(
     const float *__restrict__ partial, int64_t m, int64_t n, int64_t ldp, int splits,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y)
@@ -516,7 +564,7 @@ __global__ __launch_bounds__(256) void k_w8a16_reduce(
     v4f s = *reinterpret_cast<const v4f *>(partial + mr * ldp + nb);
     for (int sp = 1; sp < splits; ++sp)
         s += *reinterpret_cast<const v4f *>(partial + ((int64_t)sp * m + mr) * ldp + nb);
-    store_y4(y, ld_y, w_scale, mr, nb, n, s);
+    store_y4<AT>(y, ld_y, w_scale, mr, nb, n, s);
 }
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -612,46 +660,48 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
     return p;
 }
 
-template <int AF, int MB, int P, int NW>
+template <int AF, int MB, int P, int NW, int AT>
 static void launch_rows(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
                         const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
                         uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream)
 {
     float *partial = static_cast<float *>(workspace);
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m, (unsigned)p.splits);
-    hipLaunchKernelGGL((k_w8a16_rows<AF, MB, P, NW>), grid, dim3(NW * kWave), 0, stream, x, m, k,
+    hipLaunchKernelGGL((k_w8a16_rows<AF, MB, P, NW, AT>), grid, dim3(NW * kWave), 0, stream, x, m, k,
                        ld_x, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk, p.kper, partial, p.ldp);
     if (p.splits > 1) {
         const int64_t slots = m * (p.ldp / 4);
-        hipLaunchKernelGGL(k_w8a16_reduce, dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
+        hipLaunchKernelGGL((k_w8a16_reduce<AT>), dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
                            partial, m, n, p.ldp, (int)p.splits, w_scale, y, ld_y);
     }
 }
 
-template <int MB, int XD, int T>
+template <int MB, int XD, int T, int AT>
 static void launch_tile(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
                         const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
                         uint16_t *y, int64_t ld_y, float *partial, hipStream_t stream)
 {
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
-    hipLaunchKernelGGL((k_w8a16_tile<MB, XD, T>), grid, dim3(kTileThreads), 0, stream, x, m, k,
+    hipLaunchKernelGGL((k_w8a16_tile<MB, XD, T, AT>), grid, dim3(kTileThreads), 0, stream, x, m, k,
                        ld_x, w, n, ld_w, w_scale, y, ld_y, p.kper, (int)p.splits, partial, p.ldp);
     if (p.splits > 1) {
         const int64_t slots = m * (p.ldp / 4);
-        hipLaunchKernelGGL(k_w8a16_reduce, dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
+        hipLaunchKernelGGL((k_w8a16_reduce<AT>), dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
                            partial, m, n, p.ldp, (int)p.splits, w_scale, y, ld_y);
     }
 }
 
-hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
-                 const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                 uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream)
+template <int AT>
+static hipError_t dispatch(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k,
+                           int64_t ld_x, const uint8_t *w, int64_t n, int64_t ld_w,
+                           const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
+                           hipStream_t stream)
 {
     float *partial = static_cast<float *>(workspace);
     if (p.kind == W8A16Plan::kRows) {
 #define FP8Q_ROWS_CASE(AF, MB, P, NW)                                                         \
         if (p.af == AF && p.mb == MB && p.depth == P && p.waves == NW) {                      \
-            launch_rows<AF, MB, P, NW>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, workspace, \
+            launch_rows<AF, MB, P, NW, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, workspace, \
                                        stream);                                           \
             return hipGetLastError();                                                         \
         }
@@ -661,7 +711,7 @@ hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, in
     } else {
 #define FP8Q_TILE_CASE(MB, XD, T)                                                             \
         if (p.mb == MB && p.xd == XD && p.steps == T) {                                       \
-            launch_tile<MB, XD, T>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, partial,   \
+            launch_tile<MB, XD, T, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, partial,   \
                                    stream);                                                   \
             return hipGetLastError();                                                         \
         }
@@ -679,6 +729,15 @@ hipError_t w8a16(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, in
 #undef FP8Q_TILE_CASE
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t w8a16(const W8A16Plan &p, bool f16_act, const uint16_t *x, int64_t m, int64_t k,
+                 int64_t ld_x, const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
+                 uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream)
+{
+    if (f16_act)
+        return dispatch<kActF16>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, workspace, stream);
+    return dispatch<kActBF16>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, workspace, stream);
 }
 
 }  // namespace launch

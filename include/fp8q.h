@@ -55,8 +55,9 @@ typedef enum {
 
 /* The FP8 MatMul modes of the write-up (§3.1 step 3). */
 typedef enum {
-    FP8Q_W8A16 = 0,             /* "fp8_w_bf16_a": E4M3 weight, bf16 activation (decode) */
-    FP8Q_W8A8 = 1               /* "fp8_w_fp8_a":  E4M3 weight and activation (prefill)  */
+    FP8Q_W8A16 = 0,             /* "fp8_w_bf16_a": E4M3 weight, bf16 activation and output */
+    FP8Q_W8A8 = 1,              /* "fp8_w_fp8_a":  E4M3 weight and activation, bf16 output */
+    FP8Q_W8A16_F16 = 2          /* "fp8_w_fp16_a": E4M3 weight, fp16 activation and output */
 } fp8q_mode;
 
 /* FP8Q_ABI_VERSION of the built library. */
@@ -126,13 +127,15 @@ fp8q_status fp8q_quantize_act(const uint16_t *x_bf16, int64_t m, int64_t k, int6
  *   FP8Q_W8A8:  Y[m,n] = bf16_RNE( x_scale * w_scale[n] * sum_k dec(X[m,k]) * dec(W[n,k]) )
  *               x = E4M3 codes [m, k] (ld_x % 16 == 0); x_scale = device fp32[1];
  *               ld_x and ld_w must be below 2^23 in this mode.
+ *   FP8Q_W8A16_F16: as FP8Q_W8A16 with x = fp16 [m, k] and y fp16 (RNE) instead of
+ *               bf16 (E4M3 values are exact in fp16; |Y| must stay below 65504).
  * Products are exact and sums are accumulated in fp32; the result is within
  * 5e-3 relative Frobenius error of the exact value (see the tests).
  *
  *   w_fp8   [n, k] E4M3 codes, ld_w >= k, ld_w % 16 == 0, 16-byte aligned
  *   w_scale [n] fp32
- *   y_bf16  [m, n] bf16 out, ld_y >= n, ld_y % 8 == 0, 16-byte aligned; must not
- *           overlap any input
+ *   y_bf16  [m, n] out (bf16, or fp16 in FP8Q_W8A16_F16), ld_y >= n, ld_y % 8 == 0,
+ *           16-byte aligned; must not overlap any input
  *   workspace  device scratch of at least fp8q_linear_workspace_size(mode, m, n, k)
  *              bytes, 16-byte aligned (the size may be 0, then workspace may be
  *              NULL); needs no initialisation.  W8A16 uses it when it splits K

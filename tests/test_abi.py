@@ -82,6 +82,9 @@ def test_describe(L):
     assert b"splits=4" in buf.value and b"k_w8a16_reduce" in buf.value
     assert L.fp8q_linear_describe(1, 8192, 28672, 4096, buf, 256) == 0
     assert b"32x112" in buf.value
+    assert L.fp8q_linear_describe(2, 1, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
+    assert L.fp8q_linear_workspace_size(2, 64, 4096, 4096) == L.fp8q_linear_workspace_size(0, 64, 4096, 4096)
     assert L.fp8q_linear_describe(7, 1, 1, 1, buf, 256) == 1
 
 
@@ -101,6 +104,9 @@ def test_linear_host_validation(L):
         ((0, 1, 64, 64, NULL, 16, 72, 16), 1),          # ld_w not a multiple of 16
         ((0, 1, 64, 64, NULL, 16, 64, 12), 1),          # ld_y not a multiple of 8
         ((0, 1, 64, 64, fake, 16, 64, 16), 1),          # x_scale given in W8A16
+        ((2, 1, 64, 64, fake, 16, 64, 16), 1),          # x_scale given in W8A16 fp16
+        ((2, 1, 64, 68, NULL, 16, 64, 16), 1),          # fp16 ld_x not a multiple of 8
+        ((2, 0, 64, 64, NULL, 16, 64, 16), 0),          # fp16, empty M: no-op
         ((1, 1, 64, 64, NULL, 16, 64, 16), 1),          # x_scale missing in W8A8
         ((0, 0, 64, 64, NULL, 16, 64, 16), 0),          # empty M: no-op
         ((1, 4, 64, 64, fake, 0, 64, 16), 0),           # empty N: no-op

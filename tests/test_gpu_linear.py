@@ -81,6 +81,53 @@ def test_w8a16_exact_every_code(fq, orc, m, n, k):
     assert (y == ref).all(), np.argwhere(y != ref)[:5]
 
 
+def pad8_f16(bits: np.ndarray):
+    rows, cols = bits.shape
+    ld = (cols + 7) // 8 * 8
+    t = torch.zeros((rows, ld), dtype=torch.float16, device="cuda")
+    t[:, :cols] = torch.from_numpy(np.ascontiguousarray(bits).view(np.float16)).cuda()
+    return t[:, :cols]
+
+
+def run_w8a16_f16(fq, x_bits, wq, ws):
+    y = fq.linear(pad8_f16(x_bits), pad16(wq), torch.from_numpy(ws).cuda())
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float16
+    return host_bf16_as_f64(y)
+
+
+def f16_act(m: int, k: int, seed: int) -> np.ndarray:
+    """fp16 bit patterns of the workload's N(0, 1) activations."""
+    return workloads.bf16_bits_to_f32(workloads.normal_act(m, k, seed)).astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 256, 64), (1, 272, 576), (64, 272, 1600), (5, 4096, 1100),
+                                   (16, 512, 4160), (40, 320, 1536)])
+def test_w8a16_f16_exact_every_code(fq, orc, m, n, k):
+    """fp8_w_fp16_a with one-hot fp16 rows: every E4M3 code widened to fp16 exactly."""
+    wq = all_codes_weight(n, k)
+    x = np.zeros((m, k), np.uint16)
+    pos = (np.arange(m) * (k - 1)) // max(m - 1, 1)
+    x[np.arange(m), pos] = 0x3C00          # fp16 1.0
+    ws = np.ones(n, np.float32)
+    say("w8a16 fp16 exact", m, n, k, fq.describe_linear(2, m, n, k))
+    y = run_w8a16_f16(fq, x, wq, ws)
+    ref = orc.linear(2, x, wq, ws)
+    assert (y == ref).all(), np.argwhere(y != ref)[:5]
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (8, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096),
+                                   (12, 1024, 8192), (3, 100, 1000), (17, 130, 520), (100, 96, 4104),
+                                   (5, 300, 5000), (40, 522, 3000), (1, 16, 8), (12, 28672, 512)])
+def test_w8a16_f16_ragged(fq, orc, m, n, k):
+    w = workloads.heavy_tail_weight(n, k, m + n)
+    x = f16_act(m, k, k)
+    wq, ws, _ = orc.quantize_weight(w)
+    say("w8a16 fp16", m, n, k, fq.describe_linear(2, m, n, k))
+    y = run_w8a16_f16(fq, x, wq, ws)
+    assert_gemm_close(y, orc.linear(2, x, wq, ws), f"w8a16 fp16 {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("m,n,k", [(256, 256, 64), (300, 260, 128), (33, 512, 64)])
 def test_w8a8_exact_every_code(fq, orc, m, n, k):
     wq = all_codes_weight(n, k)
