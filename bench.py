@@ -246,6 +246,46 @@ def main() -> int:
             "frac_hbm": round(step_bytes / (us16 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "mode": "fp8_w_fp16_a (fp16 activations and output)"}
         log(rows["f1_w8a16_f16_q_proj_decode"])
+
+        # fp8_w_fp8_a at decode sizes: the same step on per-tensor E4M3 activations
+        # (quantized once, outside the timed region)
+        xq8 = {}
+        for m in DECODE_MS:
+            xq8[m] = fq.quantize_act(xs[m])
+        wsn8 = {m: L.fp8q_linear_workspace_size(1, m, N, K) for m in DECODE_MS}
+        wsp8 = {m: (torch.empty(wsn8[m], dtype=torch.uint8, device=dev) if wsn8[m] else None)
+                for m in DECODE_MS}
+
+        def decode_step_f8(i: int, stream: int):
+            for j, m in enumerate(DECODE_MS):
+                c = (len(DECODE_MS) * i + j) % copies_n
+                q, sc = xq8[m]
+                st = L.fp8q_linear(1, ptr(q), m, K, q.stride(0), ptr(sc), ptr(pool[c]), N, K,
+                                   ptr(w_scale), ptr(ys[m]), N, ptr(wsp8[m]), wsn8[m], stream)
+                if st != 0:
+                    raise RuntimeError(_lib.last_error())
+        g8 = torch.cuda.CUDAGraph()
+        s8 = torch.cuda.Stream(device=dev)
+        s8.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.graph(g8, stream=s8, capture_error_mode="relaxed"):
+            h = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(rot):
+                decode_step_f8(i, h)
+        torch.cuda.current_stream(dev).wait_stream(s8)
+        g8.replay()
+        torch.cuda.synchronize()
+        start.record()
+        g8.replay()
+        end.record()
+        end.synchronize()
+        us8 = start.elapsed_time(end) * 1e3 / rot
+        bytes8 = sum(N * K + 4 * N + m * K + 4 + 2 * m * N for m in DECODE_MS)
+        rows["f1_w8a8_q_proj_decode"] = {
+            "shape": "N=K=4096, M=1,8,32,64 per step", "us_per_step": round(us8, 3),
+            "GB/s": round(bytes8 / (us8 * 1e-6) / 1e9, 1),
+            "frac_hbm": round(bytes8 / (us8 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "mode": "fp8_w_fp8_a at decode sizes (E4M3 activations, per-tensor scale)"}
+        log(rows["f1_w8a8_q_proj_decode"])
         rows.update(other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev))
         result["rows"] = rows
 

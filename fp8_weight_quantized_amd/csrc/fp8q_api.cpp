@@ -244,11 +244,17 @@ fp8q_status fp8q_quantize_act(const uint16_t *x_bf16, int64_t m, int64_t k, int6
     return ok();
 }
 
+// W8A8 calls with this many activation rows or fewer run the decode kernels
+// (E4M3 activations widened to bf16), where the prefill GEMM's 256-row tiles
+// would leave most of the GPU idle.
+constexpr int64_t kW8A8DecodeMaxM = 64;
+
 size_t fp8q_linear_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k)
 {
     if (m <= 0 || n <= 0 || k < 1)
         return 0;
-    if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16)
+    if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16 ||
+        (mode == FP8Q_W8A8 && m <= kW8A8DecodeMaxM))
         return round_up(fp8q::launch::plan_w8a16(m, n, k).workspace, 256);
     if (mode == FP8Q_W8A8)
         return round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
@@ -308,11 +314,13 @@ fp8q_status fp8q_linear(fp8q_mode mode,
         return fail(FP8Q_ERR_INVALID_ARG, "the output or workspace overlaps an input");
 
     hipError_t e;
-    if (a16) {
+    if (a16 || m <= kW8A8DecodeMaxM) {
         const auto plan = fp8q::launch::plan_w8a16(m, n, k);
-        e = fp8q::launch::w8a16(plan, mode == FP8Q_W8A16_F16, static_cast<const uint16_t *>(x), m,
-                                k, ld_x, w_fp8, n,
-                                ld_w, w_scale, y_bf16, ld_y, workspace, stream);
+        const int act = mode == FP8Q_W8A16     ? fp8q::launch::kW8A16ActBF16
+                        : mode == FP8Q_W8A16_F16 ? fp8q::launch::kW8A16ActF16
+                                                 : fp8q::launch::kW8A16ActF8;
+        e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
+                                ld_y, workspace, stream);
     } else {
         const auto plan = fp8q::launch::plan_w8a8(m, n, k);
         e = fp8q::launch::w8a8(plan, static_cast<const uint8_t *>(x), m, k, ld_x, x_scale, w_fp8,
@@ -348,7 +356,8 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
         return fail(FP8Q_ERR_INVALID_ARG, "buf is NULL or empty");
     if (m < 0 || n < 0 || k < 1)
         return fail(FP8Q_ERR_INVALID_ARG, "bad sizes");
-    if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16) {
+    if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16 ||
+        (mode == FP8Q_W8A8 && m <= kW8A8DecodeMaxM)) {
         const auto p = fp8q::launch::plan_w8a16(m, n, k);
         if (p.kind == fp8q::launch::W8A16Plan::kRows)
             std::snprintf(buf, len,

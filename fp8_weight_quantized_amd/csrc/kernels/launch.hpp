@@ -49,10 +49,14 @@ struct W8A16Plan {
     size_t workspace;  // scratch bytes: the partial tiles [splits][m][ldp] (0 if no split)
 };
 W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k);
-// f16_act: the activations and the output are fp16 (fp8_w_fp16_a), else bf16.
-hipError_t w8a16(const W8A16Plan &p, bool f16_act, const uint16_t *x, int64_t m, int64_t k,
-                 int64_t ld_x, const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                 uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream);
+// act: the activation type -- 0 bf16 (fp8_w_bf16_a, bf16 out), 1 fp16
+// (fp8_w_fp16_a, fp16 out), 2 E4M3 codes with *x_scale (fp8_w_fp8_a at decode
+// sizes, bf16 out).  ld_x counts activation values.
+constexpr int kW8A16ActBF16 = 0, kW8A16ActF16 = 1, kW8A16ActF8 = 2;
+hipError_t w8a16(const W8A16Plan &p, int act, const void *x, int64_t m, int64_t k, int64_t ld_x,
+                 const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
+                 const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
+                 hipStream_t stream);
 
 // ---- W8A8 (fp8_w_fp8_a) GEMM on FP8 MFMA -----------------------------------
 struct W8A8Plan {

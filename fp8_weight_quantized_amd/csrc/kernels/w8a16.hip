@@ -100,7 +100,9 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 // fp8_w_bf16_a and fp8_w_fp16_a.  Each gives the MFMA operand type, the
 // exact widening of four E4M3 codes to it, the 16x16x32 MFMA and the RNE
 // conversion of an fp32 output to the same 16-bit type.
-enum { kActBF16 = 0, kActF16 = 1 };
+// kActF8: E4M3 activations (fp8_w_fp8_a at decode sizes), widened exactly to
+// bf16 and multiplied in bf16, bf16 output.
+enum { kActBF16 = 0, kActF16 = 1, kActF8 = 2 };
 template <int AT> struct Act;
 
 template <> struct Act<kActBF16> {
@@ -140,6 +142,9 @@ template <> struct Act<kActF16> {
     }
 };
 
+// The MFMA and output type used for an activation type.
+template <int AT> constexpr int compute_type() { return AT == kActF8 ? kActBF16 : AT; }
+
 // Widen a lane's 16 weight codes into the A operands of two MFMA k-steps.
 template <int AT>
 __device__ __forceinline__ void widen(v4u wv, typename Act<AT>::frag &a0, typename Act<AT>::frag &a1)
@@ -154,18 +159,31 @@ __device__ __forceinline__ void widen(v4u wv, typename Act<AT>::frag &a0, typena
 // Rows past N (weights) or past M (activations) were clamped to a valid row
 // when loading; they only feed output rows/columns that are never stored, so
 // no masking is needed here.
+// xv holds, per activation group, either 16 activation codes in xv[j][0]
+// (E4M3) or two 8-value halves in xv[j][0..1] (16-bit types).
 template <int AF, int MB, int AT>
 __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[MB][2],
                                           v4f (&acc)[AF][MB])
 {
+    constexpr int CT = compute_type<AT>();
+    typename Act<CT>::frag b[MB][2];
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+        if constexpr (AT == kActF8) {
+            widen<CT>(xv[j][0], b[j][0], b[j][1]);
+        } else {
+            b[j][0] = Act<CT>::cast(xv[j][0]);
+            b[j][1] = Act<CT>::cast(xv[j][1]);
+        }
+    }
 #pragma unroll
     for (int a = 0; a < AF; ++a) {
-        typename Act<AT>::frag a0, a1;
-        widen<AT>(wv[a], a0, a1);
+        typename Act<CT>::frag a0, a1;
+        widen<CT>(wv[a], a0, a1);
 #pragma unroll
         for (int j = 0; j < MB; ++j) {
-            acc[a][j] = Act<AT>::mfma(a0, Act<AT>::cast(xv[j][0]), acc[a][j]);
-            acc[a][j] = Act<AT>::mfma(a1, Act<AT>::cast(xv[j][1]), acc[a][j]);
+            acc[a][j] = Act<CT>::mfma(a0, b[j][0], acc[a][j]);
+            acc[a][j] = Act<CT>::mfma(a1, b[j][1], acc[a][j]);
         }
     }
 }
@@ -177,14 +195,21 @@ __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[M
 //     MFMAs run.  The pipelined span of a wave is a multiple of P steps; the
 //     remaining steps (and a partial step at the end of K) run one by one.
 // NW: waves per workgroup; wave w owns K range [w*kchunk, (w+1)*kchunk).
+// AT: activation type (kActBF16, kActF16 or kActF8); x is then [m, ld_x]
+// 16-bit values or E4M3 codes, and x_scale (E4M3 only) the activation scale.
 template <int AF, int MB, int P, int NW, int AT>
 __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
-    const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
+    const void *__restrict__ xv, int64_t m, int64_t k, int64_t ld_x,
+    const float *__restrict__ x_scale,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
     int rows, int64_t kchunk, int64_t kper, float *__restrict__ partial, int64_t ldp)
 {
-    constexpr int L = AF + 2 * MB;    // loads per step
+    constexpr bool F8 = AT == kActF8;
+    constexpr int CT = compute_type<AT>();
+    constexpr int ES = F8 ? 1 : 2;              // bytes per activation value
+    constexpr int XS = F8 ? 1 : 2;              // activation loads per group per step
+    constexpr int L = AF + XS * MB;             // loads per step
     __shared__ v4f red[NW][AF * MB][kWave];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -208,12 +233,14 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
         const bool ok = lr < rows && n0 + lr < n;
         wp[a] = w + (ok ? n0 + lr : n0) * ld_w + 16 * g;
     }
-    const uint16_t *xp[MB];
+    // byte pointers to this lane's 16 activation values of each group
+    const uint8_t *xp[MB];
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
         const int64_t xr = m0 + 16 * j + r;
-        xp[j] = x + (xr < m ? xr : m0) * ld_x + 16 * g;
+        xp[j] = static_cast<const uint8_t *>(xv) + ((xr < m ? xr : m0) * ld_x + 16 * g) * ES;
     }
+    const float xs = F8 ? *x_scale : 1.0f;
 
     v4f acc[2][AF][MB];
 #pragma unroll
@@ -236,8 +263,9 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
                 wb[u][a] = ldg_nt(wp[a] + k0);
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
-                xb[u][j][0] = ldg(xp[j] + k0);
-                xb[u][j][1] = ldg(xp[j] + k0 + 8);
+                xb[u][j][0] = ldg(xp[j] + k0 * ES);
+                if constexpr (!F8)
+                    xb[u][j][1] = ldg(xp[j] + k0 * ES + 16);
             }
         };
         const int64_t kend = kb + 64 * npipe;
@@ -277,8 +305,9 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
                 wv[a] = ldg(wp[a] + kk);
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
-                xv[j][0] = ldg(xp[j] + kk);
-                xv[j][1] = ldg(xp[j] + kk + 8);
+                xv[j][0] = ldg(xp[j] + kk * ES);
+                if constexpr (!F8)
+                    xv[j][1] = ldg(xp[j] + kk * ES + 16);
             }
         } else {
 #pragma unroll
@@ -286,8 +315,14 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
                 wv[a] = kw < k ? load_w16_tail(wp[a] - 16 * g, kw, k) : v4u{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
-                xv[j][0] = kw < k ? load_x8_tail(xp[j] - 16 * g, kw, k) : v4u{0u, 0u, 0u, 0u};
-                xv[j][1] = kw + 8 < k ? load_x8_tail(xp[j] - 16 * g, kw + 8, k) : v4u{0u, 0u, 0u, 0u};
+                const uint8_t *row0 = xp[j] - 16 * g * ES;     // the row's first value
+                if constexpr (F8) {
+                    xv[j][0] = kw < k ? load_w16_tail(row0, kw, k) : v4u{0u, 0u, 0u, 0u};
+                } else {
+                    const uint16_t *row16 = reinterpret_cast<const uint16_t *>(row0);
+                    xv[j][0] = kw < k ? load_x8_tail(row16, kw, k) : v4u{0u, 0u, 0u, 0u};
+                    xv[j][1] = kw + 8 < k ? load_x8_tail(row16, kw + 8, k) : v4u{0u, 0u, 0u, 0u};
+                }
             }
         }
         step_mfma<AF, MB, AT>(wv, xv, acc[0]);
@@ -325,12 +360,12 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
         const int valid = (int)min<int64_t>(min<int64_t>(4, rows - nl), n - nb);
         if (valid == 4) {
             uint2 o;
-            o.x = Act<AT>::pack2(sum[0] * w_scale[nb], sum[1] * w_scale[nb + 1]);
-            o.y = Act<AT>::pack2(sum[2] * w_scale[nb + 2], sum[3] * w_scale[nb + 3]);
+            o.x = Act<CT>::pack2(sum[0] * (xs * w_scale[nb]), sum[1] * (xs * w_scale[nb + 1]));
+            o.y = Act<CT>::pack2(sum[2] * (xs * w_scale[nb + 2]), sum[3] * (xs * w_scale[nb + 3]));
             *reinterpret_cast<uint2 *>(yp) = o;
         } else {
             for (int v = 0; v < valid; ++v)
-                yp[v] = Act<AT>::one(sum[v] * w_scale[nb + v]);
+                yp[v] = Act<CT>::one(sum[v] * (xs * w_scale[nb + v]));
         }
     }
 }
@@ -354,20 +389,22 @@ __device__ __forceinline__ void lds_barrier()
 
 // Scale 4 consecutive outputs of row mr and store them as bf16 (8 bytes when
 // all 4 columns exist; the pointer is then 8-byte aligned).
-template <int AT>
+// (xs: the activation scale of E4M3 activations, 1 otherwise -- 1 * w is
+// exact, so the 16-bit modes round exactly as without it.)
+template <int CT>
 __device__ __forceinline__ void store_y4(uint16_t *__restrict__ y, int64_t ld_y,
-                                         const float *__restrict__ w_scale, int64_t mr,
+                                         const float *__restrict__ w_scale, float xs, int64_t mr,
                                          int64_t nb, int64_t n, v4f s)
 {
     uint16_t *yp = y + mr * ld_y + nb;
     if (nb + 4 <= n) {
         uint2 o;
-        o.x = Act<AT>::pack2(s[0] * w_scale[nb], s[1] * w_scale[nb + 1]);
-        o.y = Act<AT>::pack2(s[2] * w_scale[nb + 2], s[3] * w_scale[nb + 3]);
+        o.x = Act<CT>::pack2(s[0] * (xs * w_scale[nb]), s[1] * (xs * w_scale[nb + 1]));
+        o.y = Act<CT>::pack2(s[2] * (xs * w_scale[nb + 2]), s[3] * (xs * w_scale[nb + 3]));
         *reinterpret_cast<uint2 *>(yp) = o;
     } else {
         for (int v = 0; v < (int)(n - nb); ++v)
-            yp[v] = Act<AT>::one(s[v] * w_scale[nb + v]);
+            yp[v] = Act<CT>::one(s[v] * (xs * w_scale[nb + v]));
     }
 }
 
@@ -380,7 +417,8 @@ __device__ __forceinline__ void store_y4(uint16_t *__restrict__ y, int64_t ld_y,
 // y = groups of 16*MB activation rows.
 template <int MB, int XD, int T, int AT>
 __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
-    const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
+    const void *__restrict__ xv, int64_t m, int64_t k, int64_t ld_x,
+    const float *__restrict__ x_scale,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
     int64_t kper, int splits, float *__restrict__ partial, int64_t ldp)
@@ -392,7 +430,15 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
     constexpr int XL = XD * XH;                // activation loads per wave per chunk
     static_assert(kTileWaves * XD <= XR, "staged rows exceed the buffer");
     static_assert(T % 8 == 0, "a chunk is a whole number of 1 KB row segments");
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2 * XR * RB];
+    constexpr bool F8 = AT == kActF8;
+    constexpr int CT = compute_type<AT>();
+    constexpr int ES = F8 ? 1 : 2;             // bytes per activation value
+    // staged rows are always 16-bit (E4M3 activations are widened to bf16,
+    // exactly, between their load and the LDS write)
+    typedef typename std::conditional<F8, uint2, v4u>::type XReg;
+    const uint8_t *x8 = static_cast<const uint8_t *>(xv);
+    const float xs = F8 ? *x_scale : 1.0f;
+    __shared__ __attribute__((aligned(16))) uint8_t xlds[2 * XR * RB];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
@@ -424,37 +470,46 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
     if (nchunks > 0) {
         // this wave stages activation rows wave, wave + 4, ...; lane l holds
         // 16-byte unit l of each 1 KB segment of the row's chunk
-        const uint16_t *xsrc[XD];
+        const uint8_t *xsrc[XD];
 #pragma unroll
         for (int i = 0; i < XD; ++i)
-            xsrc[i] = x + min(m0 + wave + kTileWaves * i, m - 1) * ld_x + kb + 8 * lane;
-        v4u xr[XD][XH];
+            xsrc[i] = x8 + (min(m0 + wave + kTileWaves * i, m - 1) * ld_x + kb + 8 * lane) * ES;
+        XReg xr[XD][XH];
         v4u wr[T];
         auto load_x = [&](int64_t c) {
 #pragma unroll
             for (int i = 0; i < XD; ++i)
 #pragma unroll
                 for (int h = 0; h < XH; ++h)
-                    xr[i][h] = ldg(xsrc[i] + c * CK + 512 * h);
+                    xr[i][h] = *reinterpret_cast<const XReg *>(xsrc[i] + (c * CK + 512 * h) * ES);
         };
         auto store_x = [&](int buf) {
-            uint8_t *base = xs + buf * (XR * RB);
+            uint8_t *base = xlds + buf * (XR * RB);
 #pragma unroll
             for (int i = 0; i < XD; ++i)
 #pragma unroll
                 for (int h = 0; h < XH; ++h)
-                    *reinterpret_cast<v4u *>(base + xs_off(wave + kTileWaves * i, 64 * h + lane)) = xr[i][h];
+                {
+                    v4u v;
+                    if constexpr (F8) {
+                        const uint2 lo = Act<CT>::widen4(xr[i][h].x), hi = Act<CT>::widen4(xr[i][h].y);
+                        v = v4u{lo.x, lo.y, hi.x, hi.y};
+                    } else {
+                        v = xr[i][h];
+                    }
+                    *reinterpret_cast<v4u *>(base + xs_off(wave + kTileWaves * i, 64 * h + lane)) = v;
+                }
         };
         auto compute = [&](int u, int buf, v4f(&a)[MB]) {
-            typename Act<AT>::frag a0, a1;
-            widen<AT>(wr[u], a0, a1);
-            const uint8_t *base = xs + buf * (XR * RB);
+            typename Act<CT>::frag a0, a1;
+            widen<CT>(wr[u], a0, a1);
+            const uint8_t *base = xlds + buf * (XR * RB);
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
                 const v4u b0 = *reinterpret_cast<const v4u *>(base + xs_off(16 * j + r, 8 * u + 2 * g));
                 const v4u b1 = *reinterpret_cast<const v4u *>(base + xs_off(16 * j + r, 8 * u + 2 * g + 1));
-                a[j] = Act<AT>::mfma(a0, Act<AT>::cast(b0), a[j]);
-                a[j] = Act<AT>::mfma(a1, Act<AT>::cast(b1), a[j]);
+                a[j] = Act<CT>::mfma(a0, Act<CT>::cast(b0), a[j]);
+                a[j] = Act<CT>::mfma(a1, Act<CT>::cast(b1), a[j]);
             }
         };
 
@@ -510,26 +565,34 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
             wv = ldg(wrow + kk);
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
-                const uint16_t *xrow = x + min(m0 + 16 * j + r, m - 1) * ld_x + kw;
+                const uint8_t *xrow = x8 + (min(m0 + 16 * j + r, m - 1) * ld_x + kw) * ES;
                 xv[j][0] = ldg(xrow);
-                xv[j][1] = ldg(xrow + 8);
+                if constexpr (!F8)
+                    xv[j][1] = ldg(xrow + 16);
             }
         } else {
             wv = kw < k ? load_w16_tail(wrow - 16 * g, kw, k) : v4u{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
-                const uint16_t *xrow = x + min(m0 + 16 * j + r, m - 1) * ld_x;
-                xv[j][0] = kw < k ? load_x8_tail(xrow, kw, k) : v4u{0u, 0u, 0u, 0u};
-                xv[j][1] = kw + 8 < k ? load_x8_tail(xrow, kw + 8, k) : v4u{0u, 0u, 0u, 0u};
+                const uint8_t *xrow = x8 + min(m0 + 16 * j + r, m - 1) * ld_x * ES;
+                if constexpr (F8) {
+                    xv[j][0] = kw < k ? load_w16_tail(xrow, kw, k) : v4u{0u, 0u, 0u, 0u};
+                } else {
+                    const uint16_t *row16 = reinterpret_cast<const uint16_t *>(xrow);
+                    xv[j][0] = kw < k ? load_x8_tail(row16, kw, k) : v4u{0u, 0u, 0u, 0u};
+                    xv[j][1] = kw + 8 < k ? load_x8_tail(row16, kw + 8, k) : v4u{0u, 0u, 0u, 0u};
+                }
             }
         }
-        typename Act<AT>::frag a0, a1;
-        widen<AT>(wv, a0, a1);
+        v4u wv1[1] = {wv};
+        v4f acc1[1][MB];
 #pragma unroll
-        for (int j = 0; j < MB; ++j) {
-            acc[0][j] = Act<AT>::mfma(a0, Act<AT>::cast(xv[j][0]), acc[0][j]);
-            acc[0][j] = Act<AT>::mfma(a1, Act<AT>::cast(xv[j][1]), acc[0][j]);
-        }
+        for (int j = 0; j < MB; ++j)
+            acc1[0][j] = acc[0][j];
+        step_mfma<1, MB, AT>(wv1, xv, acc1);
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+            acc[0][j] = acc1[0][j];
     }
 
     // lane (r, g) holds D rows 4g..4g+3 (weight rows n0+4g..) of column r
@@ -542,7 +605,7 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
             continue;
         const v4f s = acc[0][j] + acc[1][j];
         if (splits == 1)
-            store_y4<AT>(y, ld_y, w_scale, mr, nb, n, s);
+            store_y4<CT>(y, ld_y, w_scale, xs, mr, nb, n, s);
         else      // partial[split][m][ldp]; ldp >= n rounded up to 4, so the 16 bytes fit
             *reinterpret_cast<v4f *>(partial + ((int64_t)split * m + mr) * ldp + nb) = s;
     }
@@ -553,8 +616,11 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 template <int AT>
 __global__ __launch_bounds__(256) void k_w8a16_reduce(
     const float *__restrict__ partial, int64_t m, int64_t n, int64_t ldp, int splits,
-    const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y)
+    const float *__restrict__ x_scale, const float *__restrict__ w_scale, uint16_t *__restrict__ y,
+    int64_t ld_y)
 {
+    constexpr int CT = compute_type<AT>();
+    const float xs = AT == kActF8 ? *x_scale : 1.0f;
     const int64_t q = ldp / 4;
     const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (slot >= m * q)
@@ -564,7 +630,7 @@ __global__ __launch_bounds__(256) void k_w8a16_reduce(
     v4f s = *reinterpret_cast<const v4f *>(partial + mr * ldp + nb);
     for (int sp = 1; sp < splits; ++sp)
         s += *reinterpret_cast<const v4f *>(partial + ((int64_t)sp * m + mr) * ldp + nb);
-    store_y4<AT>(y, ld_y, w_scale, mr, nb, n, s);
+    store_y4<CT>(y, ld_y, w_scale, xs, mr, nb, n, s);
 }
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -661,48 +727,52 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
 }
 
 template <int AF, int MB, int P, int NW, int AT>
-static void launch_rows(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
-                        const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                        uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream)
+static void launch_rows(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
+                        const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
+                        const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
+                        hipStream_t stream)
 {
     float *partial = static_cast<float *>(workspace);
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m, (unsigned)p.splits);
     hipLaunchKernelGGL((k_w8a16_rows<AF, MB, P, NW, AT>), grid, dim3(NW * kWave), 0, stream, x, m, k,
-                       ld_x, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk, p.kper, partial, p.ldp);
+                       ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk, p.kper, partial,
+                       p.ldp);
     if (p.splits > 1) {
         const int64_t slots = m * (p.ldp / 4);
         hipLaunchKernelGGL((k_w8a16_reduce<AT>), dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
-                           partial, m, n, p.ldp, (int)p.splits, w_scale, y, ld_y);
+                           partial, m, n, p.ldp, (int)p.splits, x_scale, w_scale, y, ld_y);
     }
 }
 
 template <int MB, int XD, int T, int AT>
-static void launch_tile(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
-                        const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                        uint16_t *y, int64_t ld_y, float *partial, hipStream_t stream)
+static void launch_tile(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
+                        const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
+                        const float *w_scale, uint16_t *y, int64_t ld_y, float *partial,
+                        hipStream_t stream)
 {
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
     hipLaunchKernelGGL((k_w8a16_tile<MB, XD, T, AT>), grid, dim3(kTileThreads), 0, stream, x, m, k,
-                       ld_x, w, n, ld_w, w_scale, y, ld_y, p.kper, (int)p.splits, partial, p.ldp);
+                       ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, p.kper, (int)p.splits, partial,
+                       p.ldp);
     if (p.splits > 1) {
         const int64_t slots = m * (p.ldp / 4);
         hipLaunchKernelGGL((k_w8a16_reduce<AT>), dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
-                           partial, m, n, p.ldp, (int)p.splits, w_scale, y, ld_y);
+                           partial, m, n, p.ldp, (int)p.splits, x_scale, w_scale, y, ld_y);
     }
 }
 
 template <int AT>
-static hipError_t dispatch(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k,
-                           int64_t ld_x, const uint8_t *w, int64_t n, int64_t ld_w,
-                           const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
-                           hipStream_t stream)
+static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t k,
+                           int64_t ld_x, const float *x_scale, const uint8_t *w, int64_t n,
+                           int64_t ld_w, const float *w_scale, uint16_t *y, int64_t ld_y,
+                           void *workspace, hipStream_t stream)
 {
     float *partial = static_cast<float *>(workspace);
     if (p.kind == W8A16Plan::kRows) {
 #define FP8Q_ROWS_CASE(AF, MB, P, NW)                                                         \
         if (p.af == AF && p.mb == MB && p.depth == P && p.waves == NW) {                      \
-            launch_rows<AF, MB, P, NW, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, workspace, \
-                                       stream);                                           \
+            launch_rows<AF, MB, P, NW, AT>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y,    \
+                                           ld_y, workspace, stream);                      \
             return hipGetLastError();                                                         \
         }
         FP8Q_ROWS_CASE(2, 1, 8, 4)
@@ -711,8 +781,8 @@ static hipError_t dispatch(const W8A16Plan &p, const uint16_t *x, int64_t m, int
     } else {
 #define FP8Q_TILE_CASE(MB, XD, T)                                                             \
         if (p.mb == MB && p.xd == XD && p.steps == T) {                                       \
-            launch_tile<MB, XD, T, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, partial,   \
-                                   stream);                                                   \
+            launch_tile<MB, XD, T, AT>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,  \
+                                       partial, stream);                                      \
             return hipGetLastError();                                                         \
         }
         FP8Q_TILE_CASE(1, 1, 8)
@@ -731,13 +801,24 @@ static hipError_t dispatch(const W8A16Plan &p, const uint16_t *x, int64_t m, int
     return hipErrorInvalidValue;
 }
 
-hipError_t w8a16(const W8A16Plan &p, bool f16_act, const uint16_t *x, int64_t m, int64_t k,
-                 int64_t ld_x, const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                 uint16_t *y, int64_t ld_y, void *workspace, hipStream_t stream)
+hipError_t w8a16(const W8A16Plan &p, int act, const void *x, int64_t m, int64_t k, int64_t ld_x,
+                 const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
+                 const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
+                 hipStream_t stream)
 {
-    if (f16_act)
-        return dispatch<kActF16>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, workspace, stream);
-    return dispatch<kActBF16>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, workspace, stream);
+    switch (act) {
+    case kActBF16:
+        return dispatch<kActBF16>(p, x, m, k, ld_x, nullptr, w, n, ld_w, w_scale, y, ld_y,
+                                  workspace, stream);
+    case kActF16:
+        return dispatch<kActF16>(p, x, m, k, ld_x, nullptr, w, n, ld_w, w_scale, y, ld_y,
+                                 workspace, stream);
+    case kActF8:
+        return dispatch<kActF8>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,
+                                workspace, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace launch

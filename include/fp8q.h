@@ -126,7 +126,9 @@ fp8q_status fp8q_quantize_act(const uint16_t *x_bf16, int64_t m, int64_t k, int6
  *               x = bf16 [m, k] (ld_x % 8 == 0); x_scale must be NULL.
  *   FP8Q_W8A8:  Y[m,n] = bf16_RNE( x_scale * w_scale[n] * sum_k dec(X[m,k]) * dec(W[n,k]) )
  *               x = E4M3 codes [m, k] (ld_x % 16 == 0); x_scale = device fp32[1];
- *               ld_x and ld_w must be below 2^23 in this mode.
+ *               ld_x and ld_w must be below 2^23 in this mode.  Up to 64 activation
+ *               rows run the decode kernels (codes widened exactly to bf16), more
+ *               rows the FP8 MFMA GEMM; both compute the same sums.
  *   FP8Q_W8A16_F16: as FP8Q_W8A16 with x = fp16 [m, k] and y fp16 (RNE) instead of
  *               bf16 (E4M3 values are exact in fp16; |Y| must stay below 65504).
  * Products are exact and sums are accumulated in fp32; the result is within

@@ -49,8 +49,12 @@ def test_workspace_queries(L):
     assert L.fp8q_quantize_act_workspace_size(1, 8) == 256
     assert L.fp8q_quantize_act_workspace_size(0, 8) == 256
     assert L.fp8q_quantize_act_workspace_size(4, 0) == 0
-    # W8A8 needs no scratch
+    # the W8A8 GEMM (more than 64 activation rows) needs no scratch; up to 64
+    # rows W8A8 runs the decode kernels and their K-split scratch
     assert L.fp8q_linear_workspace_size(1, 8192, 28672, 4096) == 0
+    assert L.fp8q_linear_workspace_size(1, 65, 4096, 4096) == 0
+    assert L.fp8q_linear_workspace_size(1, 64, 4096, 4096) == 4 * 64 * 4096 * 4
+    assert L.fp8q_linear_workspace_size(1, 1, 4096, 4096) == 0
     # W8A16, up to 16 activation rows on a mid-sized weight: the rows kernel,
     # one launch, no scratch
     assert L.fp8q_linear_workspace_size(0, 1, 4096, 4096) == 0
@@ -82,6 +86,8 @@ def test_describe(L):
     assert b"splits=4" in buf.value and b"k_w8a16_reduce" in buf.value
     assert L.fp8q_linear_describe(1, 8192, 28672, 4096, buf, 256) == 0
     assert b"32x112" in buf.value
+    assert L.fp8q_linear_describe(1, 8, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
     assert L.fp8q_linear_describe(2, 1, 4096, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
     assert L.fp8q_linear_workspace_size(2, 64, 4096, 4096) == L.fp8q_linear_workspace_size(0, 64, 4096, 4096)

@@ -128,11 +128,14 @@ def test_w8a16_f16_ragged(fq, orc, m, n, k):
     assert_gemm_close(y, orc.linear(2, x, wq, ws), f"w8a16 fp16 {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(256, 256, 64), (300, 260, 128), (33, 512, 64)])
+@pytest.mark.parametrize("m,n,k", [(256, 256, 64), (300, 260, 128), (33, 512, 64), (8, 300, 1100),
+                                   (64, 272, 1600), (1, 4096, 640), (16, 512, 4160)])
 def test_w8a8_exact_every_code(fq, orc, m, n, k):
+    """One-hot E4M3 rows (spread over K) pick weight columns exactly; up to 64
+    rows this is the decode path, beyond it the FP8 MFMA GEMM."""
     wq = all_codes_weight(n, k)
     xq = np.zeros((m, k), np.uint8)
-    xq[np.arange(m), np.arange(m) % k] = 0x38          # 1.0
+    xq[np.arange(m), (np.arange(m) * (k - 1)) // max(m - 1, 1)] = 0x38          # 1.0
     ws = np.ones(n, np.float32)
     say("w8a8 exact", m, n, k)
     y = run_w8a8(fq, xq, 1.0, wq, ws)
@@ -187,6 +190,19 @@ def test_q_proj_decode_full(fq, orc, m):
     say("q_proj decode", m, fq.describe_linear(0, m, lin.n, lin.k))
     y = run_w8a16(fq, x, wq, ws)
     assert_gemm_close(y, orc.linear(0, x, wq, ws), f"q_proj M={m}")
+
+
+@pytest.mark.parametrize("m", [1, 8, 32, 64])
+def test_q_proj_w8a8_decode_full(fq, orc, m):
+    """fp8_w_fp8_a at decode sizes (the decode kernels with E4M3 activations)
+    on the full q_proj weight, X quantized per tensor by the oracle."""
+    wl = workloads.WORKLOADS["q_proj_decode"]
+    lin = wl.linears[0]
+    wq, ws, _ = orc.quantize_weight(workloads.weight(wl, lin))
+    xq, xs, _ = orc.quantize_act(workloads.activation(wl, m, lin.k))
+    say("q_proj w8a8 decode", m, fq.describe_linear(1, m, lin.n, lin.k))
+    y = run_w8a8(fq, xq, xs, wq, ws)
+    assert_gemm_close(y, orc.linear(1, xq, wq, ws, xs), f"q_proj w8a8 M={m}")
 
 
 @pytest.mark.parametrize("idx", range(7))
