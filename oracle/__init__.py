@@ -74,6 +74,13 @@ def _load():
             lib.oracle_quantize_weight.argtypes = [P, I64, I64, I64, P, I64, P]
             lib.oracle_quantize_act.restype = ctypes.c_int
             lib.oracle_quantize_act.argtypes = [P, I64, I64, I64, P, I64, P]
+            lib.oracle_quantize_act_static.restype = ctypes.c_int
+            lib.oracle_quantize_act_static.argtypes = [P, I64, I64, I64, ctypes.c_float, P, I64]
+            lib.oracle_ema_scale.restype = ctypes.c_float
+            lib.oracle_ema_scale.argtypes = [ctypes.c_float] * 4
+            lib.oracle_quantize_act_ema.restype = ctypes.c_int
+            lib.oracle_quantize_act_ema.argtypes = [P, I64, I64, I64, P, I64, P, ctypes.c_float,
+                                                    ctypes.c_float, ctypes.c_int, P]
             lib.oracle_linear.restype = None
             lib.oracle_linear.argtypes = [ctypes.c_int, P, I64, I64, I64, ctypes.c_float,
                                           P, I64, I64, P, P, I64, P]
@@ -156,6 +163,40 @@ def quantize_act(x_bf16: np.ndarray):
     s = np.empty(1, np.float32)
     nf = _load().oracle_quantize_act(_ptr(x_bf16), m, k, _ld(x_bf16), _ptr(q), k, _ptr(s))
     return q, np.float32(s[0]), bool(nf)
+
+
+def quantize_act_static(x_bf16: np.ndarray, scale: float):
+    """bf16 bits [M, K] and a given fp32 scale -> (codes uint8 [M, K], nonfinite)."""
+    _need(x_bf16, np.uint16, "x_bf16")
+    m, k = x_bf16.shape
+    q = np.empty((m, k), np.uint8)
+    nf = _load().oracle_quantize_act_static(_ptr(x_bf16), m, k, _ld(x_bf16),
+                                            float(np.float32(scale)), _ptr(q), k)
+    return q, bool(nf)
+
+
+def ema_scale(s_old: float, s_new: float, decay: float, temperature: float = 0.0) -> np.float32:
+    """One EMA step of the activation scale, in fp32."""
+    f = lambda v: float(np.float32(v))
+    return np.float32(_load().oracle_ema_scale(f(s_old), f(s_new), f(decay), f(temperature)))
+
+
+def quantize_act_ema(x_bf16: np.ndarray, state: float, decay: float, temperature: float = 0.0,
+                     seed: bool = False):
+    """One EMA-scaled quantization call.
+
+    Returns (codes uint8 [M, K], scale_used float32, new_state float32, nonfinite).
+    With seed=True the call is the dynamic quantization and `state` is ignored.
+    """
+    _need(x_bf16, np.uint16, "x_bf16")
+    m, k = x_bf16.shape
+    q = np.empty((m, k), np.uint8)
+    st = np.array([state], np.float32)
+    used = np.empty(1, np.float32)
+    nf = _load().oracle_quantize_act_ema(_ptr(x_bf16), m, k, _ld(x_bf16), _ptr(q), k, _ptr(st),
+                                         float(np.float32(decay)), float(np.float32(temperature)),
+                                         1 if seed else 0, _ptr(used))
+    return q, np.float32(used[0]), np.float32(st[0]), bool(nf)
 
 
 # ---------------------------------------------------------------- linear ----

@@ -23,8 +23,12 @@
  *                float8_e4m3fn; scale kept beside the weight.
  *   [P1] "Llama 3 精读" FP8 + 128K deployment write-up
  *        §2.1 -- E4M3 range is symmetric, [-448, 448].
+ *        §3.1 step 2 -- the activation scale is an exponential moving
+ *                average with decay 0.9999.
  *        §3.1 step 3 -- the FP8 MatMul modes fp8_w_bf16_a (FP8 weight, BF16
- *                activation) and fp8_w_fp8_a (FP8 weight and activation).
+ *                activation), fp8_w_fp16_a and fp8_w_fp8_a (FP8 weight and
+ *                activation).
+ *        §5.3 tip 2 -- a temperature term (1 + 0.1 T) on the new EMA term.
  *
  * Readings where the pages are silent or contradict each other (each one is
  * listed, with its reason, in the design notes of the repository):
@@ -34,7 +38,10 @@
  *   - values at or beyond 448 in magnitude saturate to +-448,
  *   - the sign of zero is kept (negatives that round to zero give code 0x80),
  *   - the activation scale uses the same formula as the weight scale, taken
- *     over the whole tensor.
+ *     over the whole tensor,
+ *   - an EMA-scaled call casts with the state held before the call and then
+ *     updates the state (the scale lags by one call); the first call is seeded
+ *     with the dynamic scale; the update is fp32, unfused, floored at 1e-12.
  *
  * Parity pins for every function live in tests/test_oracle_*.py.
  */
@@ -43,7 +50,7 @@
 #include <stddef.h>
 #include <string.h>
 
-#define ORACLE_ABI 1
+#define ORACLE_ABI 2
 
 int oracle_abi_version(void) { return ORACLE_ABI; }
 
@@ -242,19 +249,27 @@ int oracle_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w
 /* the one of [P2 §3.1] taken over all elements of the tensor, recomputed    */
 /* on every call.                                                            */
 /* ------------------------------------------------------------------------ */
-int oracle_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
-                        uint8_t *q, int64_t ld_q, float *scale_out)
+/* Largest |x| over a bf16 tensor; *nonfinite is set if any element is NaN or
+ * infinite (a NaN never becomes the maximum). */
+static float act_amax(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x, int *nonfinite)
 {
-    int nonfinite = 0;
     float amax = 0.0f;
     for (int64_t r = 0; r < m; ++r)
         for (int64_t c = 0; c < k; ++c) {
             float a = fabsf(bf16_value(x[r * ld_x + c]));
             if (!isfinite(a))
-                nonfinite = 1;
+                *nonfinite = 1;
             if (a > amax)
                 amax = a;
         }
+    return amax;
+}
+
+int oracle_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                        uint8_t *q, int64_t ld_q, float *scale_out)
+{
+    int nonfinite = 0;
+    float amax = act_amax(x, m, k, ld_x, &nonfinite);
     float s = oracle_scale_from_amax(amax);
     *scale_out = s;
 #pragma omp parallel for schedule(static)
@@ -262,6 +277,80 @@ int oracle_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
         for (int64_t c = 0; c < k; ++c)
             q[r * ld_q + c] = quantize_one(bf16_value(x[r * ld_x + c]), s);
     return nonfinite;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Static per-tensor activation quantization.                                */
+/* [P2 §1.2] one scale for the whole tensor; here the scale is given rather  */
+/* than recomputed from X (the static form of the activation scale, [P1 §3.1 */
+/* step 2]), so values beyond 448 * s occur and saturate to +-448.           */
+/* codes = cast(fl32(X / s)), the same element step as the weights.          */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_act_static(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                               float s, uint8_t *q, int64_t ld_q)
+{
+    int nonfinite = 0;
+    (void)act_amax(x, m, k, ld_x, &nonfinite);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t c = 0; c < k; ++c)
+            q[r * ld_q + c] = quantize_one(bf16_value(x[r * ld_x + c]), s);
+    return nonfinite;
+}
+
+/* ------------------------------------------------------------------------ */
+/* EMA update of the activation scale.                                       */
+/* [P1 §3.1 step 2] the per-tensor activation scale is an exponential moving */
+/* average with decay d (0.9999 there): s = d * s_old + (1 - d) * s_new,     */
+/* where s_new is the dynamic scale of the tensor just seen.                 */
+/* [P1 §5.3, tip 2] the temperature variant multiplies the new term by       */
+/* (1 + 0.1 * T); T = 0 gives the plain average.                             */
+/* Arithmetic is fp32 (the scale is a float), evaluated left to right as     */
+/* written, with no fused multiply-add; 1 - d is formed in fp32 (exact for    */
+/* d in [0.5, 1]).  The result is a scale, so it keeps the 1e-12 floor of     */
+/* [P2 §3.1].                                                                */
+/* ------------------------------------------------------------------------ */
+float oracle_ema_scale(float s_old, float s_new, float decay, float temperature)
+{
+    float keep = decay * s_old;
+    float weight = 1.0f - decay;
+    float fresh = weight * s_new;
+    float tenth = 0.1f;
+    float heat = 1.0f + tenth * temperature;
+    fresh = fresh * heat;
+    float s = keep + fresh;
+    const float floor_ = 1e-12f;
+    if (s < floor_)
+        s = floor_;
+    return s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One call of EMA-scaled activation quantization.                           */
+/* seed != 0: dynamic quantization of X (its own absmax scale); the state    */
+/*            and *scale_used both become that scale.                        */
+/* seed == 0: X is cast with the state as it stood before the call (the      */
+/*            scale is delayed by one call), then the state takes one EMA    */
+/*            step towards the dynamic scale of X; *scale_used receives the  */
+/*            scale the codes were made with.                                */
+/* Returns the non-finite flag of X.                                         */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_act_ema(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                            uint8_t *q, int64_t ld_q, float *state, float decay,
+                            float temperature, int seed, float *scale_used)
+{
+    if (seed) {
+        int nf = oracle_quantize_act(x, m, k, ld_x, q, ld_q, scale_used);
+        *state = *scale_used;
+        return nf;
+    }
+    float s_old = *state;
+    int nf = oracle_quantize_act_static(x, m, k, ld_x, s_old, q, ld_q);
+    int unused = 0;
+    float s_new = oracle_scale_from_amax(act_amax(x, m, k, ld_x, &unused));
+    *scale_used = s_old;
+    *state = oracle_ema_scale(s_old, s_new, decay, temperature);
+    return nf;
 }
 
 /* ------------------------------------------------------------------------ */
