@@ -428,6 +428,37 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
             "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "note": "two kernels (absmax, cast); X is re-read by the cast"}
         log(key, rows[f"a3a4_quantize_act_{key}"])
+
+        # held (static) and EMA scales: one read of X per call
+        held = xsc.clone()
+        state = torch.zeros(1, dtype=torch.float32, device=dev)
+        if L.fp8q_quantize_act_ema(ptr(x), m, k, k, ptr(xq), xq.stride(0), ptr(xsc), ptr(state),
+                                   0.9999, 0.0, 1, ptr(aws), aws_n, None, stream()) != 0:
+            raise RuntimeError(fq._lib.last_error())
+
+        def actq_static():
+            st = L.fp8q_quantize_act_static(ptr(x), m, k, k, ptr(held), ptr(xq), xq.stride(0),
+                                            None, stream())
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+
+        def actq_ema():
+            st = L.fp8q_quantize_act_ema(ptr(x), m, k, k, ptr(xq), xq.stride(0), ptr(xsc),
+                                         ptr(state), 0.9999, 0.1, 0, ptr(aws), aws_n, None,
+                                         stream())
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+        for name, fn, note in (
+                ("static", actq_static, "one kernel: cast with a held scale"),
+                ("ema", actq_ema, "cast with the EMA state, absmax from the same loads, "
+                                  "then a one-workgroup update")):
+            ms = time_eager(torch, fn, iters)
+            b = 3.0 * m * k + 8
+            rows[f"f2_quantize_act_{name}_{key}"] = {
+                "shape": f"M={m} K={k}", "us": round(ms * 1e3, 2),
+                "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "note": note}
+            log(key, rows[f"f2_quantize_act_{name}_{key}"])
         del w, x, wq, ws, xq, y
         torch.cuda.empty_cache()
 

@@ -7,6 +7,8 @@ computation runs in the library's HIP kernels; there is no CPU path.
 
     wq, w_scale = quantize_weight(w_bf16)             # per output channel
     xq, x_scale = quantize_act(x_bf16)                # per tensor, dynamic
+    xq = quantize_act_static(x_bf16, held_scale)      # per tensor, held scale
+    ema = EmaActScale(dev); xq, x_scale = ema(x_bf16) # per tensor, EMA scale
     y = linear(x_bf16, wq, w_scale)                   # fp8_w_bf16_a (decode)
     y = linear(xq, wq, w_scale, x_scale=x_scale)      # fp8_w_fp8_a  (prefill)
 
@@ -24,7 +26,8 @@ from . import _lib
 from ._lib import FP8Q_W8A8, FP8Q_W8A16, FP8Q_W8A16_F16, Fp8qError, check
 
 __all__ = [
-    "quantize_weight", "quantize_act", "linear", "cast_f32_to_e4m3", "describe_linear",
+    "quantize_weight", "quantize_act", "quantize_act_static", "quantize_act_ema",
+    "EmaActScale", "linear", "cast_f32_to_e4m3", "describe_linear",
     "FP8Q_W8A16", "FP8Q_W8A8", "Fp8qError", "library_path",
 ]
 
@@ -54,6 +57,8 @@ def _matrix(t: torch.Tensor, name: str, dtypes) -> tuple[int, int, int]:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     rows, cols = t.shape
+    if t.numel() == 0:
+        return rows, cols, cols        # nothing is read: the strides of an empty tensor are moot
     if cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have a contiguous last dimension")
     ld = t.stride(0) if rows > 1 else max(cols, t.stride(0))
@@ -101,6 +106,71 @@ def quantize_act(x: torch.Tensor, nonfinite_flag: torch.Tensor | None = None):
         _ptr(x), m, k, ld, _ptr(q), q.stride(0) if m else _round_up(k, 16), _ptr(scale),
         _ptr(ws), nws, _ptr(nonfinite_flag), _stream(dev)))
     return q, scale
+
+
+def _scalar_f32(t: torch.Tensor, name: str, dev: torch.device) -> None:
+    if t.dtype != torch.float32 or t.numel() != 1 or t.device != dev:
+        raise ValueError(f"{name} must be one float32 on {dev}")
+
+
+def quantize_act_static(x: torch.Tensor, scale: torch.Tensor,
+                        nonfinite_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-tensor E4M3 quantization of bf16 activations with a held scale.
+
+    `scale` is a float32 [1] GPU tensor (positive, finite); values beyond
+    448 * scale saturate.  Returns the codes, uint8 [M, K].
+    """
+    m, k, ld = _matrix(x, "x", (torch.bfloat16,))
+    dev = x.device
+    _scalar_f32(scale, "scale", dev)
+    q = _new_codes(m, k, dev)
+    check(_lib.lib().fp8q_quantize_act_static(
+        _ptr(x), m, k, ld, _ptr(scale), _ptr(q), q.stride(0) if m else _round_up(k, 16),
+        _ptr(nonfinite_flag), _stream(dev)))
+    return q
+
+
+def quantize_act_ema(x: torch.Tensor, state: torch.Tensor, decay: float = 0.9999,
+                     temperature: float = 0.0, seed: bool = False,
+                     nonfinite_flag: torch.Tensor | None = None):
+    """Per-tensor E4M3 quantization with an EMA scale carried in `state`.
+
+    `state` is a float32 [1] GPU tensor.  seed=True quantizes dynamically and
+    sets the state to that scale; otherwise the codes use the state as it was,
+    and the state then takes one EMA step towards this tensor's dynamic scale.
+    Returns (codes uint8 [M, K], scale float32 [1] the codes were made with).
+    """
+    m, k, ld = _matrix(x, "x", (torch.bfloat16,))
+    dev = x.device
+    _scalar_f32(state, "state", dev)
+    q = _new_codes(m, k, dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    L = _lib.lib()
+    nws = L.fp8q_quantize_act_workspace_size(m, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    check(L.fp8q_quantize_act_ema(
+        _ptr(x), m, k, ld, _ptr(q), q.stride(0) if m else _round_up(k, 16), _ptr(scale),
+        _ptr(state), float(decay), float(temperature), 1 if seed else 0, _ptr(ws), nws,
+        _ptr(nonfinite_flag), _stream(dev)))
+    return q, scale
+
+
+class EmaActScale:
+    """The EMA activation scale of one linear layer's input: a device state
+    and whether it has been seeded.  Calling it quantizes a bf16 [M, K]
+    activation and returns (codes, scale) for fp8_w_fp8_a."""
+
+    def __init__(self, device, decay: float = 0.9999, temperature: float = 0.0):
+        self.state = torch.zeros(1, dtype=torch.float32, device=device)
+        self.decay = float(decay)
+        self.temperature = float(temperature)
+        self.seeded = False
+
+    def __call__(self, x: torch.Tensor, nonfinite_flag: torch.Tensor | None = None):
+        out = quantize_act_ema(x, self.state, self.decay, self.temperature,
+                               seed=not self.seeded, nonfinite_flag=nonfinite_flag)
+        self.seeded = True
+        return out
 
 
 def linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,

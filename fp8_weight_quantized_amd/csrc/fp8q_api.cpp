@@ -244,6 +244,85 @@ fp8q_status fp8q_quantize_act(const uint16_t *x_bf16, int64_t m, int64_t k, int6
     return ok();
 }
 
+fp8q_status fp8q_quantize_act_static(const uint16_t *x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                                     const float *x_scale, uint8_t *x_fp8, int64_t ld_q,
+                                     int32_t *nonfinite_flag, hipStream_t stream)
+{
+    if (m < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "need m >= 0 and k >= 1 (m=%lld, k=%lld)", (long long)m,
+                    (long long)k);
+    FP8Q_TRY(check_ld(ld_x, k, 1, "ld_x"));
+    FP8Q_TRY(check_ld(ld_q, k, 1, "ld_q"));
+    if (m == 0)
+        return ok();
+    int dev = 0;
+    FP8Q_TRY(prepare(stream, &dev));
+    FP8Q_TRY(check_ptr(x_bf16, "x_bf16", dev, 2));
+    FP8Q_TRY(check_ptr(x_fp8, "x_fp8", dev, 1));
+    FP8Q_TRY(check_ptr(x_scale, "x_scale", dev, 4));
+    if (nonfinite_flag != nullptr)
+        FP8Q_TRY(check_ptr(nonfinite_flag, "nonfinite_flag", dev, 4));
+    const size_t ex = extent(m, k, ld_x, 2), eq = extent(m, k, ld_q, 1);
+    if (overlap(x_fp8, eq, x_bf16, ex) || overlap(x_fp8, eq, x_scale, 4))
+        return fail(FP8Q_ERR_INVALID_ARG, "x_fp8 overlaps the input or the scale");
+    hipError_t e = fp8q::launch::quantize_act_static(x_bf16, m, k, ld_x, x_scale, x_fp8, ld_q,
+                                                     nonfinite_flag, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "static activation quantization launch");
+    return ok();
+}
+
+fp8q_status fp8q_quantize_act_ema(const uint16_t *x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                                  uint8_t *x_fp8, int64_t ld_q, float *x_scale, float *state,
+                                  float decay, float temperature, int seed,
+                                  void *workspace, size_t workspace_bytes,
+                                  int32_t *nonfinite_flag, hipStream_t stream)
+{
+    if (m < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "need m >= 0 and k >= 1 (m=%lld, k=%lld)", (long long)m,
+                    (long long)k);
+    if (!(decay >= 0.0f && decay <= 1.0f))
+        return fail(FP8Q_ERR_INVALID_ARG, "decay must lie in [0, 1] (got %g)", (double)decay);
+    if (!(temperature >= 0.0f && temperature <= 3.0e38f))
+        return fail(FP8Q_ERR_INVALID_ARG, "temperature must be finite and >= 0 (got %g)",
+                    (double)temperature);
+    FP8Q_TRY(check_ld(ld_x, k, 1, "ld_x"));
+    FP8Q_TRY(check_ld(ld_q, k, 1, "ld_q"));
+    const size_t need = fp8q_quantize_act_workspace_size(m, k);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(FP8Q_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                    workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+    int dev = 0;
+    FP8Q_TRY(prepare(stream, &dev));
+    if (m > 0) {
+        FP8Q_TRY(check_ptr(x_bf16, "x_bf16", dev, 2));
+        FP8Q_TRY(check_ptr(x_fp8, "x_fp8", dev, 1));
+    }
+    FP8Q_TRY(check_ptr(x_scale, "x_scale", dev, 4));
+    FP8Q_TRY(check_ptr(state, "state", dev, 4));
+    FP8Q_TRY(check_ptr(workspace, "workspace", dev, 16));
+    if (nonfinite_flag != nullptr)
+        FP8Q_TRY(check_ptr(nonfinite_flag, "nonfinite_flag", dev, 4));
+    const size_t ex = extent(m, k, ld_x, 2), eq = extent(m, k, ld_q, 1);
+    const void *outs[4] = {x_fp8, x_scale, state, workspace};
+    const size_t lens[4] = {eq, 4, 4, need};
+    for (int a = 0; a < 4; ++a) {
+        if (overlap(outs[a], lens[a], x_bf16, ex))
+            return fail(FP8Q_ERR_INVALID_ARG, "outputs, state and workspace must not overlap x");
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(outs[a], lens[a], outs[b], lens[b]))
+                return fail(FP8Q_ERR_INVALID_ARG,
+                            "x_fp8, x_scale, state and workspace must not overlap");
+    }
+    hipError_t e = fp8q::launch::quantize_act_ema(x_bf16, m, k, ld_x, x_fp8, ld_q, x_scale, state,
+                                                  decay, temperature, seed != 0,
+                                                  static_cast<uint32_t *>(workspace),
+                                                  nonfinite_flag, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "EMA activation quantization launch");
+    return ok();
+}
+
 // W8A8 calls with this many activation rows or fewer run the decode kernels
 // (E4M3 activations widened to bf16), where the prefill GEMM's 256-row tiles
 // would leave most of the GPU idle.

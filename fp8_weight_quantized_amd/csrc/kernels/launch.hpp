@@ -23,6 +23,20 @@ hipError_t quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
                         uint8_t *q, int64_t ld_q, float *x_scale, uint32_t *partial,
                         int32_t *flag, hipStream_t stream);
 
+// Per-tensor quantization with a held scale (*scale, device), one pass.
+hipError_t quantize_act_static(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                               const float *scale, uint8_t *q, int64_t ld_q, int32_t *flag,
+                               hipStream_t stream);
+
+// EMA-scaled quantization.  seed: the dynamic quantization, whose scale also
+// goes to *state.  Otherwise the cast uses *state (and reports it in
+// *x_scale), then a one-workgroup kernel steps *state towards this tensor's
+// dynamic scale.  partial: act_blocks(m, k) words of scratch.
+hipError_t quantize_act_ema(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                            uint8_t *q, int64_t ld_q, float *x_scale, float *state,
+                            float decay, float temperature, bool seed, uint32_t *partial,
+                            int32_t *flag, hipStream_t stream);
+
 hipError_t cast_f32(const float *x, int64_t count, uint8_t *out, hipStream_t stream);
 
 // ---- W8A16 (fp8_w_bf16_a) skinny GEMM --------------------------------------

@@ -1,12 +1,14 @@
-// Quantization kernels: per-output-channel weight quantization, dynamic
-// per-tensor activation quantization (two passes) and the bare fp32 -> E4M3
-// cast.  The method is the conversion of the deployment guide
-// ("FP8量化与长上下文实测：Llama 3 70B部署优化指南", §3.1): absmax / 448 with the
-// scale clamped at 1e-12, an fp32 division, and an RNE cast to E4M3 that
-// saturates at +-448; weights get one scale per output row, activations one
-// scale per tensor (§1.2).
+// Quantization kernels: per-output-channel weight quantization, per-tensor
+// activation quantization -- dynamic (two passes), with a held static scale
+// (one pass) or with an EMA scale (one pass plus a one-workgroup update) --
+// and the bare fp32 -> E4M3 cast.  The method is the conversion of the
+// deployment guide ("FP8量化与长上下文实测：Llama 3 70B部署优化指南", §3.1):
+// absmax / 448 with the scale clamped at 1e-12, an fp32 division, and an RNE
+// cast to E4M3 that saturates at +-448; weights get one scale per output row,
+// activations one scale per tensor (§1.2).  The EMA scale is the one of the
+// "Llama 3 精读" write-up (§3.1 step 2, §5.3 tip 2).
 //
-// All three are HBM-bound streaming kernels: bf16 in (2 B/element), codes out
+// All of them are HBM-bound streaming kernels: bf16 in (2 B/element), codes out
 // (1 B/element).  Loads are 16 B per lane, stores 8 B per lane, fully
 // coalesced; the reductions use wave shuffles and a few words of LDS.
 #include "device_common.hpp"
@@ -179,26 +181,48 @@ __global__ __launch_bounds__(kThreads) void k_act_amax(
 }
 
 // ---------------------------------------------------------------------------
-// Activations, pass 2: every workgroup folds the partial maxima (a few KB,
-// L2-resident) into the tensor's scale, then casts its share.  Workgroup 0
-// publishes the scale and the non-finite flag.
+// Activations, the cast.  Where its scale comes from:
+//   kFromPartials  dynamic quantization, pass 2: every workgroup folds the
+//                  pass-1 maxima (a few KB, L2-resident) into the tensor's
+//                  scale; workgroup 0 publishes it (to x_scale, and to
+//                  seed_out when that is given) with the non-finite flag.
+//   kHeld          a scale held in device memory (*held), read once per
+//                  workgroup; the tensor is read once.  The |x| maximum is
+//                  reduced only to raise the non-finite flag.
+//   kHeldTrack     as kHeld, and each workgroup also writes the |x| maximum of
+//                  its share to partial_out[blockIdx.x], from the same loads,
+//                  for the EMA update that follows.
 // ---------------------------------------------------------------------------
+enum ScaleSource : int { kFromPartials = 0, kHeld = 1, kHeldTrack = 2 };
+
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void k_act_cast(
     const uint16_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
     uint8_t *__restrict__ q, int64_t ld_q,
     const uint32_t *__restrict__ partial, int npart,
-    float *__restrict__ x_scale, int32_t *__restrict__ flag, int layout)
+    float *__restrict__ x_scale, float *__restrict__ seed_out,
+    const float *__restrict__ held, uint32_t *__restrict__ partial_out,
+    int32_t *__restrict__ flag, int layout)
 {
+    constexpr bool kTrack = SRC != kFromPartials;
     __shared__ uint32_t red[kThreads / kWave];
     uint32_t key = 0;
-    for (int j = threadIdx.x; j < npart; j += kThreads)
-        key = max(key, partial[j]);
-    key = block_max_u32(key, red);
-    const float s = scale_from_key(key);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        *x_scale = s;
-        if (flag != nullptr && key >= 0x7F80u)
-            *flag = 1;
+    float s;
+    if constexpr (SRC == kFromPartials) {
+        for (int j = threadIdx.x; j < npart; j += kThreads)
+            key = max(key, partial[j]);
+        key = block_max_u32(key, red);
+        s = scale_from_key(key);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            *x_scale = s;
+            if (seed_out != nullptr)
+                *seed_out = s;
+            if (flag != nullptr && key >= 0x7F80u)
+                *flag = 1;
+        }
+        key = 0;
+    } else {
+        s = *held;
     }
 
     const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -208,7 +232,10 @@ __global__ __launch_bounds__(kThreads) void k_act_cast(
         for (; i < total; i += stride) {
             const int64_t row = i / k;
             const int64_t c = i - row * k;
-            const float t = __uint_as_float((uint32_t)x[row * ld_x + c] << 16) / s;
+            const uint16_t h = x[row * ld_x + c];
+            if constexpr (kTrack)
+                key = max(key, (uint32_t)(h & 0x7FFFu));
+            const float t = __uint_as_float((uint32_t)h << 16) / s;
             q[row * ld_q + c] = (uint8_t)(e4m3x4(t, 0.f, 0.f, 0.f) & 0xFFu);
         }
     } else if (layout == kFlat) {
@@ -217,13 +244,19 @@ __global__ __launch_bounds__(kThreads) void k_act_cast(
         const int64_t total = m * (k >> 3);
         for (; i + 3 * stride < total; i += 4 * stride) {
             uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+            if constexpr (kTrack)
+                key = max(key, max(max(key_max8(a), key_max8(b)), max(key_max8(c), key_max8(d))));
             o[i] = quantize8(a, s);
             o[i + stride] = quantize8(b, s);
             o[i + 2 * stride] = quantize8(c, s);
             o[i + 3 * stride] = quantize8(d, s);
         }
-        for (; i < total; i += stride)
-            o[i] = quantize8(p[i], s);
+        for (; i < total; i += stride) {
+            const uint4 a = p[i];
+            if constexpr (kTrack)
+                key = max(key, key_max8(a));
+            o[i] = quantize8(a, s);
+        }
     } else {
         const int64_t cpr = (k + 7) >> 3;
         const int64_t total = m * cpr;
@@ -233,14 +266,70 @@ __global__ __launch_bounds__(kThreads) void k_act_cast(
             const uint16_t *p = x + row * ld_x + j;
             uint8_t *o = q + row * ld_q + j;
             if (j + 8 <= k) {
-                *reinterpret_cast<uint2 *>(o) = quantize8(*reinterpret_cast<const uint4 *>(p), s);
+                const uint4 a = *reinterpret_cast<const uint4 *>(p);
+                if constexpr (kTrack)
+                    key = max(key, key_max8(a));
+                *reinterpret_cast<uint2 *>(o) = quantize8(a, s);
             } else {
                 for (int64_t e = 0; e < k - j; ++e) {
+                    if constexpr (kTrack)
+                        key = max(key, (uint32_t)(p[e] & 0x7FFFu));
                     const float t = __uint_as_float((uint32_t)p[e] << 16) / s;
                     o[e] = (uint8_t)(e4m3x4(t, 0.f, 0.f, 0.f) & 0xFFu);
                 }
             }
         }
+    }
+
+    if constexpr (SRC == kHeldTrack) {
+        key = block_max_u32(key, red);
+        if (threadIdx.x == 0)
+            partial_out[blockIdx.x] = key;
+    } else if constexpr (SRC == kHeld) {
+        if (flag != nullptr) {
+            key = block_max_u32(key, red);
+            if (threadIdx.x == 0 && key >= 0x7F80u)
+                *flag = 1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// EMA step of the per-tensor activation scale ("Llama 3 精读" write-up §3.1
+// step 2: a moving average with decay d; §5.3 tip 2: the new term times
+// (1 + 0.1 T)).  fp32, evaluated in the written order with every product and
+// sum rounded on its own (no fused multiply-add), then the 1e-12 floor that
+// every scale of the method keeps.
+// ---------------------------------------------------------------------------
+__device__ __noinline__ float ema_step(float s_old, float s_new, float decay, float temperature)
+{
+#pragma clang fp contract(off)
+    const float keep = decay * s_old;
+    const float weight = 1.0f - decay;
+    float fresh = weight * s_new;
+    const float heat = 1.0f + 0.1f * temperature;
+    fresh = fresh * heat;
+    const float s = keep + fresh;
+    return s < kScaleFloor ? kScaleFloor : s;
+}
+
+// One workgroup: fold the per-workgroup maxima of the tracked cast into the
+// tensor's dynamic scale, hand out the scale the cast used, step the state.
+__global__ __launch_bounds__(kThreads) void k_act_ema_update(
+    const uint32_t *__restrict__ partial, int npart, float *__restrict__ state,
+    float *__restrict__ x_scale, float decay, float temperature, int32_t *__restrict__ flag)
+{
+    __shared__ uint32_t red[kThreads / kWave];
+    uint32_t key = 0;
+    for (int j = threadIdx.x; j < npart; j += kThreads)
+        key = max(key, partial[j]);
+    key = block_max_u32(key, red);
+    if (threadIdx.x == 0) {
+        const float s_old = *state;
+        *x_scale = s_old;
+        *state = ema_step(s_old, scale_from_key(key), decay, temperature);
+        if (flag != nullptr && key >= 0x7F80u)
+            *flag = 1;
     }
 }
 
@@ -312,20 +401,69 @@ int act_blocks(int64_t m, int64_t k)
     return (int)g;
 }
 
-hipError_t quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
-                        uint8_t *q, int64_t ld_q, float *x_scale, uint32_t *partial,
-                        int32_t *flag, hipStream_t stream)
+static int act_layout(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x, const uint8_t *q,
+                      int64_t ld_q)
+{
+    (void)m;
+    const bool rows_ok = aligned(x, 16) && ld_x % 8 == 0 && aligned(q, 8) && ld_q % 8 == 0;
+    return !rows_ok ? kScalar : (ld_x == k && ld_q == k && k % 8 == 0) ? kFlat : kRows;
+}
+
+// Dynamic per-tensor quantization: the absmax pass, then the cast that folds
+// its partial maxima.  seed_out (optional) receives a copy of the scale.
+static hipError_t quantize_act_dynamic(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                                       uint8_t *q, int64_t ld_q, float *x_scale, float *seed_out,
+                                       uint32_t *partial, int32_t *flag, hipStream_t stream)
 {
     const int g = act_blocks(m, k);
-    const bool rows_ok = aligned(x, 16) && ld_x % 8 == 0 && aligned(q, 8) && ld_q % 8 == 0;
-    const int layout = !rows_ok ? kScalar : (ld_x == k && ld_q == k && k % 8 == 0) ? kFlat : kRows;
+    const int layout = act_layout(x, m, k, ld_x, q, ld_q);
     hipLaunchKernelGGL(k_act_amax, dim3(g), dim3(kThreads), 0, stream, x, m, k, ld_x, partial,
                        layout);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_act_cast, dim3(g), dim3(kThreads), 0, stream, x, m, k, ld_x, q, ld_q,
-                       (const uint32_t *)partial, g, x_scale, flag, layout);
+    hipLaunchKernelGGL(k_act_cast<kFromPartials>, dim3(g), dim3(kThreads), 0, stream, x, m, k,
+                       ld_x, q, ld_q, (const uint32_t *)partial, g, x_scale, seed_out,
+                       (const float *)nullptr, (uint32_t *)nullptr, flag, layout);
+    return hipGetLastError();
+}
+
+hipError_t quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                        uint8_t *q, int64_t ld_q, float *x_scale, uint32_t *partial,
+                        int32_t *flag, hipStream_t stream)
+{
+    return quantize_act_dynamic(x, m, k, ld_x, q, ld_q, x_scale, nullptr, partial, flag, stream);
+}
+
+hipError_t quantize_act_static(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                               const float *scale, uint8_t *q, int64_t ld_q, int32_t *flag,
+                               hipStream_t stream)
+{
+    const int g = act_blocks(m, k);
+    const int layout = act_layout(x, m, k, ld_x, q, ld_q);
+    hipLaunchKernelGGL(k_act_cast<kHeld>, dim3(g), dim3(kThreads), 0, stream, x, m, k, ld_x, q,
+                       ld_q, (const uint32_t *)nullptr, 0, (float *)nullptr, (float *)nullptr,
+                       scale, (uint32_t *)nullptr, flag, layout);
+    return hipGetLastError();
+}
+
+hipError_t quantize_act_ema(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                            uint8_t *q, int64_t ld_q, float *x_scale, float *state,
+                            float decay, float temperature, bool seed, uint32_t *partial,
+                            int32_t *flag, hipStream_t stream)
+{
+    if (seed)
+        return quantize_act_dynamic(x, m, k, ld_x, q, ld_q, x_scale, state, partial, flag, stream);
+    const int g = act_blocks(m, k);
+    const int layout = act_layout(x, m, k, ld_x, q, ld_q);
+    hipLaunchKernelGGL(k_act_cast<kHeldTrack>, dim3(g), dim3(kThreads), 0, stream, x, m, k, ld_x,
+                       q, ld_q, (const uint32_t *)nullptr, 0, (float *)nullptr, (float *)nullptr,
+                       (const float *)state, partial, (int32_t *)nullptr, layout);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_act_ema_update, dim3(1), dim3(kThreads), 0, stream,
+                       (const uint32_t *)partial, g, state, x_scale, decay, temperature, flag);
     return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@
  *   guide" below) §1.1 gives the E4M3 format, §1.2 the granularity (weights
  *   per channel, activations per tensor) and §3.1 the conversion recipe;
  *   "Llama 3 精读" FP8 + 128K write-up (called "the write-up") §3.1 step 3
- *   names the FP8 MatMul modes.
+ *   names the FP8 MatMul modes, §3.1 step 2 and §5.3 tip 2 the EMA
+ *   activation scale.
  *
  * Errors.  Arguments are validated on the host before anything is enqueued;
  * on any error nothing is launched and a status other than FP8Q_OK is
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 1
+#define FP8Q_ABI_VERSION 2
 
 typedef enum {
     FP8Q_OK = 0,
@@ -117,6 +118,59 @@ fp8q_status fp8q_quantize_act(const uint16_t *x_bf16, int64_t m, int64_t k, int6
                               uint8_t *x_fp8, int64_t ld_q, float *x_scale,
                               void *workspace, size_t workspace_bytes,
                               int32_t *nonfinite_flag, hipStream_t stream);
+
+/*
+ * Static per-tensor activation quantization: the cast of fp8q_quantize_act with
+ * a scale the caller holds instead of one recomputed from X (the per-tensor
+ * activation scale of the deployment guide §1.2, kept across calls as the
+ * write-up's §3.1 step 2 keeps it).  One pass over X:
+ *   x_fp8[m,k] = E4M3_RNE_saturating(fl32(X[m,k] / *x_scale))
+ * Values beyond 448 * scale saturate to +-448 (codes 0x7E / 0xFE).
+ *
+ *   x_bf16   [m, k] bf16, ld_x >= k;  x_fp8 [m, k] uint8 out, ld_q >= k
+ *   x_scale  one fp32 (device), read only; it must be positive and finite
+ *            (any other value gives unspecified codes)
+ *   nonfinite_flag  optional, as above
+ * m == 0 is a no-op; k must be >= 1.  Bit-exact.
+ */
+fp8q_status fp8q_quantize_act_static(const uint16_t *x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                                     const float *x_scale, uint8_t *x_fp8, int64_t ld_q,
+                                     int32_t *nonfinite_flag, hipStream_t stream);
+
+/*
+ * EMA-scaled per-tensor activation quantization (the write-up §3.1 step 2: the
+ * activation scale is an exponential moving average, decay 0.9999 there;
+ * §5.3 tip 2: a temperature T multiplies the new term by (1 + 0.1 T)).
+ * `state` is one device fp32 that carries the average from call to call.
+ *
+ *   seed != 0: dynamic quantization of X exactly as fp8q_quantize_act;
+ *              *x_scale and *state both receive X's dynamic scale.
+ *   seed == 0: one pass over X casts it with s_old = *state (the scale lags
+ *              one call behind, so X is read once), and the same pass finds
+ *              max|X|; then a one-workgroup kernel sets
+ *                *x_scale = s_old
+ *                s_new    = max(fl32(max|X| / 448), 1e-12f)
+ *                *state   = max(d*s_old + ((1-d)*s_new)*(1 + 0.1f*T), 1e-12f)
+ *              in fp32, each operation rounded on its own (no fused
+ *              multiply-add), in that order.
+ * Pass *x_scale to fp8q_linear(FP8Q_W8A8, ...) with the codes.
+ *
+ *   decay        d in [0, 1]; 1 freezes the state, 0 follows the last tensor
+ *   temperature  T, finite and >= 0 (0 gives the plain average)
+ *   state        on a call with seed == 0 it must hold a positive finite scale
+ *                (from a seeded call); read and written by the device
+ *   workspace    at least fp8q_quantize_act_workspace_size(m, k) bytes,
+ *                16-byte aligned, no initialisation needed
+ *   x_fp8, x_scale, state and workspace must not overlap each other or x.
+ * m == 0 counts as a tensor whose maximum is 0.  k must be >= 1.  Bit-exact.
+ * Two kernels run on `stream` in either case; calls that share a state must be
+ * ordered on one stream.
+ */
+fp8q_status fp8q_quantize_act_ema(const uint16_t *x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                                  uint8_t *x_fp8, int64_t ld_q, float *x_scale, float *state,
+                                  float decay, float temperature, int seed,
+                                  void *workspace, size_t workspace_bytes,
+                                  int32_t *nonfinite_flag, hipStream_t stream);
 
 /*
  * The scaled linear layer, Y = X . dequant(W)^T, in the write-up's modes

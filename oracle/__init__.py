@@ -95,7 +95,7 @@ def _ptr(a: np.ndarray) -> int:
 def _need(a: np.ndarray, dtype, name: str) -> np.ndarray:
     if a.dtype != dtype:
         raise TypeError(f"{name}: expected {np.dtype(dtype)}, got {a.dtype}")
-    if a.ndim == 2 and a.strides[1] != a.itemsize:
+    if a.ndim == 2 and a.size and a.strides[1] != a.itemsize:
         raise ValueError(f"{name}: last dimension must be contiguous")
     return a
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.fp8q_abi_version() == 1
+    assert L.fp8q_abi_version() == 2
     for s in range(5):
         assert L.fp8q_status_string(s).startswith(b"FP8Q")
     assert L.fp8q_status_string(99) == b"FP8Q: unknown status"
@@ -133,6 +133,35 @@ def test_quantize_host_validation(L):
     assert L.fp8q_quantize_act(NULL, -1, 8, 8, NULL, 8, NULL, NULL, 0, NULL, NULL) == 1
     assert L.fp8q_cast_f32_to_e4m3(NULL, -1, NULL, NULL) == 1
     assert L.fp8q_cast_f32_to_e4m3(NULL, 0, NULL, NULL) == 0
+
+
+def test_act_scale_host_validation(L):
+    """Static / EMA entry points reject bad arguments before touching a device."""
+    st = L.fp8q_quantize_act_static
+    assert st(NULL, 0, 8, 8, NULL, NULL, 8, NULL, NULL) == 0          # empty: no-op
+    assert st(NULL, -1, 8, 8, NULL, NULL, 8, NULL, NULL) == 1
+    assert st(NULL, 4, 0, 8, NULL, NULL, 8, NULL, NULL) == 1
+    assert st(NULL, 4, 8, 4, NULL, NULL, 8, NULL, NULL) == 1           # ld_x < k
+    assert st(NULL, 4, 8, 8, NULL, NULL, 7, NULL, NULL) == 1           # ld_q < k
+    ema = L.fp8q_quantize_act_ema
+    ws = ctypes.c_void_p(0x1000)
+    need = L.fp8q_quantize_act_workspace_size(4, 8)
+
+    def call(m=4, k=8, ldx=8, ldq=8, decay=0.9999, temp=0.0, w=ws, nw=need):
+        return ema(NULL, m, k, ldx, NULL, ldq, NULL, NULL, decay, temp, 0, w, nw, NULL, NULL)
+
+    for bad in (-0.1, 1.5, float("nan"), float("inf")):
+        assert call(decay=bad) == 1, bad
+        assert "decay" in L.fp8q_last_error().decode()
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert call(temp=bad) == 1, bad
+        assert "temperature" in L.fp8q_last_error().decode()
+    assert call(m=-1) == 1
+    assert call(k=0) == 1
+    assert call(ldx=7) == 1
+    assert call(ldq=7) == 1
+    assert call(w=NULL, nw=0) == 4
+    assert call(nw=need - 1) == 4
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

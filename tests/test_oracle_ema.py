@@ -165,3 +165,13 @@ def test_ema_call_page_decay_barely_moves(orc):
     _, used, s2, _ = orc.quantize_act_ema(big, s, 0.9999, 0.0)
     assert used == s
     assert 1.0008 < float(s2) / float(s) < 1.0010
+
+
+def test_ema_call_empty_tensor(orc):
+    """An empty tensor has maximum 0: one step towards the 1e-12 floor, no codes."""
+    x = np.zeros((0, 64), np.uint16)
+    q, used, st, nf = orc.quantize_act_ema(x, 0.25, 0.5, 0.0)
+    assert q.shape == (0, 64) and not nf
+    assert used == np.float32(0.25)
+    assert st == orc.ema_scale(0.25, 1e-12, 0.5, 0.0)
+    assert abs(float(st) - (0.125 + 0.5e-12)) <= 1e-7 * 0.125
