@@ -81,6 +81,9 @@ def _load():
             lib.oracle_quantize_act_ema.restype = ctypes.c_int
             lib.oracle_quantize_act_ema.argtypes = [P, I64, I64, I64, P, I64, P, ctypes.c_float,
                                                     ctypes.c_float, ctypes.c_int, P]
+            lib.oracle_kv_cache_write.restype = ctypes.c_int
+            lib.oracle_kv_cache_write.argtypes = [P, P, I64, I64, I64, I64, P, P, P, I64, P, P,
+                                                  ctypes.c_int]
             lib.oracle_linear.restype = None
             lib.oracle_linear.argtypes = [ctypes.c_int, P, I64, I64, I64, ctypes.c_float,
                                           P, I64, I64, P, P, I64, P]
@@ -197,6 +200,33 @@ def quantize_act_ema(x_bf16: np.ndarray, state: float, decay: float, temperature
                                          float(np.float32(decay)), float(np.float32(temperature)),
                                          1 if seed else 0, _ptr(used))
     return q, np.float32(used[0]), np.float32(st[0]), bool(nf)
+
+
+def kv_cache_write(k_bf16: np.ndarray, v_bf16: np.ndarray, heads: int, slot: np.ndarray,
+                   k_cache: np.ndarray, v_cache: np.ndarray, running, calibrate: bool):
+    """Write new K/V tokens ([T, heads*head_dim] bf16 bits) into the E4M3 caches
+    ([heads, S, head_dim] uint8, updated in place) at rows `slot` (int64 [T]).
+
+    Returns (running float32 [2], scales float32 [2], flags int)."""
+    _need(k_bf16, np.uint16, "k")
+    _need(v_bf16, np.uint16, "v")
+    t, width = k_bf16.shape
+    if v_bf16.shape != (t, width) or width % heads:
+        raise ValueError("shape mismatch")
+    hd = width // heads
+    for c in (k_cache, v_cache):
+        if c.dtype != np.uint8 or c.ndim != 3 or c.shape[0] != heads or c.shape[2] != hd \
+                or not c.flags.c_contiguous:
+            raise ValueError("caches must be contiguous uint8 [heads, S, head_dim]")
+    if _ld(k_bf16) != _ld(v_bf16):
+        raise ValueError("k and v must share a row stride")
+    slot = np.ascontiguousarray(slot, dtype=np.int64)
+    run = np.array(running, np.float32).reshape(2).copy()
+    sc = np.empty(2, np.float32)
+    fl = _load().oracle_kv_cache_write(_ptr(k_bf16), _ptr(v_bf16), t, heads, hd, _ld(k_bf16),
+                                       _ptr(slot), _ptr(k_cache), _ptr(v_cache), k_cache.shape[1],
+                                       _ptr(run), _ptr(sc), 1 if calibrate else 0)
+    return run, sc, int(fl)
 
 
 # ---------------------------------------------------------------- linear ----

@@ -29,6 +29,10 @@
  *                activation), fp8_w_fp16_a and fp8_w_fp8_a (FP8 weight and
  *                activation).
  *        §5.3 tip 2 -- a temperature term (1 + 0.1 T) on the new EMA term.
+ *   [P2] §3.2 -- the FP8 KV cache: a running maximum per attention layer,
+ *                raised by prefill batches, read as it stands by decode.
+ *   [P3] "Some Technical Notes About Llama 3" commentary, §3.2 -- the KV
+ *                cache layout [layers, kv_heads, seq_len, head_dim].
  *
  * Readings where the pages are silent or contradict each other (each one is
  * listed, with its reason, in the design notes of the repository):
@@ -351,6 +355,56 @@ int oracle_quantize_act_ema(const uint16_t *x, int64_t m, int64_t k, int64_t ld_
     *scale_used = s_old;
     *state = oracle_ema_scale(s_old, s_new, decay, temperature);
     return nf;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 KV-cache write with an online running-max scale.                      */
+/* [P2 §3.2] KV values appear only at inference time, so each attention      */
+/* layer keeps a running maximum: every prefill batch raises it and the      */
+/* scale is computed from it; decode quantizes the new K/V with the latest   */
+/* scale as it stands.  [P2 §3.1] gives the scale formula and the cast.      */
+/* Readings: K and V keep a running maximum each; the layer cache is         */
+/* [heads, slots, head_dim] per tensor ([P3 §3.2]'s first layout, one layer); */
+/* a calibrating call raises the maximum before it casts its own batch.      */
+/*   k, v       [t_count, ld] bf16; row t holds heads * head_dim values,      */
+/*              head h at columns h*head_dim .. (h+1)*head_dim - 1            */
+/*   slot[t]    cache row of token t; rows outside [0, slots) are skipped     */
+/*   running[2] running max of |K| and |V| (in/out)                           */
+/*   scale_out[2]  the scales the codes of this call were made with           */
+/* Returns a bit set: 1 = a non-finite input, 2 = a slot out of range.        */
+/* ------------------------------------------------------------------------ */
+int oracle_kv_cache_write(const uint16_t *k, const uint16_t *v, int64_t t_count, int64_t heads,
+                          int64_t head_dim, int64_t ld, const int64_t *slot,
+                          uint8_t *k_cache, uint8_t *v_cache, int64_t slots,
+                          float *running, float *scale_out, int calibrate)
+{
+    const uint16_t *src[2] = {k, v};
+    uint8_t *dst[2] = {k_cache, v_cache};
+    const int64_t width = heads * head_dim;
+    int flags = 0;
+    for (int which = 0; which < 2; ++which) {
+        int nonfinite = 0;
+        float amax = act_amax(src[which], t_count, width, ld, &nonfinite);
+        if (nonfinite)
+            flags |= 1;
+        if (calibrate && amax > running[which])
+            running[which] = amax;
+        const float s = oracle_scale_from_amax(running[which]);
+        scale_out[which] = s;
+        for (int64_t t = 0; t < t_count; ++t) {
+            const int64_t row = slot[t];
+            if (row < 0 || row >= slots) {
+                flags |= 2;
+                continue;
+            }
+            for (int64_t h = 0; h < heads; ++h)
+                for (int64_t d = 0; d < head_dim; ++d) {
+                    const uint16_t x = src[which][t * ld + h * head_dim + d];
+                    dst[which][(h * slots + row) * head_dim + d] = quantize_one(bf16_value(x), s);
+                }
+        }
+    }
+    return flags;
 }
 
 /* ------------------------------------------------------------------------ */
