@@ -526,6 +526,80 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
     log(rows["a5_layer_decode_70b"])
     del layer
     torch.cuda.empty_cache()
+    rows.update(kv_rows(fq, L, up_bf16, ptr, workloads, np, torch, dev, iters, stream))
+    return rows
+
+
+def kv_rows(fq, L, up_bf16, ptr, workloads, np, torch, dev, iters, stream) -> dict:
+    """FP8 KV-cache writes of Llama-3-70B (8 KV heads x 128): a calibrating
+    8192-token prefill chunk, and one decode step (12 tokens) over 80 layers."""
+    rows = {}
+    heads, hd, layers = 8, 128, 80
+    width = heads * hd
+
+    def make_call(k, v, t, slot, kc, vc, run, sc, ws, nws, cal):
+        def call(h=None):
+            st = L.fp8q_kv_cache_write(ptr(k), ptr(v), t, heads, hd, width, ptr(slot), ptr(kc),
+                                       ptr(vc), kc.shape[1], ptr(run), ptr(sc), cal, ptr(ws), nws,
+                                       None, stream() if h is None else h)
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+        return call
+
+    t, s_rows = 8192, 8192
+    k = up_bf16(workloads.outlier_act(t, width, 901))
+    v = up_bf16(workloads.normal_act(t, width, 902))
+    slot = torch.arange(t, dtype=torch.int64, device=dev)
+    kc = torch.zeros((heads, s_rows, hd), dtype=torch.uint8, device=dev)
+    vc = torch.zeros_like(kc)
+    run = torch.zeros(2, dtype=torch.float32, device=dev)
+    sc = torch.zeros(2, dtype=torch.float32, device=dev)
+    nws = L.fp8q_kv_cache_workspace_size(t, heads, hd)
+    ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev)
+    b = 2 * (3.0 * t * width) + 8 * t
+    for name, cal, note in (("prefill_calibrate", 1, "K and V, 8192 tokens: absmax pass, "
+                             "then the cast with the raised running max"),
+                            ("prefill_held", 0, "K and V, 8192 tokens: one cast pass")):
+        ms = time_eager(torch, make_call(k, v, t, slot, kc, vc, run, sc, ws, nws, cal), iters)
+        rows[f"f3_kv_cache_write_{name}_70b"] = {
+            "shape": f"T={t} heads={heads} head_dim={hd}", "us": round(ms * 1e3, 2),
+            "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "note": note}
+        log(rows[f"f3_kv_cache_write_{name}_70b"])
+    del k, v, kc, vc, ws
+
+    # decode: 12 sequences append one token each, in every one of 80 layers
+    t = 12
+    per_layer = []
+    for layer in range(layers):
+        k = up_bf16(workloads.outlier_act(t, width, 1000 + layer))
+        v = up_bf16(workloads.normal_act(t, width, 2000 + layer))
+        kc = torch.zeros((heads, s_rows, hd), dtype=torch.uint8, device=dev)
+        vc = torch.zeros_like(kc)
+        run = torch.full((2,), 4.0, dtype=torch.float32, device=dev)
+        sc = torch.zeros(2, dtype=torch.float32, device=dev)
+        slot = torch.arange(t, dtype=torch.int64, device=dev) * 600 + 7
+        nws = L.fp8q_kv_cache_workspace_size(t, heads, hd)
+        ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev)
+        per_layer.append(make_call(k, v, t, slot, kc, vc, run, sc, ws, nws, 0))
+        per_layer[-1].keep = (k, v, kc, vc, run, sc, slot, ws)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+        for call in per_layer:
+            call(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    ms = time_eager(torch, g.replay, iters)
+    b = layers * (2 * (3.0 * t * width) + 8 * t)
+    rows["f3_kv_cache_write_decode_step_70b"] = {
+        "shape": f"{layers} layers x T={t} heads={heads} head_dim={hd}", "us": round(ms * 1e3, 2),
+        "us_per_layer": round(ms * 1e3 / layers, 2), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+        "timing": "one HIP graph of 80 single-launch writes",
+        "note": "launch-bound: 24 KB in and 24 KB out per layer"}
+    log(rows["f3_kv_cache_write_decode_step_70b"])
+    del per_layer, g
+    torch.cuda.empty_cache()
     return rows
 
 

@@ -9,6 +9,7 @@ computation runs in the library's HIP kernels; there is no CPU path.
     xq, x_scale = quantize_act(x_bf16)                # per tensor, dynamic
     xq = quantize_act_static(x_bf16, held_scale)      # per tensor, held scale
     ema = EmaActScale(dev); xq, x_scale = ema(x_bf16) # per tensor, EMA scale
+    kv_scale = kv_cache_write(k, v, slot, k_cache, v_cache, running, calibrate)
     y = linear(x_bf16, wq, w_scale)                   # fp8_w_bf16_a (decode)
     y = linear(xq, wq, w_scale, x_scale=x_scale)      # fp8_w_fp8_a  (prefill)
 
@@ -27,7 +28,7 @@ from ._lib import FP8Q_W8A8, FP8Q_W8A16, FP8Q_W8A16_F16, Fp8qError, check
 
 __all__ = [
     "quantize_weight", "quantize_act", "quantize_act_static", "quantize_act_ema",
-    "EmaActScale", "linear", "cast_f32_to_e4m3", "describe_linear",
+    "EmaActScale", "kv_cache_write", "linear", "cast_f32_to_e4m3", "describe_linear",
     "FP8Q_W8A16", "FP8Q_W8A8", "Fp8qError", "library_path",
 ]
 
@@ -171,6 +172,46 @@ class EmaActScale:
                                seed=not self.seeded, nonfinite_flag=nonfinite_flag)
         self.seeded = True
         return out
+
+
+def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, running_max: torch.Tensor,
+                   calibrate: bool, flags: torch.Tensor | None = None) -> torch.Tensor:
+    """Write new K/V tokens of one layer into its E4M3 caches.
+
+    k, v: bf16 [T, heads * head_dim] (token-major); slot: int64 [T] cache rows;
+    k_cache, v_cache: uint8 [heads, S, head_dim], contiguous; running_max:
+    float32 [2] (max |K|, max |V|), raised when `calibrate` (prefill), read as
+    it stands otherwise (decode).  Returns the float32 [2] K/V scales used.
+    """
+    t, width, ld = _matrix(k, "k", (torch.bfloat16,))
+    t2, width2, ld2 = _matrix(v, "v", (torch.bfloat16,))
+    if (t2, width2) != (t, width) or (t and ld2 != ld):
+        raise ValueError("k and v must have the same shape and row stride")
+    dev = k.device
+    for c, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if c.dtype != torch.uint8 or c.dim() != 3 or not c.is_contiguous() or c.device != dev:
+            raise ValueError(f"{name} must be a contiguous uint8 [heads, S, head_dim] on {dev}")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache differ in shape")
+    heads, slots, head_dim = k_cache.shape
+    if heads * head_dim != width:
+        raise ValueError(f"k has {width} values per token, the cache holds {heads} x {head_dim}")
+    if slot.dtype != torch.int64 or slot.shape != (t,) or slot.device != dev or \
+            (t and slot.stride(0) != 1):
+        raise ValueError(f"slot must be a contiguous int64 [{t}] on {dev}")
+    if running_max.dtype != torch.float32 or running_max.numel() != 2 or \
+            running_max.device != dev or not running_max.is_contiguous():
+        raise ValueError("running_max must be a contiguous float32 [2] on the same device")
+    scale = torch.empty(2, dtype=torch.float32, device=dev)
+    L = _lib.lib()
+    nws = L.fp8q_kv_cache_workspace_size(t, heads, head_dim)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    check(L.fp8q_kv_cache_write(
+        _ptr(k), _ptr(v), t, heads, head_dim, ld if t else width, _ptr(slot), _ptr(k_cache),
+        _ptr(v_cache), slots, _ptr(running_max), _ptr(scale), 1 if calibrate else 0, _ptr(ws),
+        nws, _ptr(flags), _stream(dev)))
+    return scale
 
 
 def linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,

@@ -115,6 +115,25 @@ fp8q_status check_ptr(const void *p, const char *name, int dev, size_t align)
     return FP8Q_OK;
 }
 
+// The bytes [p, p + bytes) must lie inside one device allocation (the one
+// hipMemGetAddressRange reports for p).  A runtime that cannot answer skips
+// the check.
+fp8q_status check_within_allocation(const void *p, size_t bytes, const char *name)
+{
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    hipError_t e = hipMemGetAddressRange(&base, &size, const_cast<void *>(p));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return FP8Q_OK;
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+    if (q < b || q - b + bytes > size)
+        return fail(FP8Q_ERR_INVALID_ARG, "%s: %zu bytes from this pointer run past its allocation",
+                    name, bytes);
+    return FP8Q_OK;
+}
+
 // Byte extent of a row-major [rows, cols] matrix with row stride ld.
 size_t extent(int64_t rows, int64_t cols, int64_t ld, size_t elem)
 {
@@ -320,6 +339,80 @@ fp8q_status fp8q_quantize_act_ema(const uint16_t *x_bf16, int64_t m, int64_t k, 
                                                   nonfinite_flag, stream);
     if (e != hipSuccess)
         return hip_fail(e, "EMA activation quantization launch");
+    return ok();
+}
+
+size_t fp8q_kv_cache_workspace_size(int64_t tokens, int64_t heads, int64_t head_dim)
+{
+    if (tokens < 0 || heads < 1 || head_dim < 8)
+        return 0;
+    return round_up((size_t)2 * fp8q::launch::kv_blocks(tokens, heads, head_dim) * sizeof(uint32_t),
+                    256);
+}
+
+fp8q_status fp8q_kv_cache_write(const uint16_t *k_bf16, const uint16_t *v_bf16, int64_t tokens,
+                                int64_t heads, int64_t head_dim, int64_t ld,
+                                const int64_t *slot, uint8_t *k_cache, uint8_t *v_cache,
+                                int64_t slots, float *running_max, float *scale_out,
+                                int calibrate, void *workspace, size_t workspace_bytes,
+                                int32_t *flags, hipStream_t stream)
+{
+    if (tokens < 0 || heads < 1 || slots < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "need tokens >= 0, heads >= 1 and slots >= 1");
+    if (head_dim < 8 || head_dim % 8 != 0)
+        return fail(FP8Q_ERR_INVALID_ARG, "head_dim must be a positive multiple of 8 (got %lld)",
+                    (long long)head_dim);
+    const int64_t width = heads * head_dim;
+    if (width > ((int64_t)1 << 30) || slots > ((int64_t)1 << 40))
+        return fail(FP8Q_ERR_INVALID_ARG, "heads * head_dim or slots too large");
+    FP8Q_TRY(check_ld(ld, width, 8, "ld"));
+    if (tokens > 0 && tokens > (((int64_t)1 << 31) - 1) / (width / 8))
+        return fail(FP8Q_ERR_INVALID_ARG, "tokens * heads * head_dim / 8 must stay below 2^31");
+    const size_t need = fp8q_kv_cache_workspace_size(tokens, heads, head_dim);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(FP8Q_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                    workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+    int dev = 0;
+    FP8Q_TRY(prepare(stream, &dev));
+    if (tokens > 0) {
+        FP8Q_TRY(check_ptr(k_bf16, "k_bf16", dev, 16));
+        FP8Q_TRY(check_ptr(v_bf16, "v_bf16", dev, 16));
+        FP8Q_TRY(check_ptr(slot, "slot", dev, 8));
+    }
+    FP8Q_TRY(check_ptr(k_cache, "k_cache", dev, 8));
+    FP8Q_TRY(check_ptr(v_cache, "v_cache", dev, 8));
+    FP8Q_TRY(check_ptr(running_max, "running_max", dev, 4));
+    FP8Q_TRY(check_ptr(scale_out, "scale_out", dev, 4));
+    FP8Q_TRY(check_ptr(workspace, "workspace", dev, 16));
+    if (flags != nullptr)
+        FP8Q_TRY(check_ptr(flags, "flags", dev, 4));
+    const size_t ein = tokens > 0 ? extent(tokens, width, ld, 2) : 0;
+    const size_t ecache = (size_t)heads * (size_t)slots * (size_t)head_dim;
+    FP8Q_TRY(check_within_allocation(k_cache, ecache, "k_cache"));
+    FP8Q_TRY(check_within_allocation(v_cache, ecache, "v_cache"));
+    const void *outs[5] = {k_cache, v_cache, running_max, scale_out, workspace};
+    const size_t lens[5] = {ecache, ecache, 8, 8, need};
+    const void *ins[3] = {k_bf16, v_bf16, slot};
+    const size_t inl[3] = {ein, ein, tokens > 0 ? (size_t)tokens * 8 : 0};
+    for (int a = 0; a < 5; ++a) {
+        for (int b = 0; b < 3; ++b)
+            if (inl[b] > 0 && overlap(outs[a], lens[a], ins[b], inl[b]))
+                return fail(FP8Q_ERR_INVALID_ARG, "an output overlaps k, v or slot");
+        for (int b = a + 1; b < 5; ++b)
+            if (overlap(outs[a], lens[a], outs[b], lens[b]))
+                return fail(FP8Q_ERR_INVALID_ARG,
+                            "caches, running_max, scale_out and workspace must not overlap");
+    }
+    if (flags != nullptr)
+        for (int a = 0; a < 5; ++a)
+            if (overlap(flags, 4, outs[a], lens[a]))
+                return fail(FP8Q_ERR_INVALID_ARG, "flags overlaps an output");
+    hipError_t e = fp8q::launch::kv_cache_write(k_bf16, v_bf16, tokens, heads, head_dim, ld, slot,
+                                                k_cache, v_cache, slots, running_max, scale_out,
+                                                calibrate != 0, static_cast<uint32_t *>(workspace),
+                                                flags, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "KV-cache write launch");
     return ok();
 }
 

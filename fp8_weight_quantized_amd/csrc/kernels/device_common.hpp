@@ -39,6 +39,12 @@ __device__ __forceinline__ uint32_t abs_key_max2(uint32_t pair)
     return lo > hi ? lo : hi;
 }
 
+// Largest |bf16| key of a 16-byte chunk (8 values).
+__device__ __forceinline__ uint32_t key_max8(uint4 v)
+{
+    return max(max(abs_key_max2(v.x), abs_key_max2(v.y)), max(abs_key_max2(v.z), abs_key_max2(v.w)));
+}
+
 // Scale from an absolute maximum given as a |bf16| key:
 // s = max(fl32(amax / 448), 1e-12f), with an IEEE division.
 __device__ __forceinline__ float scale_from_key(uint32_t key)

@@ -39,6 +39,14 @@ hipError_t quantize_act_ema(const uint16_t *x, int64_t m, int64_t k, int64_t ld_
 
 hipError_t cast_f32(const float *x, int64_t count, uint8_t *out, hipStream_t stream);
 
+// ---- FP8 KV cache ------------------------------------------------------------
+// Blocks per tensor of the KV kernels (the workspace holds 2 * that many words).
+int kv_blocks(int64_t tokens, int64_t heads, int64_t head_dim);
+hipError_t kv_cache_write(const uint16_t *k, const uint16_t *v, int64_t tokens, int64_t heads,
+                          int64_t head_dim, int64_t ld, const int64_t *slot, uint8_t *k_cache,
+                          uint8_t *v_cache, int64_t slots, float *running, float *scale_out,
+                          bool calibrate, uint32_t *partial, int32_t *flags, hipStream_t stream);
+
 // ---- W8A16 (fp8_w_bf16_a) skinny GEMM --------------------------------------
 struct W8A16Plan {
     enum Kind { kRows = 0, kTile = 1 };

@@ -124,10 +124,6 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight_scalar(
 // Activations, pass 1: each workgroup writes the |x| key maximum of its share
 // of the tensor to partial[blockIdx.x].  No atomics, no initialisation.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t key_max8(uint4 v)
-{
-    return max(max(abs_key_max2(v.x), abs_key_max2(v.y)), max(abs_key_max2(v.z), abs_key_max2(v.w)));
-}
 
 // Layouts of an activation tensor, from fastest to most general.
 enum ActLayout : int {

@@ -19,7 +19,7 @@
  *   per channel, activations per tensor) and §3.1 the conversion recipe;
  *   "Llama 3 精读" FP8 + 128K write-up (called "the write-up") §3.1 step 3
  *   names the FP8 MatMul modes, §3.1 step 2 and §5.3 tip 2 the EMA
- *   activation scale.
+ *   activation scale; the deployment guide §3.2 gives the FP8 KV cache.
  *
  * Errors.  Arguments are validated on the host before anything is enqueued;
  * on any error nothing is launched and a status other than FP8Q_OK is
@@ -171,6 +171,51 @@ fp8q_status fp8q_quantize_act_ema(const uint16_t *x_bf16, int64_t m, int64_t k, 
                                   float decay, float temperature, int seed,
                                   void *workspace, size_t workspace_bytes,
                                   int32_t *nonfinite_flag, hipStream_t stream);
+
+/*
+ * FP8 KV-cache write with an online running-max scale (deployment guide §3.2:
+ * KV values exist only at inference time, so each attention layer keeps a
+ * running maximum that prefill batches raise and from which the scale is
+ * computed; decode quantizes new K/V with the latest scale).  K and V keep a
+ * running maximum each; scale and cast are those of §3.1.  One call writes
+ * the new tokens of one layer.
+ *
+ *   k_bf16, v_bf16  [tokens, ld] bf16, token-major as the k/v projections
+ *                   produce them; row t holds heads * head_dim values, head h
+ *                   at columns h*head_dim ... ; 16-byte aligned, ld % 8 == 0
+ *   slot     [tokens] int64: the cache row of each token (e.g. its position);
+ *            rows must be distinct within a call (else which token lands
+ *            there is unspecified).  A row outside [0, slots) is not written
+ *            and sets flag bit 2.
+ *   k_cache, v_cache  [heads, slots, head_dim] E4M3 codes of one layer (the
+ *            contiguous [layers, kv_heads, seq_len, head_dim] layout of the
+ *            "Some Technical Notes About Llama 3" commentary §3.2, one layer);
+ *            8-byte aligned; each must lie inside one device allocation
+ *   running_max  [2] fp32: max |K|, max |V| seen by calibrating calls (in/out;
+ *            start at 0)
+ *   scale_out    [2] fp32 out: the K and V scales this call's codes use,
+ *            max(fl32(running / 448), 1e-12f)
+ *   calibrate != 0 (prefill / warm-up): running = max(running, max|batch|)
+ *            first, then the batch is cast with the raised scales (two passes
+ *            over the batch, nothing saturates).
+ *   calibrate == 0 (decode): one pass with the scales of the running maxima
+ *            as they stand; values beyond 448 * scale saturate.  Before any
+ *            calibrating call the scale is the 1e-12 floor (the page's cold
+ *            start: warm up first).
+ *   workspace  fp8q_kv_cache_workspace_size(tokens, heads, head_dim) bytes,
+ *            16-byte aligned, no initialisation needed
+ *   flags    optional int32, OR-ed: 1 = NaN/Inf input, 2 = slot out of range
+ * head_dim must be a multiple of 8; tokens * heads * head_dim / 8 < 2^31.
+ * Codes already in the cache keep the scale they were written with: a
+ * calibrating call that raises the maximum does not rewrite them.  Bit-exact.
+ */
+size_t fp8q_kv_cache_workspace_size(int64_t tokens, int64_t heads, int64_t head_dim);
+fp8q_status fp8q_kv_cache_write(const uint16_t *k_bf16, const uint16_t *v_bf16, int64_t tokens,
+                                int64_t heads, int64_t head_dim, int64_t ld,
+                                const int64_t *slot, uint8_t *k_cache, uint8_t *v_cache,
+                                int64_t slots, float *running_max, float *scale_out,
+                                int calibrate, void *workspace, size_t workspace_bytes,
+                                int32_t *flags, hipStream_t stream);
 
 /*
  * The scaled linear layer, Y = X . dequant(W)^T, in the write-up's modes

@@ -164,6 +164,30 @@ def test_act_scale_host_validation(L):
     assert call(nw=need - 1) == 4
 
 
+def test_kv_cache_host_validation(L):
+    """The KV-cache write rejects bad shapes before touching a device."""
+    kv = L.fp8q_kv_cache_write
+    ws = ctypes.c_void_p(0x1000)
+
+    def call(t=4, heads=8, hd=128, ld=1024, slots=16, w=ws, nw=None):
+        if nw is None:
+            nw = L.fp8q_kv_cache_workspace_size(max(t, 0), heads, hd)
+        return kv(NULL, NULL, t, heads, hd, ld, NULL, NULL, NULL, slots, NULL, NULL, 1, w, nw,
+                  NULL, NULL)
+
+    assert call(t=-1) == 1
+    assert call(heads=0) == 1
+    assert call(slots=0) == 1
+    assert call(hd=0) == 1 and call(hd=12) == 1 and call(hd=4, ld=32) == 1
+    assert call(ld=1000) == 1                     # below heads * head_dim
+    assert call(ld=1028) == 1                     # not a multiple of 8
+    assert call(t=1 << 28) == 1                   # tokens * width / 8 reaches 2^31
+    assert call(w=NULL, nw=0) == 4
+    assert call(nw=L.fp8q_kv_cache_workspace_size(4, 8, 128) - 1) == 4
+    assert L.fp8q_kv_cache_workspace_size(8192, 8, 128) == 2 * 1024 * 4
+    assert L.fp8q_kv_cache_workspace_size(12, 8, 128) == 256
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     from fp8_weight_quantized_amd import _lib
     monkeypatch.setattr(_lib, "_lib", None)
