@@ -84,6 +84,11 @@ def _load():
             lib.oracle_kv_cache_write.restype = ctypes.c_int
             lib.oracle_kv_cache_write.argtypes = [P, P, I64, I64, I64, I64, P, P, P, I64, P, P,
                                                   ctypes.c_int]
+            lib.oracle_quantize_weight_grouped.restype = ctypes.c_int
+            lib.oracle_quantize_weight_grouped.argtypes = [P, I64, I64, I64, I64, P, I64, P]
+            lib.oracle_linear_grouped.restype = None
+            lib.oracle_linear_grouped.argtypes = [ctypes.c_int, P, I64, I64, I64, ctypes.c_float,
+                                                  P, I64, I64, P, I64, P, I64, P]
             lib.oracle_linear.restype = None
             lib.oracle_linear.argtypes = [ctypes.c_int, P, I64, I64, I64, ctypes.c_float,
                                           P, I64, I64, P, P, I64, P]
@@ -155,6 +160,19 @@ def quantize_weight(w_bf16: np.ndarray):
     q = np.empty((n, k), np.uint8)
     s = np.empty(n, np.float32)
     nf = _load().oracle_quantize_weight(_ptr(w_bf16), n, k, _ld(w_bf16), _ptr(q), k, _ptr(s))
+    return q, s, bool(nf)
+
+
+def quantize_weight_grouped(w_bf16: np.ndarray, group: int):
+    """bf16 bits [N, K] -> (codes uint8 [N, K], scale float32 [N, ceil(K/group)], nonfinite)."""
+    _need(w_bf16, np.uint16, "w_bf16")
+    if group < 1:
+        raise ValueError("group must be >= 1")
+    n, k = w_bf16.shape
+    q = np.empty((n, k), np.uint8)
+    s = np.empty((n, -(-k // group)), np.float32)
+    nf = _load().oracle_quantize_weight_grouped(_ptr(w_bf16), n, k, _ld(w_bf16), group, _ptr(q),
+                                                k, _ptr(s))
     return q, s, bool(nf)
 
 
@@ -230,6 +248,41 @@ def kv_cache_write(k_bf16: np.ndarray, v_bf16: np.ndarray, heads: int, slot: np.
 
 
 # ---------------------------------------------------------------- linear ----
+def linear_grouped(mode: int, x: np.ndarray, wq: np.ndarray, w_scale: np.ndarray, group: int,
+                   x_scale: float | None = None, rows: np.ndarray | None = None) -> np.ndarray:
+    """fp64 Y = X . dequant(Wq)^T with per-group weight scales [N, ceil(K/group)]."""
+    if mode in (MODE_W8A16, MODE_W8A16_F16):
+        _need(x, np.uint16, "x")
+        if x_scale is not None:
+            raise ValueError("the 16-bit activation modes take no activation scale")
+        xs = 0.0
+    elif mode == MODE_W8A8:
+        _need(x, np.uint8, "x")
+        if x_scale is None:
+            raise ValueError("fp8_w_fp8_a needs the activation scale")
+        xs = float(np.float32(x_scale))
+    else:
+        raise ValueError("unknown mode")
+    _need(wq, np.uint8, "wq")
+    m, k = x.shape
+    n, k2 = wq.shape
+    w_scale = np.ascontiguousarray(w_scale, dtype=np.float32)
+    if k2 != k or group < 1 or w_scale.shape != (n, -(-k // group)):
+        raise ValueError("shape mismatch")
+    if rows is None:
+        nrows, rp = m, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        if rows.size and (rows.min() < 0 or rows.max() >= m):
+            raise IndexError("row index out of range")
+        nrows, rp = rows.size, _ptr(rows)
+    y = np.empty((nrows, n), np.float64)
+    if nrows and n:
+        _load().oracle_linear_grouped(mode, _ptr(x), m, k, _ld(x), xs, _ptr(wq), n, _ld(wq),
+                                      _ptr(w_scale), group, rp, nrows, _ptr(y))
+    return y
+
+
 def f16_value(bits: int) -> float:
     """IEEE binary16 value of a 16-bit pattern, decoded from its bit fields."""
     return _load().oracle_f16_value(int(bits) & 0xFFFF)

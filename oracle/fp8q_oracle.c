@@ -29,6 +29,7 @@
  *                activation), fp8_w_fp16_a and fp8_w_fp8_a (FP8 weight and
  *                activation).
  *        §5.3 tip 2 -- a temperature term (1 + 0.1 T) on the new EMA term.
+ *   [P2] §4.3 -- per-group granularity, the step beyond per-channel.
  *   [P2] §3.2 -- the FP8 KV cache: a running maximum per attention layer,
  *                raised by prefill batches, read as it stands by decode.
  *   [P3] "Some Technical Notes About Llama 3" commentary, §3.2 -- the KV
@@ -243,6 +244,42 @@ int oracle_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w
         scale[r] = s;
         for (int64_t c = 0; c < k; ++c)
             q[r * ld_q + c] = quantize_one(bf16_value(row[c]), s);
+    }
+    return nonfinite;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-group weight quantization.                                            */
+/* [P2 §4.3] names per-group granularity as the step beyond per-channel      */
+/* scales.  Reading: each output row is cut along the input dimension into   */
+/* groups of `group` consecutive values (the last one may be shorter), and   */
+/* each group gets the scale of [P2 §3.1] over its own values.               */
+/* scale is [n, ceil(k / group)], row-major.  group == k is per-channel.     */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_weight_grouped(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                                   int64_t group, uint8_t *q, int64_t ld_q, float *scale)
+{
+    const int64_t ngroups = (k + group - 1) / group;
+    int nonfinite = 0;
+#pragma omp parallel for schedule(static) reduction(| : nonfinite)
+    for (int64_t r = 0; r < n; ++r) {
+        const uint16_t *row = w + r * ld_w;
+        for (int64_t g = 0; g < ngroups; ++g) {
+            const int64_t c0 = g * group;
+            const int64_t c1 = c0 + group < k ? c0 + group : k;
+            float amax = 0.0f;
+            for (int64_t c = c0; c < c1; ++c) {
+                float a = fabsf(bf16_value(row[c]));
+                if (!isfinite(a))
+                    nonfinite = 1;
+                if (a > amax)
+                    amax = a;
+            }
+            float s = oracle_scale_from_amax(amax);
+            scale[r * ngroups + g] = s;
+            for (int64_t c = c0; c < c1; ++c)
+                q[r * ld_q + c] = quantize_one(bf16_value(row[c]), s);
+        }
     }
     return nonfinite;
 }
@@ -473,6 +510,51 @@ void oracle_linear(int mode, const void *x, int64_t m, int64_t k, int64_t ld_x,
                     acc += tab[xrow[c]] * tab[wrow[c]];
                 y[i * n + j] = acc * ((double)x_scale * (double)w_scale[j]);
             }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* The linear layer with per-group weight scales, in fp64.                   */
+/* Each group's products are summed, then scaled by that group's scale:      */
+/*   Y[m,n] = s_x * sum_g s_w[n,g] * sum_{k in g} a(X[m,k]) * dec(Wq[n,k])   */
+/* with a() the activation value of the mode (as in oracle_linear) and       */
+/* s_x = 1 in the 16-bit modes.  Groups and scales as in                     */
+/* oracle_quantize_weight_grouped.                                           */
+/* ------------------------------------------------------------------------ */
+void oracle_linear_grouped(int mode, const void *x, int64_t m, int64_t k, int64_t ld_x,
+                           float x_scale, const uint8_t *wq, int64_t n, int64_t ld_w,
+                           const float *w_scale, int64_t group, const int64_t *rows,
+                           int64_t nrows, double *y)
+{
+    double tab[256];
+    oracle_e4m3_table(tab);
+    const int64_t ngroups = (k + group - 1) / group;
+    if (rows == NULL)
+        nrows = m;
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int64_t i = 0; i < nrows; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t r = rows ? rows[i] : i;
+            const uint8_t *wrow = wq + j * ld_w;
+            double total = 0.0;
+            for (int64_t g = 0; g < ngroups; ++g) {
+                const int64_t c0 = g * group;
+                const int64_t c1 = c0 + group < k ? c0 + group : k;
+                double acc = 0.0;
+                for (int64_t c = c0; c < c1; ++c) {
+                    double a;
+                    if (mode == 0)
+                        a = (double)bf16_value(((const uint16_t *)x)[r * ld_x + c]);
+                    else if (mode == 2)
+                        a = oracle_f16_value(((const uint16_t *)x)[r * ld_x + c]);
+                    else
+                        a = tab[((const uint8_t *)x)[r * ld_x + c]];
+                    acc += a * tab[wrow[c]];
+                }
+                total += acc * (double)w_scale[j * ngroups + g];
+            }
+            y[i * n + j] = mode == 1 ? total * (double)x_scale : total;
         }
     }
 }
