@@ -286,6 +286,49 @@ def main() -> int:
             "frac_hbm": round(bytes8 / (us8 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "mode": "fp8_w_fp8_a at decode sizes (E4M3 activations, per-tensor scale)"}
         log(rows["f1_w8a8_q_proj_decode"])
+
+        # per-group weight scales (groups of 128) on the same decode step
+        G = 128
+        wqg, wsg = fq.quantize_weight_grouped(up_bf16(w_bits), G)
+        pool_g = torch.empty((copies_n, N, K), dtype=torch.uint8, device=dev)
+        pool_g[:] = wqg.unsqueeze(0)
+        del wqg
+        wsng = {m: L.fp8q_linear_grouped_workspace_size(0, m, N, K, G) for m in DECODE_MS}
+        wspg = {m: (torch.zeros(wsng[m], dtype=torch.uint8, device=dev) if wsng[m] else None)
+                for m in DECODE_MS}
+
+        def decode_step_g(i: int, stream: int):
+            for j, m in enumerate(DECODE_MS):
+                c = (len(DECODE_MS) * i + j) % copies_n
+                st = L.fp8q_linear_grouped(0, ptr(xs[m]), m, K, K, None, ptr(pool_g[c]), N, K,
+                                           ptr(wsg), G, ptr(ys[m]), N, ptr(wspg[m]), wsng[m],
+                                           stream)
+                if st != 0:
+                    raise RuntimeError(_lib.last_error())
+        gg = torch.cuda.CUDAGraph()
+        sg = torch.cuda.Stream(device=dev)
+        sg.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.graph(gg, stream=sg, capture_error_mode="relaxed"):
+            h = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(rot):
+                decode_step_g(i, h)
+        torch.cuda.current_stream(dev).wait_stream(sg)
+        gg.replay()
+        torch.cuda.synchronize()
+        start.record()
+        gg.replay()
+        end.record()
+        end.synchronize()
+        usg = start.elapsed_time(end) * 1e3 / rot
+        bytes_g = sum(N * K + 4 * N * (K // G) + 2 * m * K + 2 * m * N for m in DECODE_MS)
+        rows["f4_grouped_q_proj_decode"] = {
+            "shape": "N=K=4096, M=1,8,32,64 per step, groups of 128", "us_per_step": round(usg, 3),
+            "GB/s": round(bytes_g / (usg * 1e-6) / 1e9, 1),
+            "frac_hbm": round(bytes_g / (usg * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "mode": "fp8_w_bf16_a with per-group weight scales (k_w8a16_tile, grouped)"}
+        log(rows["f4_grouped_q_proj_decode"])
+        del pool_g, gg
+        torch.cuda.empty_cache()
         rows.update(other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev))
         result["rows"] = rows
 
@@ -484,6 +527,21 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
                 "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             log(rows["a1a2_quantize_weight_gate_proj_70b"])
+            sg_ = torch.empty((lin.n, lin.k // 128), dtype=torch.float32, device=dev)
+
+            def wquant_g(w=w, q=q, s=sg_, lin=lin):
+                st = L.fp8q_quantize_weight_grouped(ptr(w), lin.n, lin.k, lin.k, 128, ptr(q), lin.k,
+                                                    ptr(s), None, stream())
+                if st != 0:
+                    raise RuntimeError(fq._lib.last_error())
+            ms = time_eager(torch, wquant_g, iters)
+            b = 3.0 * lin.n * lin.k + 4 * lin.n * (lin.k // 128)
+            rows["f4_quantize_weight_grouped_gate_proj_70b"] = {
+                "shape": f"N={lin.n} K={lin.k}, groups of 128", "us": round(ms * 1e3, 2),
+                "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(rows["f4_quantize_weight_grouped_gate_proj_70b"])
+            del sg_
         wq, ws = fq.quantize_weight(w)
         del w
         x = up_bf16(workloads.activation(wl, m, lin.k))
@@ -519,6 +577,38 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
         mso = time_eager(torch, one, iters)
         bb = lin.n * lin.k + 4 * lin.n + 2 * m * lin.k + 2 * m * lin.n
         per[lin.name] = {"us": round(mso * 1e3, 2), "GB/s": round(bb / (mso * 1e-3) / 1e9, 1)}
+    # the same layer with per-group weight scales (groups of 128)
+    G = 128
+    layer_g = []
+    for lin, wq, ws, x, y, wsb, nws in layer:
+        wsg = torch.ones((lin.n, lin.k // G), dtype=torch.float32, device=dev) * ws[:, None]
+        nwg = L.fp8q_linear_grouped_workspace_size(0, m, lin.n, lin.k, G)
+        wsbg = torch.zeros(nwg, dtype=torch.uint8, device=dev) if nwg else None
+        layer_g.append((lin, wq, wsg.contiguous(), x, y, wsbg, nwg))
+
+    def layer_step_g(h):
+        for lin, wq, wsg, x, y, wsb, nws in layer_g:
+            st = L.fp8q_linear_grouped(0, ptr(x), m, lin.k, lin.k, None, ptr(wq), lin.n,
+                                       wq.stride(0), ptr(wsg), G, ptr(y), lin.n, ptr(wsb), nws, h)
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+    gg = torch.cuda.CUDAGraph()
+    sgs = torch.cuda.Stream(device=dev)
+    sgs.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(gg, stream=sgs, capture_error_mode="relaxed"):
+        layer_step_g(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.current_stream(dev).wait_stream(sgs)
+    msg = time_eager(torch, gg.replay, iters)
+    bg = sum(lin.n * lin.k + 4 * lin.n * (lin.k // G) + 2 * m * lin.k + 2 * m * lin.n
+             for lin, *_ in layer_g)
+    rows["f4_grouped_layer_decode_70b"] = {
+        "shape": "7 linears, M=12, groups of 128", "us": round(msg * 1e3, 2),
+        "GB/s": round(bg / (msg * 1e-3) / 1e9, 1),
+        "frac_hbm": round(bg / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "timing": "one HIP graph per layer step"}
+    log(rows["f4_grouped_layer_decode_70b"])
+    del layer_g, gg
+
     rows["a5_layer_decode_70b"] = {
         "shape": "7 linears, M=12", "weight_MB": round(b / 1e6, 1), "us": round(ms * 1e3, 2),
         "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

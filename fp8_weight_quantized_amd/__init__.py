@@ -6,6 +6,7 @@ only) and passes raw pointers and the current HIP stream.  Every step of the
 computation runs in the library's HIP kernels; there is no CPU path.
 
     wq, w_scale = quantize_weight(w_bf16)             # per output channel
+    wq, w_scale = quantize_weight_grouped(w_bf16, 128)  # per group of 128 inputs
     xq, x_scale = quantize_act(x_bf16)                # per tensor, dynamic
     xq = quantize_act_static(x_bf16, held_scale)      # per tensor, held scale
     ema = EmaActScale(dev); xq, x_scale = ema(x_bf16) # per tensor, EMA scale
@@ -27,7 +28,7 @@ from . import _lib
 from ._lib import FP8Q_W8A8, FP8Q_W8A16, FP8Q_W8A16_F16, Fp8qError, check
 
 __all__ = [
-    "quantize_weight", "quantize_act", "quantize_act_static", "quantize_act_ema",
+    "quantize_weight", "quantize_weight_grouped", "quantize_act", "quantize_act_static", "quantize_act_ema",
     "EmaActScale", "kv_cache_write", "linear", "cast_f32_to_e4m3", "describe_linear",
     "FP8Q_W8A16", "FP8Q_W8A8", "Fp8qError", "library_path",
 ]
@@ -214,13 +215,32 @@ def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot: torch.Tensor,
     return scale
 
 
+def quantize_weight_grouped(w: torch.Tensor, group: int = 128,
+                            nonfinite_flag: torch.Tensor | None = None):
+    """Per-group E4M3 quantization of a bf16 [N, K] weight: groups of `group`
+    (64, 128, 256 or 512) consecutive input values per output row.
+
+    Returns (codes uint8 [N, K], scale float32 [N, ceil(K / group)]).
+    """
+    n, k, ld = _matrix(w, "w", (torch.bfloat16,))
+    dev = w.device
+    q = _new_codes(n, k, dev)
+    scale = torch.empty((n, -(-k // group)), dtype=torch.float32, device=dev)
+    check(_lib.lib().fp8q_quantize_weight_grouped(
+        _ptr(w), n, k, ld, group, _ptr(q), q.stride(0) if n else _round_up(k, 16), _ptr(scale),
+        _ptr(nonfinite_flag), _stream(dev)))
+    return q, scale
+
+
 def linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
-           x_scale: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+           x_scale: torch.Tensor | None = None, out: torch.Tensor | None = None,
+           group: int | None = None) -> torch.Tensor:
     """Y = X . dequant(Wq)^T.
 
     x bf16 [M, K] with x_scale None  -> fp8_w_bf16_a (W8A16), bf16 Y.
     x fp16 [M, K] with x_scale None  -> fp8_w_fp16_a (W8A16, fp16), fp16 Y.
     x E4M3 codes [M, K] with x_scale -> fp8_w_fp8_a  (W8A8), bf16 Y.
+    group None: w_scale [N] (per channel); else w_scale [N, ceil(K / group)].
     """
     wq = _codes(wq)
     x = _codes(x)
@@ -238,11 +258,12 @@ def linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
     n, k2, ldw = _matrix(wq, "wq", (torch.uint8,))
     if k2 != k:
         raise ValueError(f"inner dimensions differ: x has K={k}, wq has K={k2}")
-    if w_scale.dtype != torch.float32 or w_scale.numel() != n or not w_scale.is_cuda:
-        raise ValueError("w_scale must be a float32 GPU tensor with N elements")
-    w_scale = w_scale.reshape(-1)
+    n_scales = n if group is None else n * -(-k // group)
+    if w_scale.dtype != torch.float32 or w_scale.numel() != n_scales or not w_scale.is_cuda:
+        raise ValueError(f"w_scale must be a float32 GPU tensor with {n_scales} elements")
     if not w_scale.is_contiguous():
         raise ValueError("w_scale must be contiguous")
+    w_scale = w_scale.reshape(-1)
     if x_scale is not None and (x_scale.dtype != torch.float32 or x_scale.numel() != 1 or not x_scale.is_cuda):
         raise ValueError("x_scale must be a float32 GPU tensor with one element")
     dev = x.device
@@ -253,10 +274,17 @@ def linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
     if (om, on) != (m, n):
         raise ValueError(f"out must be [{m}, {n}]")
     L = _lib.lib()
-    nws = L.fp8q_linear_workspace_size(mode, m, n, k)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
-    check(L.fp8q_linear(mode, _ptr(x), m, k, ldx, _ptr(x_scale), _ptr(wq), n, ldw,
-                        _ptr(w_scale), _ptr(out), ldy, _ptr(ws), nws, _stream(dev)))
+    if group is None:
+        nws = L.fp8q_linear_workspace_size(mode, m, n, k)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+        check(L.fp8q_linear(mode, _ptr(x), m, k, ldx, _ptr(x_scale), _ptr(wq), n, ldw,
+                            _ptr(w_scale), _ptr(out), ldy, _ptr(ws), nws, _stream(dev)))
+    else:
+        nws = L.fp8q_linear_grouped_workspace_size(mode, m, n, k, group)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+        check(L.fp8q_linear_grouped(mode, _ptr(x), m, k, ldx, _ptr(x_scale), _ptr(wq), n, ldw,
+                                    _ptr(w_scale), group, _ptr(out), ldy, _ptr(ws), nws,
+                                    _stream(dev)))
     return out
 
 

@@ -45,6 +45,9 @@ SIGNATURES = {
     "fp8q_quantize_act_static": (ST, [P, I64, I64, I64, P, P, I64, P, P]),
     "fp8q_quantize_act_ema": (ST, [P, I64, I64, I64, P, I64, P, P, ctypes.c_float,
                                    ctypes.c_float, ctypes.c_int, P, SZ, P, P]),
+    "fp8q_quantize_weight_grouped": (ST, [P, I64, I64, I64, I64, P, I64, P, P, P]),
+    "fp8q_linear_grouped_workspace_size": (SZ, [ST, I64, I64, I64, I64]),
+    "fp8q_linear_grouped": (ST, [ST, P, I64, I64, I64, P, P, I64, I64, P, I64, P, I64, P, SZ, P]),
     "fp8q_kv_cache_workspace_size": (SZ, [I64, I64, I64]),
     "fp8q_kv_cache_write": (ST, [P, P, I64, I64, I64, I64, P, P, P, I64, P, P, ctypes.c_int, P,
                                  SZ, P, P]),

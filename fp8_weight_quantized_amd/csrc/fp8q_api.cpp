@@ -421,10 +421,22 @@ fp8q_status fp8q_kv_cache_write(const uint16_t *k_bf16, const uint16_t *v_bf16, 
 // would leave most of the GPU idle.
 constexpr int64_t kW8A8DecodeMaxM = 64;
 
-size_t fp8q_linear_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k)
+namespace {
+
+bool valid_group(int64_t group)
+{
+    return group == 64 || group == 128 || group == 256 || group == 512;
+}
+
+// group == 0: one weight scale per output row; else per-group scales
+size_t linear_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t group)
 {
     if (m <= 0 || n <= 0 || k < 1)
         return 0;
+    if (group > 0)
+        return valid_group(group)
+                   ? round_up(fp8q::launch::plan_w8a16_grouped(m, n, k, group).workspace, 256)
+                   : 0;
     if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16 ||
         (mode == FP8Q_W8A8 && m <= kW8A8DecodeMaxM))
         return round_up(fp8q::launch::plan_w8a16(m, n, k).workspace, 256);
@@ -433,10 +445,9 @@ size_t fp8q_linear_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t 
     return 0;
 }
 
-fp8q_status fp8q_linear(fp8q_mode mode,
-                        const void *x, int64_t m, int64_t k, int64_t ld_x, const float *x_scale,
-                        const uint8_t *w_fp8, int64_t n, int64_t ld_w, const float *w_scale,
-                        uint16_t *y_bf16, int64_t ld_y,
+fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int64_t ld_x,
+                        const float *x_scale, const uint8_t *w_fp8, int64_t n, int64_t ld_w,
+                        const float *w_scale, int64_t group, uint16_t *y_bf16, int64_t ld_y,
                         void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (mode != FP8Q_W8A16 && mode != FP8Q_W8A8 && mode != FP8Q_W8A16_F16)
@@ -445,6 +456,9 @@ fp8q_status fp8q_linear(fp8q_mode mode,
     if (m < 0 || n < 0 || k < 1)
         return fail(FP8Q_ERR_INVALID_ARG, "need m >= 0, n >= 0, k >= 1 (m=%lld, n=%lld, k=%lld)",
                     (long long)m, (long long)n, (long long)k);
+    if (group != 0 && !valid_group(group))
+        return fail(FP8Q_ERR_INVALID_ARG, "group must be 64, 128, 256 or 512 (got %lld)",
+                    (long long)group);
     if (a16 && x_scale != nullptr)
         return fail(FP8Q_ERR_INVALID_ARG,
                     "fp8_w_bf16_a and fp8_w_fp16_a take no activation scale (x_scale must be NULL)");
@@ -458,11 +472,11 @@ fp8q_status fp8q_linear(fp8q_mode mode,
         (!fp8q::launch::w8a8_supports_ld(ld_x) || !fp8q::launch::w8a8_supports_ld(ld_w)))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_fp8_a needs ld_x and ld_w below 2^23 (got %lld, %lld)",
                     (long long)ld_x, (long long)ld_w);
-    if (a16 && (m + 63) / 64 > 65535)
-        return fail(FP8Q_ERR_INVALID_ARG, "the 16-bit activation modes take at most 65535 * 64 rows");
+    if ((a16 || group > 0) && (m + 63) / 64 > 65535)
+        return fail(FP8Q_ERR_INVALID_ARG, "the decode kernels take at most 65535 * 64 rows");
     if (m == 0 || n == 0)
         return ok();
-    const size_t need = fp8q_linear_workspace_size(mode, m, n, k);
+    const size_t need = linear_workspace(mode, m, n, k, group);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(FP8Q_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
                     workspace == nullptr ? (size_t)0 : workspace_bytes, need);
@@ -478,19 +492,27 @@ fp8q_status fp8q_linear(fp8q_mode mode,
         FP8Q_TRY(check_ptr(workspace, "workspace", dev, 16));
     const size_t ex = extent(m, k, ld_x, xelem), ew = extent(n, k, ld_w, 1),
                  ey = extent(m, n, ld_y, 2);
+    const size_t es = (size_t)n * 4 * (group > 0 ? (size_t)((k + group - 1) / group) : 1);
+    if (group > 0)
+        FP8Q_TRY(check_within_allocation(w_scale, es, "w_scale"));
     if (overlap(y_bf16, ey, x, ex) || overlap(y_bf16, ey, w_fp8, ew) ||
-        overlap(y_bf16, ey, w_scale, (size_t)n * 4) ||
+        overlap(y_bf16, ey, w_scale, es) ||
         (x_scale != nullptr && overlap(y_bf16, ey, x_scale, 4)) ||
         (need > 0 && (overlap(workspace, need, y_bf16, ey) || overlap(workspace, need, x, ex) ||
-                      overlap(workspace, need, w_fp8, ew))))
+                      overlap(workspace, need, w_fp8, ew) ||
+                      overlap(workspace, need, w_scale, es))))
         return fail(FP8Q_ERR_INVALID_ARG, "the output or workspace overlaps an input");
 
+    const int act = mode == FP8Q_W8A16     ? fp8q::launch::kW8A16ActBF16
+                    : mode == FP8Q_W8A16_F16 ? fp8q::launch::kW8A16ActF16
+                                             : fp8q::launch::kW8A16ActF8;
     hipError_t e;
-    if (a16 || m <= kW8A8DecodeMaxM) {
+    if (group > 0) {
+        const auto plan = fp8q::launch::plan_w8a16_grouped(m, n, k, group);
+        e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
+                                ld_y, workspace, stream);
+    } else if (a16 || m <= kW8A8DecodeMaxM) {
         const auto plan = fp8q::launch::plan_w8a16(m, n, k);
-        const int act = mode == FP8Q_W8A16     ? fp8q::launch::kW8A16ActBF16
-                        : mode == FP8Q_W8A16_F16 ? fp8q::launch::kW8A16ActF16
-                                                 : fp8q::launch::kW8A16ActF8;
         e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
                                 ld_y, workspace, stream);
     } else {
@@ -500,6 +522,78 @@ fp8q_status fp8q_linear(fp8q_mode mode,
     }
     if (e != hipSuccess)
         return hip_fail(e, "linear launch");
+    return ok();
+}
+
+}  // namespace
+
+size_t fp8q_linear_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k)
+{
+    return linear_workspace(mode, m, n, k, 0);
+}
+
+fp8q_status fp8q_linear(fp8q_mode mode,
+                        const void *x, int64_t m, int64_t k, int64_t ld_x, const float *x_scale,
+                        const uint8_t *w_fp8, int64_t n, int64_t ld_w, const float *w_scale,
+                        uint16_t *y_bf16, int64_t ld_y,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return linear_impl(mode, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, 0, y_bf16, ld_y,
+                       workspace, workspace_bytes, stream);
+}
+
+size_t fp8q_linear_grouped_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
+                                          int64_t group)
+{
+    return valid_group(group) ? linear_workspace(mode, m, n, k, group) : 0;
+}
+
+fp8q_status fp8q_linear_grouped(fp8q_mode mode,
+                                const void *x, int64_t m, int64_t k, int64_t ld_x,
+                                const float *x_scale, const uint8_t *w_fp8, int64_t n,
+                                int64_t ld_w, const float *w_scale, int64_t group,
+                                uint16_t *y_bf16, int64_t ld_y,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!valid_group(group))
+        return fail(FP8Q_ERR_INVALID_ARG, "group must be 64, 128, 256 or 512 (got %lld)",
+                    (long long)group);
+    return linear_impl(mode, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, group, y_bf16, ld_y,
+                       workspace, workspace_bytes, stream);
+}
+
+fp8q_status fp8q_quantize_weight_grouped(const uint16_t *w_bf16, int64_t n, int64_t k,
+                                         int64_t ld_w, int64_t group, uint8_t *w_fp8,
+                                         int64_t ld_q, float *w_scale, int32_t *nonfinite_flag,
+                                         hipStream_t stream)
+{
+    if (n < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "need n >= 0 and k >= 1 (n=%lld, k=%lld)", (long long)n,
+                    (long long)k);
+    if (!valid_group(group))
+        return fail(FP8Q_ERR_INVALID_ARG, "group must be 64, 128, 256 or 512 (got %lld)",
+                    (long long)group);
+    FP8Q_TRY(check_ld(ld_w, k, 1, "ld_w"));
+    FP8Q_TRY(check_ld(ld_q, k, 1, "ld_q"));
+    if (n == 0)
+        return ok();
+    int dev = 0;
+    FP8Q_TRY(prepare(stream, &dev));
+    FP8Q_TRY(check_ptr(w_bf16, "w_bf16", dev, 2));
+    FP8Q_TRY(check_ptr(w_fp8, "w_fp8", dev, 1));
+    FP8Q_TRY(check_ptr(w_scale, "w_scale", dev, 4));
+    if (nonfinite_flag != nullptr)
+        FP8Q_TRY(check_ptr(nonfinite_flag, "nonfinite_flag", dev, 4));
+    const size_t ew = extent(n, k, ld_w, 2), eq = extent(n, k, ld_q, 1),
+                 es = (size_t)n * (size_t)((k + group - 1) / group) * 4;
+    FP8Q_TRY(check_within_allocation(w_scale, es, "w_scale"));
+    if (overlap(w_fp8, eq, w_bf16, ew) || overlap(w_scale, es, w_bf16, ew) ||
+        overlap(w_scale, es, w_fp8, eq))
+        return fail(FP8Q_ERR_INVALID_ARG, "outputs overlap each other or the input");
+    hipError_t e = fp8q::launch::quantize_weight_grouped(w_bf16, n, k, ld_w, group, w_fp8, ld_q,
+                                                         w_scale, nonfinite_flag, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "grouped weight quantization launch");
     return ok();
 }
 

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fp8q {
 namespace dev {
 
@@ -110,6 +112,40 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         uint32_t o = __shfl_xor(v, off, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Unsigned max over aligned groups of L lanes (L = 2..64, a power of two);
+// every lane of a group gets the group's maximum.  Within a row of 16 lanes
+// the exchanges are DPP moves (quad permutes, then the half-row and row
+// mirrors, which pair each lane with one in the other half); 32-lane groups
+// add a swizzle that swaps the two rows of each half-wave, 64-lane groups a
+// permute across the halves.
+template <int L>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v)
+{
+    static_assert(L >= 2 && L <= kWave && (L & (L - 1)) == 0, "group size");
+    auto dpp_max = [](uint32_t x, auto ctrl) {
+        const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value,
+                                                                 0xF, 0xF, false);
+        return o > x ? o : x;
+    };
+    v = dpp_max(v, std::integral_constant<int, 0xB1>{});       // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (L >= 4)
+        v = dpp_max(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (L >= 8)
+        v = dpp_max(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    if constexpr (L >= 16)
+        v = dpp_max(v, std::integral_constant<int, 0x140>{});  // row_mirror
+    if constexpr (L >= 32) {
+        // swizzle, bit mode: and 0x1F, xor 0x10 (lane ^ 16 within 32)
+        const uint32_t o = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+        v = o > v ? o : v;
+    }
+    if constexpr (L >= 64) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, 32, kWave);
         v = o > v ? o : v;
     }
     return v;

@@ -23,6 +23,12 @@ hipError_t quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
                         uint8_t *q, int64_t ld_q, float *x_scale, uint32_t *partial,
                         int32_t *flag, hipStream_t stream);
 
+// Per-group weight quantization: scale [n, ceil(k / group)], group 64..512
+// (a power of two).
+hipError_t quantize_weight_grouped(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                                   int64_t group, uint8_t *q, int64_t ld_q, float *scale,
+                                   int32_t *flag, hipStream_t stream);
+
 // Per-tensor quantization with a held scale (*scale, device), one pass.
 hipError_t quantize_act_static(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
                                const float *scale, uint8_t *q, int64_t ld_q, int32_t *flag,
@@ -69,8 +75,12 @@ struct W8A16Plan {
     int64_t kper;      // K range per split (a multiple of 64)
     int64_t ldp;       // row stride of the fp32 partial tiles (n rounded up to 4)
     size_t workspace;  // scratch bytes: the partial tiles [splits][m][ldp] (0 if no split)
+    int64_t group;     // 0: one weight scale per row; else k per weight-scale group
 };
 W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k);
+// Per-group weight scales (w_scale [n, ceil(k / group)]); group is 64, 128,
+// 256 or 512.  The tile kernel serves every activation type and M.
+W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group);
 // act: the activation type -- 0 bf16 (fp8_w_bf16_a, bf16 out), 1 fp16
 // (fp8_w_fp16_a, fp16 out), 2 E4M3 codes with *x_scale (fp8_w_fp8_a at decode
 // sizes, bf16 out).  ld_x counts activation values.

@@ -121,6 +121,119 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight_scalar(
 }
 
 // ---------------------------------------------------------------------------
+// Weights, per-group scales (the deployment guide §4.3 names per-group
+// granularity as the step beyond per-channel): one workgroup per output row.
+// A group of 8 * LPG values is the 16-byte chunks of LPG consecutive lanes
+// (256 threads hold 256 consecutive chunks per round, and LPG divides 64, so
+// a group never straddles a wave); its maximum is a shuffle reduction over
+// those lanes.  Every weight byte is read once.  The row's last chunk may be
+// partial: its missing values count as 0 (which cannot raise a maximum) and
+// are not stored.
+// ---------------------------------------------------------------------------
+// One 16-byte chunk of a row; a partial chunk is filled with zeros.
+__device__ __forceinline__ uint4 load_chunk(const uint16_t *wr, int64_t e0, int valid)
+{
+    if (valid == 8)
+        return *reinterpret_cast<const uint4 *>(wr + e0);
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (valid > 0) {
+        uint32_t h[8];
+        for (int i = 0; i < 8; ++i)
+            h[i] = i < valid ? wr[e0 + i] : 0u;
+        v = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+    return v;
+}
+
+// Group maximum, scale, codes and (first lane of the group) the scale store
+// for one 16-byte chunk c of the row.
+template <int LPG>
+__device__ __forceinline__ void quant_chunk(uint4 v, int64_t c, int valid, uint8_t *qr, float *sr,
+                                            int32_t *flag)
+{
+    const uint32_t key = group_max_u32<LPG>(key_max8(v));
+    const float s = scale_from_key(key);
+    const int64_t e0 = c * 8;
+    if (valid == 8) {
+        *reinterpret_cast<uint2 *>(qr + e0) = quantize8(v, s);
+    } else if (valid > 0) {
+        const uint2 codes = quantize8(v, s);
+        for (int i = 0; i < valid; ++i)
+            qr[e0 + i] = (uint8_t)(((i < 4 ? codes.x : codes.y) >> (8 * (i & 3))) & 0xFFu);
+    }
+    if (valid > 0 && (threadIdx.x & (LPG - 1)) == 0) {
+        sr[c / LPG] = s;
+        if (flag != nullptr && key >= 0x7F80u)
+            *flag = 1;
+    }
+}
+
+// CH > 0: the row has at most CH * 256 chunks, all loaded into registers
+// before any is reduced, so every lane has CH loads in flight; CH == 0:
+// longer rows, one round of 256 chunks at a time.
+template <int LPG, int CH>
+__global__ __launch_bounds__(kThreads) void k_quant_weight_grouped(
+    const uint16_t *__restrict__ w, int64_t k, int64_t ld_w,
+    uint8_t *__restrict__ q, int64_t ld_q, float *__restrict__ scale, int64_t ngroups,
+    int32_t *__restrict__ flag)
+{
+    static_assert(LPG >= 1 && LPG <= kWave && (LPG & (LPG - 1)) == 0, "lanes per group");
+    const int64_t row = blockIdx.x;
+    const uint16_t *wr = w + row * ld_w;
+    uint8_t *qr = q + row * ld_q;
+    float *sr = scale + row * ngroups;
+    auto valid_of = [&](int64_t c) {
+        const int64_t e0 = c * 8;
+        return e0 >= k ? 0 : (int)min<int64_t>(8, k - e0);
+    };
+    if constexpr (CH > 0) {
+        uint4 buf[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * kThreads;
+            buf[i] = load_chunk(wr, c * 8, valid_of(c));
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * kThreads;
+            quant_chunk<LPG>(buf[i], c, valid_of(c), qr, sr, flag);
+        }
+    } else {
+        const int64_t nch = (k + 7) >> 3;
+        for (int64_t base = 0; base < nch; base += kThreads) {
+            const int64_t c = base + threadIdx.x;
+            quant_chunk<LPG>(load_chunk(wr, c * 8, valid_of(c)), c, valid_of(c), qr, sr, flag);
+        }
+    }
+}
+
+// Rows that are not 16-byte aligned: one thread per group, element by element.
+__global__ __launch_bounds__(kThreads) void k_quant_weight_grouped_scalar(
+    const uint16_t *__restrict__ w, int64_t k, int64_t ld_w, int64_t group,
+    uint8_t *__restrict__ q, int64_t ld_q, float *__restrict__ scale, int64_t ngroups,
+    int32_t *__restrict__ flag)
+{
+    const int64_t row = blockIdx.x;
+    const uint16_t *wr = w + row * ld_w;
+    uint8_t *qr = q + row * ld_q;
+    for (int64_t gi = threadIdx.x; gi < ngroups; gi += kThreads) {
+        const int64_t c0 = gi * group;
+        const int64_t c1 = min(k, c0 + group);
+        uint32_t key = 0;
+        for (int64_t c = c0; c < c1; ++c)
+            key = max(key, (uint32_t)(wr[c] & 0x7FFFu));
+        const float s = scale_from_key(key);
+        scale[row * ngroups + gi] = s;
+        if (flag != nullptr && key >= 0x7F80u)
+            *flag = 1;
+        for (int64_t c = c0; c < c1; ++c) {
+            const float t = __uint_as_float((uint32_t)wr[c] << 16) / s;
+            qr[c] = (uint8_t)(e4m3x4(t, 0.f, 0.f, 0.f) & 0xFFu);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Activations, pass 1: each workgroup writes the |x| key maximum of its share
 // of the tensor to partial[blockIdx.x].  No atomics, no initialisation.
 // ---------------------------------------------------------------------------
@@ -383,6 +496,50 @@ hipError_t quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w
         hipLaunchKernelGGL(k_quant_weight<16>, grid, block, 0, stream, w, k, ld_w, q, ld_q, scale, flag);
     else
         hipLaunchKernelGGL(k_quant_weight<0>, grid, block, 0, stream, w, k, ld_w, q, ld_q, scale, flag);
+    return hipGetLastError();
+}
+
+hipError_t quantize_weight_grouped(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                                   int64_t group, uint8_t *q, int64_t ld_q, float *scale,
+                                   int32_t *flag, hipStream_t stream)
+{
+    if (n == 0)
+        return hipSuccess;
+    const int64_t ngroups = div_up(k, group);
+    const dim3 grid((unsigned)n), block(kThreads);
+    const bool vec = aligned(w, 16) && ld_w % 8 == 0 && aligned(q, 8) && ld_q % 8 == 0;
+    if (!vec) {
+        hipLaunchKernelGGL(k_quant_weight_grouped_scalar, grid, block, 0, stream, w, k, ld_w, group,
+                           q, ld_q, scale, ngroups, flag);
+        return hipGetLastError();
+    }
+    const int64_t rounds = div_up(div_up(k, 8), kThreads);     // chunks per thread
+#define FP8Q_GQ(LPG)                                                                          \
+    do {                                                                                      \
+        if (rounds <= 1)                                                                      \
+            hipLaunchKernelGGL((k_quant_weight_grouped<LPG, 1>), grid, block, 0, stream, w, k,   \
+                               ld_w, q, ld_q, scale, ngroups, flag);                          \
+        else if (rounds <= 2)                                                                 \
+            hipLaunchKernelGGL((k_quant_weight_grouped<LPG, 2>), grid, block, 0, stream, w, k,   \
+                               ld_w, q, ld_q, scale, ngroups, flag);                          \
+        else if (rounds <= 4)                                                                 \
+            hipLaunchKernelGGL((k_quant_weight_grouped<LPG, 4>), grid, block, 0, stream, w, k,   \
+                               ld_w, q, ld_q, scale, ngroups, flag);                          \
+        else if (rounds <= 8)                                                                 \
+            hipLaunchKernelGGL((k_quant_weight_grouped<LPG, 8>), grid, block, 0, stream, w, k,   \
+                               ld_w, q, ld_q, scale, ngroups, flag);                          \
+        else                                                                                  \
+            hipLaunchKernelGGL((k_quant_weight_grouped<LPG, 0>), grid, block, 0, stream, w, k,   \
+                               ld_w, q, ld_q, scale, ngroups, flag);                          \
+    } while (0)
+    switch (group) {
+    case 64: FP8Q_GQ(8); break;
+    case 128: FP8Q_GQ(16); break;
+    case 256: FP8Q_GQ(32); break;
+    case 512: FP8Q_GQ(64); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef FP8Q_GQ
     return hipGetLastError();
 }
 

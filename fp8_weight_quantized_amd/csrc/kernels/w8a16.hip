@@ -161,7 +161,10 @@ __device__ __forceinline__ void widen(v4u wv, typename Act<AT>::frag &a0, typena
 // no masking is needed here.
 // xv holds, per activation group, either 16 activation codes in xv[j][0]
 // (E4M3) or two 8-value halves in xv[j][0..1] (16-bit types).
-template <int AF, int MB, int AT>
+// SWAP puts the activations in the A operand and the weights in B, so each
+// lane's 4 accumulators are 4 activation rows of one weight row (one output
+// column) instead of 4 weight rows of one activation row.
+template <int AF, int MB, int AT, bool SWAP = false>
 __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[MB][2],
                                           v4f (&acc)[AF][MB])
 {
@@ -182,8 +185,13 @@ __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[M
         widen<CT>(wv[a], a0, a1);
 #pragma unroll
         for (int j = 0; j < MB; ++j) {
-            acc[a][j] = Act<CT>::mfma(a0, b[j][0], acc[a][j]);
-            acc[a][j] = Act<CT>::mfma(a1, b[j][1], acc[a][j]);
+            if constexpr (SWAP) {
+                acc[a][j] = Act<CT>::mfma(b[j][0], a0, acc[a][j]);
+                acc[a][j] = Act<CT>::mfma(b[j][1], a1, acc[a][j]);
+            } else {
+                acc[a][j] = Act<CT>::mfma(a0, b[j][0], acc[a][j]);
+                acc[a][j] = Act<CT>::mfma(a1, b[j][1], acc[a][j]);
+            }
         }
     }
 }
@@ -397,14 +405,16 @@ __device__ __forceinline__ void store_y4(uint16_t *__restrict__ y, int64_t ld_y,
                                          int64_t nb, int64_t n, v4f s)
 {
     uint16_t *yp = y + mr * ld_y + nb;
+    // no w_scale: the group scales were applied inside the K loop
+    auto ws = [&](int v) { return w_scale != nullptr ? w_scale[nb + v] : 1.0f; };
     if (nb + 4 <= n) {
         uint2 o;
-        o.x = Act<CT>::pack2(s[0] * (xs * w_scale[nb]), s[1] * (xs * w_scale[nb + 1]));
-        o.y = Act<CT>::pack2(s[2] * (xs * w_scale[nb + 2]), s[3] * (xs * w_scale[nb + 3]));
+        o.x = Act<CT>::pack2(s[0] * (xs * ws(0)), s[1] * (xs * ws(1)));
+        o.y = Act<CT>::pack2(s[2] * (xs * ws(2)), s[3] * (xs * ws(3)));
         *reinterpret_cast<uint2 *>(yp) = o;
     } else {
         for (int v = 0; v < (int)(n - nb); ++v)
-            yp[v] = Act<CT>::one(s[v] * (xs * w_scale[nb + v]));
+            yp[v] = Act<CT>::one(s[v] * (xs * ws(v)));
     }
 }
 
@@ -413,16 +423,31 @@ __device__ __forceinline__ void store_y4(uint16_t *__restrict__ y, int64_t ld_y,
 //     past M are clamped to row M-1; LDS rows past 4*XD are never written and
 //     only feed output columns that are never stored).
 // T:  64-k steps per chunk; a chunk's weights are loaded one chunk ahead.
+// SPG: 0 for one scale per weight row (w_scale [n]); else per-group weight
+//     scales, w_scale [n, ngroups] for groups of 64*SPG k (the deployment
+//     guide §4.3): each group's products are summed on their own, multiplied
+//     by the group's scale at the group's end and added to the row's total.
+//     The MFMA operands are then swapped (activations in A, weights in B), so
+//     every lane's accumulators belong to one weight row and one scale.
 // Grid: x = tiles of 64 weight rows times K splits (split index fastest),
 // y = groups of 16*MB activation rows.
-template <int MB, int XD, int T, int AT>
+template <int MB, int XD, int T, int AT, int SPG>
 __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
     const void *__restrict__ xv, int64_t m, int64_t k, int64_t ld_x,
     const float *__restrict__ x_scale,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
-    int64_t kper, int splits, float *__restrict__ partial, int64_t ldp)
+    int64_t kper, int splits, float *__restrict__ partial, int64_t ldp, int64_t ngroups)
 {
+    constexpr bool GS = SPG > 0;
+    constexpr int GK = 64 * (GS ? SPG : 1);    // k per scale group
+    constexpr int SPGD = GS ? SPG : 1;         // SPG as a divisor
+    constexpr int SC = GS ? T / SPG : 0;       // scale groups per chunk
+    // a chunk's scales are adjacent floats, which the compiler may merge into
+    // fewer load instructions: the waits below count them as at least one
+    // (a smaller count only waits for more)
+    constexpr int SCL = GS ? 1 : 0;
+    static_assert(!GS || T % SPG == 0, "a chunk is a whole number of scale groups");
     constexpr int XR = 16 * MB;                // LDS rows per buffer
     constexpr int CK = 64 * T;                 // k per chunk
     constexpr int RB = 2 * CK;                 // LDS bytes of one staged row
@@ -454,6 +479,20 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 
     const uint8_t *wrow = w + min(n0 + r, n - 1) * ld_w + 16 * g;
     const uint8_t *wp = wrow + kb;
+    // grouped: this lane's weight row is its output column; its group scales
+    const float *srow = w_scale + (GS ? min(n0 + r, n - 1) * ngroups : 0);
+    v4f tot[MB];
+    float sc_cur[SC > 0 ? SC : 1], sc_nxt[SC > 0 ? SC : 1];
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+        tot[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    // scales of chunk c's groups (chunks start on group boundaries: kb and CK
+    // are multiples of GK)
+    auto load_sc = [&](int64_t c) {
+#pragma unroll
+        for (int i = 0; i < SC; ++i)
+            sc_nxt[i] = srow[(kb + c * CK) / GK + i];
+    };
 
     // LDS byte offset of 16-byte unit u of staged row rho.  The units of a row
     // are XOR-permuted by the row's low 4 bits, so the 16 rows one B-operand
@@ -466,6 +505,15 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 #pragma unroll
         for (int j = 0; j < MB; ++j)
             acc[h][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    // close a scale group: its sum, times its scale, joins the total
+    auto fold = [&](float s) {
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+            tot[j] += s * (acc[0][j] + acc[1][j]);
+            acc[0][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            acc[1][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    };
 
     if (nchunks > 0) {
         // this wave stages activation rows wave, wave + 4, ...; lane l holds
@@ -508,42 +556,65 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
             for (int j = 0; j < MB; ++j) {
                 const v4u b0 = *reinterpret_cast<const v4u *>(base + xs_off(16 * j + r, 8 * u + 2 * g));
                 const v4u b1 = *reinterpret_cast<const v4u *>(base + xs_off(16 * j + r, 8 * u + 2 * g + 1));
-                a[j] = Act<CT>::mfma(a0, Act<CT>::cast(b0), a[j]);
-                a[j] = Act<CT>::mfma(a1, Act<CT>::cast(b1), a[j]);
+                if constexpr (GS) {
+                    a[j] = Act<CT>::mfma(Act<CT>::cast(b0), a0, a[j]);
+                    a[j] = Act<CT>::mfma(Act<CT>::cast(b1), a1, a[j]);
+                } else {
+                    a[j] = Act<CT>::mfma(a0, Act<CT>::cast(b0), a[j]);
+                    a[j] = Act<CT>::mfma(a1, Act<CT>::cast(b1), a[j]);
+                }
             }
         };
 
-        // prologue: chunk 0's activations, then its weights
+        // prologue: chunk 0's scales and activations, then its weights
+        if constexpr (GS)
+            load_sc(0);
         load_x(0);
         static_for<0, T>([&](auto uc) {
             constexpr int u = decltype(uc)::value;
             wr[u] = ldg_nt(wp + 64 * u);
         });
-        wait_vmcnt<T>();                      // the activation loads (issued first) landed
+        wait_vmcnt<T>();                      // the scale and activation loads (issued first) landed
         __builtin_amdgcn_sched_barrier(0);
         store_x(0);
+        if constexpr (GS) {
+#pragma unroll
+            for (int i = 0; i < SC; ++i)
+                sc_cur[i] = sc_nxt[i];
+        }
         lds_barrier();
 
         int64_t c = 0;
         for (; c + 1 < nchunks; ++c) {
             const int buf = (int)(c & 1);
+            if constexpr (GS)
+                load_sc(c + 1);
             load_x(c + 1);
             __builtin_amdgcn_sched_barrier(0);
             static_for<0, T>([&](auto uc) {
                 constexpr int u = decltype(uc)::value;
                 // loads retire in order; issued after this step's weights:
-                // T-1 weight loads and the XL activation loads of chunk c+1
-                wait_vmcnt<T - 1 + XL>();
+                // T-1 weight loads and the scale and XL activation loads of
+                // chunk c+1
+                wait_vmcnt<T - 1 + XL + SCL>();
                 __builtin_amdgcn_sched_barrier(0);
                 compute(u, buf, acc[u & 1]);
                 wr[u] = ldg_nt(wp + (c + 1) * CK + 64 * u);
+                if constexpr (GS && (u + 1) % SPGD == 0)
+                    fold(sc_cur[u / SPGD]);
                 __builtin_amdgcn_sched_barrier(0);
             });
-            // chunk c+1's activations: only its T weight loads were issued after them
+            // chunk c+1's scales and activations: only its T weight loads were
+            // issued after them
             wait_vmcnt<T>();
             __builtin_amdgcn_sched_barrier(0);
             store_x(buf ^ 1);     // that buffer was last read in chunk c-1, before the
-            lds_barrier();        // previous barrier
+            if constexpr (GS) {   // previous barrier
+#pragma unroll
+                for (int i = 0; i < SC; ++i)
+                    sc_cur[i] = sc_nxt[i];
+            }
+            lds_barrier();
         }
         // last chunk: nothing more to load
         static_for<0, T>([&](auto uc) {
@@ -551,13 +622,21 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
             wait_vmcnt<T - 1 - u>();
             __builtin_amdgcn_sched_barrier(0);
             compute(u, (int)(c & 1), acc[u & 1]);
+            if constexpr (GS && (u + 1) % SPGD == 0)
+                fold(sc_cur[u / SPGD]);
         });
     }
 
     // K left after the whole chunks (less than one chunk, only in the last
     // split): one 64-k step at a time straight from global memory, the last
-    // step masked at k
+    // step masked at k.  It starts on a group boundary; a group's scale is
+    // read at its first step and applied after its last (or K's end).
+    float s_tail = 0.f;
     for (int64_t kk = kb + nchunks * CK; kk < ke; kk += 64) {
+        if constexpr (GS) {
+            if ((kk - kb) % GK == 0)
+                s_tail = srow[kk / GK];
+        }
         const int64_t kw = kk + 16 * g;
         v4u wv;
         v4u xv[MB][2];
@@ -589,10 +668,34 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 #pragma unroll
         for (int j = 0; j < MB; ++j)
             acc1[0][j] = acc[0][j];
-        step_mfma<1, MB, AT>(wv1, xv, acc1);
+        step_mfma<1, MB, AT, GS>(wv1, xv, acc1);
 #pragma unroll
         for (int j = 0; j < MB; ++j)
             acc[0][j] = acc1[0][j];
+        if constexpr (GS) {
+            if ((kk + 64 - kb) % GK == 0 || kk + 64 >= ke)
+                fold(s_tail);
+        }
+    }
+
+    if constexpr (GS) {
+        // lane (r, g) holds D rows 4g..4g+3 (activation rows m0 + 16j + 4g..)
+        // of column r (weight row n0 + r); every group is folded into tot
+        const int64_t nc = n0 + r;
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t mr = m0 + 16 * j + 4 * g + v;
+                if (mr >= m || nc >= n)
+                    continue;
+                if (splits == 1)
+                    y[mr * ld_y + nc] = Act<CT>::one(tot[j][v] * xs);
+                else
+                    partial[((int64_t)split * m + mr) * ldp + nc] = tot[j][v];
+            }
+        }
+        return;
     }
 
     // lane (r, g) holds D rows 4g..4g+3 (weight rows n0+4g..) of column r
@@ -612,7 +715,8 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 }
 
 // Sum of the K splits' partial tiles in split order, scaled and stored as
-// bf16: one thread per 4 consecutive outputs of a row.
+// bf16: one thread per 4 consecutive outputs of a row.  w_scale == nullptr:
+// the partials already carry the per-group weight scales.
 template <int AT>
 __global__ __launch_bounds__(256) void k_w8a16_reduce(
     const float *__restrict__ partial, int64_t m, int64_t n, int64_t ldp, int splits,
@@ -642,6 +746,33 @@ namespace launch {
 // Register-pipeline depth of the rows kernel: about 24-36 16-byte loads in
 // flight per lane.
 static int rows_depth(int af, int mb) { return (af + 2 * mb) <= 4 ? 8 : ((af + 2 * mb) <= 6 ? 4 : 2); }
+
+// The tile kernel's part of a plan: rows staged per wave, chunk length, and
+// the K split towards 256 workgroups.
+static void plan_tile(W8A16Plan &p, int64_t m, int64_t k, int steps_mb1)
+{
+    const int64_t tiles = p.tiles_n * p.grid_m;
+    p.kind = W8A16Plan::kTile;
+    if (p.mb == 1) {
+        // stage only the activation rows that exist: 4, 8 or 16 of the 16
+        p.xd = (int)div_up(m, kTileWaves);
+        p.steps = steps_mb1;
+    } else {
+        p.xd = 4 * p.mb;
+        p.steps = 8;
+    }
+    // split K (in whole chunks) towards 256 workgroups, keeping at least two
+    // chunks per split so each workgroup's pipeline gets past its prologue
+    const int64_t chunk = 64 * p.steps;
+    int64_t s = 256 / tiles;
+    const int64_t s_max = k / (2 * chunk);
+    s = s > s_max ? s_max : s;
+    s = s < 1 ? 1 : s;
+    p.kper = div_up(div_up(k, s), chunk) * chunk;
+    p.splits = div_up(k, p.kper);
+    p.workspace = p.splits > 1 ? (size_t)p.splits * m * p.ldp * sizeof(float) : 0;
+    p.grid_n = p.tiles_n * p.splits;
+}
 
 W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
 {
@@ -702,27 +833,22 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
         p.kper = p.kchunk * p.waves;
         return p;
     }
-    p.kind = W8A16Plan::kTile;
-    if (p.mb == 1) {
-        // stage only the activation rows that exist: 4, 8 or 16 of the 16
-        p.xd = (int)div_up(m, kTileWaves);   // stage only the rows that exist
-        p.steps = (k >= 16384 || tiles >= 256) ? 16 : 8;
-    } else {
-        p.xd = 4 * p.mb;
-        p.steps = 8;
-    }
-    // split K (in whole chunks) towards 256 workgroups, keeping at least two
-    // chunks per split so each workgroup's pipeline gets past its prologue
-    const int64_t chunk = 64 * p.steps;
-    int64_t s = 256 / tiles;
-    const int64_t s_max = k / (2 * chunk);
-    s = s > s_max ? s_max : s;
-    s = s < 1 ? 1 : s;
-    p.kper = div_up(div_up(k, s), chunk) * chunk;
-    p.splits = div_up(k, p.kper);
-    if (p.splits > 1)
-        p.workspace = (size_t)p.splits * m * p.ldp * sizeof(float);
-    p.grid_n = p.tiles_n * p.splits;
+    plan_tile(p, m, k, (k >= 16384 || tiles >= 256) ? 16 : 8);
+    return p;
+}
+
+W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group)
+{
+    // the tile kernel for every shape: 512-k chunks (8 steps), so a chunk
+    // holds a whole number of groups of 64..512 k
+    W8A16Plan p{};
+    const int64_t mgroups = div_up(m, 16);
+    p.mb = (int)(mgroups >= 4 ? 4 : (mgroups < 1 ? 1 : mgroups));
+    p.grid_m = div_up(m, 16 * p.mb);
+    p.tiles_n = div_up(n, kTileN);
+    p.ldp = div_up(n, 4) * 4;
+    p.group = group;
+    plan_tile(p, m, k, 8);
     return p;
 }
 
@@ -744,20 +870,22 @@ static void launch_rows(const W8A16Plan &p, const void *x, int64_t m, int64_t k,
     }
 }
 
-template <int MB, int XD, int T, int AT>
+template <int MB, int XD, int T, int AT, int SPG = 0>
 static void launch_tile(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
                         const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
                         const float *w_scale, uint16_t *y, int64_t ld_y, float *partial,
                         hipStream_t stream)
 {
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
-    hipLaunchKernelGGL((k_w8a16_tile<MB, XD, T, AT>), grid, dim3(kTileThreads), 0, stream, x, m, k,
-                       ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, p.kper, (int)p.splits, partial,
-                       p.ldp);
+    const int64_t ngroups = SPG > 0 ? div_up(k, 64 * SPG) : 0;
+    hipLaunchKernelGGL((k_w8a16_tile<MB, XD, T, AT, SPG>), grid, dim3(kTileThreads), 0, stream, x,
+                       m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, p.kper, (int)p.splits,
+                       partial, p.ldp, ngroups);
     if (p.splits > 1) {
         const int64_t slots = m * (p.ldp / 4);
         hipLaunchKernelGGL((k_w8a16_reduce<AT>), dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
-                           partial, m, n, p.ldp, (int)p.splits, x_scale, w_scale, y, ld_y);
+                           partial, m, n, p.ldp, (int)p.splits, x_scale,
+                           SPG > 0 ? nullptr : w_scale, y, ld_y);
     }
 }
 
@@ -778,6 +906,25 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
         FP8Q_ROWS_CASE(2, 1, 8, 4)
         FP8Q_ROWS_CASE(1, 1, 8, 4)
 #undef FP8Q_ROWS_CASE
+    } else if (p.group > 0) {
+#define FP8Q_GROUP_CASE(MB, XD, SPG)                                                          \
+        if (p.mb == MB && p.xd == XD && p.steps == 8 && p.group == 64 * SPG) {                \
+            launch_tile<MB, XD, 8, AT, SPG>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y,   \
+                                            ld_y, partial, stream);                           \
+            return hipGetLastError();                                                         \
+        }
+#define FP8Q_GROUP_SIZES(MB, XD)                                                              \
+        FP8Q_GROUP_CASE(MB, XD, 1) FP8Q_GROUP_CASE(MB, XD, 2)                                 \
+        FP8Q_GROUP_CASE(MB, XD, 4) FP8Q_GROUP_CASE(MB, XD, 8)
+        FP8Q_GROUP_SIZES(1, 1)
+        FP8Q_GROUP_SIZES(1, 2)
+        FP8Q_GROUP_SIZES(1, 3)
+        FP8Q_GROUP_SIZES(1, 4)
+        FP8Q_GROUP_SIZES(2, 8)
+        FP8Q_GROUP_SIZES(3, 12)
+        FP8Q_GROUP_SIZES(4, 16)
+#undef FP8Q_GROUP_SIZES
+#undef FP8Q_GROUP_CASE
     } else {
 #define FP8Q_TILE_CASE(MB, XD, T)                                                             \
         if (p.mb == MB && p.xd == XD && p.steps == T) {                                       \

@@ -19,7 +19,8 @@
  *   per channel, activations per tensor) and §3.1 the conversion recipe;
  *   "Llama 3 精读" FP8 + 128K write-up (called "the write-up") §3.1 step 3
  *   names the FP8 MatMul modes, §3.1 step 2 and §5.3 tip 2 the EMA
- *   activation scale; the deployment guide §3.2 gives the FP8 KV cache.
+ *   activation scale; the deployment guide §3.2 gives the FP8 KV cache and
+ *   §4.3 per-group weight scales.
  *
  * Errors.  Arguments are validated on the host before anything is enqueued;
  * on any error nothing is launched and a status other than FP8Q_OK is
@@ -95,6 +96,25 @@ const char *fp8q_last_error(void);
 fp8q_status fp8q_quantize_weight(const uint16_t *w_bf16, int64_t n, int64_t k, int64_t ld_w,
                                  uint8_t *w_fp8, int64_t ld_q, float *w_scale,
                                  int32_t *nonfinite_flag, hipStream_t stream);
+
+/*
+ * Per-group weight quantization (deployment guide §4.3 names per-group
+ * granularity as the step beyond per-channel scales).  Each row of W is cut
+ * along K into groups of `group` consecutive values (the last may be
+ * shorter); each group gets the §3.1 scale over its own values:
+ *   s[n,g]     = max(fl32(max_{k in g} |W[n,k]| / 448), 1e-12f)   -> w_scale[n*G + g]
+ *   w_fp8[n,k] = E4M3_RNE_saturating(fl32(W[n,k] / s[n, k / group]))
+ * with G = ceil(k / group).  group = 64, 128, 256 or 512.
+ *
+ *   w_bf16  [n, k] bf16, ld_w >= k;  w_fp8 [n, k] uint8 out, ld_q >= k
+ *   w_scale [n, G] fp32 out, row-major; must lie inside one device allocation
+ *   nonfinite_flag  optional, as above
+ * n == 0 is a no-op; k must be >= 1.  Bit-exact.
+ */
+fp8q_status fp8q_quantize_weight_grouped(const uint16_t *w_bf16, int64_t n, int64_t k,
+                                         int64_t ld_w, int64_t group, uint8_t *w_fp8,
+                                         int64_t ld_q, float *w_scale, int32_t *nonfinite_flag,
+                                         hipStream_t stream);
 
 /*
  * Dynamic per-tensor activation quantization (deployment guide §1.2: one scale
@@ -253,6 +273,26 @@ fp8q_status fp8q_linear(fp8q_mode mode,
                         const uint8_t *w_fp8, int64_t n, int64_t ld_w, const float *w_scale,
                         uint16_t *y_bf16, int64_t ld_y,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The linear layer with per-group weight scales (w_scale [n, ceil(k/group)]
+ * from fp8q_quantize_weight_grouped), in the same three modes:
+ *   Y[m,n] = out_RNE( s_x * sum_g w_scale[n,g] * sum_{k in g} a(X[m,k]) * dec(W[n,k]) )
+ * with s_x = *x_scale for FP8Q_W8A8 and 1 otherwise.  Each group's products
+ * are summed in fp32 and multiplied by the group's scale as the group ends.
+ * Arguments as fp8q_linear, plus group (64, 128, 256 or 512); w_scale must lie
+ * inside one device allocation.  Every M runs the decode tile kernel (at
+ * prefill sizes W is re-read once per 64 activation rows).  Tolerance and
+ * determinism as fp8q_linear.
+ */
+size_t fp8q_linear_grouped_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
+                                          int64_t group);
+fp8q_status fp8q_linear_grouped(fp8q_mode mode,
+                                const void *x, int64_t m, int64_t k, int64_t ld_x,
+                                const float *x_scale, const uint8_t *w_fp8, int64_t n,
+                                int64_t ld_w, const float *w_scale, int64_t group,
+                                uint16_t *y_bf16, int64_t ld_y,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The element cast used by both quantizers, exposed on its own: fp32 -> E4M3

@@ -188,6 +188,32 @@ def test_kv_cache_host_validation(L):
     assert L.fp8q_kv_cache_workspace_size(12, 8, 128) == 256
 
 
+def test_grouped_host_validation(L):
+    """Per-group entry points: group sizes, shapes and workspace before any device work."""
+    for bad in (0, 32, 100, 1024, -128):
+        assert L.fp8q_quantize_weight_grouped(NULL, 4, 512, 512, bad, NULL, 512, NULL, NULL,
+                                              NULL) == 1, bad
+        assert L.fp8q_linear_grouped(0, NULL, 4, 512, 512, NULL, NULL, 8, 512, NULL, bad, NULL, 8,
+                                     NULL, 0, NULL) == 1, bad
+        assert L.fp8q_linear_grouped_workspace_size(0, 4, 8, 512, bad) == 0
+    assert L.fp8q_quantize_weight_grouped(NULL, 0, 512, 512, 128, NULL, 512, NULL, NULL, NULL) == 0
+    assert L.fp8q_quantize_weight_grouped(NULL, 4, 0, 512, 128, NULL, 512, NULL, NULL, NULL) == 1
+    assert L.fp8q_quantize_weight_grouped(NULL, 4, 512, 500, 128, NULL, 512, NULL, NULL, NULL) == 1
+    lg = L.fp8q_linear_grouped
+    assert lg(0, NULL, 0, 512, 512, NULL, NULL, 8, 512, NULL, 128, NULL, 8, NULL, 0, NULL) == 0
+    assert lg(0, NULL, 4, 512, 500, NULL, NULL, 8, 512, NULL, 128, NULL, 8, NULL, 0, NULL) == 1
+    assert lg(1, NULL, 4, 512, 512, NULL, NULL, 8, 512, NULL, 128, NULL, 8, NULL, 0, NULL) == 1
+    # a K split at decode: workspace needed, none given
+    # 2 tiles of 64 rows: 28 splits of 1024 k (2 chunks each) -> [28][12][128] fp32
+    assert L.fp8q_linear_grouped_workspace_size(0, 12, 128, 28672, 128) == 28 * 12 * 128 * 4
+    assert lg(0, NULL, 12, 28672, 28672, NULL, NULL, 128, 28672, NULL, 128, NULL, 128, NULL, 0,
+              NULL) == 4
+    # 64 tiles: 4 splits of 1024 k
+    assert L.fp8q_linear_grouped_workspace_size(0, 1, 4096, 4096, 128) == 4 * 1 * 4096 * 4
+    # 448 tiles x 128 row blocks: no split
+    assert L.fp8q_linear_grouped_workspace_size(1, 8192, 28672, 4096, 128) == 0
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     from fp8_weight_quantized_amd import _lib
     monkeypatch.setattr(_lib, "_lib", None)
