@@ -577,6 +577,46 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
         mso = time_eager(torch, one, iters)
         bb = lin.n * lin.k + 4 * lin.n + 2 * m * lin.k + 2 * m * lin.n
         per[lin.name] = {"us": round(mso * 1e3, 2), "GB/s": round(bb / (mso * 1e-3) / 1e9, 1)}
+    # the same layer with the weights that share an input concatenated along
+    # N, as serving engines store them: q/k/v -> qkv [10240, 8192] and
+    # gate/up -> gate_up [57344, 8192]; the same bytes in 4 launches, not 7
+    by_name = {lin.name: (lin, wq, ws, x) for lin, wq, ws, x, *_ in layer}
+    fused = []
+    for name, parts in (("qkv_proj", ("q_proj", "k_proj", "v_proj")), ("o_proj", ("o_proj",)),
+                        ("gate_up_proj", ("gate_proj", "up_proj")), ("down_proj", ("down_proj",))):
+        lins = [by_name[p_][0] for p_ in parts]
+        nf, kf = sum(l_.n for l_ in lins), lins[0].k
+        wqf = torch.cat([by_name[p_][1] for p_ in parts]) if len(parts) > 1 else by_name[parts[0]][1]
+        wsf = torch.cat([by_name[p_][2] for p_ in parts]) if len(parts) > 1 else by_name[parts[0]][2]
+        xf = by_name[parts[0]][3]
+        yf = torch.empty((m, nf), dtype=torch.bfloat16, device=dev)
+        nwf = L.fp8q_linear_workspace_size(0, m, nf, kf)
+        wsbf = torch.zeros(nwf, dtype=torch.uint8, device=dev) if nwf else None
+        fused.append((name, nf, kf, wqf, wsf, xf, yf, wsbf, nwf))
+
+    def layer_step_fused(h):
+        for name, nf, kf, wqf, wsf, xf, yf, wsbf, nwf in fused:
+            st = L.fp8q_linear(0, ptr(xf), m, kf, kf, None, ptr(wqf), nf, wqf.stride(0), ptr(wsf),
+                               ptr(yf), nf, ptr(wsbf), nwf, h)
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+    gf = torch.cuda.CUDAGraph()
+    sfs = torch.cuda.Stream(device=dev)
+    sfs.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(gf, stream=sfs, capture_error_mode="relaxed"):
+        layer_step_fused(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.current_stream(dev).wait_stream(sfs)
+    msf = time_eager(torch, gf.replay, iters)
+    bf = sum(nf * kf + 4 * nf + 2 * m * kf + 2 * m * nf for _, nf, kf, *_ in fused)
+    rows["a5_layer_decode_70b_fused"] = {
+        "shape": "qkv [10240,8192], o [8192,8192], gate_up [57344,8192], down [8192,28672], M=12",
+        "us": round(msf * 1e3, 2), "GB/s": round(bf / (msf * 1e-3) / 1e9, 1),
+        "frac_hbm": round(bf / (msf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "timing": "one HIP graph per layer step",
+        "kernels": {name: fq.describe_linear(0, m, nf, kf) for name, nf, kf, *_ in fused}}
+    log(rows["a5_layer_decode_70b_fused"])
+    del fused, gf
+
     # the same layer with per-group weight scales (groups of 128)
     G = 128
     layer_g = []

@@ -783,10 +783,10 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
     p.tiles_n = div_up(n, kTileN);
     p.splits = 1;
     p.workspace = 0;
-    // The rows kernel wins for up to 16 activation rows on a mid-sized weight
-    // (N <= 16K, K < 16K); a weight large in N or K, a small N, or more
-    // activation rows go to the tile kernel (measured on MI355X across the
-    // Llama-3 8B/70B decode shapes).
+    // The rows kernel wins for up to 16 activation rows on a weight of up to
+    // 4096 rows with K < 16K; a wider weight takes the split tile kernel
+    // below, a long K, a small N or more activation rows the tile kernel
+    // (measured on MI355X across the Llama-3 8B/70B decode shapes).
     const int64_t tiles = p.tiles_n * p.grid_m;
     const bool small_n_long_k = p.mb == 1 && tiles <= 32 && k >= 4096 && k < 16384;
     const bool tile = !small_n_long_k && (p.mb > 1 || tiles >= 256 || tiles <= 32 || k >= 16384);
@@ -812,6 +812,28 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
         p.kchunk = p.kper / p.waves;
         if (p.splits > 1)
             p.workspace = (size_t)p.splits * m * p.ldp * sizeof(float);
+        return p;
+    }
+    if (p.mb == 1 && p.tiles_n > 64 && k >= 8192 && k < 16384) {
+        // up to 16 activation rows on a weight wider than 4096 rows with
+        // 8K <= K < 16K (the Llama-3-70B q/o, fused qkv and gate/up at
+        // decode): the tile kernel with K split 4 ways -- more, smaller
+        // workgroups even out the CUs.  Measured on MI355X at M = 12: fused
+        // qkv [10240, 8192] 25.9 us against 34.5 us for the rows kernel, gate
+        // [28672, 8192] 55.7 us against 58.1 us unsplit.  At K = 4096 the
+        // split chunks get too short and the unsplit plans below stay faster.
+        p.kind = W8A16Plan::kTile;
+        p.xd = (int)div_up(m, kTileWaves);
+        p.steps = p.tiles_n >= 256 ? 16 : 8;
+        const int64_t chunk = 64 * p.steps;
+        int64_t s = 4;
+        const int64_t s_max = k / (2 * chunk);
+        s = s > s_max ? s_max : s;
+        s = s < 1 ? 1 : s;
+        p.kper = div_up(div_up(k, s), chunk) * chunk;
+        p.splits = div_up(k, p.kper);
+        p.workspace = p.splits > 1 ? (size_t)p.splits * m * p.ldp * sizeof(float) : 0;
+        p.grid_n = p.tiles_n * p.splits;
         return p;
     }
     if (!tile) {
@@ -849,6 +871,18 @@ W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group)
     p.ldp = div_up(n, 4) * 4;
     p.group = group;
     plan_tile(p, m, k, 8);
+    if (p.mb == 1 && p.tiles_n > 64 && k >= 8192 && k < 16384) {
+        // as the per-channel plan: wide weights split K 4 ways at decode
+        const int64_t chunk = 64 * p.steps;
+        int64_t s = 4;
+        const int64_t s_max = k / (2 * chunk);
+        s = s > s_max ? s_max : s;
+        s = s < 1 ? 1 : s;
+        p.kper = div_up(div_up(k, s), chunk) * chunk;
+        p.splits = div_up(k, p.kper);
+        p.workspace = p.splits > 1 ? (size_t)p.splits * m * p.ldp * sizeof(float) : 0;
+        p.grid_n = p.tiles_n * p.splits;
+    }
     return p;
 }
 

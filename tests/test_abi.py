@@ -55,12 +55,16 @@ def test_workspace_queries(L):
     assert L.fp8q_linear_workspace_size(1, 65, 4096, 4096) == 0
     assert L.fp8q_linear_workspace_size(1, 64, 4096, 4096) == 4 * 64 * 4096 * 4
     assert L.fp8q_linear_workspace_size(1, 1, 4096, 4096) == 0
-    # W8A16, up to 16 activation rows on a mid-sized weight: the rows kernel,
-    # one launch, no scratch
+    # W8A16, up to 16 activation rows on a weight of up to 4096 rows: the rows
+    # kernel, one launch, no scratch
     assert L.fp8q_linear_workspace_size(0, 1, 4096, 4096) == 0
-    assert L.fp8q_linear_workspace_size(0, 12, 8192, 8192) == 0
-    # 64-row tiles: no K split when 448 tiles cover the GPU or K is under two chunks
-    assert L.fp8q_linear_workspace_size(0, 12, 28672, 8192) == 0
+    # wider weights at up to 16 rows with 8K <= K < 16K: the tile kernel with
+    # K split 4 ways
+    assert L.fp8q_linear_workspace_size(0, 12, 8192, 8192) == 4 * 12 * 8192 * 4
+    assert L.fp8q_linear_workspace_size(0, 12, 28672, 8192) == 4 * 12 * 28672 * 4
+    # K = 4096: 448 tiles cover the GPU unsplit
+    assert L.fp8q_linear_workspace_size(0, 12, 28672, 4096) == 0
+    # a small N on a short K: 64-row tiles, no split (K under two chunks)
     assert L.fp8q_linear_workspace_size(0, 4, 64, 500) == 0
     # otherwise K splits towards 256 workgroups (at least two chunks each),
     # with fp32 partial tiles [splits][m][n rounded up to 4]
