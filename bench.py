@@ -456,6 +456,23 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
             "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4), "kernel": fq.describe_linear(1, m, n, k)}
         log(key, rows[f"a6a7_w8a8_{key}"])
 
+        # the same GEMM with per-group weight scales (groups of 128)
+        wqg, wsg = fq.quantize_weight_grouped(w, 128)
+
+        def gemm_g():
+            st = L.fp8q_linear_grouped(1, ptr(xq), m, k, xq.stride(0), ptr(xsc), ptr(wqg), n,
+                                       wqg.stride(0), ptr(wsg), 128, ptr(y), n, None, 0, stream())
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+        ms = time_eager(torch, gemm_g, iters)
+        tf = flops / (ms * 1e-3) / 1e12
+        rows[f"f4_grouped_w8a8_{key}"] = {
+            "shape": f"M={m} N={n} K={k}, groups of 128", "us": round(ms * 1e3, 2),
+            "TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+            "kernel": "k_w8a8<true>: accumulators rescaled by s[g-1]/s[g] as each group opens"}
+        log(key, rows[f"f4_grouped_w8a8_{key}"])
+        del wqg, wsg
+
         aws_n = L.fp8q_quantize_act_workspace_size(m, k)
         aws = torch.empty(aws_n, dtype=torch.uint8, device=dev)
 

@@ -428,15 +428,25 @@ bool valid_group(int64_t group)
     return group == 64 || group == 128 || group == 256 || group == 512;
 }
 
+// Grouped fp8_w_fp8_a with more than the decode rows runs the FP8 MFMA GEMM,
+// which folds group scales at its 128-k stages (groups of 128 k or more).
+bool grouped_uses_gemm(fp8q_mode mode, int64_t m, int64_t group)
+{
+    return mode == FP8Q_W8A8 && m > kW8A8DecodeMaxM && group >= 128;
+}
+
 // group == 0: one weight scale per output row; else per-group scales
 size_t linear_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t group)
 {
     if (m <= 0 || n <= 0 || k < 1)
         return 0;
-    if (group > 0)
-        return valid_group(group)
-                   ? round_up(fp8q::launch::plan_w8a16_grouped(m, n, k, group).workspace, 256)
-                   : 0;
+    if (group > 0) {
+        if (!valid_group(group))
+            return 0;
+        if (grouped_uses_gemm(mode, m, group))
+            return round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
+        return round_up(fp8q::launch::plan_w8a16_grouped(m, n, k, group).workspace, 256);
+    }
     if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16 ||
         (mode == FP8Q_W8A8 && m <= kW8A8DecodeMaxM))
         return round_up(fp8q::launch::plan_w8a16(m, n, k).workspace, 256);
@@ -507,7 +517,11 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
                     : mode == FP8Q_W8A16_F16 ? fp8q::launch::kW8A16ActF16
                                              : fp8q::launch::kW8A16ActF8;
     hipError_t e;
-    if (group > 0) {
+    if (group > 0 && grouped_uses_gemm(mode, m, group)) {
+        const auto plan = fp8q::launch::plan_w8a8(m, n, k);
+        e = fp8q::launch::w8a8(plan, static_cast<const uint8_t *>(x), m, k, ld_x, x_scale, w_fp8,
+                               n, ld_w, w_scale, y_bf16, ld_y, stream, group);
+    } else if (group > 0) {
         const auto plan = fp8q::launch::plan_w8a16_grouped(m, n, k, group);
         e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
                                 ld_y, workspace, stream);

@@ -99,7 +99,8 @@ W8A8Plan plan_w8a8(int64_t m, int64_t n, int64_t k);
 bool w8a8_supports_ld(int64_t ld);
 hipError_t w8a8(const W8A8Plan &p, const uint8_t *x, int64_t m, int64_t k, int64_t ld_x,
                 const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
-                const float *w_scale, uint16_t *y, int64_t ld_y, hipStream_t stream);
+                const float *w_scale, uint16_t *y, int64_t ld_y, hipStream_t stream,
+                int64_t group = 0);
 
 }  // namespace launch
 }  // namespace fp8q

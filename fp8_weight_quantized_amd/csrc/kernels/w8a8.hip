@@ -187,14 +187,26 @@ constexpr int vmcnt_lgkm0_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x
 // moving LDS accesses across it.
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
+// GS: per-group weight scales (the deployment guide §4.3), w_scale
+// [n, ngroups] for groups of gstages * 128 k, so a group is a whole number of
+// stages.  The accumulators then hold the running sum in units of the
+// current group's scale: when stage ks opens group g, every accumulator of
+// weight row n is multiplied by s[n][g-1] / s[n][g] before the stage's
+// MFMAs, and the epilogue multiplies by the last group's scale.  That is
+// sum_g s_g * P_g with one accumulator set (a second set would not fit the
+// register file next to the 256 x 256 tile).  The ratios use the hardware
+// reciprocal (about 1 ulp); group scales come through a 4-slot LDS ring of
+// the tile's 256 rows, loaded one stage ahead.
+template <bool GS>
 __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     const uint8_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
     const float *__restrict__ x_scale,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
-    int tiles_m, int tiles_n)
+    int tiles_m, int tiles_n, int64_t ngroups, int gstages)
 {
     __shared__ __align__(16) uint8_t lds[kLdsBytes];
+    __shared__ __align__(16) float gsc[GS ? 4 * BN : 4];
 
     // ---- tile order: XCD bands, then groups of kGroupM tile-rows ----------
     const int nblocks = tiles_m * tiles_n;
@@ -237,7 +249,66 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
             for (int v = 0; v < 16; ++v)
                 acc[i][j][v] = 0.f;
 
+    // grouped: the scale of tile row tid (< BN) for group g, loaded into a
+    // register one stage ahead and written to LDS slot g & 3 before the barrier
+    // of the stage that opens group g
+    const int64_t last_stage = k / BK - (k % BK == 0 ? 1 : 0);
+    const float *srow = w_scale + (GS ? min(n0 + tid, n - 1) * ngroups : 0);
+    float pend = 0.f;
+    int pend_g = -1;
+    auto fetch_scale = [&](int64_t st) {
+        if constexpr (GS) {
+            if (st <= last_stage && st % gstages == 0) {
+                pend_g = (int)(st / gstages);
+                if (tid < BN)
+                    pend = srow[pend_g];
+            }
+        }
+    };
+    auto store_scale = [&]() {
+        if constexpr (GS) {
+            if (pend_g >= 0) {
+                if (tid < BN)
+                    gsc[(pend_g & 3) * BN + tid] = pend;
+                pend_g = -1;
+            }
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(63));   // lgkmcnt(0): the write is done
+        }
+    };
+    // stage st opens group g > 0: bring the accumulators from units of
+    // s[g-1] to units of s[g] before the stage's MFMAs.  Lane (col, h) of a
+    // 32 x 32 block holds rows 8 * q + 4 * h + e (e = 0..3) of W block i, so
+    // one ratio serves the TM blocks of that row.  (Interleaving these
+    // multiplies with the stage's MFMAs measured slower: each then waits for
+    // the previous stage's last MFMA on its block, and the ratios held live
+    // cost 27 registers.)
+    auto rescale = [&](int64_t st) {
+        if constexpr (GS) {
+            if (st == 0 || st % gstages != 0)
+                return;
+            const int g = (int)(st / gstages);
+            const float *sp = gsc + ((g - 1) & 3) * BN;
+            const float *sc = gsc + (g & 3) * BN;
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = wn * WN + i * 32 + 8 * q + 4 * lh;
+                    const float4 a = *reinterpret_cast<const float4 *>(sp + r);
+                    const float4 b = *reinterpret_cast<const float4 *>(sc + r);
+                    const float ra[4] = {a.x * __builtin_amdgcn_rcpf(b.x), a.y * __builtin_amdgcn_rcpf(b.y),
+                                         a.z * __builtin_amdgcn_rcpf(b.z), a.w * __builtin_amdgcn_rcpf(b.w)};
+#pragma unroll
+                    for (int j = 0; j < TM; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][j][4 * q + e] *= ra[e];
+                }
+        }
+    };
+
     auto compute = [&](int64_t st) {
+        rescale(st);
         const uint8_t *tx = lds + (int)(st % kStages) * kStageBytes;
         const uint8_t *tw = tx + kTileBytes;
 #pragma unroll
@@ -265,6 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     // Full stages run through the ring, loaded kStages-1 stages ahead; a
     // partial last stage (k not a multiple of BK) is peeled off after the loop.
     const int64_t nfull = k / BK;
+    fetch_scale(0);
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st)
         if (st < nfull)
@@ -283,9 +355,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
             __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kOps));
         else
             __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+        // (grouped: the scale load issued during the previous stage has landed
+        // with this wait; its LDS write goes before the barrier)
+        store_scale();
         barrier_no_fence();
         if (ks + kStages - 1 < nfull)
             issue_full(ks + kStages - 1);
+        fetch_scale(ks + 1);
         compute(ks);
     }
     if (k % BK != 0) {
@@ -298,6 +374,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
         lx.load_tail(t, nfull * BK, k, wave, lane);
         lw.load_tail(t + kTileBytes, nfull * BK, k, wave, lane);
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+        store_scale();
         barrier_no_fence();
         compute(nfull);
     }
@@ -306,6 +383,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     // holds D rows 8 * (v / 4) + 4 * h + v % 4, v = 0..15.  D = Y^T here, so
     // the lane holds Y[m = col][n = ... + 4 consecutive], stored as 8 bytes.
     const float xs = *x_scale;
+    // grouped: the last group's scales (every group's LDS write preceded a
+    // barrier that every wave has passed)
+    const float *slast = gsc + (GS ? ((int)(last_stage / (gstages > 0 ? gstages : 1)) & 3) * BN : 0);
+    auto wsc = [&](int64_t nb, int v) {
+        if constexpr (GS)
+            return slast[nb - n0 + v];
+        else
+            return w_scale[nb + v];
+    };
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
         const int64_t mr = m0 + wm * WM + j * 32 + lr;
@@ -320,12 +406,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
                 const v16f &a = acc[i][j];
                 if (nb + 4 <= n) {
                     uint2 o;
-                    o.x = pack_bf16x2(a[4 * q + 0] * (xs * w_scale[nb + 0]), a[4 * q + 1] * (xs * w_scale[nb + 1]));
-                    o.y = pack_bf16x2(a[4 * q + 2] * (xs * w_scale[nb + 2]), a[4 * q + 3] * (xs * w_scale[nb + 3]));
+                    o.x = pack_bf16x2(a[4 * q + 0] * (xs * wsc(nb, 0)), a[4 * q + 1] * (xs * wsc(nb, 1)));
+                    o.y = pack_bf16x2(a[4 * q + 2] * (xs * wsc(nb, 2)), a[4 * q + 3] * (xs * wsc(nb, 3)));
                     *reinterpret_cast<uint2 *>(yrow + nb) = o;
                 } else {
                     for (int v = 0; v < 4 && nb + v < n; ++v)
-                        yrow[nb + v] = (uint16_t)f32_to_bf16_rne(a[4 * q + v] * (xs * w_scale[nb + v]));
+                        yrow[nb + v] = (uint16_t)f32_to_bf16_rne(a[4 * q + v] * (xs * wsc(nb, v)));
                 }
             }
         }
@@ -351,12 +437,22 @@ W8A8Plan plan_w8a8(int64_t m, int64_t n, int64_t k)
 
 hipError_t w8a8(const W8A8Plan &p, const uint8_t *x, int64_t m, int64_t k, int64_t ld_x,
                 const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
-                const float *w_scale, uint16_t *y, int64_t ld_y, hipStream_t stream)
+                const float *w_scale, uint16_t *y, int64_t ld_y, hipStream_t stream,
+                int64_t group)
 {
     const int64_t blocks = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL(k_w8a8, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,
-                       (int)p.tiles_m, (int)p.tiles_n);
+    if (group > 0) {
+        if (group % BK != 0)
+            return hipErrorInvalidValue;
+        const int64_t ngroups = (k + group - 1) / group;
+        hipLaunchKernelGGL(k_w8a8<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                           x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,
+                           (int)p.tiles_m, (int)p.tiles_n, ngroups, (int)(group / BK));
+    } else {
+        hipLaunchKernelGGL(k_w8a8<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                           x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,
+                           (int)p.tiles_m, (int)p.tiles_n, (int64_t)0, 0);
+    }
     return hipGetLastError();
 }
 

@@ -281,9 +281,15 @@ fp8q_status fp8q_linear(fp8q_mode mode,
  * with s_x = *x_scale for FP8Q_W8A8 and 1 otherwise.  Each group's products
  * are summed in fp32 and multiplied by the group's scale as the group ends.
  * Arguments as fp8q_linear, plus group (64, 128, 256 or 512); w_scale must lie
- * inside one device allocation.  Every M runs the decode tile kernel (at
- * prefill sizes W is re-read once per 64 activation rows).  Tolerance and
- * determinism as fp8q_linear.
+ * inside one device allocation and hold positive finite scales.
+ * FP8Q_W8A8 with more than 64 activation rows and group >= 128 runs the FP8
+ * MFMA GEMM: its accumulators are kept in units of the current group's scale,
+ * multiplied by s[n][g-1] / s[n][g] (hardware reciprocal) as group g opens, and
+ * scaled by the last group's scale at the end.  This needs adjacent group scales
+ * of a row within a factor of about 1e28 of each other, which holds for weights
+ * of magnitude below 1e16.  Every other case runs the decode tile kernel (at
+ * prefill sizes with group 64, W is re-read once per 64 activation rows).
+ * Tolerance and determinism as fp8q_linear.
  */
 size_t fp8q_linear_grouped_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
                                           int64_t group);

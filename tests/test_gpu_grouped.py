@@ -184,3 +184,78 @@ def test_full_decode_70b_down_proj(fq, orc):
     rows = np.arange(12)
     assert_gemm_close(host_bf16_as_f64(y), orc.linear_grouped(0, x, qr, sr, 128, rows=rows),
                       "70b down_proj")
+
+
+# ---- fp8_w_fp8_a past the decode rows: the FP8 MFMA GEMM with group scales
+# folded at its 128-k stages (groups of 128, 256, 512)
+
+@pytest.mark.parametrize("group", (128, 256, 512))
+@pytest.mark.parametrize("m,n,k", [(65, 256, 128), (300, 300, 1000), (513, 1022, 4096),
+                                   (130, 64, 640), (257, 100, 100), (70, 520, 1536)])
+def test_w8a8_gemm_grouped(fq, orc, group, m, n, k):
+    run_grouped(fq, orc, 1, m, n, k, group, 3000 + m + n + k, "gemm")
+
+
+@pytest.mark.parametrize("group", (128, 512))
+def test_w8a8_gemm_grouped_wide_scale_range(fq, orc, group):
+    """Adjacent groups whose scales differ by many orders of magnitude: an
+    all-zero group (scale at the 1e-12 floor) between large-valued groups."""
+    m, n, k = 200, 256, 2048
+    w = workloads.heavy_tail_weight(n, k, 55)
+    wf = workloads.bf16_bits_to_f32(w)
+    wf[:, group:2 * group] = 0.0                      # group 1 all zero in every row
+    wf[::3, 3 * group:4 * group] *= np.float32(1e4)   # group 3 large in a third of the rows
+    wf[1::5, :group] *= np.float32(1e-6)              # group 0 tiny in a fifth of the rows
+    w = workloads.f32_to_bf16_bits(wf)
+    wq, ws, _ = orc.quantize_weight_grouped(w, group)
+    assert (ws[:, 1] == np.float32(1e-12)).all()
+    xq, xs, _ = orc.quantize_act(workloads.outlier_act(m, k, 56))
+    say("grouped gemm wide scale range", group)
+    y = fq.linear(dev_u8(xq), dev_u8(wq), torch.from_numpy(ws).cuda(),
+                  x_scale=torch.tensor([np.float32(xs)], device="cuda"), group=group)
+    torch.cuda.synchronize()
+    ref = orc.linear_grouped(1, xq, wq, ws, group, x_scale=xs)
+    assert_gemm_close(host_bf16_as_f64(y), ref, f"wide scale range g={group}")
+
+
+def test_w8a8_gemm_grouped_equals_per_channel_on_shared_scales(fq, orc):
+    """Every group scale equal to the row scale: the grouped GEMM computes the
+    per-channel layer (the ratios are all 1)."""
+    m, n, k = 300, 512, 4096
+    wq, ws, _ = orc.quantize_weight(workloads.heavy_tail_weight(n, k, 57))
+    xq, xs, _ = orc.quantize_act(workloads.outlier_act(m, k, 58))
+    wsg = np.ascontiguousarray(np.repeat(ws[:, None], k // 128, axis=1))
+    say("grouped gemm vs per-channel gemm")
+    xs_d = torch.tensor([np.float32(xs)], device="cuda")
+    y1 = fq.linear(dev_u8(xq), dev_u8(wq), torch.from_numpy(ws).cuda(), x_scale=xs_d)
+    y2 = fq.linear(dev_u8(xq), dev_u8(wq), torch.from_numpy(wsg).cuda(), x_scale=xs_d, group=128)
+    torch.cuda.synchronize()
+    ref = orc.linear(1, xq, wq, ws, xs)
+    assert_gemm_close(host_bf16_as_f64(y1), ref, "per-channel gemm")
+    assert_gemm_close(host_bf16_as_f64(y2), ref, "grouped gemm, shared scales")
+
+
+def test_w8a8_gemm_grouped_full_mlp_prefill_sampled(fq, orc):
+    """Llama-3-8B gate+up prefill, W[28672, 4096], X[8192, 4096], groups of 128:
+    codes and scales bit-exact, GEMM checked on sampled rows."""
+    wl = workloads.WORKLOADS["mlp_prefill"]
+    lin = wl.linears[0]
+    m = wl.ms[0]
+    w = workloads.weight(wl, lin)
+    x = workloads.activation(wl, m, lin.k)
+    say("grouped mlp prefill quantize")
+    q, s = fq.quantize_weight_grouped(dev_bf16(w), 128)
+    xq, xs = fq.quantize_act(dev_bf16(x))
+    torch.cuda.synchronize()
+    qr, sr, _ = orc.quantize_weight_grouped(w, 128)
+    assert (host_u8(q) == qr).all()
+    assert (host_f32(s).view(np.uint32) == sr.view(np.uint32)).all()
+    del w
+    say("grouped mlp prefill gemm")
+    y = fq.linear(xq, q, s, x_scale=xs, group=128)
+    torch.cuda.synchronize()
+    xqr, xsr, _ = orc.quantize_act(x)
+    rows = np.unique(np.concatenate([np.arange(0, m, 509), [m - 1]]))
+    ref = orc.linear_grouped(1, xqr, qr, sr, 128, x_scale=xsr, rows=rows)
+    got = host_bf16_as_f64(y[torch.from_numpy(rows).cuda()])
+    assert_gemm_close(got, ref, "grouped mlp prefill sampled rows")
