@@ -325,7 +325,8 @@ def main() -> int:
             "shape": "N=K=4096, M=1,8,32,64 per step, groups of 128", "us_per_step": round(usg, 3),
             "GB/s": round(bytes_g / (usg * 1e-6) / 1e9, 1),
             "frac_hbm": round(bytes_g / (usg * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "mode": "fp8_w_bf16_a with per-group weight scales (k_w8a16_tile, grouped)"}
+            "mode": "fp8_w_bf16_a with per-group weight scales",
+            "kernels": {str(m): fq.describe_linear(0, m, N, K, G) for m in DECODE_MS}}
         log(rows["f4_grouped_q_proj_decode"])
         del pool_g, gg
         torch.cuda.empty_cache()
@@ -469,7 +470,8 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
         rows[f"f4_grouped_w8a8_{key}"] = {
             "shape": f"M={m} N={n} K={k}, groups of 128", "us": round(ms * 1e3, 2),
             "TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
-            "kernel": "k_w8a8<true>: accumulators rescaled by s[g-1]/s[g] as each group opens"}
+            "kernel": fq.describe_linear(1, m, n, k, 128),
+            "note": "accumulators rescaled by s[g-1]/s[g] as each group opens"}
         log(key, rows[f"f4_grouped_w8a8_{key}"])
         del wqg, wsg
 
@@ -662,7 +664,8 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
         "shape": "7 linears, M=12, groups of 128", "us": round(msg * 1e3, 2),
         "GB/s": round(bg / (msg * 1e-3) / 1e9, 1),
         "frac_hbm": round(bg / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "timing": "one HIP graph per layer step"}
+        "timing": "one HIP graph per layer step",
+        "kernels": {lin.name: fq.describe_linear(0, m, lin.n, lin.k, G) for lin, *_ in layer_g}}
     log(rows["f4_grouped_layer_decode_70b"])
     del layer_g, gg
 

@@ -297,7 +297,10 @@ def cast_f32_to_e4m3(x: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def describe_linear(mode: int, m: int, n: int, k: int) -> str:
+def describe_linear(mode: int, m: int, n: int, k: int, group: int | None = None) -> str:
     buf = ctypes.create_string_buffer(256)
-    check(_lib.lib().fp8q_linear_describe(mode, m, n, k, buf, 256))
+    if group is None:
+        check(_lib.lib().fp8q_linear_describe(mode, m, n, k, buf, 256))
+    else:
+        check(_lib.lib().fp8q_linear_grouped_describe(mode, m, n, k, group, buf, 256))
     return buf.value.decode()

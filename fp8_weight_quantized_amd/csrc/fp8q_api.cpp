@@ -629,6 +629,43 @@ fp8q_status fp8q_cast_f32_to_e4m3(const float *x, int64_t count, uint8_t *out, h
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+void describe_w8a16(const fp8q::launch::W8A16Plan &p, char *buf, size_t len)
+{
+    char spg[16] = "";
+    if (p.group > 0)
+        std::snprintf(spg, sizeof spg, ", %lld", (long long)(p.group / 64));
+    if (p.kind == fp8q::launch::W8A16Plan::kRows)
+        std::snprintf(buf, len,
+                      "k_w8a16_rows<%d, %d, %d, %d%s> rows=%d grid=(%lld,%lld,%lld) block=%d "
+                      "kchunk=%lld splits=%lld%s",
+                      p.af, p.mb, p.depth, p.waves, spg, p.rows, (long long)p.grid_n,
+                      (long long)p.grid_m, (long long)p.splits, 64 * p.waves,
+                      (long long)p.kchunk, (long long)p.splits,
+                      p.splits > 1 ? " + k_w8a16_reduce" : "");
+    else
+        std::snprintf(buf, len,
+                      "k_w8a16_tile<%d, %d, %d%s> grid=(%lld,%lld) block=256 splits=%lld kper=%lld%s",
+                      p.mb, p.xd, p.steps, spg, (long long)p.grid_n, (long long)p.grid_m,
+                      (long long)p.splits, (long long)p.kper,
+                      p.splits > 1 ? " + k_w8a16_reduce" : "");
+}
+
+void describe_w8a8(int64_t m, int64_t n, int64_t k, bool grouped, char *buf, size_t len)
+{
+    const auto p = fp8q::launch::plan_w8a8(m, n, k);
+    std::snprintf(buf, len, "k_w8a8%s tile=256x256x128 grid=%lld (%lldx%lld) block=512",
+                  grouped ? "<true>" : "", (long long)(p.tiles_m * p.tiles_n),
+                  (long long)p.tiles_m, (long long)p.tiles_n);
+}
+
+}  // namespace
+
+extern "C" {
+
 fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k, char *buf,
                                  size_t len)
 {
@@ -636,31 +673,31 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
         return fail(FP8Q_ERR_INVALID_ARG, "buf is NULL or empty");
     if (m < 0 || n < 0 || k < 1)
         return fail(FP8Q_ERR_INVALID_ARG, "bad sizes");
-    if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16 ||
-        (mode == FP8Q_W8A8 && m <= kW8A8DecodeMaxM)) {
-        const auto p = fp8q::launch::plan_w8a16(m, n, k);
-        if (p.kind == fp8q::launch::W8A16Plan::kRows)
-            std::snprintf(buf, len,
-                          "k_w8a16_rows<%d, %d, %d, %d> rows=%d grid=(%lld,%lld,%lld) block=%d "
-                          "kchunk=%lld splits=%lld%s",
-                          p.af, p.mb, p.depth, p.waves, p.rows, (long long)p.grid_n,
-                          (long long)p.grid_m, (long long)p.splits, 64 * p.waves,
-                          (long long)p.kchunk, (long long)p.splits,
-                          p.splits > 1 ? " + k_w8a16_reduce" : "");
-        else
-            std::snprintf(buf, len,
-                          "k_w8a16_tile<%d, %d, %d> grid=(%lld,%lld) block=256 splits=%lld kper=%lld%s",
-                          p.mb, p.xd, p.steps, (long long)p.grid_n, (long long)p.grid_m,
-                          (long long)p.splits, (long long)p.kper,
-                          p.splits > 1 ? " + k_w8a16_reduce" : "");
-    } else if (mode == FP8Q_W8A8) {
-        const auto p = fp8q::launch::plan_w8a8(m, n, k);
-        std::snprintf(buf, len, "k_w8a8 tile=256x256x128 grid=%lld (%lldx%lld) block=512",
-                      (long long)(p.tiles_m * p.tiles_n), (long long)p.tiles_m,
-                      (long long)p.tiles_n);
-    } else {
+    if (mode != FP8Q_W8A16 && mode != FP8Q_W8A16_F16 && mode != FP8Q_W8A8)
         return fail(FP8Q_ERR_INVALID_ARG, "unknown mode %d", (int)mode);
-    }
+    if (mode == FP8Q_W8A8 && m > kW8A8DecodeMaxM)
+        describe_w8a8(m, n, k, false, buf, len);
+    else
+        describe_w8a16(fp8q::launch::plan_w8a16(m, n, k), buf, len);
+    return ok();
+}
+
+fp8q_status fp8q_linear_grouped_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
+                                         int64_t group, char *buf, size_t len)
+{
+    if (buf == nullptr || len == 0)
+        return fail(FP8Q_ERR_INVALID_ARG, "buf is NULL or empty");
+    if (m < 0 || n < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "bad sizes");
+    if (mode != FP8Q_W8A16 && mode != FP8Q_W8A16_F16 && mode != FP8Q_W8A8)
+        return fail(FP8Q_ERR_INVALID_ARG, "unknown mode %d", (int)mode);
+    if (!valid_group(group))
+        return fail(FP8Q_ERR_INVALID_ARG, "group must be 64, 128, 256 or 512 (got %lld)",
+                    (long long)group);
+    if (grouped_uses_gemm(mode, m, group))
+        describe_w8a8(m, n, k, true, buf, len);
+    else
+        describe_w8a16(fp8q::launch::plan_w8a16_grouped(m, n, k, group), buf, len);
     return ok();
 }
 

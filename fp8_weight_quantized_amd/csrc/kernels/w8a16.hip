@@ -205,14 +205,28 @@ __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[M
 // NW: waves per workgroup; wave w owns K range [w*kchunk, (w+1)*kchunk).
 // AT: activation type (kActBF16, kActF16 or kActF8); x is then [m, ld_x]
 // 16-bit values or E4M3 codes, and x_scale (E4M3 only) the activation scale.
-template <int AF, int MB, int P, int NW, int AT>
+// SPG: 0 for one scale per weight row; else per-group scales w_scale [n,
+//     ngroups] for groups of 64*SPG k (the deployment guide §4.3), as in
+//     k_w8a16_tile: the MFMA operands are swapped so a lane's accumulators
+//     belong to one weight row, each group's sum is multiplied by its scale
+//     as the group ends, and wave K ranges start on group boundaries (the
+//     plan makes kchunk a multiple of 512, so each P = 8 round of 512 k is a
+//     whole number of groups and the folds sit at fixed steps).  A group's
+//     scale for the next round is loaded right after this round folds it.
+template <int AF, int MB, int P, int NW, int AT, int SPG = 0>
 __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
     const void *__restrict__ xv, int64_t m, int64_t k, int64_t ld_x,
     const float *__restrict__ x_scale,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
-    int rows, int64_t kchunk, int64_t kper, float *__restrict__ partial, int64_t ldp)
+    int rows, int64_t kchunk, int64_t kper, float *__restrict__ partial, int64_t ldp,
+    int64_t ngroups = 0)
 {
+    constexpr bool GS = SPG > 0;
+    constexpr int SPGD = GS ? SPG : 1;         // SPG as a divisor
+    constexpr int GK = 64 * SPGD;              // k per scale group
+    constexpr int GR = GS ? P / SPGD : 1;      // scale groups per pipelined round
+    static_assert(!GS || P % SPGD == 0, "a round is a whole number of scale groups");
     constexpr bool F8 = AT == kActF8;
     constexpr int CT = compute_type<AT>();
     constexpr int ES = F8 ? 1 : 2;              // bytes per activation value
@@ -258,6 +272,33 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
 #pragma unroll
             for (int j = 0; j < MB; ++j)
                 acc[h][a][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    // grouped: this lane's weight row of fragment a is its output column
+    const float *srow[AF];
+    v4f tot[AF][MB];
+    float sc[GR][AF];
+#pragma unroll
+    for (int a = 0; a < AF; ++a) {
+        srow[a] = w_scale + (GS ? min(n0 + min(16 * a + r, rows - 1), n - 1) * ngroups : 0);
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+            tot[a][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    // close a scale group: each fragment's sum, times its row's scale
+    auto fold = [&](const float (&s)[AF]) {
+#pragma unroll
+        for (int a = 0; a < AF; ++a)
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                tot[a][j] += s[a] * (acc[0][a][j] + acc[1][a][j]);
+                acc[0][a][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                acc[1][a][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            }
+    };
+    auto load_sc = [&](int gi, int64_t k0) {      // group gi of the round starting at k0
+#pragma unroll
+        for (int a = 0; a < AF; ++a)
+            sc[gi][a] = srow[a][(k0 + (int64_t)GK * gi) / GK];
+    };
 
     const int64_t nfull = (ke - kb) / 64;          // whole 64-k steps
     const int64_t npipe = nfull - nfull % P;       // pipelined span
@@ -277,6 +318,11 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
             }
         };
         const int64_t kend = kb + 64 * npipe;
+        if constexpr (GS) {
+#pragma unroll
+            for (int gi = 0; gi < GR; ++gi)
+                load_sc(gi, kb);
+        }
 #pragma unroll
         for (int u = 0; u < P; ++u)
             issue(u, kb + 64 * u);
@@ -285,11 +331,16 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
             static_for<0, P>([&](auto uc) {
                 constexpr int u = decltype(uc)::value;
                 // loads retire in order: with (P-1) steps' loads still in
-                // flight, step u's loads have landed
+                // flight, step u's loads have landed (a scale load issued among
+                // them only makes this wait for more)
                 wait_vmcnt<(P - 1) * L>();
                 __builtin_amdgcn_sched_barrier(0);
-                step_mfma<AF, MB, AT>(wb[u], xb[u], acc[u & 1]);
+                step_mfma<AF, MB, AT, GS>(wb[u], xb[u], acc[u & 1]);
                 issue(u, kk + 64 * (P + u));
+                if constexpr (GS && (u + 1) % SPGD == 0) {
+                    fold(sc[u / SPGD]);
+                    load_sc(u / SPGD, kk + 64 * P);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
@@ -298,12 +349,24 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
             constexpr int u = decltype(uc)::value;
             wait_vmcnt<(P - 1 - u) * L>();
             __builtin_amdgcn_sched_barrier(0);
-            step_mfma<AF, MB, AT>(wb[u], xb[u], acc[u & 1]);
+            step_mfma<AF, MB, AT, GS>(wb[u], xb[u], acc[u & 1]);
+            if constexpr (GS && (u + 1) % SPGD == 0)
+                fold(sc[u / SPGD]);
         });
         kk = kend;
     }
-    // remaining steps one at a time; the last one may be partial (masked at k)
+    // remaining steps one at a time; the last one may be partial (masked at k).
+    // They start on a group boundary; a group's scale is read at its first
+    // step and applied after its last (or at the end of the wave's range).
+    float s_tail[AF];
     for (; kk < ke; kk += 64) {
+        if constexpr (GS) {
+            if ((kk - kb) % GK == 0) {
+#pragma unroll
+                for (int a = 0; a < AF; ++a)
+                    s_tail[a] = srow[a][kk / GK];
+            }
+        }
         const int64_t kw = kk + 16 * g;
         v4u wv[AF];
         v4u xv[MB][2];
@@ -333,7 +396,11 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
                 }
             }
         }
-        step_mfma<AF, MB, AT>(wv, xv, acc[0]);
+        step_mfma<AF, MB, AT, GS>(wv, xv, acc[0]);
+        if constexpr (GS) {
+            if ((kk + 64 - kb) % GK == 0 || kk + 64 >= ke)
+                fold(s_tail);
+        }
     }
 
     // ---- sum the waves' partial tiles in wave order, then scale and store --
@@ -341,8 +408,37 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
     for (int a = 0; a < AF; ++a)
 #pragma unroll
         for (int j = 0; j < MB; ++j)
-            red[wave][a * MB + j][lane] = acc[0][a][j] + acc[1][a][j];
+            red[wave][a * MB + j][lane] = GS ? tot[a][j] : acc[0][a][j] + acc[1][a][j];
     __syncthreads();
+
+    if constexpr (GS) {
+        // lane slot sl holds D rows 4 * (sl >> 4) + v (activation rows) of
+        // column sl & 15 (weight row 16a + (sl & 15)); group scales are applied
+        for (int slot = threadIdx.x; slot < AF * MB * kWave; slot += blockDim.x) {
+            const int f = slot / kWave;
+            const int sl = slot % kWave;
+            const int a = f / MB;
+            const int j = f % MB;
+            const int nl = 16 * a + (sl & 15);
+            const int64_t nc = n0 + nl;
+            if (nl >= rows || nc >= n)
+                continue;
+            v4f sum = red[0][f][sl];
+            for (int wv = 1; wv < NW; ++wv)
+                sum += red[wv][f][sl];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t mr = m0 + 16 * j + 4 * (sl >> 4) + v;
+                if (mr >= m)
+                    continue;
+                if (gridDim.z > 1)
+                    partial[((int64_t)split * m + mr) * ldp + nc] = sum[v];
+                else
+                    y[mr * ld_y + nc] = Act<CT>::one(sum[v] * xs);
+            }
+        }
+        return;
+    }
 
     // one thread per (fragment, lane) slot: 4 outputs of one row of Y
     for (int slot = threadIdx.x; slot < AF * MB * kWave; slot += blockDim.x) {
@@ -861,8 +957,26 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
 
 W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group)
 {
-    // the tile kernel for every shape: 512-k chunks (8 steps), so a chunk
-    // holds a whole number of groups of 64..512 k
+    // where the per-channel plan takes the rows kernel, so does the grouped
+    // one, with wave K ranges in whole 512-k rounds (so groups of up to 512 k
+    // never straddle a round).  A K split (small N on a long K) already cuts
+    // K into multiples of 4 waves x 512 k; unsplit, the wave ranges are
+    // rounded up to 512 k.
+    {
+        W8A16Plan r = plan_w8a16(m, n, k);
+        if (r.kind == W8A16Plan::kRows && r.mb == 1 && r.depth == 8) {
+            if (r.splits == 1) {
+                r.kchunk = div_up(div_up(k, r.waves), 512) * 512;
+                r.kper = r.kchunk * r.waves;
+            }
+            if (r.kchunk % 512 == 0) {
+                r.group = group;
+                return r;
+            }
+        }
+    }
+    // else the tile kernel, with the per-channel plan's chunks of 512 or
+    // 1024 k (8 or 16 steps), each a whole number of groups of 64..512 k
     W8A16Plan p{};
     const int64_t mgroups = div_up(m, 16);
     p.mb = (int)(mgroups >= 4 ? 4 : (mgroups < 1 ? 1 : mgroups));
@@ -870,9 +984,11 @@ W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group)
     p.tiles_n = div_up(n, kTileN);
     p.ldp = div_up(n, 4) * 4;
     p.group = group;
-    plan_tile(p, m, k, 8);
+    const int64_t tiles = p.tiles_n * p.grid_m;
+    plan_tile(p, m, k, (k >= 16384 || tiles >= 256) ? 16 : 8);
     if (p.mb == 1 && p.tiles_n > 64 && k >= 8192 && k < 16384) {
         // as the per-channel plan: wide weights split K 4 ways at decode
+        p.steps = p.tiles_n >= 256 ? 16 : 8;
         const int64_t chunk = 64 * p.steps;
         int64_t s = 4;
         const int64_t s_max = k / (2 * chunk);
@@ -886,7 +1002,7 @@ W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group)
     return p;
 }
 
-template <int AF, int MB, int P, int NW, int AT>
+template <int AF, int MB, int P, int NW, int AT, int SPG = 0>
 static void launch_rows(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
                         const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
                         const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
@@ -894,13 +1010,15 @@ static void launch_rows(const W8A16Plan &p, const void *x, int64_t m, int64_t k,
 {
     float *partial = static_cast<float *>(workspace);
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m, (unsigned)p.splits);
-    hipLaunchKernelGGL((k_w8a16_rows<AF, MB, P, NW, AT>), grid, dim3(NW * kWave), 0, stream, x, m, k,
-                       ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk, p.kper, partial,
-                       p.ldp);
+    const int64_t ngroups = SPG > 0 ? div_up(k, 64 * SPG) : 0;
+    hipLaunchKernelGGL((k_w8a16_rows<AF, MB, P, NW, AT, SPG>), grid, dim3(NW * kWave), 0, stream, x, m,
+                       k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk, p.kper,
+                       partial, p.ldp, ngroups);
     if (p.splits > 1) {
         const int64_t slots = m * (p.ldp / 4);
         hipLaunchKernelGGL((k_w8a16_reduce<AT>), dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
-                           partial, m, n, p.ldp, (int)p.splits, x_scale, w_scale, y, ld_y);
+                           partial, m, n, p.ldp, (int)p.splits, x_scale,
+                           SPG > 0 ? nullptr : w_scale, y, ld_y);
     }
 }
 
@@ -930,7 +1048,7 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
                            void *workspace, hipStream_t stream)
 {
     float *partial = static_cast<float *>(workspace);
-    if (p.kind == W8A16Plan::kRows) {
+    if (p.group == 0 && p.kind == W8A16Plan::kRows) {
 #define FP8Q_ROWS_CASE(AF, MB, P, NW)                                                         \
         if (p.af == AF && p.mb == MB && p.depth == P && p.waves == NW) {                      \
             launch_rows<AF, MB, P, NW, AT>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y,    \
@@ -940,23 +1058,39 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
         FP8Q_ROWS_CASE(2, 1, 8, 4)
         FP8Q_ROWS_CASE(1, 1, 8, 4)
 #undef FP8Q_ROWS_CASE
+    } else if (p.group > 0 && p.kind == W8A16Plan::kRows) {
+#define FP8Q_GROUP_ROWS_CASE(AF, SPG)                                                         \
+        if (p.af == AF && p.mb == 1 && p.depth == 8 && p.waves == 4 && p.group == 64 * SPG) {  \
+            launch_rows<AF, 1, 8, 4, AT, SPG>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, \
+                                              ld_y, workspace, stream);                      \
+            return hipGetLastError();                                                         \
+        }
+        FP8Q_GROUP_ROWS_CASE(1, 1) FP8Q_GROUP_ROWS_CASE(1, 2)
+        FP8Q_GROUP_ROWS_CASE(1, 4) FP8Q_GROUP_ROWS_CASE(1, 8)
+        FP8Q_GROUP_ROWS_CASE(2, 1) FP8Q_GROUP_ROWS_CASE(2, 2)
+        FP8Q_GROUP_ROWS_CASE(2, 4) FP8Q_GROUP_ROWS_CASE(2, 8)
+#undef FP8Q_GROUP_ROWS_CASE
     } else if (p.group > 0) {
-#define FP8Q_GROUP_CASE(MB, XD, SPG)                                                          \
-        if (p.mb == MB && p.xd == XD && p.steps == 8 && p.group == 64 * SPG) {                \
-            launch_tile<MB, XD, 8, AT, SPG>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y,   \
+#define FP8Q_GROUP_CASE(MB, XD, T, SPG)                                                       \
+        if (p.mb == MB && p.xd == XD && p.steps == T && p.group == 64 * SPG) {                \
+            launch_tile<MB, XD, T, AT, SPG>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y,   \
                                             ld_y, partial, stream);                           \
             return hipGetLastError();                                                         \
         }
-#define FP8Q_GROUP_SIZES(MB, XD)                                                              \
-        FP8Q_GROUP_CASE(MB, XD, 1) FP8Q_GROUP_CASE(MB, XD, 2)                                 \
-        FP8Q_GROUP_CASE(MB, XD, 4) FP8Q_GROUP_CASE(MB, XD, 8)
-        FP8Q_GROUP_SIZES(1, 1)
-        FP8Q_GROUP_SIZES(1, 2)
-        FP8Q_GROUP_SIZES(1, 3)
-        FP8Q_GROUP_SIZES(1, 4)
-        FP8Q_GROUP_SIZES(2, 8)
-        FP8Q_GROUP_SIZES(3, 12)
-        FP8Q_GROUP_SIZES(4, 16)
+#define FP8Q_GROUP_SIZES(MB, XD, T)                                                           \
+        FP8Q_GROUP_CASE(MB, XD, T, 1) FP8Q_GROUP_CASE(MB, XD, T, 2)                           \
+        FP8Q_GROUP_CASE(MB, XD, T, 4) FP8Q_GROUP_CASE(MB, XD, T, 8)
+        FP8Q_GROUP_SIZES(1, 1, 8)
+        FP8Q_GROUP_SIZES(1, 2, 8)
+        FP8Q_GROUP_SIZES(1, 3, 8)
+        FP8Q_GROUP_SIZES(1, 4, 8)
+        FP8Q_GROUP_SIZES(1, 1, 16)
+        FP8Q_GROUP_SIZES(1, 2, 16)
+        FP8Q_GROUP_SIZES(1, 3, 16)
+        FP8Q_GROUP_SIZES(1, 4, 16)
+        FP8Q_GROUP_SIZES(2, 8, 8)
+        FP8Q_GROUP_SIZES(3, 12, 8)
+        FP8Q_GROUP_SIZES(4, 16, 8)
 #undef FP8Q_GROUP_SIZES
 #undef FP8Q_GROUP_CASE
     } else {

@@ -287,8 +287,9 @@ fp8q_status fp8q_linear(fp8q_mode mode,
  * multiplied by s[n][g-1] / s[n][g] (hardware reciprocal) as group g opens, and
  * scaled by the last group's scale at the end.  This needs adjacent group scales
  * of a row within a factor of about 1e28 of each other, which holds for weights
- * of magnitude below 1e16.  Every other case runs the decode tile kernel (at
- * prefill sizes with group 64, W is re-read once per 64 activation rows).
+ * of magnitude below 1e16.  Every other case runs the decode kernels: the rows
+ * kernel where fp8q_linear would, else the tile kernel (at prefill sizes with
+ * group 64, W is then re-read once per 64 activation rows).
  * Tolerance and determinism as fp8q_linear.
  */
 size_t fp8q_linear_grouped_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
@@ -316,6 +317,13 @@ fp8q_status fp8q_cast_f32_to_e4m3(const float *x, int64_t count, uint8_t *out, h
  */
 fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
                                  char *buf, size_t len);
+
+/*
+ * The same for fp8q_linear_grouped with this group (64, 128, 256 or 512; any
+ * other value is FP8Q_ERR_INVALID_ARG).  Host-only; launches nothing.
+ */
+fp8q_status fp8q_linear_grouped_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
+                                         int64_t group, char *buf, size_t len);
 
 #ifdef __cplusplus
 }

@@ -98,6 +98,29 @@ def test_describe(L):
     assert L.fp8q_linear_describe(7, 1, 1, 1, buf, 256) == 1
 
 
+def test_describe_grouped(L):
+    buf = ctypes.create_string_buffer(256)
+    # up to 16 rows on a 4096-row weight: the rows kernel, 1024-k wave ranges
+    assert L.fp8q_linear_grouped_describe(0, 1, 4096, 4096, 128, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4, 2>") and b"kchunk=1024" in buf.value
+    # K = 1000: wave ranges rounded up to one 512-k round
+    assert L.fp8q_linear_grouped_describe(2, 12, 4096, 1000, 64, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4, 1>") and b"kchunk=512" in buf.value
+    # a small N on a long K: the rows kernel with K splits, as per channel
+    assert L.fp8q_linear_grouped_describe(0, 12, 1024, 8192, 512, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4, 8>") and b"k_w8a16_reduce" in buf.value
+    # 64 rows: the tile kernel
+    assert L.fp8q_linear_grouped_describe(0, 64, 4096, 4096, 128, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_tile<4, 16, 8, 2>")
+    # prefill W8A8: the FP8 GEMM for groups of 128 and up, the tile kernel for 64
+    assert L.fp8q_linear_grouped_describe(1, 8192, 28672, 4096, 128, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a8<true>") and b"32x112" in buf.value
+    assert L.fp8q_linear_grouped_describe(1, 8192, 28672, 4096, 64, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_tile<4, 16, 8, 1>")
+    assert L.fp8q_linear_grouped_describe(0, 1, 4096, 4096, 96, buf, 256) == 1
+    assert L.fp8q_linear_grouped_describe(7, 1, 1, 1, 128, buf, 256) == 1
+
+
 NULL = None
 
 
@@ -208,12 +231,16 @@ def test_grouped_host_validation(L):
     assert lg(0, NULL, 4, 512, 500, NULL, NULL, 8, 512, NULL, 128, NULL, 8, NULL, 0, NULL) == 1
     assert lg(1, NULL, 4, 512, 512, NULL, NULL, 8, 512, NULL, 128, NULL, 8, NULL, 0, NULL) == 1
     # a K split at decode: workspace needed, none given
-    # 2 tiles of 64 rows: 28 splits of 1024 k (2 chunks each) -> [28][12][128] fp32
-    assert L.fp8q_linear_grouped_workspace_size(0, 12, 128, 28672, 128) == 28 * 12 * 128 * 4
+    # 2 tiles of 64 rows, K >= 16K: 1024-k chunks, 14 splits of 2048 k (2
+    # chunks each) -> [14][12][128] fp32, as per channel
+    assert L.fp8q_linear_grouped_workspace_size(0, 12, 128, 28672, 128) == 14 * 12 * 128 * 4
+    assert L.fp8q_linear_workspace_size(0, 12, 128, 28672) == 14 * 12 * 128 * 4
     assert lg(0, NULL, 12, 28672, 28672, NULL, NULL, 128, 28672, NULL, 128, NULL, 128, NULL, 0,
               NULL) == 4
-    # 64 tiles: 4 splits of 1024 k
-    assert L.fp8q_linear_grouped_workspace_size(0, 1, 4096, 4096, 128) == 4 * 1 * 4096 * 4
+    # up to 16 rows on a 4096-row weight: the rows kernel, unsplit, as per channel
+    assert L.fp8q_linear_grouped_workspace_size(0, 1, 4096, 4096, 128) == 0
+    # 64 rows: 64 tiles, 4 splits of 1024 k
+    assert L.fp8q_linear_grouped_workspace_size(0, 64, 4096, 4096, 128) == 4 * 64 * 4096 * 4
     # 448 tiles x 128 row blocks: no split
     assert L.fp8q_linear_grouped_workspace_size(1, 8192, 28672, 4096, 128) == 0
 

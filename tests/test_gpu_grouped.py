@@ -122,6 +122,41 @@ def test_linear_shapes(fq, orc, mode, group, m, n, k):
     run_grouped(fq, orc, mode, m, n, k, group, 1000 + m + n + k)
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("group", GROUPS)
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (8, 3000, 4096), (16, 4096, 8192),
+                                   (3, 2100, 700), (12, 4096, 1000), (1, 2050, 520),
+                                   (16, 8200, 2048), (2, 12000, 1100)])
+def test_linear_rows_kernel(fq, orc, mode, group, m, n, k):
+    """Up to 16 rows on weights of 2049 to ~16K rows (short K past 4096): the
+    rows kernel with group folds at fixed steps of its 512-k rounds.  N = 3000,
+    2100 and 2050 give 8-row workgroups, 4096 16-row ones, 8200 and 12000
+    32-row ones; K = 520 and 700 leave waves with no K range."""
+    run_grouped(fq, orc, mode, m, n, k, group, 4000 + m + n + k, "rows")
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("group", GROUPS)
+@pytest.mark.parametrize("m,n,k", [(12, 1024, 8192), (1, 1000, 4100), (16, 2048, 16000),
+                                   (5, 130, 9000)])
+def test_linear_rows_kernel_k_splits(fq, orc, mode, group, m, n, k):
+    """A small N on a long K: the rows kernel with K split across workgroups in
+    ranges of 2048 k; each split writes its group-scaled partial sums and the
+    reduce applies only the activation scale (N = 1000 and 130 leave part of
+    a workgroup's rows past N; K = 4100 ends in a partial step)."""
+    run_grouped(fq, orc, mode, m, n, k, group, 5000 + m + n + k, "rows split")
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("group", GROUPS)
+@pytest.mark.parametrize("m,n,k", [(12, 16448, 8192), (4, 300, 20000), (16, 4160, 17000)])
+def test_linear_tile_1024k_chunks(fq, orc, mode, group, m, n, k):
+    """The tile kernel with 1024-k chunks (16 steps): a weight of more than 256
+    tiles with 8K <= K < 16K (K split 4 ways), or K >= 16K (K = 20000 and
+    17000 leave a ragged tail of steps after the whole chunks)."""
+    run_grouped(fq, orc, mode, m, n, k, group, 6000 + m + n + k, "tile 1024k")
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("m,n,k,group", [(1, 64, 8192, 128), (12, 128, 28672, 128),
                                          (4, 64, 12288, 64), (64, 64, 16384, 512)])
