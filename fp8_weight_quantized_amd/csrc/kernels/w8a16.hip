@@ -827,10 +827,39 @@ __global__ __launch_bounds__(256) void k_w8a16_reduce(
         return;
     const int64_t mr = slot / q;
     const int64_t nb = 4 * (slot % q);
-    v4f s = *reinterpret_cast<const v4f *>(partial + mr * ldp + nb);
-    for (int sp = 1; sp < splits; ++sp)
-        s += *reinterpret_cast<const v4f *>(partial + ((int64_t)sp * m + mr) * ldp + nb);
-    store_y4<CT>(y, ld_y, w_scale, xs, mr, nb, n, s);
+    // every load is issued before the first add: the weight scales (clamped
+    // to row n-1; only valid columns are stored) and up to 8 splits per
+    // batch.  The sum still runs in split order.
+    float ws[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        ws[v] = w_scale != nullptr ? w_scale[min(nb + v, n - 1)] : 1.0f;
+    auto part = [&](int sp) {
+        return *reinterpret_cast<const v4f *>(partial + ((int64_t)sp * m + mr) * ldp + nb);
+    };
+    constexpr int kBatch = 8;
+    v4f s = part(0);
+    for (int sb = 1; sb < splits; sb += kBatch) {
+        v4f p[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (sb + i < splits)
+                p[i] = part(sb + i);
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (sb + i < splits)
+                s += p[i];
+    }
+    uint16_t *yp = y + mr * ld_y + nb;
+    if (nb + 4 <= n) {
+        uint2 o;
+        o.x = Act<CT>::pack2(s[0] * (xs * ws[0]), s[1] * (xs * ws[1]));
+        o.y = Act<CT>::pack2(s[2] * (xs * ws[2]), s[3] * (xs * ws[3]));
+        *reinterpret_cast<uint2 *>(yp) = o;
+    } else {
+        for (int v = 0; v < (int)(n - nb); ++v)
+            yp[v] = Act<CT>::one(s[v] * (xs * ws[v]));
+    }
 }
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
