@@ -155,6 +155,28 @@ def main() -> int:
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"decode step {ms_per_step * 1e3:.2f} us, {value:.1f} GB/s")
 
+    # spread of the step time, outside the timed region: one event pair per
+    # replay of a whole rotation of the weight pool
+    g_dist = g_full if g_full is not None else capture(rot)
+    if g_full is None:
+        g_dist.replay()
+    samples = []
+    for _ in range(20):
+        a_ev = torch.cuda.Event(enable_timing=True)
+        b_ev = torch.cuda.Event(enable_timing=True)
+        a_ev.record()
+        g_dist.replay()
+        b_ev.record()
+        b_ev.synchronize()
+        samples.append(a_ev.elapsed_time(b_ev) * 1e3 / rot)
+    samples.sort()
+
+    def pct(q: float) -> float:
+        return round(samples[min(len(samples) - 1, int(q * (len(samples) - 1) + 0.5))], 3)
+    step_spread = {"median_us": pct(0.5), "p10_us": pct(0.1), "p90_us": pct(0.9),
+                   "samples": len(samples), "steps_per_sample": rot}
+    log("step spread", step_spread)
+
     # per-M breakdown (each call alone, graph of one rotation)
     per_m = {}
     for j, m in enumerate(DECODE_MS):
@@ -208,6 +230,7 @@ def main() -> int:
                           "fp32 accumulation, fp32 per-channel scale, bf16 output",
         },
         "per_m": per_m,
+        "step_spread": step_spread,
         "roofline": roofline_decode(per_m, N, K),
     }
 
