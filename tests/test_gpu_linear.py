@@ -129,7 +129,7 @@ def test_w8a16_f16_ragged(fq, orc, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(256, 256, 64), (300, 260, 128), (33, 512, 64), (8, 300, 1100),
-                                   (64, 272, 1600), (1, 4096, 640), (16, 512, 4160)])
+                                   (64, 272, 1600), (1, 4096, 640), (16, 512, 4160), (520, 300, 640)])
 def test_w8a8_exact_every_code(fq, orc, m, n, k):
     """One-hot E4M3 rows (spread over K) pick weight columns exactly; up to 64
     rows this is the decode path, beyond it the FP8 MFMA GEMM."""
@@ -170,7 +170,12 @@ def test_w8a16_ragged(fq, orc, m, n, k):
     assert_gemm_close(y, orc.linear(0, x, wq, ws), f"w8a16 {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", RAGGED + [(300, 520, 1000), (256, 256, 4096), (513, 257, 200)])
+# K a multiple of the prefill kernel's 128-byte stage: one stage, two, an odd
+# count, with ragged M and N around the 256 x 256 tile
+WHOLE_STAGES = [(257, 300, 128), (300, 520, 384), (513, 257, 256), (1000, 1000, 1280), (777, 64, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", RAGGED + [(300, 520, 1000), (256, 256, 4096), (513, 257, 200)] + WHOLE_STAGES)
 def test_w8a8_ragged(fq, orc, m, n, k):
     w = workloads.heavy_tail_weight(n, k, m + n)
     x = workloads.outlier_act(m, k, k)
