@@ -430,13 +430,26 @@ def roofline_decode(per_m: dict, n: int, k: int) -> dict:
     }
 
 
-def time_eager(torch, fn, iters: int, warm: int = 2) -> float:
-    """Average ms per call of fn() over `iters` calls, HIP events on the current stream."""
-    for _ in range(warm):
+def time_eager(torch, fn, iters: int, warm: int = 2, warm_ms: float = 30.0) -> float:
+    """Average ms per call of fn() over `iters` calls, HIP events on the current stream.
+
+    Warm-up runs at least `warm` calls and at least `warm_ms` of GPU time: under
+    sustained matrix-core load the clock drops after the first few calls and
+    recovers over the next ~20 ms (seen in kernel traces of the prefill GEMM),
+    so timing right after a short warm-up would measure that transient instead
+    of the sustained rate."""
+    for _ in range(max(1, warm)):
         fn()
-    torch.cuda.synchronize()
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    fn()
+    e.record()
+    e.synchronize()
+    once = max(s.elapsed_time(e), 1e-3)
+    for _ in range(min(500, int(warm_ms / once))):
+        fn()
+    torch.cuda.synchronize()
     s.record()
     for _ in range(iters):
         fn()

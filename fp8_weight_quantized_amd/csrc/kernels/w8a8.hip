@@ -46,6 +46,8 @@ namespace {
 
 using namespace dev;
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 128;              // bytes (= k values) per stage
@@ -381,7 +383,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
 
     // ---- epilogue.  In a 32 x 32 block, lane (col = lane % 32, h = lane / 32)
     // holds D rows 8 * (v / 4) + 4 * h + v % 4, v = 0..15.  D = Y^T here, so
-    // the lane holds Y[m = col][n = ... + 4 consecutive], stored as 8 bytes.
+    // the lane holds Y[m = col][n = ... + 4 consecutive]: 8 bytes in each of
+    // 32 rows per store instruction, which measured at about 2.3 TB/s of
+    // output (15 us per tile at M = 8192).  Instead the scaled bf16 tile is
+    // staged row-major in the LDS ring, free once every wave is past its last
+    // stage, and written out as whole rows: each lane stores 16 bytes and a
+    // wave covers two 512-byte rows.  A staged row is 32 chunks of 16 bytes,
+    // chunk c of row r stored at c ^ (r & 31), so the 32 rows of one write
+    // instruction and the 32 chunks of one row's read spread over the banks.
     const float xs = *x_scale;
     // grouped: the last group's scales (every group's LDS write preceded a
     // barrier that every wave has passed)
@@ -390,30 +399,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
         if constexpr (GS)
             return slast[nb - n0 + v];
         else
-            return w_scale[nb + v];
+            return w_scale[min(nb + v, n - 1)];
     };
+    constexpr int kRowBytes = BN * 2;             // one staged output row (512 bytes)
+    constexpr int kRowChunks = kRowBytes / 16;    // 32
+    static_assert(BM * kRowBytes <= kLdsBytes, "the output tile fits the ring");
+    auto out_off = [](int r, int c) { return r * kRowBytes + ((c ^ (r & (kRowChunks - 1))) * 16); };
+    // every wave's reads of the last stage have returned before any wave
+    // overwrites the ring (the direct loads all landed with the last vmcnt(0))
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(63));   // lgkmcnt(0)
+    barrier_no_fence();
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-        const int64_t mr = m0 + wm * WM + j * 32 + lr;
-        if (mr >= m)
-            continue;
-        uint16_t *yrow = y + mr * ld_y;
+        const int r = wm * WM + j * 32 + lr;
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t nb = n0 + wn * WN + i * 32 + 8 * q + 4 * lh;
+                const int nl = wn * WN + i * 32 + 8 * q + 4 * lh;   // multiple of 4
+                const int64_t nb = n0 + nl;
                 const v16f &a = acc[i][j];
-                if (nb + 4 <= n) {
-                    uint2 o;
-                    o.x = pack_bf16x2(a[4 * q + 0] * (xs * wsc(nb, 0)), a[4 * q + 1] * (xs * wsc(nb, 1)));
-                    o.y = pack_bf16x2(a[4 * q + 2] * (xs * wsc(nb, 2)), a[4 * q + 3] * (xs * wsc(nb, 3)));
-                    *reinterpret_cast<uint2 *>(yrow + nb) = o;
-                } else {
-                    for (int v = 0; v < 4 && nb + v < n; ++v)
-                        yrow[nb + v] = (uint16_t)f32_to_bf16_rne(a[4 * q + v] * (xs * wsc(nb, v)));
-                }
+                uint2 o;
+                o.x = pack_bf16x2(a[4 * q + 0] * (xs * wsc(nb, 0)), a[4 * q + 1] * (xs * wsc(nb, 1)));
+                o.y = pack_bf16x2(a[4 * q + 2] * (xs * wsc(nb, 2)), a[4 * q + 3] * (xs * wsc(nb, 3)));
+                *reinterpret_cast<uint2 *>(lds + out_off(r, nl / 8) + (nl & 4) * 2) = o;
             }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(63));   // lgkmcnt(0)
+    barrier_no_fence();
+    constexpr int kRowsPerPass = kThreads / kRowChunks;   // 16
+    const int c = tid % kRowChunks;
+#pragma unroll 4
+    for (int r = tid / kRowChunks; r < BM; r += kRowsPerPass) {
+        const int64_t mr = m0 + r;
+        const int64_t nb = n0 + 8 * c;
+        if (mr >= m || nb >= n)
+            continue;
+        const uint4 v = *reinterpret_cast<const uint4 *>(lds + out_off(r, c));
+        uint16_t *yp = y + mr * ld_y + nb;
+        if (nb + 8 <= n) {
+            // non-temporal: the output (470 MB for Llama-3-8B gate+up at 8192
+            // tokens) streams past the caches instead of evicting the X and W
+            // panels later tiles re-read (about 5% at M = 8192)
+            __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u *>(yp));
+        } else {
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < (int)(n - nb); ++e)
+                yp[e] = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
         }
     }
 }
