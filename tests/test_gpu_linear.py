@@ -336,3 +336,41 @@ def test_host_pointer_and_device_checks(fq):
     assert st == 0, L.fp8q_last_error()
     torch.cuda.synchronize()
     assert (y.float() == 0).all()
+
+
+@pytest.mark.parametrize("mode,m,n,k", [(1, 300, 300, 256), (1, 520, 1000, 384), (1, 300, 300, 200),
+                                        (1, 257, 9, 128), (0, 12, 300, 8192), (0, 64, 1000, 4096)])
+def test_output_stride_guard(fq, orc, mode, m, n, k):
+    """Y written into a wider buffer (ld_y = n rounded up to 8, plus 24) with
+    rows to spare: every element past column n or row m keeps its sentinel,
+    and the [m, n] block is in tolerance.  Covers the prefill GEMM's staged
+    row stores (ragged last 16-byte chunk) and the decode kernels."""
+    from fp8_weight_quantized_amd import _lib
+    L = _lib.lib()
+    w = workloads.heavy_tail_weight(n, k, 70 + m)
+    wq, ws, _ = orc.quantize_weight(w)
+    if mode == 1:
+        xq, xs, _ = orc.quantize_act(workloads.outlier_act(m, k, 80 + m))
+        xd, ref = pad16(xq), orc.linear(1, xq, wq, ws, xs)
+        xsd = torch.tensor([xs], dtype=torch.float32, device="cuda")
+    else:
+        x = workloads.normal_act(m, k, 80 + m)
+        xd, ref, xsd = pad8_bf16(x), orc.linear(0, x, wq, ws), None
+    wd, wsd = pad16(wq), torch.from_numpy(ws).cuda()
+    ld_y = (n + 7) // 8 * 8 + 24
+    sentinel = 0x7FC1
+    ybuf = torch.full((m + 3, ld_y), sentinel, dtype=torch.int16, device="cuda")
+    need = L.fp8q_linear_workspace_size(mode, m, n, k)
+    wk = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    say("output stride guard", mode, m, n, k, fq.describe_linear(mode, m, n, k))
+    st = L.fp8q_linear(mode, xd.data_ptr(), m, k, xd.stride(0),
+                       xsd.data_ptr() if xsd is not None else None, wd.data_ptr(), n, wd.stride(0),
+                       wsd.data_ptr(), ybuf.data_ptr(), ld_y, wk.data_ptr(), need,
+                       torch.cuda.current_stream().cuda_stream)
+    assert st == 0, _lib.last_error()
+    torch.cuda.synchronize()
+    yb = ybuf.cpu().numpy()
+    assert (yb[:m, n:] == sentinel).all(), "wrote past column n"
+    assert (yb[m:, :] == sentinel).all(), "wrote past row m"
+    y = host_bf16_as_f64(ybuf[:m, :n].view(torch.bfloat16))
+    assert_gemm_close(y, ref, f"stride guard mode {mode} {m}x{n}x{k}")
