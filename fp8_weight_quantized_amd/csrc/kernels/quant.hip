@@ -12,6 +12,7 @@
 // (1 B/element).  Loads are 16 B per lane, stores 8 B per lane, fully
 // coalesced; the reductions use wave shuffles and a few words of LDS.
 #include "device_common.hpp"
+#include "e4m3_div.hpp"
 #include "launch.hpp"
 
 namespace fp8q {
@@ -73,17 +74,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight(
             *flag = 1;
     }
 
+    const E4M3Div div(s);
     if constexpr (CH > 0) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int64_t idx = tid + (int64_t)c * kThreads;
             if (idx < nfull)
-                *reinterpret_cast<uint2 *>(qr + idx * 8) = quantize8(buf[c], s);
+                *reinterpret_cast<uint2 *>(qr + idx * 8) = div.codes8(buf[c]);
         }
     } else {
         for (int64_t idx = tid; idx < nfull; idx += kThreads) {
             uint4 v = *reinterpret_cast<const uint4 *>(wr + idx * 8);
-            *reinterpret_cast<uint2 *>(qr + idx * 8) = quantize8(v, s);
+            *reinterpret_cast<uint2 *>(qr + idx * 8) = div.codes8(v);
         }
     }
     if (tid < tail) {
@@ -334,6 +336,7 @@ __global__ __launch_bounds__(kThreads) void k_act_cast(
         s = *held;
     }
 
+    const E4M3Div div(s);
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (layout == kScalar) {
@@ -355,16 +358,16 @@ __global__ __launch_bounds__(kThreads) void k_act_cast(
             uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
             if constexpr (kTrack)
                 key = max(key, max(max(key_max8(a), key_max8(b)), max(key_max8(c), key_max8(d))));
-            o[i] = quantize8(a, s);
-            o[i + stride] = quantize8(b, s);
-            o[i + 2 * stride] = quantize8(c, s);
-            o[i + 3 * stride] = quantize8(d, s);
+            o[i] = div.codes8(a);
+            o[i + stride] = div.codes8(b);
+            o[i + 2 * stride] = div.codes8(c);
+            o[i + 3 * stride] = div.codes8(d);
         }
         for (; i < total; i += stride) {
             const uint4 a = p[i];
             if constexpr (kTrack)
                 key = max(key, key_max8(a));
-            o[i] = quantize8(a, s);
+            o[i] = div.codes8(a);
         }
     } else {
         const int64_t cpr = (k + 7) >> 3;
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void k_act_cast(
                 const uint4 a = *reinterpret_cast<const uint4 *>(p);
                 if constexpr (kTrack)
                     key = max(key, key_max8(a));
-                *reinterpret_cast<uint2 *>(o) = quantize8(a, s);
+                *reinterpret_cast<uint2 *>(o) = div.codes8(a);
             } else {
                 for (int64_t e = 0; e < k - j; ++e) {
                     if constexpr (kTrack)
