@@ -4,7 +4,7 @@
 // E4M3_RNE_SAT(fl32(x / s)).
 //
 // A correctly rounded fp32 division costs about ten vector instructions, and
-// in the activation and weight casts that work, not the memory traffic, set
+// in the per-tensor activation cast that work, not the memory traffic, set
 // the time.  With r = fl32(1 / s) computed once, t = fl32(x * r) is within
 // 1.5 * 2^-23 * |x / s| of x / s, so within 2^-22 * |t| of fl32(x / s) (both
 // normal).  E4M3 rounding (with the saturating clamp) is a monotone step

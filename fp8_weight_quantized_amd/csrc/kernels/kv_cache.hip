@@ -16,7 +16,6 @@
 // grid-strided index; blockIdx.y selects K (0) or V (1).  HBM-bound: 2 B in
 // and 1 B out per value, plus a second read of the batch when calibrating.
 #include "device_common.hpp"
-#include "e4m3_div.hpp"
 #include "launch.hpp"
 
 namespace fp8q {
@@ -89,7 +88,6 @@ __global__ __launch_bounds__(kThreads) void k_kv_cast(KvArgs a)
     }
     float s = r / kE4M3Max;
     s = s < kScaleFloor ? kScaleFloor : s;
-    const E4M3Div div(s);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if constexpr (CAL)
             a.running[which] = r;
@@ -114,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void k_kv_cast(KvArgs a)
             continue;
         }
         *reinterpret_cast<uint2 *>(cache + ((int64_t)h * a.slots + row) * a.head_dim + j * 8) =
-            div.codes8(v);
+            quantize8(v, s);
     }
     if (a.flags != nullptr) {
         if (local != 0)

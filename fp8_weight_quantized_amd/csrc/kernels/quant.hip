@@ -74,18 +74,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight(
             *flag = 1;
     }
 
-    const E4M3Div div(s);
     if constexpr (CH > 0) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int64_t idx = tid + (int64_t)c * kThreads;
             if (idx < nfull)
-                *reinterpret_cast<uint2 *>(qr + idx * 8) = div.codes8(buf[c]);
+                *reinterpret_cast<uint2 *>(qr + idx * 8) = quantize8(buf[c], s);
         }
     } else {
         for (int64_t idx = tid; idx < nfull; idx += kThreads) {
             uint4 v = *reinterpret_cast<const uint4 *>(wr + idx * 8);
-            *reinterpret_cast<uint2 *>(qr + idx * 8) = div.codes8(v);
+            *reinterpret_cast<uint2 *>(qr + idx * 8) = quantize8(v, s);
         }
     }
     if (tid < tail) {
