@@ -294,3 +294,37 @@ def test_w8a8_gemm_grouped_full_mlp_prefill_sampled(fq, orc):
     ref = orc.linear_grouped(1, xqr, qr, sr, 128, x_scale=xsr, rows=rows)
     got = host_bf16_as_f64(y[torch.from_numpy(rows).cuda()])
     assert_gemm_close(got, ref, "grouped mlp prefill sampled rows")
+
+
+@pytest.mark.parametrize("mode,m,n,k,group", [(1, 300, 300, 512, 128), (1, 257, 9, 256, 256),
+                                              (0, 12, 300, 4096, 128)])
+def test_grouped_output_stride_guard(fq, orc, mode, m, n, k, group):
+    """Grouped linear written into a wider, sentinel-filled buffer: nothing
+    past column n or row m changes, and the [m, n] block is in tolerance."""
+    from fp8_weight_quantized_amd import _lib
+    L = _lib.lib()
+    w = workloads.heavy_tail_weight(n, k, 4100 + m)
+    wq, ws, _ = orc.quantize_weight_grouped(w, group)
+    x, xs = make_x(mode, m, k, 4200 + m, orc)
+    xd = dev_x(mode, x)
+    wd = dev_u8(padded(wq, 16))[:, :k]
+    wsd = torch.from_numpy(ws).cuda()
+    xsd = None if xs is None else torch.tensor([xs], dtype=torch.float32, device="cuda")
+    ld_y = (n + 7) // 8 * 8 + 24
+    sentinel = 0x7FC1
+    ybuf = torch.full((m + 3, ld_y), sentinel, dtype=torch.int16, device="cuda")
+    need = L.fp8q_linear_grouped_workspace_size(mode, m, n, k, group)
+    wk = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    say("grouped output stride guard", mode, m, n, k, group)
+    st = L.fp8q_linear_grouped(mode, xd.data_ptr(), m, k, xd.stride(0),
+                               xsd.data_ptr() if xsd is not None else None, wd.data_ptr(), n,
+                               wd.stride(0), wsd.data_ptr(), group, ybuf.data_ptr(), ld_y,
+                               wk.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, _lib.last_error()
+    torch.cuda.synchronize()
+    yb = ybuf.cpu().numpy()
+    assert (yb[:m, n:] == sentinel).all(), "wrote past column n"
+    assert (yb[m:, :] == sentinel).all(), "wrote past row m"
+    got = ybuf[:m, :n].view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
+    ref = orc.linear_grouped(mode, x, wq, ws, group, x_scale=xs)
+    assert_gemm_close(got, ref, f"grouped stride guard mode {mode} {m}x{n}x{k} g={group}")
