@@ -209,6 +209,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
 {
     __shared__ __align__(16) uint8_t lds[kLdsBytes];
     __shared__ __align__(16) float gsc[GS ? 4 * BN : 4];
+    // per-row scales: xs * w_scale[n] of the tile's 256 weight rows, fetched
+    // into LDS before the main loop hides the load; read by the epilogue
+    __shared__ __align__(16) float wsl[GS ? 4 : BN];
 
     // ---- tile order: XCD bands, then groups of kGroupM tile-rows ----------
     const int nblocks = tiles_m * tiles_n;
@@ -343,6 +346,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     for (int st = 0; st < kStages - 1; ++st)
         if (st < nfull)
             issue_full(st);
+    // (its LDS write is visible after the first barrier of the loop; with K
+    // under one stage, after the tail stage's barrier)
+    if constexpr (!GS) {
+        if (tid < BN)
+            wsl[tid] = *x_scale * w_scale[min(n0 + tid, n - 1)];
+    }
 
     for (int64_t ks = 0; ks < nfull; ++ks) {
         // This wave's loads for stage ks have landed once no more than the
@@ -395,11 +404,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     // grouped: the last group's scales (every group's LDS write preceded a
     // barrier that every wave has passed)
     const float *slast = gsc + (GS ? ((int)(last_stage / (gstages > 0 ? gstages : 1)) & 3) * BN : 0);
+    // xs * w_scale of output column nb + v
     auto wsc = [&](int64_t nb, int v) {
         if constexpr (GS)
-            return slast[nb - n0 + v];
+            return xs * slast[nb - n0 + v];
         else
-            return w_scale[min(nb + v, n - 1)];
+            return wsl[nb - n0 + v];
     };
     constexpr int kRowBytes = BN * 2;             // one staged output row (512 bytes)
     constexpr int kRowChunks = kRowBytes / 16;    // 32
@@ -420,8 +430,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
                 const int64_t nb = n0 + nl;
                 const v16f &a = acc[i][j];
                 uint2 o;
-                o.x = pack_bf16x2(a[4 * q + 0] * (xs * wsc(nb, 0)), a[4 * q + 1] * (xs * wsc(nb, 1)));
-                o.y = pack_bf16x2(a[4 * q + 2] * (xs * wsc(nb, 2)), a[4 * q + 3] * (xs * wsc(nb, 3)));
+                o.x = pack_bf16x2(a[4 * q + 0] * wsc(nb, 0), a[4 * q + 1] * wsc(nb, 1));
+                o.y = pack_bf16x2(a[4 * q + 2] * wsc(nb, 2), a[4 * q + 3] * wsc(nb, 3));
                 *reinterpret_cast<uint2 *>(lds + out_off(r, nl / 8) + (nl & 4) * 2) = o;
             }
         }
