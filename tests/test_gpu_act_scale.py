@@ -76,11 +76,15 @@ def test_static_layouts(fq, orc):
 
 
 def test_static_every_bf16_numerator(fq, orc):
-    """Every finite bf16 value, cast with held scales that clip most of them."""
+    """Every finite bf16 value, cast with held scales that clip most of them.
+    Scales 1 and 2^-20 put quotients exactly on E4M3 midpoints (the cast's
+    exact-division fallback); 1e38, 3e38 and 2^-126 have a reciprocal outside
+    the range where the reciprocal product is used, so every element takes
+    the exact division."""
     allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     finite = allbits[(allbits & 0x7F80) != 0x7F80]
     x = finite.reshape(-1, 8)
-    for s in (1.0, 3.7e-3, 2.0 ** -20, 1.234e5, 1e-12, 7.1e30):
+    for s in (1.0, 3.7e-3, 2.0 ** -20, 1.234e5, 1e-12, 7.1e30, 1e38, 3e38, 2.0 ** -126):
         check_static(fq, orc, x, np.float32(s), f"all bf16, scale {s!r}")
 
 
