@@ -233,6 +233,11 @@ def main() -> int:
         "step_spread": step_spread,
         "roofline": roofline_decode(per_m, N, K),
     }
+    # secondary denominator: what a plain device copy reaches on this GPU
+    copy_gbs = measured_copy_gbs(torch, dev)
+    result["roofline"]["measured_copy_GBps"] = round(copy_gbs, 1)
+    result["roofline"]["frac_of_measured_copy"] = round(result["roofline"]["achieved"] / copy_gbs, 4)
+    log("device copy", round(copy_gbs, 1), "GB/s (read + write)")
 
     # --------------------------------------------------------------- other rows
     if not args.quick:
@@ -406,6 +411,27 @@ def measured_traffic(m: int):
         return None
     val = fields.get(f"traffic_bytes_per_launch_m{m}")
     return float(val) if val else None
+
+
+def measured_copy_gbs(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Read + write bandwidth of a plain 1 GiB device-to-device copy (torch),
+    after a warm-up: a measured ceiling for streaming kernels, reported beside
+    the published 8 TB/s."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    e.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
 def roofline_decode(per_m: dict, n: int, k: int) -> dict:
