@@ -13,6 +13,7 @@ computation runs in the library's HIP kernels; there is no CPU path.
     kv_scale = kv_cache_write(k, v, slot, k_cache, v_cache, running, calibrate)
     y = linear(x_bf16, wq, w_scale)                   # fp8_w_bf16_a (decode)
     y = linear(xq, wq, w_scale, x_scale=x_scale)      # fp8_w_fp8_a  (prefill)
+    y, x_scale = linear_w8a8_dynamic(x_bf16, wq, w_scale)  # fp8_w_fp8_a, X quantized inside
 
 Codes are returned as uint8 tensors holding raw e4m3fn bit patterns (view
 them with .view(torch.float8_e4m3fn)).  Code matrices are allocated with a
@@ -29,7 +30,8 @@ from ._lib import FP8Q_W8A8, FP8Q_W8A16, FP8Q_W8A16_F16, Fp8qError, check
 
 __all__ = [
     "quantize_weight", "quantize_weight_grouped", "quantize_act", "quantize_act_static", "quantize_act_ema",
-    "EmaActScale", "kv_cache_write", "linear", "cast_f32_to_e4m3", "describe_linear",
+    "EmaActScale", "kv_cache_write", "linear", "linear_w8a8_dynamic", "cast_f32_to_e4m3",
+    "describe_linear",
     "FP8Q_W8A16", "FP8Q_W8A8", "Fp8qError", "library_path",
 ]
 
@@ -286,6 +288,38 @@ def linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
                                     _ptr(w_scale), group, _ptr(out), ldy, _ptr(ws), nws,
                                     _stream(dev)))
     return out
+
+
+def linear_w8a8_dynamic(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                        out: torch.Tensor | None = None,
+                        nonfinite_flag: torch.Tensor | None = None):
+    """fp8_w_fp8_a on bf16 activations quantized per tensor inside the call.
+
+    Equals quantize_act(x) followed by linear(xq, wq, w_scale, x_scale=...):
+    same codes and scale, same sums.  Returns (Y bf16 [M, N], x_scale float32 [1]).
+    """
+    wq = _codes(wq)
+    m, k, ldx = _matrix(x, "x", (torch.bfloat16,))
+    n, k2, ldw = _matrix(wq, "wq", (torch.uint8,))
+    if k2 != k:
+        raise ValueError(f"inner dimensions differ: x has K={k}, wq has K={k2}")
+    if w_scale.dtype != torch.float32 or w_scale.numel() != n or not w_scale.is_cuda \
+            or not w_scale.is_contiguous():
+        raise ValueError(f"w_scale must be a contiguous float32 GPU tensor with {n} elements")
+    dev = x.device
+    if out is None:
+        out = torch.empty((m, _round_up(max(n, 1), 8)), dtype=torch.bfloat16, device=dev)[:, :n]
+    om, on, ldy = _matrix(out, "out", (torch.bfloat16,))
+    if (om, on) != (m, n):
+        raise ValueError(f"out must be [{m}, {n}]")
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    L = _lib.lib()
+    nws = L.fp8q_linear_w8a8_dynamic_workspace_size(m, n, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    check(L.fp8q_linear_w8a8_dynamic(_ptr(x), m, k, ldx, _ptr(wq), n, ldw, _ptr(w_scale),
+                                     _ptr(out), ldy, _ptr(scale), _ptr(ws), nws,
+                                     _ptr(nonfinite_flag), _stream(dev)))
+    return out, scale
 
 
 def cast_f32_to_e4m3(x: torch.Tensor) -> torch.Tensor:

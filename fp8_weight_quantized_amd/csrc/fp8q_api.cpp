@@ -435,6 +435,13 @@ bool grouped_uses_gemm(fp8q_mode mode, int64_t m, int64_t group)
     return mode == FP8Q_W8A8 && m > kW8A8DecodeMaxM && group >= 128;
 }
 
+int act_type(fp8q_mode mode)
+{
+    return mode == FP8Q_W8A16       ? fp8q::launch::kW8A16ActBF16
+           : mode == FP8Q_W8A16_F16 ? fp8q::launch::kW8A16ActF16
+                                    : fp8q::launch::kW8A16ActF8;
+}
+
 // group == 0: one weight scale per output row; else per-group scales
 size_t linear_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t group)
 {
@@ -449,7 +456,7 @@ size_t linear_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t
     }
     if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16 ||
         (mode == FP8Q_W8A8 && m <= kW8A8DecodeMaxM))
-        return round_up(fp8q::launch::plan_w8a16(m, n, k).workspace, 256);
+        return round_up(fp8q::launch::plan_w8a16(m, n, k, act_type(mode)).workspace, 256);
     if (mode == FP8Q_W8A8)
         return round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
     return 0;
@@ -490,6 +497,17 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(FP8Q_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
                     workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+    const size_t ex = extent(m, k, ld_x, xelem), ew = extent(n, k, ld_w, 1),
+                 ey = extent(m, n, ld_y, 2);
+    const size_t es = (size_t)n * 4 * (group > 0 ? (size_t)((k + group - 1) / group) : 1);
+    if (overlap(y_bf16, ey, x, ex) || overlap(y_bf16, ey, w_fp8, ew) ||
+        overlap(y_bf16, ey, w_scale, es) ||
+        (x_scale != nullptr && overlap(y_bf16, ey, x_scale, 4)) ||
+        (need > 0 && (overlap(workspace, need, y_bf16, ey) || overlap(workspace, need, x, ex) ||
+                      overlap(workspace, need, w_fp8, ew) ||
+                      overlap(workspace, need, w_scale, es) ||
+                      (x_scale != nullptr && overlap(workspace, need, x_scale, 4)))))
+        return fail(FP8Q_ERR_INVALID_ARG, "the output or workspace overlaps an input");
     int dev = 0;
     FP8Q_TRY(prepare(stream, &dev));
     FP8Q_TRY(check_ptr(x, "x", dev, 16));
@@ -500,22 +518,10 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
         FP8Q_TRY(check_ptr(x_scale, "x_scale", dev, 4));
     if (need > 0)
         FP8Q_TRY(check_ptr(workspace, "workspace", dev, 16));
-    const size_t ex = extent(m, k, ld_x, xelem), ew = extent(n, k, ld_w, 1),
-                 ey = extent(m, n, ld_y, 2);
-    const size_t es = (size_t)n * 4 * (group > 0 ? (size_t)((k + group - 1) / group) : 1);
     if (group > 0)
         FP8Q_TRY(check_within_allocation(w_scale, es, "w_scale"));
-    if (overlap(y_bf16, ey, x, ex) || overlap(y_bf16, ey, w_fp8, ew) ||
-        overlap(y_bf16, ey, w_scale, es) ||
-        (x_scale != nullptr && overlap(y_bf16, ey, x_scale, 4)) ||
-        (need > 0 && (overlap(workspace, need, y_bf16, ey) || overlap(workspace, need, x, ex) ||
-                      overlap(workspace, need, w_fp8, ew) ||
-                      overlap(workspace, need, w_scale, es))))
-        return fail(FP8Q_ERR_INVALID_ARG, "the output or workspace overlaps an input");
 
-    const int act = mode == FP8Q_W8A16     ? fp8q::launch::kW8A16ActBF16
-                    : mode == FP8Q_W8A16_F16 ? fp8q::launch::kW8A16ActF16
-                                             : fp8q::launch::kW8A16ActF8;
+    const int act = act_type(mode);
     hipError_t e;
     if (group > 0 && grouped_uses_gemm(mode, m, group)) {
         const auto plan = fp8q::launch::plan_w8a8(m, n, k);
@@ -526,7 +532,7 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
         e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
                                 ld_y, workspace, stream);
     } else if (a16 || m <= kW8A8DecodeMaxM) {
-        const auto plan = fp8q::launch::plan_w8a16(m, n, k);
+        const auto plan = fp8q::launch::plan_w8a16(m, n, k, act);
         e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
                                 ld_y, workspace, stream);
     } else {
@@ -554,6 +560,115 @@ fp8q_status fp8q_linear(fp8q_mode mode,
 {
     return linear_impl(mode, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, 0, y_bf16, ld_y,
                        workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// Workspace of fp8q_linear_w8a8_dynamic: [0, 256) the scale slot (used when the
+// caller passes no x_scale_out), then the absmax pass's maxima, then either
+// the decode plan's partial tiles (m <= 64) or the E4M3 codes [m, ldq] of the
+// activations (m > 64).
+struct DynLayout {
+    size_t part_off, part_bytes, rest_off, total;
+    int64_t ldq;
+};
+
+DynLayout dyn_layout(int64_t m, int64_t n, int64_t k)
+{
+    DynLayout l{};
+    l.part_off = 256;
+    l.part_bytes = round_up((size_t)fp8q::launch::act_blocks(m, k) * sizeof(uint32_t), 256);
+    l.rest_off = l.part_off + l.part_bytes;
+    l.ldq = (k + 15) / 16 * 16;
+    size_t rest;
+    if (m <= kW8A8DecodeMaxM)
+        rest = round_up(fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActQ).workspace, 256);
+    else
+        rest = round_up((size_t)m * (size_t)l.ldq, 256) +
+               round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
+    l.total = l.rest_off + rest;
+    return l;
+}
+
+}  // namespace
+
+size_t fp8q_linear_w8a8_dynamic_workspace_size(int64_t m, int64_t n, int64_t k)
+{
+    if (m <= 0 || n <= 0 || k < 1)
+        return 0;
+    return dyn_layout(m, n, k).total;
+}
+
+fp8q_status fp8q_linear_w8a8_dynamic(const uint16_t *x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                                     const uint8_t *w_fp8, int64_t n, int64_t ld_w,
+                                     const float *w_scale, uint16_t *y_bf16, int64_t ld_y,
+                                     float *x_scale_out, void *workspace, size_t workspace_bytes,
+                                     int32_t *nonfinite_flag, hipStream_t stream)
+{
+    if (m < 0 || n < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "need m >= 0, n >= 0, k >= 1 (m=%lld, n=%lld, k=%lld)",
+                    (long long)m, (long long)n, (long long)k);
+    FP8Q_TRY(check_ld(ld_x, k, 8, "ld_x"));
+    FP8Q_TRY(check_ld(ld_w, k, 16, "ld_w"));
+    FP8Q_TRY(check_ld(ld_y, n, 8, "ld_y"));
+    if (!fp8q::launch::w8a8_supports_ld(ld_w) || !fp8q::launch::w8a8_supports_ld((k + 15) / 16 * 16))
+        return fail(FP8Q_ERR_INVALID_ARG, "ld_w and k must be below 2^23");
+    if (m == 0 || n == 0)
+        return ok();
+    const DynLayout lay = dyn_layout(m, n, k);
+    if (workspace == nullptr || workspace_bytes < lay.total)
+        return fail(FP8Q_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                    workspace == nullptr ? (size_t)0 : workspace_bytes, lay.total);
+    const size_t ex = extent(m, k, ld_x, 2), ew = extent(n, k, ld_w, 1), ey = extent(m, n, ld_y, 2),
+                 es = (size_t)n * 4;
+    const void *outs[4] = {y_bf16, workspace, x_scale_out, nonfinite_flag};
+    const size_t olen[4] = {ey, lay.total, x_scale_out ? (size_t)4 : 0, nonfinite_flag ? (size_t)4 : 0};
+    const void *ins[3] = {x_bf16, w_fp8, w_scale};
+    const size_t ilen[3] = {ex, ew, es};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 3; ++b)
+            if (overlap(outs[a], olen[a], ins[b], ilen[b]))
+                return fail(FP8Q_ERR_INVALID_ARG, "an output or the workspace overlaps an input");
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(outs[a], olen[a], outs[b], olen[b]))
+                return fail(FP8Q_ERR_INVALID_ARG,
+                            "y, workspace, x_scale_out and nonfinite_flag must not overlap");
+    }
+    int dev = 0;
+    FP8Q_TRY(prepare(stream, &dev));
+    FP8Q_TRY(check_ptr(x_bf16, "x_bf16", dev, 16));
+    FP8Q_TRY(check_ptr(w_fp8, "w_fp8", dev, 16));
+    FP8Q_TRY(check_ptr(w_scale, "w_scale", dev, 4));
+    FP8Q_TRY(check_ptr(y_bf16, "y_bf16", dev, 16));
+    FP8Q_TRY(check_ptr(workspace, "workspace", dev, 16));
+    if (x_scale_out != nullptr)
+        FP8Q_TRY(check_ptr(x_scale_out, "x_scale_out", dev, 4));
+    if (nonfinite_flag != nullptr)
+        FP8Q_TRY(check_ptr(nonfinite_flag, "nonfinite_flag", dev, 4));
+
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    float *scale = x_scale_out != nullptr ? x_scale_out : reinterpret_cast<float *>(ws);
+    uint32_t *part = reinterpret_cast<uint32_t *>(ws + lay.part_off);
+    void *rest = ws + lay.rest_off;
+    hipError_t e;
+    if (m <= kW8A8DecodeMaxM) {
+        e = fp8q::launch::act_amax(x_bf16, m, k, ld_x, part, stream);
+        if (e == hipSuccess)
+            e = fp8q::launch::w8a16_quant_act(
+                fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActQ), x_bf16, m, k, ld_x,
+                part, fp8q::launch::act_blocks(m, k), scale, nonfinite_flag, w_fp8, n, ld_w,
+                w_scale, y_bf16, ld_y, rest, stream);
+    } else {
+        uint8_t *codes = static_cast<uint8_t *>(rest);
+        e = fp8q::launch::quantize_act(x_bf16, m, k, ld_x, codes, lay.ldq, scale, part,
+                                       nonfinite_flag, stream);
+        if (e == hipSuccess)
+            e = fp8q::launch::w8a8(fp8q::launch::plan_w8a8(m, n, k), codes, m, k, lay.ldq, scale,
+                                   w_fp8, n, ld_w, w_scale, y_bf16, ld_y, stream);
+    }
+    if (e != hipSuccess)
+        return hip_fail(e, "dynamic W8A8 linear launch");
+    return ok();
 }
 
 size_t fp8q_linear_grouped_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
@@ -638,7 +753,11 @@ void describe_w8a16(const fp8q::launch::W8A16Plan &p, char *buf, size_t len)
     char spg[16] = "";
     if (p.group > 0)
         std::snprintf(spg, sizeof spg, ", %lld", (long long)(p.group / 64));
-    if (p.kind == fp8q::launch::W8A16Plan::kRows)
+    if (p.kind == fp8q::launch::W8A16Plan::kPanel)
+        std::snprintf(buf, len, "k_w8a16_panel<%d, %d, %d, %d, %d> grid=(%lld,%lld) block=%d splits=1",
+                      p.af, p.mb, p.steps, p.depth, p.waves, (long long)p.grid_n,
+                      (long long)p.grid_m, 64 * p.waves);
+    else if (p.kind == fp8q::launch::W8A16Plan::kRows)
         std::snprintf(buf, len,
                       "k_w8a16_rows<%d, %d, %d, %d%s> rows=%d grid=(%lld,%lld,%lld) block=%d "
                       "kchunk=%lld splits=%lld%s",
@@ -678,7 +797,7 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
     if (mode == FP8Q_W8A8 && m > kW8A8DecodeMaxM)
         describe_w8a8(m, n, k, false, buf, len);
     else
-        describe_w8a16(fp8q::launch::plan_w8a16(m, n, k), buf, len);
+        describe_w8a16(fp8q::launch::plan_w8a16(m, n, k, act_type(mode)), buf, len);
     return ok();
 }
 

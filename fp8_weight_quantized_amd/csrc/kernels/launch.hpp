@@ -19,6 +19,10 @@ hipError_t quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w
                            hipStream_t stream);
 
 int act_blocks(int64_t m, int64_t k);
+// The absmax pass alone: act_blocks(m, k) maxima |x| (as bf16 magnitude keys)
+// into partial.
+hipError_t act_amax(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x, uint32_t *partial,
+                    hipStream_t stream);
 hipError_t quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
                         uint8_t *q, int64_t ld_q, float *x_scale, uint32_t *partial,
                         int32_t *flag, hipStream_t stream);
@@ -55,7 +59,7 @@ hipError_t kv_cache_write(const uint16_t *k, const uint16_t *v, int64_t tokens, 
 
 // ---- W8A16 (fp8_w_bf16_a) skinny GEMM --------------------------------------
 struct W8A16Plan {
-    enum Kind { kRows = 0, kTile = 1 };
+    enum Kind { kRows = 0, kTile = 1, kPanel = 2 };
     int kind;
     int mb;            // 16-row activation groups per workgroup (1..4)
     int64_t grid_m;    // workgroups along M (16 * mb activation rows each)
@@ -66,7 +70,7 @@ struct W8A16Plan {
     int waves;         // waves per workgroup; they split K
     int depth;         // 64-k steps of loads in flight per wave
     int64_t kchunk;    // K range per wave
-    // k_w8a16_tile
+    // k_w8a16_tile (and k_w8a16_panel: steps, and depth = chunks in flight)
     int xd;            // activation rows each of the 4 waves stages per chunk
     int steps;         // 64-k steps per staged chunk
     int64_t tiles_n;   // tiles of 64 weight rows
@@ -77,18 +81,32 @@ struct W8A16Plan {
     size_t workspace;  // scratch bytes: the partial tiles [splits][m][ldp] (0 if no split)
     int64_t group;     // 0: one weight scale per row; else k per weight-scale group
 };
-W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k);
+// act: the activation type (kW8A16Act* below); E4M3 codes cannot take the
+// panel kernel, which stages 16-bit rows.
+W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act = 0);
 // Per-group weight scales (w_scale [n, ceil(k / group)]); group is 64, 128,
 // 256 or 512.  The tile kernel serves every activation type and M.
 W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group);
 // act: the activation type -- 0 bf16 (fp8_w_bf16_a, bf16 out), 1 fp16
 // (fp8_w_fp16_a, fp16 out), 2 E4M3 codes with *x_scale (fp8_w_fp8_a at decode
 // sizes, bf16 out).  ld_x counts activation values.
-constexpr int kW8A16ActBF16 = 0, kW8A16ActF16 = 1, kW8A16ActF8 = 2;
+// 3: bf16 activations quantized per tensor on the fly (fp8_w_fp8_a with the
+// dynamic activation quantization folded in): see w8a16_quant_act.
+constexpr int kW8A16ActBF16 = 0, kW8A16ActF16 = 1, kW8A16ActF8 = 2, kW8A16ActQ = 3;
 hipError_t w8a16(const W8A16Plan &p, int act, const void *x, int64_t m, int64_t k, int64_t ld_x,
                  const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
                  const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
                  hipStream_t stream);
+// fp8_w_fp8_a on bf16 activations, quantized per tensor inside the GEMM: the
+// plan is plan_w8a16(m, n, k, kW8A16ActQ); act_part holds the npart maxima of
+// act_amax over x.  The scale used goes to *x_scale_out (always written;
+// the K-split reduction reads it back), a non-finite maximum raises *flag.
+// workspace: the plan's partial tiles.
+hipError_t w8a16_quant_act(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k,
+                           int64_t ld_x, const uint32_t *act_part, int npart, float *x_scale_out,
+                           int32_t *flag, const uint8_t *w, int64_t n, int64_t ld_w,
+                           const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
+                           hipStream_t stream);
 
 // ---- W8A8 (fp8_w_fp8_a) GEMM on FP8 MFMA -----------------------------------
 struct W8A8Plan {

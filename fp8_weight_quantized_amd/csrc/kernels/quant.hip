@@ -564,6 +564,17 @@ static int act_layout(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x, con
     return !rows_ok ? kScalar : (ld_x == k && ld_q == k && k % 8 == 0) ? kFlat : kRows;
 }
 
+hipError_t act_amax(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x, uint32_t *partial,
+                    hipStream_t stream)
+{
+    const int g = act_blocks(m, k);
+    const bool rows_ok = aligned(x, 16) && ld_x % 8 == 0;
+    const int layout = !rows_ok ? kScalar : (ld_x == k && k % 8 == 0) ? kFlat : kRows;
+    hipLaunchKernelGGL(k_act_amax, dim3(g), dim3(kThreads), 0, stream, x, m, k, ld_x, partial,
+                       layout);
+    return hipGetLastError();
+}
+
 // Dynamic per-tensor quantization: the absmax pass, then the cast that folds
 // its partial maxima.  seed_out (optional) receives a copy of the scale.
 static hipError_t quantize_act_dynamic(const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,

@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "device_common.hpp"
+#include "e4m3_div.hpp"
 #include "launch.hpp"
 
 namespace fp8q {
@@ -102,7 +103,9 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 // conversion of an fp32 output to the same 16-bit type.
 // kActF8: E4M3 activations (fp8_w_fp8_a at decode sizes), widened exactly to
 // bf16 and multiplied in bf16, bf16 output.
-enum { kActBF16 = 0, kActF16 = 1, kActF8 = 2 };
+// kActQ: bf16 activations quantized per tensor as they are loaded (see
+// QuantArgs below), then widened back to bf16 exactly for the MFMA.
+enum { kActBF16 = 0, kActF16 = 1, kActF8 = 2, kActQ = 3 };
 template <int AT> struct Act;
 
 template <> struct Act<kActBF16> {
@@ -143,7 +146,63 @@ template <> struct Act<kActF16> {
 };
 
 // The MFMA and output type used for an activation type.
-template <int AT> constexpr int compute_type() { return AT == kActF8 ? kActBF16 : AT; }
+template <int AT> constexpr int compute_type() { return AT == kActF8 || AT == kActQ ? kActBF16 : AT; }
+
+// fp8_w_fp8_a with the dynamic per-tensor activation quantization folded into
+// the GEMM (the deployment guide, "FP8量化与长上下文实测", §1.2 per-tensor
+// activations and §3.1 scale formula).  An absmax pass over X left one
+// maximum |x| key per block in part[0, npart).  Every workgroup folds them
+// into s = max(fl32(amax / 448), 1e-12f), casts each activation it loads to
+// E4M3 with E4M3Div (bit for bit the codes the per-tensor quantizer writes),
+// and widens the codes back to bf16, which is exact; the epilogue multiplies
+// by s * w_scale[n].  Workgroup (0, 0, 0) stores s to scale_out (read back by
+// the K-split reduction) and raises *flag on a non-finite maximum.
+struct QuantArgs {
+    const uint32_t *part;
+    int npart;
+    float *scale_out;
+    int32_t *flag;       // may be null
+};
+
+// Fold the absmax pass's maxima into the scale.  Contains __syncthreads: every
+// thread of the workgroup calls it, at the start of the kernel.
+__device__ __forceinline__ float fold_act_scale(const QuantArgs &qa)
+{
+    __shared__ uint32_t red[16];
+    uint32_t key = 0;
+    for (int j = threadIdx.x; j < qa.npart; j += blockDim.x)
+        key = max(key, qa.part[j]);
+    key = block_max_u32(key, red);
+    const float s = scale_from_key(key);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+        *qa.scale_out = s;
+        if (qa.flag != nullptr && key >= 0x7F80u)
+            *qa.flag = 1;
+    }
+    return s;
+}
+
+// The scale the epilogue applies for activation type AT: 1 for 16-bit
+// activations, *x_scale for E4M3 codes, the folded per-tensor scale for kActQ.
+template <int AT>
+__device__ __forceinline__ float act_scale(const float *x_scale, const QuantArgs &qa)
+{
+    if constexpr (AT == kActF8)
+        return *x_scale;
+    else if constexpr (AT == kActQ)
+        return fold_act_scale(qa);
+    else
+        return 1.0f;
+}
+
+// Eight bf16 activations -> their E4M3 codes under div -> the codes' values
+// as eight bf16 (exact), in the same order.
+__device__ __forceinline__ v4u qdq8(v4u v, const E4M3Div &div)
+{
+    const uint2 c = div.codes8(uint4{v.x, v.y, v.z, v.w});
+    const uint2 lo = e4m3x4_to_bf16(c.x), hi = e4m3x4_to_bf16(c.y);
+    return v4u{lo.x, lo.y, hi.x, hi.y};
+}
 
 // Widen a lane's 16 weight codes into the A operands of two MFMA k-steps.
 template <int AT>
@@ -166,7 +225,7 @@ __device__ __forceinline__ void widen(v4u wv, typename Act<AT>::frag &a0, typena
 // column) instead of 4 weight rows of one activation row.
 template <int AF, int MB, int AT, bool SWAP = false>
 __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[MB][2],
-                                          v4f (&acc)[AF][MB])
+                                          v4f (&acc)[AF][MB], const E4M3Div &div)
 {
     constexpr int CT = compute_type<AT>();
     typename Act<CT>::frag b[MB][2];
@@ -174,6 +233,9 @@ __device__ __forceinline__ void step_mfma(const v4u (&wv)[AF], const v4u (&xv)[M
     for (int j = 0; j < MB; ++j) {
         if constexpr (AT == kActF8) {
             widen<CT>(xv[j][0], b[j][0], b[j][1]);
+        } else if constexpr (AT == kActQ) {
+            b[j][0] = Act<CT>::cast(qdq8(xv[j][0], div));
+            b[j][1] = Act<CT>::cast(qdq8(xv[j][1], div));
         } else {
             b[j][0] = Act<CT>::cast(xv[j][0]);
             b[j][1] = Act<CT>::cast(xv[j][1]);
@@ -220,7 +282,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
     int rows, int64_t kchunk, int64_t kper, float *__restrict__ partial, int64_t ldp,
-    int64_t ngroups = 0)
+    int64_t ngroups, QuantArgs qa)
 {
     constexpr bool GS = SPG > 0;
     constexpr int SPGD = GS ? SPG : 1;         // SPG as a divisor
@@ -262,7 +324,8 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
         const int64_t xr = m0 + 16 * j + r;
         xp[j] = static_cast<const uint8_t *>(xv) + ((xr < m ? xr : m0) * ld_x + 16 * g) * ES;
     }
-    const float xs = F8 ? *x_scale : 1.0f;
+    const float xs = act_scale<AT>(x_scale, qa);
+    const E4M3Div div(AT == kActQ ? xs : 1.0f);
 
     v4f acc[2][AF][MB];
 #pragma unroll
@@ -335,7 +398,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
                 // them only makes this wait for more)
                 wait_vmcnt<(P - 1) * L>();
                 __builtin_amdgcn_sched_barrier(0);
-                step_mfma<AF, MB, AT, GS>(wb[u], xb[u], acc[u & 1]);
+                step_mfma<AF, MB, AT, GS>(wb[u], xb[u], acc[u & 1], div);
                 issue(u, kk + 64 * (P + u));
                 if constexpr (GS && (u + 1) % SPGD == 0) {
                     fold(sc[u / SPGD]);
@@ -349,7 +412,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
             constexpr int u = decltype(uc)::value;
             wait_vmcnt<(P - 1 - u) * L>();
             __builtin_amdgcn_sched_barrier(0);
-            step_mfma<AF, MB, AT, GS>(wb[u], xb[u], acc[u & 1]);
+            step_mfma<AF, MB, AT, GS>(wb[u], xb[u], acc[u & 1], div);
             if constexpr (GS && (u + 1) % SPGD == 0)
                 fold(sc[u / SPGD]);
         });
@@ -396,7 +459,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
                 }
             }
         }
-        step_mfma<AF, MB, AT, GS>(wv, xv, acc[0]);
+        step_mfma<AF, MB, AT, GS>(wv, xv, acc[0], div);
         if constexpr (GS) {
             if ((kk + 64 - kb) % GK == 0 || kk + 64 >= ke)
                 fold(s_tail);
@@ -533,12 +596,13 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
     const float *__restrict__ x_scale,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
-    int64_t kper, int splits, float *__restrict__ partial, int64_t ldp, int64_t ngroups)
+    int64_t kper, int splits, float *__restrict__ partial, int64_t ldp, int64_t ngroups,
+    QuantArgs qa)
 {
     constexpr bool GS = SPG > 0;
     constexpr int GK = 64 * (GS ? SPG : 1);    // k per scale group
     constexpr int SPGD = GS ? SPG : 1;         // SPG as a divisor
-    constexpr int SC = GS ? T / SPG : 0;       // scale groups per chunk
+    constexpr int SC = GS ? T / SPGD : 0;      // scale groups per chunk
     // a chunk's scales are adjacent floats, which the compiler may merge into
     // fewer load instructions: the waits below count them as at least one
     // (a smaller count only waits for more)
@@ -558,7 +622,8 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
     // exactly, between their load and the LDS write)
     typedef typename std::conditional<F8, uint2, v4u>::type XReg;
     const uint8_t *x8 = static_cast<const uint8_t *>(xv);
-    const float xs = F8 ? *x_scale : 1.0f;
+    const float xs = act_scale<AT>(x_scale, qa);
+    const E4M3Div div(AT == kActQ ? xs : 1.0f);
     __shared__ __attribute__((aligned(16))) uint8_t xlds[2 * XR * RB];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -638,6 +703,8 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
                     if constexpr (F8) {
                         const uint2 lo = Act<CT>::widen4(xr[i][h].x), hi = Act<CT>::widen4(xr[i][h].y);
                         v = v4u{lo.x, lo.y, hi.x, hi.y};
+                    } else if constexpr (AT == kActQ) {
+                        v = qdq8(xr[i][h], div);
                     } else {
                         v = xr[i][h];
                     }
@@ -764,7 +831,7 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 #pragma unroll
         for (int j = 0; j < MB; ++j)
             acc1[0][j] = acc[0][j];
-        step_mfma<1, MB, AT, GS>(wv1, xv, acc1);
+        step_mfma<1, MB, AT, GS>(wv1, xv, acc1, div);
 #pragma unroll
         for (int j = 0; j < MB; ++j)
             acc[0][j] = acc1[0][j];
@@ -810,6 +877,192 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
     }
 }
 
+// ---------------------------------------------------------------------------
+// k_w8a16_panel
+// ---------------------------------------------------------------------------
+//
+// One workgroup per output panel of 16*AF weight rows x 16*MB activation rows
+// over the whole K range, so no partial sums leave the workgroup and a call
+// is a single launch.  The NWV waves take 1/NWV of K each; their fp32 panels
+// are added through LDS in wave order at the end.
+//
+// The activation panel is re-read by every workgroup of its column of
+// panels, from L2.  Loaded in the MFMA operand layout (16 rows x 32 bytes per
+// load instruction) those reads run at about half the rate of plain
+// coalesced loads, so here every load instruction reads 1 KB of whole
+// 512-byte row segments, D chunks ahead, into registers.  Each wave then
+// writes its chunk into its own LDS slot and reads it back in the B layout;
+// the 16-byte units of a staged row are XOR-swizzled by the row's low 4 bits,
+// so both the row-wise writes and the 16-row operand reads are free of bank
+// conflicts.  Weights stream straight into registers (non-temporal), one
+// 16-byte load per lane per fragment and 64-k step, as in the other kernels.
+//
+// CS: 64-k steps per chunk.  D: chunks in flight per wave.  The host plans
+// this kernel only for K a multiple of NWV * 64 * CS with at least D chunks
+// per wave.  Rows past N or M are clamped to a valid row when loading and their
+// outputs are never stored.
+template <int AF, int MB, int CS, int D, int NWV, int AT>
+__global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
+    const void *__restrict__ xv, int64_t m, int64_t k, int64_t ld_x,
+    const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
+    const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y, QuantArgs qa)
+{
+    static_assert(AT == kActBF16 || AT == kActF16 || AT == kActQ, "16-bit activations in memory");
+    constexpr int CT = compute_type<AT>();
+    constexpr int XR = 16 * MB;                 // activation rows of the panel
+    constexpr int CK = 64 * CS;                 // k per chunk
+    constexpr int RU = CK * 2 / 16;             // 16-byte units of a staged row segment
+    constexpr int RB = 16 * RU;                 // bytes of a staged row segment
+    constexpr int NI = XR * RU / kWave;         // activation loads per lane per chunk
+    constexpr int LC = NI + CS * AF;            // loads per lane per chunk
+    static_assert(RU % 16 == 0 && (XR * RU) % kWave == 0, "chunk shape");
+    static_assert(D >= 1 && D <= 4, "chunks in flight");
+    __shared__ __attribute__((aligned(16))) uint8_t xl[NWV][XR * RB];
+    static_assert(sizeof(v4f) * NWV * AF * MB * kWave <= sizeof(xl), "reduction fits the slots");
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int r = lane & 15;          // row of the A (weight) / B (activation) operand
+    const int g = lane >> 4;          // which 16 k-values of a 64-k step this lane holds
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * AF;
+    const int64_t m0 = (int64_t)blockIdx.y * XR;
+    const int64_t kq = k / NWV;
+    const int64_t kb = (int64_t)wave * kq;
+    const int nch = (int)(kq / CK);
+    uint8_t *slot = xl[wave];
+    const float xs = act_scale<AT>(nullptr, qa);
+    const E4M3Div div(AT == kActQ ? xs : 1.0f);
+
+    const uint8_t *wp[AF];
+#pragma unroll
+    for (int a = 0; a < AF; ++a)
+        wp[a] = w + min(n0 + 16 * a + r, n - 1) * ld_w + kb + 16 * g;
+    // activation load i of a chunk: unit f = 64 i + lane of the chunk's
+    // XR x RU units, i.e. row f / RU, 16-byte unit f % RU of that row
+    const uint8_t *x8 = static_cast<const uint8_t *>(xv);
+    const uint8_t *xp[NI];
+    int xo[NI];                       // LDS byte offset of that unit, swizzled
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int f = kWave * i + lane;
+        const int rho = f / RU, u = f % RU;
+        xp[i] = x8 + (min(m0 + rho, m - 1) * ld_x + kb) * 2 + 16 * u;
+        xo[i] = rho * RB + 16 * (u ^ (rho & 15));
+    }
+
+    v4u xr[D][NI];
+    v4u wr[D][CS][AF];
+    v4f acc[AF][MB];
+#pragma unroll
+    for (int a = 0; a < AF; ++a)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+            acc[a][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    auto issue_x = [&](int u, int c) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            xr[u][i] = ldg(xp[i] + (int64_t)c * CK * 2);
+    };
+    auto issue_w = [&](int u, int c) {
+#pragma unroll
+        for (int s = 0; s < CS; ++s)
+#pragma unroll
+            for (int a = 0; a < AF; ++a)
+                wr[u][s][a] = ldg_nt(wp[a] + (int64_t)c * CK + 64 * s);
+    };
+    // the wait for chunk c: loads retire in order, and the chunks issued after
+    // it are min(D - 1, nch - 1 - c) whole chunks of LC loads each
+    auto wait_chunk = [&](int c) {
+        const int after = min(D - 1, nch - 1 - c);
+        static_for<0, D>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if (after == j)
+                wait_vmcnt<j * LC>();
+        });
+    };
+    auto compute = [&](int u) {
+#pragma unroll
+        for (int s = 0; s < CS; ++s) {
+            typename Act<CT>::frag a0[AF], a1[AF];
+#pragma unroll
+            for (int a = 0; a < AF; ++a)
+                widen<CT>(wr[u][s][a], a0[a], a1[a]);
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                const int rho = 16 * j + r;
+                const int u0 = 8 * s + 2 * g;
+                const v4u b0 = *reinterpret_cast<const v4u *>(slot + rho * RB + 16 * (u0 ^ (rho & 15)));
+                const v4u b1 = *reinterpret_cast<const v4u *>(slot + rho * RB + 16 * ((u0 + 1) ^ (rho & 15)));
+#pragma unroll
+                for (int a = 0; a < AF; ++a) {
+                    acc[a][j] = Act<CT>::mfma(a0[a], Act<CT>::cast(b0), acc[a][j]);
+                    acc[a][j] = Act<CT>::mfma(a1[a], Act<CT>::cast(b1), acc[a][j]);
+                }
+            }
+        }
+    };
+
+    // prologue: the first D chunks (nch >= D)
+    static_for<0, D>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        issue_x(u, u);
+        issue_w(u, u);
+    });
+    for (int c0 = 0; c0 < nch; c0 += D) {
+        static_for<0, D>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            const int c = c0 + u;
+            if (c < nch) {
+                wait_chunk(c);
+                __builtin_amdgcn_sched_barrier(0);
+                // this wave's slot: the previous chunk's reads were consumed
+                // by its MFMAs; LDS operations of one wave run in order
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    *reinterpret_cast<v4u *>(slot + xo[i]) =
+                        AT == kActQ ? qdq8(xr[u][i], div) : xr[u][i];
+                const bool more = c + D < nch;
+                if (more)
+                    issue_x(u, c + D);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(u);
+                __builtin_amdgcn_sched_barrier(0);
+                if (more)
+                    issue_w(u, c + D);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    }
+
+    // ---- the waves' panels, added in wave order, then scaled and stored ----
+    __syncthreads();
+    v4f *red = reinterpret_cast<v4f *>(&xl[0][0]);     // [wave][AF * MB][lane]
+#pragma unroll
+    for (int a = 0; a < AF; ++a)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+            red[(wave * AF * MB + a * MB + j) * kWave + lane] = acc[a][j];
+    __syncthreads();
+    // one thread per (fragment, lane) slot: weight rows 4g'..4g'+3 of
+    // fragment a, activation row 16j + r' (lane layout of the MFMA result)
+    for (int sl = threadIdx.x; sl < AF * MB * kWave; sl += blockDim.x) {
+        const int f = sl / kWave;
+        const int ln = sl % kWave;
+        const int a = f / MB;
+        const int j = f % MB;
+        const int64_t mr = m0 + 16 * j + (ln & 15);
+        const int64_t nb = n0 + 16 * a + 4 * (ln >> 4);
+        if (mr >= m || nb >= n)
+            continue;
+        v4f sum = red[f * kWave + ln];
+#pragma unroll
+        for (int wv = 1; wv < NWV; ++wv)
+            sum += red[(wv * AF * MB + f) * kWave + ln];
+        store_y4<CT>(y, ld_y, w_scale, xs, mr, nb, n, sum);
+    }
+}
+
 // Sum of the K splits' partial tiles in split order, scaled and stored as
 // bf16: one thread per 4 consecutive outputs of a row.  w_scale == nullptr:
 // the partials already carry the per-group weight scales.
@@ -820,7 +1073,7 @@ __global__ __launch_bounds__(256) void k_w8a16_reduce(
     int64_t ld_y)
 {
     constexpr int CT = compute_type<AT>();
-    const float xs = AT == kActF8 ? *x_scale : 1.0f;
+    const float xs = AT == kActF8 || AT == kActQ ? *x_scale : 1.0f;
     const int64_t q = ldp / 4;
     const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (slot >= m * q)
@@ -899,7 +1152,7 @@ static void plan_tile(W8A16Plan &p, int64_t m, int64_t k, int steps_mb1)
     p.grid_n = p.tiles_n * p.splits;
 }
 
-W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
+W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
 {
     W8A16Plan p{};
     const int64_t mgroups = div_up(m, 16);
@@ -908,6 +1161,32 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k)
     p.tiles_n = div_up(n, kTileN);
     p.splits = 1;
     p.workspace = 0;
+    p.ldp = div_up(n, 4) * 4;
+    // 17..64 activation rows with 16-bit activations in memory: one launch
+    // of k_w8a16_panel (panels of 32 activation rows x 16 weight rows, or
+    // x 32 above 32 activation rows, whole K per workgroup, no partial sums)
+    // where that makes about one workgroup per CU.  Measured on MI355X on the
+    // Llama-3-8B q_proj (N = K = 4096), in graphs: M = 32 9.9 us against
+    // 10.3 us for the split tile kernel + reduce, M = 64 11.9 us against
+    // 13.7 us.
+    if (act != kW8A16ActF8 && m > 16 && m <= 64 && k % 1024 == 0 && k >= 2048) {
+        const int af = m > 32 ? 2 : 1;
+        const int64_t gn = div_up(n, 16 * af), gm = div_up(m, 32);
+        if (gn * gm >= 192 && gn * gm <= 320) {
+            p.kind = W8A16Plan::kPanel;
+            p.af = af;
+            p.mb = 2;
+            p.rows = 16 * af;
+            p.waves = 4;
+            p.steps = 4;
+            p.depth = 2;
+            p.grid_n = gn;
+            p.grid_m = gm;
+            p.kper = k;
+            p.kchunk = k / 4;
+            return p;
+        }
+    }
     // The rows kernel wins for up to 16 activation rows on a weight of up to
     // 4096 rows with K < 16K; a wider weight takes the split tile kernel
     // below, a long K, a small N or more activation rows the tile kernel
@@ -1035,18 +1314,19 @@ template <int AF, int MB, int P, int NW, int AT, int SPG = 0>
 static void launch_rows(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
                         const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
                         const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
-                        hipStream_t stream)
+                        const QuantArgs &qa, hipStream_t stream)
 {
     float *partial = static_cast<float *>(workspace);
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m, (unsigned)p.splits);
     const int64_t ngroups = SPG > 0 ? div_up(k, 64 * SPG) : 0;
     hipLaunchKernelGGL((k_w8a16_rows<AF, MB, P, NW, AT, SPG>), grid, dim3(NW * kWave), 0, stream, x, m,
                        k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, p.rows, p.kchunk, p.kper,
-                       partial, p.ldp, ngroups);
+                       partial, p.ldp, ngroups, qa);
     if (p.splits > 1) {
         const int64_t slots = m * (p.ldp / 4);
         hipLaunchKernelGGL((k_w8a16_reduce<AT>), dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
-                           partial, m, n, p.ldp, (int)p.splits, x_scale,
+                           partial, m, n, p.ldp, (int)p.splits,
+                           AT == kActQ ? (const float *)qa.scale_out : x_scale,
                            SPG > 0 ? nullptr : w_scale, y, ld_y);
     }
 }
@@ -1055,43 +1335,90 @@ template <int MB, int XD, int T, int AT, int SPG = 0>
 static void launch_tile(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
                         const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
                         const float *w_scale, uint16_t *y, int64_t ld_y, float *partial,
-                        hipStream_t stream)
+                        const QuantArgs &qa, hipStream_t stream)
 {
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
     const int64_t ngroups = SPG > 0 ? div_up(k, 64 * SPG) : 0;
     hipLaunchKernelGGL((k_w8a16_tile<MB, XD, T, AT, SPG>), grid, dim3(kTileThreads), 0, stream, x,
                        m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, p.kper, (int)p.splits,
-                       partial, p.ldp, ngroups);
+                       partial, p.ldp, ngroups, qa);
     if (p.splits > 1) {
         const int64_t slots = m * (p.ldp / 4);
         hipLaunchKernelGGL((k_w8a16_reduce<AT>), dim3((unsigned)div_up(slots, 256)), dim3(256), 0, stream,
-                           partial, m, n, p.ldp, (int)p.splits, x_scale,
+                           partial, m, n, p.ldp, (int)p.splits,
+                           AT == kActQ ? (const float *)qa.scale_out : x_scale,
                            SPG > 0 ? nullptr : w_scale, y, ld_y);
     }
+}
+
+// k_w8a16_panel with 32 activation rows, 64-k x 4 chunks, 2 chunks in flight
+// and 4 waves (the measured best on the Llama-3-8B q_proj decode shapes).
+template <int AF, int AT>
+static void launch_panel(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
+                         const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
+                         uint16_t *y, int64_t ld_y, const QuantArgs &qa, hipStream_t stream)
+{
+    const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
+    hipLaunchKernelGGL((k_w8a16_panel<AF, 2, 4, 2, 4, AT>), grid, dim3(4 * kWave), 0, stream, x, m,
+                       k, ld_x, w, n, ld_w, w_scale, y, ld_y, qa);
 }
 
 template <int AT>
 static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t k,
                            int64_t ld_x, const float *x_scale, const uint8_t *w, int64_t n,
                            int64_t ld_w, const float *w_scale, uint16_t *y, int64_t ld_y,
-                           void *workspace, hipStream_t stream)
+                           void *workspace, const QuantArgs &qa, hipStream_t stream)
 {
     float *partial = static_cast<float *>(workspace);
-    if (p.group == 0 && p.kind == W8A16Plan::kRows) {
+    if (p.group == 0 && p.kind == W8A16Plan::kPanel) {
+        if constexpr (AT != kActF8) {
+            if (p.mb == 2 && p.steps == 4 && p.depth == 2 && p.waves == 4) {
+                if (p.af == 1) {
+                    launch_panel<1, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, qa, stream);
+                    return hipGetLastError();
+                }
+                if (p.af == 2) {
+                    launch_panel<2, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, qa, stream);
+                    return hipGetLastError();
+                }
+            }
+        }
+    } else if (p.group == 0 && p.kind == W8A16Plan::kRows) {
 #define FP8Q_ROWS_CASE(AF, MB, P, NW)                                                         \
         if (p.af == AF && p.mb == MB && p.depth == P && p.waves == NW) {                      \
             launch_rows<AF, MB, P, NW, AT>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y,    \
-                                           ld_y, workspace, stream);                      \
+                                           ld_y, workspace, qa, stream);                  \
             return hipGetLastError();                                                         \
         }
         FP8Q_ROWS_CASE(2, 1, 8, 4)
         FP8Q_ROWS_CASE(1, 1, 8, 4)
 #undef FP8Q_ROWS_CASE
-    } else if (p.group > 0 && p.kind == W8A16Plan::kRows) {
+    } else if (p.group == 0) {
+#define FP8Q_TILE_CASE(MB, XD, T)                                                             \
+        if (p.mb == MB && p.xd == XD && p.steps == T) {                                       \
+            launch_tile<MB, XD, T, AT>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,  \
+                                       partial, qa, stream);                                  \
+            return hipGetLastError();                                                         \
+        }
+        FP8Q_TILE_CASE(1, 1, 8)
+        FP8Q_TILE_CASE(1, 2, 8)
+        FP8Q_TILE_CASE(1, 3, 8)
+        FP8Q_TILE_CASE(1, 4, 8)
+        FP8Q_TILE_CASE(1, 1, 16)
+        FP8Q_TILE_CASE(1, 2, 16)
+        FP8Q_TILE_CASE(1, 3, 16)
+        FP8Q_TILE_CASE(1, 4, 16)
+        FP8Q_TILE_CASE(2, 8, 8)
+        FP8Q_TILE_CASE(3, 12, 8)
+        FP8Q_TILE_CASE(4, 16, 8)
+#undef FP8Q_TILE_CASE
+    } else if constexpr (AT != kActQ) {
+        // per-group weight scales (not with on-the-fly activation quantization)
+        if (p.kind == W8A16Plan::kRows) {
 #define FP8Q_GROUP_ROWS_CASE(AF, SPG)                                                         \
         if (p.af == AF && p.mb == 1 && p.depth == 8 && p.waves == 4 && p.group == 64 * SPG) {  \
             launch_rows<AF, 1, 8, 4, AT, SPG>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, \
-                                              ld_y, workspace, stream);                      \
+                                              ld_y, workspace, qa, stream);                  \
             return hipGetLastError();                                                         \
         }
         FP8Q_GROUP_ROWS_CASE(1, 1) FP8Q_GROUP_ROWS_CASE(1, 2)
@@ -1099,11 +1426,11 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
         FP8Q_GROUP_ROWS_CASE(2, 1) FP8Q_GROUP_ROWS_CASE(2, 2)
         FP8Q_GROUP_ROWS_CASE(2, 4) FP8Q_GROUP_ROWS_CASE(2, 8)
 #undef FP8Q_GROUP_ROWS_CASE
-    } else if (p.group > 0) {
+        } else {
 #define FP8Q_GROUP_CASE(MB, XD, T, SPG)                                                       \
         if (p.mb == MB && p.xd == XD && p.steps == T && p.group == 64 * SPG) {                \
             launch_tile<MB, XD, T, AT, SPG>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y,   \
-                                            ld_y, partial, stream);                           \
+                                            ld_y, partial, qa, stream);                       \
             return hipGetLastError();                                                         \
         }
 #define FP8Q_GROUP_SIZES(MB, XD, T)                                                           \
@@ -1122,25 +1449,7 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
         FP8Q_GROUP_SIZES(4, 16, 8)
 #undef FP8Q_GROUP_SIZES
 #undef FP8Q_GROUP_CASE
-    } else {
-#define FP8Q_TILE_CASE(MB, XD, T)                                                             \
-        if (p.mb == MB && p.xd == XD && p.steps == T) {                                       \
-            launch_tile<MB, XD, T, AT>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,  \
-                                       partial, stream);                                      \
-            return hipGetLastError();                                                         \
         }
-        FP8Q_TILE_CASE(1, 1, 8)
-        FP8Q_TILE_CASE(1, 2, 8)
-        FP8Q_TILE_CASE(1, 3, 8)
-        FP8Q_TILE_CASE(1, 4, 8)
-        FP8Q_TILE_CASE(1, 1, 16)
-        FP8Q_TILE_CASE(1, 2, 16)
-        FP8Q_TILE_CASE(1, 3, 16)
-        FP8Q_TILE_CASE(1, 4, 16)
-        FP8Q_TILE_CASE(2, 8, 8)
-        FP8Q_TILE_CASE(3, 12, 8)
-        FP8Q_TILE_CASE(4, 16, 8)
-#undef FP8Q_TILE_CASE
     }
     return hipErrorInvalidValue;
 }
@@ -1150,19 +1459,33 @@ hipError_t w8a16(const W8A16Plan &p, int act, const void *x, int64_t m, int64_t 
                  const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
                  hipStream_t stream)
 {
+    const QuantArgs none{nullptr, 0, nullptr, nullptr};
     switch (act) {
     case kActBF16:
         return dispatch<kActBF16>(p, x, m, k, ld_x, nullptr, w, n, ld_w, w_scale, y, ld_y,
-                                  workspace, stream);
+                                  workspace, none, stream);
     case kActF16:
         return dispatch<kActF16>(p, x, m, k, ld_x, nullptr, w, n, ld_w, w_scale, y, ld_y,
-                                 workspace, stream);
+                                 workspace, none, stream);
     case kActF8:
         return dispatch<kActF8>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,
-                                workspace, stream);
+                                workspace, none, stream);
     default:
         return hipErrorInvalidValue;
     }
+}
+
+hipError_t w8a16_quant_act(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k,
+                           int64_t ld_x, const uint32_t *act_part, int npart, float *x_scale_out,
+                           int32_t *flag, const uint8_t *w, int64_t n, int64_t ld_w,
+                           const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
+                           hipStream_t stream)
+{
+    if (p.group != 0)
+        return hipErrorInvalidValue;
+    const QuantArgs qa{act_part, npart, x_scale_out, flag};
+    return dispatch<kActQ>(p, x, m, k, ld_x, nullptr, w, n, ld_w, w_scale, y, ld_y, workspace, qa,
+                           stream);
 }
 
 }  // namespace launch

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 2
+#define FP8Q_ABI_VERSION 3
 
 typedef enum {
     FP8Q_OK = 0,
@@ -259,10 +259,10 @@ fp8q_status fp8q_kv_cache_write(const uint16_t *k_bf16, const uint16_t *v_bf16, 
  *           16-byte aligned; must not overlap any input
  *   workspace  device scratch of at least fp8q_linear_workspace_size(mode, m, n, k)
  *              bytes, 16-byte aligned (the size may be 0, then workspace may be
- *              NULL); needs no initialisation.  W8A16 uses it when it splits K
- *              across workgroups (N / 64 row tiles too few to fill the GPU): it
- *              then holds fp32 partial sums that a second kernel on `stream`
- *              adds up.
+ *              NULL); needs no initialisation.  The decode kernels use it when
+ *              they split K across workgroups (too few output tiles to fill
+ *              the GPU): it then holds fp32 partial sums that a second kernel
+ *              on `stream` adds up.
  * m == 0 or n == 0 is a no-op; k must be >= 1.  Deterministic: the same inputs
  * give the same bits on every call (K-split partial sums are added in split
  * order).
@@ -273,6 +273,37 @@ fp8q_status fp8q_linear(fp8q_mode mode,
                         const uint8_t *w_fp8, int64_t n, int64_t ld_w, const float *w_scale,
                         uint16_t *y_bf16, int64_t ld_y,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fp8_w_fp8_a (the write-up §3.1 step 3) on bf16 activations, with the dynamic
+ * per-tensor activation quantization of the deployment guide §1.2 (scale by the
+ * §3.1 formula) folded into the linear layer:
+ *   s_x = max(fl32(max_{m,k} |X[m,k]| / 448), 1e-12f)
+ *   Y[m,n] = bf16_RNE( s_x * w_scale[n] * sum_k dec(E4M3_RNE_SAT(fl32(X[m,k] / s_x))) * dec(W[n,k]) )
+ * i.e. fp8q_quantize_act followed by fp8q_linear(FP8Q_W8A8, ...): the codes and
+ * the scale are bit for bit those of fp8q_quantize_act, the sums are exact
+ * products accumulated in fp32 (tolerance and determinism as fp8q_linear).
+ * Up to 64 activation rows (decode) this is two kernels: the absmax pass, then
+ * the decode GEMM, whose workgroups fold the pass's maxima into s_x and cast
+ * the activations they load in registers, so the E4M3 activations never go
+ * through memory.  More rows run fp8q_quantize_act into the workspace and the
+ * FP8 MFMA GEMM (three kernels).
+ *
+ *   x_bf16       [m, k] bf16, ld_x >= k, ld_x % 8 == 0, 16-byte aligned
+ *   w_fp8, w_scale, y_bf16, ld_*   as fp8q_linear
+ *   x_scale_out  optional device fp32[1]: receives s_x
+ *   workspace    at least fp8q_linear_w8a8_dynamic_workspace_size(m, n, k) bytes,
+ *                16-byte aligned, no initialisation needed; it must not overlap
+ *                any other argument
+ *   nonfinite_flag  optional; set to 1 if any |x| is NaN or Inf
+ * m == 0 or n == 0 launches nothing (x_scale_out is then not written).
+ */
+size_t fp8q_linear_w8a8_dynamic_workspace_size(int64_t m, int64_t n, int64_t k);
+fp8q_status fp8q_linear_w8a8_dynamic(const uint16_t *x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                                     const uint8_t *w_fp8, int64_t n, int64_t ld_w,
+                                     const float *w_scale, uint16_t *y_bf16, int64_t ld_y,
+                                     float *x_scale_out, void *workspace, size_t workspace_bytes,
+                                     int32_t *nonfinite_flag, hipStream_t stream);
 
 /*
  * The linear layer with per-group weight scales (w_scale [n, ceil(k/group)]

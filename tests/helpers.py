@@ -65,3 +65,19 @@ def assert_gemm_close(y: np.ndarray, ref: np.ndarray, what: str = "") -> dict:
     assert e["rel_fro"] <= TOL_FRO, (what, e)
     assert e["max_abs"] <= TOL_MAX * e["max_ref"], (what, e)
     return e
+
+
+def rows_every_tile(m: int, seed: int, tile: int = 256, per_tile: int = 2,
+                    min_total: int = 64) -> np.ndarray:
+    """Seeded output rows to compare on a full-size GEMM: at least `per_tile`
+    rows in every band of `tile` rows (more per band when that is needed to
+    reach `min_total`), plus the first and last row.  With every column of
+    those rows compared, every tile x tile output tile is checked."""
+    bands = (m + tile - 1) // tile
+    per = max(per_tile, -(-min_total // bands))
+    rng = np.random.default_rng(seed)
+    picks = [0, m - 1]
+    for b in range(bands):
+        lo, hi = b * tile, min(m, (b + 1) * tile)
+        picks.extend(rng.choice(np.arange(lo, hi), size=min(per, hi - lo), replace=False).tolist())
+    return np.unique(np.asarray(picks, dtype=np.int64))

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.fp8q_abi_version() == 2
+    assert L.fp8q_abi_version() == 3
     for s in range(5):
         assert L.fp8q_status_string(s).startswith(b"FP8Q")
     assert L.fp8q_status_string(99) == b"FP8Q: unknown status"
@@ -66,10 +66,15 @@ def test_workspace_queries(L):
     assert L.fp8q_linear_workspace_size(0, 12, 28672, 4096) == 0
     # a small N on a short K: 64-row tiles, no split (K under two chunks)
     assert L.fp8q_linear_workspace_size(0, 4, 64, 500) == 0
+    # 17..64 rows with about one workgroup per CU: the panel kernel, whole K
+    # per workgroup, one launch, no scratch (bf16 and fp16 activations; E4M3
+    # codes keep the split tile kernel)
+    assert L.fp8q_linear_workspace_size(0, 64, 4096, 4096) == 0
+    assert L.fp8q_linear_workspace_size(2, 32, 4096, 4096) == 0
     # otherwise K splits towards 256 workgroups (at least two chunks each),
     # with fp32 partial tiles [splits][m][n rounded up to 4]
-    #   M=64, N=K=4096: 64 tiles -> 4 splits of 1024
-    assert L.fp8q_linear_workspace_size(0, 64, 4096, 4096) == 4 * 64 * 4096 * 4
+    #   M=64, N=1024, K=4096: 16 tiles -> 4 splits of 1024
+    assert L.fp8q_linear_workspace_size(0, 64, 1024, 4096) == 4 * 64 * 1024 * 4
     #   a small N on a long K (k/v projections): 16-row workgroups, K split in
     #   ranges of 2048 (4 waves x 512): N=1022, K=8192 -> 64 x 4 workgroups,
     #   partial rows padded to 1024
@@ -79,6 +84,42 @@ def test_workspace_queries(L):
     #   M=40, N=100, K=3000: 2 tiles, at most 2 splits of whole 512-k chunks
     assert L.fp8q_linear_workspace_size(0, 40, 100, 3000) == 2 * 40 * 100 * 4
     assert L.fp8q_linear_workspace_size(0, 0, 4096, 4096) == 0
+    # dynamic W8A8: a 256-byte scale slot, the absmax maxima (rounded to 256
+    # bytes), then the decode plan's partial tiles, or the E4M3 codes above 64 rows
+    assert L.fp8q_linear_w8a8_dynamic_workspace_size(1, 4096, 4096) == 256 + 256
+    assert L.fp8q_linear_w8a8_dynamic_workspace_size(64, 4096, 4096) == 256 + 256
+    assert L.fp8q_linear_w8a8_dynamic_workspace_size(12, 1022, 8192) == 256 + 256 + 4 * 12 * 1024 * 4
+    assert L.fp8q_linear_w8a8_dynamic_workspace_size(8192, 28672, 4096) == 256 + 4096 + 8192 * 4096
+    assert L.fp8q_linear_w8a8_dynamic_workspace_size(100, 300, 13) == 256 + 256 + 100 * 16 + 256 - 100 * 16 % 256
+    assert L.fp8q_linear_w8a8_dynamic_workspace_size(0, 4096, 4096) == 0
+
+
+def test_dynamic_host_validation(L):
+    # (m, k, ld_x, n, ld_w, ld_y, ws_bytes) -> status, with NULL pointers: the
+    # host checks come first
+    cases = [
+        ((-1, 64, 64, 16, 64, 16, 0), 1),               # m < 0
+        ((1, 0, 64, 16, 64, 16, 0), 1),                 # k < 1
+        ((1, 64, 60, 16, 64, 16, 0), 1),                # ld_x < k
+        ((1, 64, 68, 16, 64, 16, 0), 1),                # ld_x not a multiple of 8
+        ((1, 64, 64, 16, 72, 16, 0), 1),                # ld_w not a multiple of 16
+        ((1, 64, 64, 16, 64, 12, 0), 1),                # ld_y not a multiple of 8
+        ((0, 64, 64, 16, 64, 16, 0), 0),                # empty M: no-op
+        ((4, 64, 64, 0, 64, 16, 0), 0),                 # empty N: no-op
+        ((4, 64, 64, 16, 64, 16, 0), 4),                # workspace missing
+    ]
+    for (m, k, ldx, n, ldw, ldy, wsb), want in cases:
+        got = L.fp8q_linear_w8a8_dynamic(NULL, m, k, ldx, NULL, n, ldw, NULL, NULL, ldy, NULL,
+                                         NULL, wsb, NULL, NULL)
+        assert got == want, ((m, k, ldx, n, ldw, ldy), got, L.fp8q_last_error())
+    # the workspace overlapping the output is refused before any device query
+    base = 0x20000000
+    m, n, k = 8, 256, 1024
+    need = L.fp8q_linear_w8a8_dynamic_workspace_size(m, n, k)
+    got = L.fp8q_linear_w8a8_dynamic(base, m, k, k, base + (1 << 24), n, k, base + (2 << 24),
+                                     base + (3 << 24), n, NULL, base + (3 << 24) + 64, need,
+                                     NULL, NULL)
+    assert got == 1 and "overlap" in L.fp8q_last_error().decode()
 
 
 def test_describe(L):
@@ -86,6 +127,10 @@ def test_describe(L):
     assert L.fp8q_linear_describe(0, 1, 4096, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
     assert L.fp8q_linear_describe(0, 64, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<2, 2, 4, 2, 4>") and b"grid=(128,2)" in buf.value
+    assert L.fp8q_linear_describe(0, 32, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<1, 2, 4, 2, 4>") and b"grid=(256,1)" in buf.value
+    assert L.fp8q_linear_describe(1, 64, 4096, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_tile<4, 16, 8>")
     assert b"splits=4" in buf.value and b"k_w8a16_reduce" in buf.value
     assert L.fp8q_linear_describe(1, 8192, 28672, 4096, buf, 256) == 0
@@ -149,6 +194,23 @@ def test_linear_host_validation(L):
         assert got == want, ((mode, m, k, ldx, n, ldw, ldy), got, L.fp8q_last_error())
         if want:
             assert L.fp8q_last_error()
+
+
+def test_linear_overlap_rejected_on_host(L):
+    """Aliasing is refused from the pointer values alone, before any device
+    query: here an activation scale placed inside the K-split workspace, which
+    the split GEMM would overwrite before the reduction reads the scale."""
+    m, n, k = 12, 1024, 8192          # a K-split decode plan
+    need = L.fp8q_linear_workspace_size(1, m, n, k)
+    assert need > 0
+    base = 0x10000000
+    x, w, ws, y = base, base + (1 << 24), base + (2 << 24), base + (3 << 24)
+    wk = base + (4 << 24)
+    args = lambda xs: (1, x, m, k, k, xs, w, n, k, ws, y, n, wk, need, NULL)
+    assert L.fp8q_linear(*args(wk + 64)) == 1
+    assert "overlap" in L.fp8q_last_error().decode()
+    assert L.fp8q_linear(*args(y + 16)) == 1            # scale inside the output
+    assert L.fp8q_linear(*args(base + (5 << 24))) != 1 or "overlap" not in L.fp8q_last_error().decode()
 
 
 def test_quantize_host_validation(L):

@@ -13,7 +13,7 @@ import pytest
 
 import workloads
 from helpers import (assert_gemm_close, dev_bf16, dev_u8, host_bf16_as_f64, host_f32, host_u8,
-                     say)
+                     rows_every_tile, say)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -290,7 +290,8 @@ def test_w8a8_gemm_grouped_full_mlp_prefill_sampled(fq, orc):
     y = fq.linear(xq, q, s, x_scale=xs, group=128)
     torch.cuda.synchronize()
     xqr, xsr, _ = orc.quantize_act(x)
-    rows = np.unique(np.concatenate([np.arange(0, m, 509), [m - 1]]))
+    rows = rows_every_tile(m, 9)
+    assert rows.size >= 64 and len(set(rows // 256)) == (m + 255) // 256
     ref = orc.linear_grouped(1, xqr, qr, sr, 128, x_scale=xsr, rows=rows)
     got = host_bf16_as_f64(y[torch.from_numpy(rows).cuda()])
     assert_gemm_close(got, ref, "grouped mlp prefill sampled rows")

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import workloads
-from helpers import assert_gemm_close, dev_bf16, dev_u8, host_bf16_as_f64, say
+from helpers import assert_gemm_close, dev_bf16, dev_u8, host_bf16_as_f64, rows_every_tile, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -61,10 +61,17 @@ def all_codes_weight(n: int, k: int) -> np.ndarray:
     return w
 
 
+# shapes that take k_w8a16_panel (17..64 rows, K a multiple of 1024, about one
+# workgroup per CU), including a ragged last panel of weight rows and of
+# activation rows
+PANEL_SHAPES = [(40, 4096, 2048), (20, 3200, 3072), (33, 4000, 2048), (64, 4096, 4096),
+                (17, 4096, 2048), (64, 3584, 8192)]
+
+
 @pytest.mark.parametrize("m,n,k", [(16, 256, 64), (1, 256, 64), (64, 272, 64), (12, 256, 64),
                                    (1, 272, 576), (7, 300, 1100), (16, 256, 2048), (40, 320, 1536),
                                    (64, 272, 1600), (5, 4096, 1100), (1, 2304, 640),
-                                   (16, 512, 4160), (2, 300, 8200)])
+                                   (16, 512, 4160), (2, 300, 8200)] + PANEL_SHAPES)
 def test_w8a16_exact_every_code(fq, orc, m, n, k):
     """X = one-hot rows: Y[i, j] = dec(W[j, p_i]) exactly, for all 254 finite codes.
     The one-hot positions p_i are spread evenly over K (first to last), so
@@ -102,7 +109,7 @@ def f16_act(m: int, k: int, seed: int) -> np.ndarray:
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 64), (1, 272, 576), (64, 272, 1600), (5, 4096, 1100),
-                                   (16, 512, 4160), (40, 320, 1536)])
+                                   (16, 512, 4160), (40, 320, 1536), (33, 4000, 2048)])
 def test_w8a16_f16_exact_every_code(fq, orc, m, n, k):
     """fp8_w_fp16_a with one-hot fp16 rows: every E4M3 code widened to fp16 exactly."""
     wq = all_codes_weight(n, k)
@@ -118,7 +125,8 @@ def test_w8a16_f16_exact_every_code(fq, orc, m, n, k):
 
 @pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (8, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096),
                                    (12, 1024, 8192), (3, 100, 1000), (17, 130, 520), (100, 96, 4104),
-                                   (5, 300, 5000), (40, 522, 3000), (1, 16, 8), (12, 28672, 512)])
+                                   (5, 300, 5000), (40, 522, 3000), (1, 16, 8), (12, 28672, 512),
+                                   (50, 4096, 4096)])
 def test_w8a16_f16_ragged(fq, orc, m, n, k):
     w = workloads.heavy_tail_weight(n, k, m + n)
     x = f16_act(m, k, k)
@@ -160,7 +168,7 @@ RAGGED = [(3, 100, 1000), (17, 130, 520), (65, 64, 64), (100, 96, 4104), (1, 16,
           (5, 300, 5000), (12, 1022, 8192), (1, 100, 4096), (16, 64, 12288)]
 
 
-@pytest.mark.parametrize("m,n,k", RAGGED)
+@pytest.mark.parametrize("m,n,k", RAGGED + PANEL_SHAPES)
 def test_w8a16_ragged(fq, orc, m, n, k):
     w = workloads.heavy_tail_weight(n, k, m + n)
     x = workloads.normal_act(m, k, k)
@@ -173,9 +181,13 @@ def test_w8a16_ragged(fq, orc, m, n, k):
 # K a multiple of the prefill kernel's 128-byte stage: one stage, two, an odd
 # count, with ragged M and N around the 256 x 256 tile
 WHOLE_STAGES = [(257, 300, 128), (300, 520, 384), (513, 257, 256), (1000, 1000, 1280), (777, 64, 2048)]
+# more than 8 tile-rows, so the XCD-banded tile order has a full band and a
+# partial one: 10 x 8 = 80 tiles (a multiple of the 8 XCDs) and 17 x 3 = 51
+MANY_TILE_ROWS = [(2305, 2048, 640), (4100, 600, 256)]
 
 
-@pytest.mark.parametrize("m,n,k", RAGGED + [(300, 520, 1000), (256, 256, 4096), (513, 257, 200)] + WHOLE_STAGES)
+@pytest.mark.parametrize("m,n,k", RAGGED + [(300, 520, 1000), (256, 256, 4096), (513, 257, 200)] + WHOLE_STAGES
+                         + MANY_TILE_ROWS)
 def test_w8a8_ragged(fq, orc, m, n, k):
     w = workloads.heavy_tail_weight(n, k, m + n)
     x = workloads.outlier_act(m, k, k)
@@ -223,8 +235,10 @@ def test_layer_decode_70b_full(fq, orc, idx):
 
 @pytest.mark.parametrize("key", ["mlp_prefill", "down_prefill_70b"])
 def test_prefill_full_size_sampled(fq, orc, key):
-    """Full-size W8A8 GEMM as the benchmark launches it; 24 seeded rows x all N
-    columns compared with the fp64 oracle."""
+    """Full-size W8A8 GEMM as the benchmark launches it.  Seeded rows, at least
+    two in every 256-row band of the GEMM's tiles and at least 64 in all,
+    times all N columns, so every 256 x 256 output tile is compared with the
+    fp64 oracle."""
     wl = workloads.WORKLOADS[key]
     lin = wl.linears[0]
     m = wl.ms[0]
@@ -234,8 +248,8 @@ def test_prefill_full_size_sampled(fq, orc, key):
     y = fq.linear(pad16(xq), pad16(wq), torch.from_numpy(ws).cuda(),
                   x_scale=torch.tensor([xs], dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(7).choice(m, 24, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, m - 1]]))
+    rows = rows_every_tile(m, 7)
+    assert rows.size >= 64 and len(set(rows // 256)) == (m + 255) // 256
     ysel = host_bf16_as_f64(y[torch.from_numpy(rows).cuda()])
     ref = orc.linear(1, xq, wq, ws, xs, rows=rows)
     assert_gemm_close(ysel, ref, key)
@@ -284,6 +298,14 @@ def test_w8a16_split_workspace_reuse(fq, orc, shapes):
                               f"reuse {m}x{n}x{k} call {rep}")
 
 
+def test_panel_plans_are_taken(fq):
+    """The panel shapes above run k_w8a16_panel (so their parity tests cover it)."""
+    for m, n, k in PANEL_SHAPES:
+        assert fq.describe_linear(0, m, n, k).startswith("k_w8a16_panel"), (m, n, k)
+        assert fq.describe_linear(2, m, n, k).startswith("k_w8a16_panel"), (m, n, k)
+        assert not fq.describe_linear(1, m, n, k).startswith("k_w8a16_panel"), (m, n, k)
+
+
 def test_deterministic(fq, orc):
     w = workloads.heavy_tail_weight(1024, 8192, 3)
     wq, ws = fq.quantize_weight(dev_bf16(w))
@@ -297,6 +319,12 @@ def test_deterministic(fq, orc):
     z1 = fq.linear(xq, wq, ws, x_scale=xs)
     z2 = fq.linear(xq, wq, ws, x_scale=xs)
     assert torch.equal(z1.view(torch.int16), z2.view(torch.int16))
+    wp, wps = fq.quantize_weight(dev_bf16(workloads.heavy_tail_weight(4096, 4096, 6)))
+    xp = dev_bf16(workloads.normal_act(64, 4096, 7))
+    say("determinism w8a16 panel", fq.describe_linear(0, 64, 4096, 4096))
+    p1 = fq.linear(xp, wp, wps)
+    p2 = fq.linear(xp, wp, wps)
+    assert torch.equal(p1.view(torch.int16), p2.view(torch.int16))
 
 
 def test_host_pointer_and_device_checks(fq):
@@ -339,7 +367,8 @@ def test_host_pointer_and_device_checks(fq):
 
 
 @pytest.mark.parametrize("mode,m,n,k", [(1, 300, 300, 256), (1, 520, 1000, 384), (1, 300, 300, 200),
-                                        (1, 257, 9, 128), (0, 12, 300, 8192), (0, 64, 1000, 4096)])
+                                        (1, 257, 9, 128), (0, 12, 300, 8192), (0, 64, 1000, 4096),
+                                        (0, 48, 4000, 2048)])
 def test_output_stride_guard(fq, orc, mode, m, n, k):
     """Y written into a wider buffer (ld_y = n rounded up to 8, plus 24) with
     rows to spare: every element past column n or row m keeps its sentinel,
