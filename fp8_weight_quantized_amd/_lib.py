@@ -54,6 +54,7 @@ SIGNATURES = {
     "fp8q_linear_workspace_size": (SZ, [ST, I64, I64, I64]),
     "fp8q_linear": (ST, [ST, P, I64, I64, I64, P, P, I64, I64, P, P, I64, P, SZ, P]),
     "fp8q_cast_f32_to_e4m3": (ST, [P, I64, P, P]),
+    "fp8q_linear_noalloc": (ST, [ST, P, I64, I64, I64, P, P, I64, I64, P, P, I64, P]),
     "fp8q_linear_w8a8_dynamic_workspace_size": (SZ, [I64, I64, I64]),
     "fp8q_linear_w8a8_dynamic": (ST, [P, I64, I64, I64, P, I64, I64, P, P, I64, P, P, SZ, P, P]),
     "fp8q_linear_describe": (ST, [ST, I64, I64, I64, ctypes.c_char_p, SZ]),

@@ -671,6 +671,36 @@ fp8q_status fp8q_linear_w8a8_dynamic(const uint16_t *x_bf16, int64_t m, int64_t 
     return ok();
 }
 
+fp8q_status fp8q_linear_noalloc(fp8q_mode mode,
+                                const void *x, int64_t m, int64_t k, int64_t ld_x,
+                                const float *x_scale, const uint8_t *w_fp8, int64_t n,
+                                int64_t ld_w, const float *w_scale,
+                                uint16_t *y_bf16, int64_t ld_y, hipStream_t stream)
+{
+    if (m > 0 && n > 0 && k >= 1 && (mode == FP8Q_W8A16 || mode == FP8Q_W8A8 || mode == FP8Q_W8A16_F16)) {
+        const size_t need = linear_workspace(mode, m, n, k, 0);
+        if (need > fp8q::kNoallocScratchBytes)
+            return fail(FP8Q_ERR_WORKSPACE,
+                        "this shape needs %zu bytes of K-split scratch; the allocation-free "
+                        "entry point has %zu (use fp8q_linear with a workspace)",
+                        need, fp8q::kNoallocScratchBytes);
+        if (need > 0) {
+            int dev = 0;
+            FP8Q_TRY(prepare(stream, &dev));
+            void *scr = nullptr;
+            hipError_t e = fp8q::launch::noalloc_scratch(dev, &scr);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return hip_fail(e, "resolving the device scratch (hipGetSymbolAddress)");
+            }
+            return linear_impl(mode, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, 0, y_bf16,
+                               ld_y, scr, fp8q::kNoallocScratchBytes, stream);
+        }
+    }
+    return linear_impl(mode, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, 0, y_bf16, ld_y,
+                       nullptr, 0, stream);
+}
+
 size_t fp8q_linear_grouped_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
                                           int64_t group)
 {

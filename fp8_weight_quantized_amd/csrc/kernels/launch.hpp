@@ -12,6 +12,12 @@ namespace fp8q {
 // partial maxima kept in the workspace).
 constexpr int kActMaxBlocks = 1024;
 
+// The allocation-free linear layer's device scratch: 8 MiB per GPU, which
+// holds the K-split partial tiles of the Llama-3 8B/70B decode shapes (at
+// most 5.5 MB, the 70B gate/up projection at 12 rows).
+constexpr size_t kNoallocScratchBytes = (size_t)8 << 20;
+constexpr int kNoallocMaxDevices = 64;
+
 namespace launch {
 
 hipError_t quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
@@ -107,6 +113,11 @@ hipError_t w8a16_quant_act(const W8A16Plan &p, const uint16_t *x, int64_t m, int
                            int32_t *flag, const uint8_t *w, int64_t n, int64_t ld_w,
                            const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
                            hipStream_t stream);
+
+// Device address of this GPU's kNoallocScratchBytes scratch array, looked up
+// (hipGetSymbolAddress, with `device` made current for the call) on the first
+// request for that device and kept.
+hipError_t noalloc_scratch(int device, void **ptr);
 
 // ---- W8A8 (fp8_w_fp8_a) GEMM on FP8 MFMA -----------------------------------
 struct W8A8Plan {

@@ -32,6 +32,7 @@
 //   N / 64 tiles cannot fill the GPU, K is split across workgroups: each
 //   split writes an fp32 partial tile, and k_w8a16_reduce adds the splits in
 //   split order (deterministic), scales and stores.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -1119,7 +1120,43 @@ int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
+// Device-resident scratch for callers that cannot allocate (fp8q_linear_noalloc):
+// the K-split partial tiles of the decode kernels.  Each GPU holds its own copy
+// from the library's load to the end of the process.  In host code the name
+// `scratch` is only a stand-in for the device symbol; its device address comes
+// from hipGetSymbolAddress, resolved once per device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
 namespace launch {
+
+hipError_t noalloc_scratch(int device, void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[kNoallocMaxDevices] = {};
+    if (device < 0 || device >= kNoallocMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[device] == nullptr) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess)
+            return e;
+        if (cur != device && (e = hipSetDevice(device)) != hipSuccess)
+            return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = cur != device ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess)
+            return e;
+        if (back != hipSuccess)
+            return back;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        addr[device] = p;
+    }
+    *ptr = addr[device];
+    return hipSuccess;
+}
 
 // Register-pipeline depth of the rows kernel: about 24-36 16-byte loads in
 // flight per lane.

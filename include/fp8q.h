@@ -275,6 +275,28 @@ fp8q_status fp8q_linear(fp8q_mode mode,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fp8q_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, the same kernels and results.  When
+ * the plan splits K, the fp32 partial tiles go to a device-resident scratch
+ * array of 8 MiB per GPU that the library holds until the process ends
+ * (enough for the Llama-3 8B/70B decode shapes); a shape whose
+ * fp8q_linear_workspace_size exceeds 8 MiB returns FP8Q_ERR_WORKSPACE and
+ * launches nothing.  The first call on a device that needs the scratch looks
+ * up its address (hipGetSymbolAddress); make that first call outside graph
+ * capture.  Nothing is allocated, freed or cleared (the partial tiles need no
+ * initialisation).  Every call on one GPU shares that GPU's scratch, which
+ * keeps the last call's contents: calls that may overlap in time on one GPU
+ * (different streams without ordering, several threads) race and give
+ * undefined results; order them on one stream.
+ */
+fp8q_status fp8q_linear_noalloc(fp8q_mode mode,
+                                const void *x, int64_t m, int64_t k, int64_t ld_x,
+                                const float *x_scale, const uint8_t *w_fp8, int64_t n,
+                                int64_t ld_w, const float *w_scale,
+                                uint16_t *y_bf16, int64_t ld_y, hipStream_t stream);
+
+/*
  * fp8_w_fp8_a (the write-up §3.1 step 3) on bf16 activations, with the dynamic
  * per-tensor activation quantization of the deployment guide §1.2 (scale by the
  * §3.1 formula) folded into the linear layer:
