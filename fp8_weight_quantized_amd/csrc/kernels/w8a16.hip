@@ -918,8 +918,11 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     constexpr int LC = NI + CS * AF;            // loads per lane per chunk
     static_assert(RU % 16 == 0 && (XR * RU) % kWave == 0, "chunk shape");
     static_assert(D >= 1 && D <= 4, "chunks in flight");
-    __shared__ __attribute__((aligned(16))) uint8_t xl[NWV][XR * RB];
-    static_assert(sizeof(v4f) * NWV * AF * MB * kWave <= sizeof(xl), "reduction fits the slots");
+    // the waves' staging slots; after the K loop the same bytes hold the
+    // waves' fp32 panels for the reduction
+    constexpr int SLOT = XR * RB;
+    constexpr int RED = (int)sizeof(v4f) * NWV * AF * MB * kWave;
+    __shared__ __attribute__((aligned(16))) uint8_t xl[NWV * SLOT > RED ? NWV * SLOT : RED];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
@@ -930,7 +933,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const int64_t kq = k / NWV;
     const int64_t kb = (int64_t)wave * kq;
     const int nch = (int)(kq / CK);
-    uint8_t *slot = xl[wave];
+    uint8_t *slot = xl + wave * SLOT;
     const float xs = act_scale<AT>(nullptr, qa);
     const E4M3Div div(AT == kActQ ? xs : 1.0f);
 
@@ -1038,7 +1041,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
 
     // ---- the waves' panels, added in wave order, then scaled and stored ----
     __syncthreads();
-    v4f *red = reinterpret_cast<v4f *>(&xl[0][0]);     // [wave][AF * MB][lane]
+    v4f *red = reinterpret_cast<v4f *>(xl);     // [wave][AF * MB][lane]
 #pragma unroll
     for (int a = 0; a < AF; ++a)
 #pragma unroll
@@ -1206,6 +1209,42 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
     // Llama-3-8B q_proj (N = K = 4096), in graphs: M = 32 9.9 us against
     // 10.3 us for the split tile kernel + reduce, M = 64 11.9 us against
     // 13.7 us.
+    // Up to 16 activation rows on a wide weight (N >= 8192) with K < 16K: the
+    // panel kernel with one activation group and AF = 2, 3, 4 or 7 weight
+    // fragments per workgroup, the AF whose grid is closest to whole waves of
+    // 256 workgroups (least rows per CU: rounds of 256 workgroups x 16 AF).
+    // Measured on MI355X at M = 12 (graphs): Llama-3-70B gate/up [28672,
+    // 8192] 47.7 us (AF = 7, 256 workgroups) against 53.3 us for the 4-way
+    // split tile kernel + reduce, q/o [8192, 8192] 18.3-18.7 us against
+    // 19.1 us, fused gate_up [57344, 8192] 92.6 against 102.6 us, Llama-3-8B
+    // gate_up [28672, 4096] 26.2 against 28.9 us; AF = 8 (224 workgroups)
+    // measured 53.1 us on gate/up.  A long K (the 70B down_proj, 28672)
+    // stays on the split tile kernel (51.4 us against 57.7 us).
+    if (act != kW8A16ActF8 && m <= 16 && n >= 8192 && k % 512 == 0 && k >= 2048 && k < 16384) {
+        static const int kAf[4] = {2, 3, 4, 7};
+        int best = 0;
+        int64_t best_cost = 0;
+        for (int i = 0; i < 4; ++i) {
+            const int64_t wgs = div_up(n, 16 * kAf[i]);
+            const int64_t cost = div_up(wgs, 256) * kAf[i];
+            if (i == 0 || cost < best_cost || (cost == best_cost && kAf[i] > kAf[best])) {
+                best = i;
+                best_cost = cost;
+            }
+        }
+        p.kind = W8A16Plan::kPanel;
+        p.af = kAf[best];
+        p.mb = 1;
+        p.rows = 16 * p.af;
+        p.waves = 4;
+        p.steps = 2;
+        p.depth = 3;
+        p.grid_n = div_up(n, 16 * p.af);
+        p.grid_m = 1;
+        p.kper = k;
+        p.kchunk = k / 4;
+        return p;
+    }
     if (act != kW8A16ActF8 && m > 16 && m <= 64 && k % 1024 == 0 && k >= 2048) {
         const int af = m > 32 ? 2 : 1;
         const int64_t gn = div_up(n, 16 * af), gm = div_up(m, 32);
@@ -1388,16 +1427,17 @@ static void launch_tile(const W8A16Plan &p, const void *x, int64_t m, int64_t k,
     }
 }
 
-// k_w8a16_panel with 32 activation rows, 64-k x 4 chunks, 2 chunks in flight
-// and 4 waves (the measured best on the Llama-3-8B q_proj decode shapes).
-template <int AF, int AT>
+// k_w8a16_panel, 4 waves.  32 activation rows: chunks of 4 x 64 k, 2 in
+// flight (the measured best on the Llama-3-8B q_proj decode shapes); 16
+// activation rows: chunks of 2 x 64 k, 3 in flight (Llama-3-70B shapes).
+template <int AF, int MB, int CS, int D, int AT>
 static void launch_panel(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
                          const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
                          uint16_t *y, int64_t ld_y, const QuantArgs &qa, hipStream_t stream)
 {
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
-    hipLaunchKernelGGL((k_w8a16_panel<AF, 2, 4, 2, 4, AT>), grid, dim3(4 * kWave), 0, stream, x, m,
-                       k, ld_x, w, n, ld_w, w_scale, y, ld_y, qa);
+    hipLaunchKernelGGL((k_w8a16_panel<AF, MB, CS, D, 4, AT>), grid, dim3(4 * kWave), 0, stream, x,
+                       m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, qa);
 }
 
 template <int AT>
@@ -1409,16 +1449,19 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
     float *partial = static_cast<float *>(workspace);
     if (p.group == 0 && p.kind == W8A16Plan::kPanel) {
         if constexpr (AT != kActF8) {
-            if (p.mb == 2 && p.steps == 4 && p.depth == 2 && p.waves == 4) {
-                if (p.af == 1) {
-                    launch_panel<1, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, qa, stream);
-                    return hipGetLastError();
-                }
-                if (p.af == 2) {
-                    launch_panel<2, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, qa, stream);
-                    return hipGetLastError();
-                }
+#define FP8Q_PANEL_CASE(AF, MB, CS, D)                                                        \
+            if (p.af == AF && p.mb == MB && p.steps == CS && p.depth == D && p.waves == 4) {    \
+                launch_panel<AF, MB, CS, D, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y,  \
+                                                qa, stream);                                  \
+                return hipGetLastError();                                                     \
             }
+            FP8Q_PANEL_CASE(1, 2, 4, 2)
+            FP8Q_PANEL_CASE(2, 2, 4, 2)
+            FP8Q_PANEL_CASE(2, 1, 2, 3)
+            FP8Q_PANEL_CASE(3, 1, 2, 3)
+            FP8Q_PANEL_CASE(4, 1, 2, 3)
+            FP8Q_PANEL_CASE(7, 1, 2, 3)
+#undef FP8Q_PANEL_CASE
         }
     } else if (p.group == 0 && p.kind == W8A16Plan::kRows) {
 #define FP8Q_ROWS_CASE(AF, MB, P, NW)                                                         \

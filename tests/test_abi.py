@@ -58,12 +58,14 @@ def test_workspace_queries(L):
     # W8A16, up to 16 activation rows on a weight of up to 4096 rows: the rows
     # kernel, one launch, no scratch
     assert L.fp8q_linear_workspace_size(0, 1, 4096, 4096) == 0
-    # wider weights at up to 16 rows with 8K <= K < 16K: the tile kernel with
-    # K split 4 ways
-    assert L.fp8q_linear_workspace_size(0, 12, 8192, 8192) == 4 * 12 * 8192 * 4
-    assert L.fp8q_linear_workspace_size(0, 12, 28672, 8192) == 4 * 12 * 28672 * 4
-    # K = 4096: 448 tiles cover the GPU unsplit
+    # wider weights (N >= 8192) at up to 16 rows with K < 16K: the panel
+    # kernel, whole K per workgroup, no scratch; E4M3 codes at 8K <= K < 16K
+    # take the tile kernel with K split 4 ways
+    assert L.fp8q_linear_workspace_size(0, 12, 8192, 8192) == 0
+    assert L.fp8q_linear_workspace_size(0, 12, 28672, 8192) == 0
     assert L.fp8q_linear_workspace_size(0, 12, 28672, 4096) == 0
+    assert L.fp8q_linear_workspace_size(1, 12, 8192, 8192) == 4 * 12 * 8192 * 4
+    assert L.fp8q_linear_workspace_size(1, 12, 28672, 8192) == 4 * 12 * 28672 * 4
     # a small N on a short K: 64-row tiles, no split (K under two chunks)
     assert L.fp8q_linear_workspace_size(0, 4, 64, 500) == 0
     # 17..64 rows with about one workgroup per CU: the panel kernel, whole K

@@ -65,7 +65,10 @@ def all_codes_weight(n: int, k: int) -> np.ndarray:
 # workgroup per CU), including a ragged last panel of weight rows and of
 # activation rows
 PANEL_SHAPES = [(40, 4096, 2048), (20, 3200, 3072), (33, 4000, 2048), (64, 4096, 4096),
-                (17, 4096, 2048), (64, 3584, 8192)]
+                (17, 4096, 2048), (64, 3584, 8192),
+                # up to 16 rows on a wide weight: 2, 3, 4 or 7 weight fragments
+                (12, 8192, 2048), (5, 10240, 2048), (16, 28672, 2048), (1, 16384, 3072),
+                (7, 9000, 2560)]
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 64), (1, 256, 64), (64, 272, 64), (12, 256, 64),

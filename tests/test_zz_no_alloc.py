@@ -57,7 +57,7 @@ def _call(L, fn, mode, xd, xsd, m, k, wd, n, wsd, y, extra):
 
 # (mode, m, n, k): the first call of each pair is the larger one; every shape
 # splits K (so the scratch carries partial tiles between two kernels)
-PAIRS = [[(0, 12, 28672, 8192), (0, 12, 1022, 8192)],
+PAIRS = [[(1, 12, 28672, 8192), (0, 12, 1022, 8192)],
          [(1, 64, 4096, 4096), (1, 24, 1024, 8192)],
          [(0, 40, 300, 3000), (0, 12, 1024, 8192)]]
 
@@ -97,18 +97,20 @@ def test_noalloc_without_split_and_refusal(L, orc):
     torch.cuda.synchronize()
     assert_gemm_close(host_bf16_as_f64(y), ref, "noalloc no split")
     # a K-split scratch above the maximum: refused, nothing launched (the
-    # output keeps its sentinel).  16 bf16 rows on a 57344-row weight (the
-    # Llama-3-70B fused gate_up) split K 4 ways: 4 * 16 * 57344 * 4 bytes.
-    # Every buffer has its full size, so nothing could be read out of bounds.
-    mode, m, n, k = 0, 16, 57344, 8192
+    # output keeps its sentinel).  16 rows of E4M3 codes on a 57344-row weight
+    # (the Llama-3-70B fused gate_up) split K 4 ways: 4 * 16 * 57344 * 4
+    # bytes.  Every buffer has its full size, so nothing could be read out of
+    # bounds.
+    mode, m, n, k = 1, 16, 57344, 8192
     need = L.fp8q_linear_workspace_size(mode, m, n, k)
     assert need == 4 * 16 * 57344 * 4 > SCRATCH_BYTES
-    xb = torch.zeros((m, k), dtype=torch.bfloat16, device="cuda")
+    xb = torch.zeros((m, k), dtype=torch.uint8, device="cuda")
+    xs1 = torch.ones(1, dtype=torch.float32, device="cuda")
     w8 = torch.zeros((n, k), dtype=torch.uint8, device="cuda")
     ws1 = torch.ones(n, dtype=torch.float32, device="cuda")
     ysent = torch.full((m, n), 0x7FC1, dtype=torch.int16, device="cuda")
     say("noalloc refusal")
-    st = L.fp8q_linear_noalloc(mode, xb.data_ptr(), m, k, k, None, w8.data_ptr(), n, k,
+    st = L.fp8q_linear_noalloc(mode, xb.data_ptr(), m, k, k, xs1.data_ptr(), w8.data_ptr(), n, k,
                                ws1.data_ptr(), ysent.data_ptr(), n,
                                torch.cuda.current_stream().cuda_stream)
     assert st == 4, st
