@@ -14,12 +14,18 @@ throughput: (N*K codes + 4N scale bytes + 2MK activation bytes + 2MN output
 bytes) summed over the step's calls, divided by the step time.
 
 Unless --quick, the same line carries measurements of the other rows of the
-path on their own workloads ("rows"): weight quantization, activation
-quantization, the W8A8 prefill GEMM (Llama-3-8B gate+up and Llama-3-70B
-down_proj) and the Llama-3-70B decoder layer's seven linears at M = 12.
+path on their own workloads ("rows"): the Tiny workload, weight quantization,
+activation quantization, the W8A8 prefill GEMM (Llama-3-8B gate+up and
+Llama-3-70B down_proj), the Llama-3-70B decoder layer's seven linears at
+M = 12, and the next rows (fp16 and fused-quantization fp8 activations,
+held/EMA scales, the FP8 KV cache, per-group scales).  Prefill GEMM and
+activation-cast rows rotate through copies of their inputs whose other copies
+together exceed the 256 MB Infinity Cache, so each call reads HBM.
 
-`cpu_baseline` is the CPU oracle (tests' checker) timed on this host on one
-full decode step.  Inputs are seeded synthetic data (workloads.py).
+`cpu_baseline` is the CPU oracle (tests' checker) timed on this host on full
+decode steps; `cpu_oracle_by_config` times it on every workload (quantization
+in full, the GEMM in full or on 64 seeded rows of the prefill GEMMs).  Inputs
+are seeded synthetic data (workloads.py).
 """
 from __future__ import annotations
 
@@ -51,6 +57,11 @@ def parse():
                     help="size of the rotating pool of quantized weight copies")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time spent repeating the headline oracle decode step")
+    ap.add_argument("--sections", default="all",
+                    help="comma-separated rows to run after the headline: decode-next, tiny, "
+                         "prefill, layer, kv (default all); e.g. a profiler run of one section")
     return ap.parse_args()
 
 
@@ -240,126 +251,173 @@ def main() -> int:
     log("device copy", round(copy_gbs, 1), "GB/s (read + write)")
 
     # --------------------------------------------------------------- other rows
+    sections = {"decode-next", "tiny", "prefill", "layer", "kv"} if args.sections == "all" \
+        else set(args.sections.split(","))
     if not args.quick:
         rows = {}
-        # fp8_w_fp16_a on the same decode step: fp16 copies of the activations
-        xs16 = {m: xs[m].to(torch.float16) for m in DECODE_MS}
-        ys16 = {m: torch.empty((m, N), dtype=torch.float16, device=dev) for m in DECODE_MS}
+        if "decode-next" in sections:
+            # fp8_w_fp16_a on the same decode step: fp16 copies of the activations
+            xs16 = {m: xs[m].to(torch.float16) for m in DECODE_MS}
+            ys16 = {m: torch.empty((m, N), dtype=torch.float16, device=dev) for m in DECODE_MS}
 
-        def decode_step_f16(i: int, stream: int):
-            for j, m in enumerate(DECODE_MS):
-                c = (len(DECODE_MS) * i + j) % copies_n
-                st = L.fp8q_linear(2, ptr(xs16[m]), m, K, K, None, ptr(pool[c]), N, K, ptr(w_scale),
-                                   ptr(ys16[m]), N, ptr(wsp[m]), wsn[m], stream)
-                if st != 0:
-                    raise RuntimeError(_lib.last_error())
-        g16 = torch.cuda.CUDAGraph()
-        s16 = torch.cuda.Stream(device=dev)
-        s16.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.graph(g16, stream=s16, capture_error_mode="relaxed"):
-            h = torch.cuda.current_stream(dev).cuda_stream
-            for i in range(rot):
-                decode_step_f16(i, h)
-        torch.cuda.current_stream(dev).wait_stream(s16)
-        g16.replay()
-        torch.cuda.synchronize()
-        start.record()
-        g16.replay()
-        end.record()
-        end.synchronize()
-        us16 = start.elapsed_time(end) * 1e3 / rot
-        rows["f1_w8a16_f16_q_proj_decode"] = {
-            "shape": "N=K=4096, M=1,8,32,64 per step", "us_per_step": round(us16, 3),
-            "GB/s": round(step_bytes / (us16 * 1e-6) / 1e9, 1),
-            "frac_hbm": round(step_bytes / (us16 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "mode": "fp8_w_fp16_a (fp16 activations and output)"}
-        log(rows["f1_w8a16_f16_q_proj_decode"])
+            def decode_step_f16(i: int, stream: int):
+                for j, m in enumerate(DECODE_MS):
+                    c = (len(DECODE_MS) * i + j) % copies_n
+                    st = L.fp8q_linear(2, ptr(xs16[m]), m, K, K, None, ptr(pool[c]), N, K, ptr(w_scale),
+                                       ptr(ys16[m]), N, ptr(wsp[m]), wsn[m], stream)
+                    if st != 0:
+                        raise RuntimeError(_lib.last_error())
+            g16 = torch.cuda.CUDAGraph()
+            s16 = torch.cuda.Stream(device=dev)
+            s16.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.graph(g16, stream=s16, capture_error_mode="relaxed"):
+                h = torch.cuda.current_stream(dev).cuda_stream
+                for i in range(rot):
+                    decode_step_f16(i, h)
+            torch.cuda.current_stream(dev).wait_stream(s16)
+            g16.replay()
+            torch.cuda.synchronize()
+            start.record()
+            g16.replay()
+            end.record()
+            end.synchronize()
+            us16 = start.elapsed_time(end) * 1e3 / rot
+            rows["f1_w8a16_f16_q_proj_decode"] = {
+                "shape": "N=K=4096, M=1,8,32,64 per step", "us_per_step": round(us16, 3),
+                "GB/s": round(step_bytes / (us16 * 1e-6) / 1e9, 1),
+                "frac_hbm": round(step_bytes / (us16 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "mode": "fp8_w_fp16_a (fp16 activations and output)"}
+            log(rows["f1_w8a16_f16_q_proj_decode"])
 
-        # fp8_w_fp8_a at decode sizes: the same step on per-tensor E4M3 activations
-        # (quantized once, outside the timed region)
-        xq8 = {}
-        for m in DECODE_MS:
-            xq8[m] = fq.quantize_act(xs[m])
-        wsn8 = {m: L.fp8q_linear_workspace_size(1, m, N, K) for m in DECODE_MS}
-        wsp8 = {m: (torch.empty(wsn8[m], dtype=torch.uint8, device=dev) if wsn8[m] else None)
-                for m in DECODE_MS}
+            # fp8_w_fp8_a at decode sizes: the same step on per-tensor E4M3 activations
+            # (quantized once, outside the timed region)
+            xq8 = {}
+            for m in DECODE_MS:
+                xq8[m] = fq.quantize_act(xs[m])
+            wsn8 = {m: L.fp8q_linear_workspace_size(1, m, N, K) for m in DECODE_MS}
+            wsp8 = {m: (torch.empty(wsn8[m], dtype=torch.uint8, device=dev) if wsn8[m] else None)
+                    for m in DECODE_MS}
 
-        def decode_step_f8(i: int, stream: int):
-            for j, m in enumerate(DECODE_MS):
-                c = (len(DECODE_MS) * i + j) % copies_n
-                q, sc = xq8[m]
-                st = L.fp8q_linear(1, ptr(q), m, K, q.stride(0), ptr(sc), ptr(pool[c]), N, K,
-                                   ptr(w_scale), ptr(ys[m]), N, ptr(wsp8[m]), wsn8[m], stream)
-                if st != 0:
-                    raise RuntimeError(_lib.last_error())
-        g8 = torch.cuda.CUDAGraph()
-        s8 = torch.cuda.Stream(device=dev)
-        s8.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.graph(g8, stream=s8, capture_error_mode="relaxed"):
-            h = torch.cuda.current_stream(dev).cuda_stream
-            for i in range(rot):
-                decode_step_f8(i, h)
-        torch.cuda.current_stream(dev).wait_stream(s8)
-        g8.replay()
-        torch.cuda.synchronize()
-        start.record()
-        g8.replay()
-        end.record()
-        end.synchronize()
-        us8 = start.elapsed_time(end) * 1e3 / rot
-        bytes8 = sum(N * K + 4 * N + m * K + 4 + 2 * m * N for m in DECODE_MS)
-        rows["f1_w8a8_q_proj_decode"] = {
-            "shape": "N=K=4096, M=1,8,32,64 per step", "us_per_step": round(us8, 3),
-            "GB/s": round(bytes8 / (us8 * 1e-6) / 1e9, 1),
-            "frac_hbm": round(bytes8 / (us8 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "mode": "fp8_w_fp8_a at decode sizes (E4M3 activations, per-tensor scale)"}
-        log(rows["f1_w8a8_q_proj_decode"])
+            def decode_step_f8(i: int, stream: int):
+                for j, m in enumerate(DECODE_MS):
+                    c = (len(DECODE_MS) * i + j) % copies_n
+                    q, sc = xq8[m]
+                    st = L.fp8q_linear(1, ptr(q), m, K, q.stride(0), ptr(sc), ptr(pool[c]), N, K,
+                                       ptr(w_scale), ptr(ys[m]), N, ptr(wsp8[m]), wsn8[m], stream)
+                    if st != 0:
+                        raise RuntimeError(_lib.last_error())
+            g8 = torch.cuda.CUDAGraph()
+            s8 = torch.cuda.Stream(device=dev)
+            s8.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.graph(g8, stream=s8, capture_error_mode="relaxed"):
+                h = torch.cuda.current_stream(dev).cuda_stream
+                for i in range(rot):
+                    decode_step_f8(i, h)
+            torch.cuda.current_stream(dev).wait_stream(s8)
+            g8.replay()
+            torch.cuda.synchronize()
+            start.record()
+            g8.replay()
+            end.record()
+            end.synchronize()
+            us8 = start.elapsed_time(end) * 1e3 / rot
+            bytes8 = sum(N * K + 4 * N + m * K + 4 + 2 * m * N for m in DECODE_MS)
+            rows["f1_w8a8_codes_q_proj_decode"] = {
+                "shape": "N=K=4096, M=1,8,32,64 per step", "us_per_step": round(us8, 3),
+                "GB/s": round(bytes8 / (us8 * 1e-6) / 1e9, 1),
+                "frac_hbm": round(bytes8 / (us8 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "mode": "fp8_w_fp8_a GEMM alone, on E4M3 codes and a scale made outside the timed "
+                        "region (not the mode's whole per-call cost: see f1_w8a8_dynamic_q_proj_decode)"}
+            log(rows["f1_w8a8_codes_q_proj_decode"])
 
-        # per-group weight scales (groups of 128) on the same decode step
-        G = 128
-        wqg, wsg = fq.quantize_weight_grouped(up_bf16(w_bits), G)
-        pool_g = torch.empty((copies_n, N, K), dtype=torch.uint8, device=dev)
-        pool_g[:] = wqg.unsqueeze(0)
-        del wqg
-        wsng = {m: L.fp8q_linear_grouped_workspace_size(0, m, N, K, G) for m in DECODE_MS}
-        wspg = {m: (torch.zeros(wsng[m], dtype=torch.uint8, device=dev) if wsng[m] else None)
-                for m in DECODE_MS}
+            # fp8_w_fp8_a from bf16 activations: the per-tensor quantization folded
+            # into the GEMM (absmax kernel + GEMM kernel per call), the mode's
+            # whole per-call cost
+            wsnd = {m: L.fp8q_linear_w8a8_dynamic_workspace_size(m, N, K) for m in DECODE_MS}
+            wspd = {m: torch.empty(wsnd[m], dtype=torch.uint8, device=dev) for m in DECODE_MS}
 
-        def decode_step_g(i: int, stream: int):
-            for j, m in enumerate(DECODE_MS):
-                c = (len(DECODE_MS) * i + j) % copies_n
-                st = L.fp8q_linear_grouped(0, ptr(xs[m]), m, K, K, None, ptr(pool_g[c]), N, K,
-                                           ptr(wsg), G, ptr(ys[m]), N, ptr(wspg[m]), wsng[m],
-                                           stream)
-                if st != 0:
-                    raise RuntimeError(_lib.last_error())
-        gg = torch.cuda.CUDAGraph()
-        sg = torch.cuda.Stream(device=dev)
-        sg.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.graph(gg, stream=sg, capture_error_mode="relaxed"):
-            h = torch.cuda.current_stream(dev).cuda_stream
-            for i in range(rot):
-                decode_step_g(i, h)
-        torch.cuda.current_stream(dev).wait_stream(sg)
-        gg.replay()
-        torch.cuda.synchronize()
-        start.record()
-        gg.replay()
-        end.record()
-        end.synchronize()
-        usg = start.elapsed_time(end) * 1e3 / rot
-        bytes_g = sum(N * K + 4 * N * (K // G) + 2 * m * K + 2 * m * N for m in DECODE_MS)
-        rows["f4_grouped_q_proj_decode"] = {
-            "shape": "N=K=4096, M=1,8,32,64 per step, groups of 128", "us_per_step": round(usg, 3),
-            "GB/s": round(bytes_g / (usg * 1e-6) / 1e9, 1),
-            "frac_hbm": round(bytes_g / (usg * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "mode": "fp8_w_bf16_a with per-group weight scales",
-            "kernels": {str(m): fq.describe_linear(0, m, N, K, G) for m in DECODE_MS}}
-        log(rows["f4_grouped_q_proj_decode"])
-        del pool_g, gg
-        torch.cuda.empty_cache()
-        rows.update(other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev))
+            def decode_step_dyn(i: int, stream: int):
+                for j, m in enumerate(DECODE_MS):
+                    c = (len(DECODE_MS) * i + j) % copies_n
+                    st = L.fp8q_linear_w8a8_dynamic(ptr(xs[m]), m, K, K, ptr(pool[c]), N, K,
+                                                    ptr(w_scale), ptr(ys[m]), N, None, ptr(wspd[m]),
+                                                    wsnd[m], None, stream)
+                    if st != 0:
+                        raise RuntimeError(_lib.last_error())
+            usd = time_graph(torch, dev, [lambda h, i=i: decode_step_dyn(i, h) for i in range(rot)])
+            bytesd = sum(N * K + 4 * N + 2 * m * K + 4 + 2 * m * N for m in DECODE_MS)
+            rows["f1_w8a8_dynamic_q_proj_decode"] = {
+                "shape": "N=K=4096, M=1,8,32,64 per step", "us_per_step": round(usd, 3),
+                "GB/s": round(bytesd / (usd * 1e-6) / 1e9, 1),
+                "frac_hbm": round(bytesd / (usd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "mode": "fp8_w_fp8_a from bf16 X (fp8q_linear_w8a8_dynamic): absmax kernel, then the "
+                        "decode GEMM casting X to E4M3 in registers; 2 launches per call",
+                "kernels": {str(m): fq.describe_linear(0, m, N, K) for m in DECODE_MS}}
+            log(rows["f1_w8a8_dynamic_q_proj_decode"])
+            del wspd
+
+            # per-group weight scales (groups of 128) on the same decode step
+            G = 128
+            wqg, wsg = fq.quantize_weight_grouped(up_bf16(w_bits), G)
+            pool_g = torch.empty((copies_n, N, K), dtype=torch.uint8, device=dev)
+            pool_g[:] = wqg.unsqueeze(0)
+            del wqg
+            wsng = {m: L.fp8q_linear_grouped_workspace_size(0, m, N, K, G) for m in DECODE_MS}
+            wspg = {m: (torch.zeros(wsng[m], dtype=torch.uint8, device=dev) if wsng[m] else None)
+                    for m in DECODE_MS}
+
+            def decode_step_g(i: int, stream: int):
+                for j, m in enumerate(DECODE_MS):
+                    c = (len(DECODE_MS) * i + j) % copies_n
+                    st = L.fp8q_linear_grouped(0, ptr(xs[m]), m, K, K, None, ptr(pool_g[c]), N, K,
+                                               ptr(wsg), G, ptr(ys[m]), N, ptr(wspg[m]), wsng[m],
+                                               stream)
+                    if st != 0:
+                        raise RuntimeError(_lib.last_error())
+            gg = torch.cuda.CUDAGraph()
+            sg = torch.cuda.Stream(device=dev)
+            sg.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.graph(gg, stream=sg, capture_error_mode="relaxed"):
+                h = torch.cuda.current_stream(dev).cuda_stream
+                for i in range(rot):
+                    decode_step_g(i, h)
+            torch.cuda.current_stream(dev).wait_stream(sg)
+            gg.replay()
+            torch.cuda.synchronize()
+            start.record()
+            gg.replay()
+            end.record()
+            end.synchronize()
+            usg = start.elapsed_time(end) * 1e3 / rot
+            bytes_g = sum(N * K + 4 * N * (K // G) + 2 * m * K + 2 * m * N for m in DECODE_MS)
+            rows["f4_grouped_q_proj_decode"] = {
+                "shape": "N=K=4096, M=1,8,32,64 per step, groups of 128", "us_per_step": round(usg, 3),
+                "GB/s": round(bytes_g / (usg * 1e-6) / 1e9, 1),
+                "frac_hbm": round(bytes_g / (usg * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "mode": "fp8_w_bf16_a with per-group weight scales",
+                "kernels": {str(m): fq.describe_linear(0, m, N, K, G) for m in DECODE_MS}}
+            log(rows["f4_grouped_q_proj_decode"])
+            del pool_g, gg
+            torch.cuda.empty_cache()
+        cpu = None if args.no_cpu_baseline else {}
+        if "tiny" in sections:
+            rows.update(tiny_rows(fq, L, up_bf16, ptr, workloads, torch, dev, cpu))
+        rows.update(other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev, cpu, sections))
         result["rows"] = rows
+        if cpu is not None:
+            for key in ("mlp_prefill", "down_prefill_70b"):
+                if key in cpu and f"a6a7_w8a8_{key}" in rows:
+                    g_us = rows[f"a6a7_w8a8_{key}"]["us"]
+                    cpu[key]["gpu_us_gemm"] = g_us
+                    cpu[key]["speedup_gemm_extrapolated"] = round(
+                        cpu[key]["gemm_full_s_extrapolated"] * 1e6 / g_us, 1)
+            result["cpu_oracle_by_config"] = {
+                "cores": cpu_threads(), "cpu_model": cpu_model(), "kind": "oracle",
+                "note": "the fp64 oracle as the tests use it, on this host's cores; quantization "
+                        "in full for every workload, the GEMM in full for Tiny, q_proj decode and "
+                        "the 70B layer, on 64 seeded rows for the prefill GEMMs (full size "
+                        "extrapolated linearly in M, labelled)",
+                **cpu}
 
     if args.copy_calibration:
         # a plain elementwise copy of known size (1 GiB read + 1 GiB written) whose
@@ -374,14 +432,22 @@ def main() -> int:
 
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, lin, w_bits, xs_bits, step_bytes)
+        result["cpu_baseline"] = cpu_baseline(wl, lin, w_bits, xs_bits, step_bytes,
+                                              args.cpu_seconds)
+        if "rows" in result and "cpu_oracle_by_config" in result:
+            result["cpu_oracle_by_config"]["q_proj_decode"] = {
+                "gemm_step_s": result["cpu_baseline"]["seconds_per_step"],
+                "quantize_weight_s": result["cpu_baseline"]["quantize_weight_s"],
+                "gpu_us_step": round(ms_per_step * 1e3, 3),
+                "speedup_gemm": round(result["cpu_baseline"]["seconds_per_step"] * 1e3 / ms_per_step, 1)}
 
     print(json.dumps(result), flush=True)
     return 0
 
 
 KERNEL_SOURCES = ("fp8_weight_quantized_amd/csrc/kernels/w8a16.hip",
-                  "fp8_weight_quantized_amd/csrc/kernels/device_common.hpp")
+                  "fp8_weight_quantized_amd/csrc/kernels/device_common.hpp",
+                  "fp8_weight_quantized_amd/csrc/kernels/e4m3_div.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_w8a16_q_proj_decode_hbm_traffic.txt")
 
 
@@ -456,6 +522,66 @@ def roofline_decode(per_m: dict, n: int, k: int) -> dict:
     }
 
 
+def cpu_threads() -> int:
+    """Threads the oracle's OpenMP loops use: the affinity mask, capped by
+    OMP_NUM_THREADS when that is set."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))
+    return cores
+
+
+def cpu_time(fn, min_s: float = 0.3, max_reps: int = 50) -> float:
+    """Seconds per call of fn() on the host: at least one call, repeated until
+    min_s has passed (or max_reps calls)."""
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s or reps >= max_reps:
+            return dt / reps
+
+
+def time_graph(torch, dev, calls, reps: int = 3) -> float:
+    """Average us per call of a list of no-argument launch functions (each takes
+    the stream handle), captured once into a HIP graph and replayed; the best
+    of `reps` replays after one untimed replay."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+        h = torch.cuda.current_stream(dev).cuda_stream
+        for c in calls:
+            c(h)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(reps):
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e3 / len(calls))
+    del g
+    return best
+
+
+def rotation_sets(nbytes_per_set: int) -> int:
+    """Input copies to rotate through so that every call finds its inputs
+    evicted from the 256 MB Infinity Cache: the other copies together exceed
+    it."""
+    return max(2, -(-MALL_BYTES // max(1, nbytes_per_set)) + 1)
+
+
 def time_eager(torch, fn, iters: int, warm: int = 2, warm_ms: float = 30.0) -> float:
     """Average ms per call of fn() over `iters` calls, HIP events on the current stream.
 
@@ -484,30 +610,43 @@ def time_eager(torch, fn, iters: int, warm: int = 2, warm_ms: float = 30.0) -> f
     return s.elapsed_time(e) / iters
 
 
-def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
+def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev, cpu, sections) -> dict:
+    """The rows besides the headline; `cpu` (a dict, or None to skip) collects
+    the oracle's timings on the same host inputs."""
     rows = {}
     iters = max(3, min(args.steps, 20))
     stream = lambda: torch.cuda.current_stream(dev).cuda_stream  # noqa: E731
 
-    # prefill: activation quantization + W8A8 GEMM
-    for key in ("mlp_prefill", "down_prefill_70b"):
+    # prefill: activation quantization + W8A8 GEMM.  Every timed call finds
+    # its inputs outside the Infinity Cache: calls rotate through copies of
+    # the inputs whose other copies together exceed its 256 MB.
+    for key in ("mlp_prefill", "down_prefill_70b") if "prefill" in sections else ():
         wl = workloads.WORKLOADS[key]
         lin = wl.linears[0]
         m = wl.ms[0]
+        n, k = lin.n, lin.k
         t0 = time.time()
         w_bits = workloads.weight(wl, lin)
         x_bits = workloads.activation(wl, m, lin.k)
         log(f"generated {key} inputs in {time.time() - t0:.1f}s")
+        if cpu is not None:
+            cpu[key] = cpu_prefill(key, w_bits, x_bits, m, n, k)
+            log("oracle", key, cpu[key])
         w = up_bf16(w_bits)
         x = up_bf16(x_bits)
         del w_bits, x_bits
         wq, ws = fq.quantize_weight(w)
         xq, xsc = fq.quantize_act(x)
-        y = torch.empty((m, lin.n), dtype=torch.bfloat16, device=dev)
-        n, k = lin.n, lin.k
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+        nset = rotation_sets(xq.numel() + wq.numel())
+        sets = [(xq, wq)] + [(xq.clone(), wq.clone()) for _ in range(nset - 1)]
+        ctr = [0]
 
         def gemm():
-            st = L.fp8q_linear(1, ptr(xq), m, k, xq.stride(0), ptr(xsc), ptr(wq), n, wq.stride(0),
+            xq_, wq_ = sets[ctr[0] % nset]
+            ctr[0] += 1
+            st = L.fp8q_linear(1, ptr(xq_), m, k, xq_.stride(0), ptr(xsc), ptr(wq_), n, wq_.stride(0),
                                ptr(ws), ptr(y), n, None, 0, stream())
             if st != 0:
                 raise RuntimeError(fq._lib.last_error())
@@ -516,15 +655,20 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
         tf = flops / (ms * 1e-3) / 1e12
         rows[f"a6a7_w8a8_{key}"] = {
             "shape": f"M={m} N={n} K={k}", "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
-            "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4), "kernel": fq.describe_linear(1, m, n, k)}
+            "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4), "kernel": fq.describe_linear(1, m, n, k),
+            "input_sets_rotated": nset}
         log(key, rows[f"a6a7_w8a8_{key}"])
+        del sets
 
         # the same GEMM with per-group weight scales (groups of 128)
         wqg, wsg = fq.quantize_weight_grouped(w, 128)
+        gsets = [(xq, wqg)] + [(xq.clone(), wqg.clone()) for _ in range(nset - 1)]
 
         def gemm_g():
-            st = L.fp8q_linear_grouped(1, ptr(xq), m, k, xq.stride(0), ptr(xsc), ptr(wqg), n,
-                                       wqg.stride(0), ptr(wsg), 128, ptr(y), n, None, 0, stream())
+            xq_, wq_ = gsets[ctr[0] % nset]
+            ctr[0] += 1
+            st = L.fp8q_linear_grouped(1, ptr(xq_), m, k, xq_.stride(0), ptr(xsc), ptr(wq_), n,
+                                       wq_.stride(0), ptr(wsg), 128, ptr(y), n, None, 0, stream())
             if st != 0:
                 raise RuntimeError(fq._lib.last_error())
         ms = time_eager(torch, gemm_g, iters)
@@ -532,16 +676,36 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
         rows[f"f4_grouped_w8a8_{key}"] = {
             "shape": f"M={m} N={n} K={k}, groups of 128", "us": round(ms * 1e3, 2),
             "TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
-            "kernel": fq.describe_linear(1, m, n, k, 128),
+            "kernel": fq.describe_linear(1, m, n, k, 128), "input_sets_rotated": nset,
             "note": "accumulators rescaled by s[g-1]/s[g] as each group opens"}
         log(key, rows[f"f4_grouped_w8a8_{key}"])
-        del wqg, wsg
+        del wqg, wsg, gsets
+
+        # weight quantization (offline in deployment; timed for completeness)
+        wqb = torch.empty((n, k), dtype=torch.uint8, device=dev)
+        wsb_ = torch.empty(n, dtype=torch.float32, device=dev)
+
+        def wquant():
+            st = L.fp8q_quantize_weight(ptr(w), n, k, k, ptr(wqb), k, ptr(wsb_), None, stream())
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+        ms = time_eager(torch, wquant, iters)
+        b = 3.0 * n * k + 4 * n
+        rows[f"a1a2_quantize_weight_{key}"] = {
+            "shape": f"N={n} K={k}", "us": round(ms * 1e3, 2),
+            "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(key, rows[f"a1a2_quantize_weight_{key}"])
+        del w, wqb, wsb_
 
         aws_n = L.fp8q_quantize_act_workspace_size(m, k)
         aws = torch.empty(aws_n, dtype=torch.uint8, device=dev)
+        aset = rotation_sets(x.numel() * 2 + xq.numel())
+        asets = [(x, xq)] + [(x.clone(), torch.empty_like(xq)) for _ in range(aset - 1)]
 
         def actq():
-            st = L.fp8q_quantize_act(ptr(x), m, k, k, ptr(xq), xq.stride(0), ptr(xsc), ptr(aws),
+            x_, q_ = asets[ctr[0] % aset]
+            ctr[0] += 1
+            st = L.fp8q_quantize_act(ptr(x_), m, k, k, ptr(q_), q_.stride(0), ptr(xsc), ptr(aws),
                                      aws_n, None, stream())
             if st != 0:
                 raise RuntimeError(fq._lib.last_error())
@@ -550,8 +714,30 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
         rows[f"a3a4_quantize_act_{key}"] = {
             "shape": f"M={m} K={k}", "us": round(ms * 1e3, 2),
             "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "note": "two kernels (absmax, cast); X is re-read by the cast"}
+            "input_sets_rotated": aset, "note": "two kernels (absmax, cast); X is re-read by the cast"}
         log(key, rows[f"a3a4_quantize_act_{key}"])
+
+        # the whole prefill linear from bf16 X: the dynamic fp8_w_fp8_a entry
+        # point (quantizer into its workspace, then the FP8 MFMA GEMM)
+        dws_n = L.fp8q_linear_w8a8_dynamic_workspace_size(m, n, k)
+        dws = torch.empty(dws_n, dtype=torch.uint8, device=dev)
+        dsets = [(x, wq)] + [(asets[i % aset][0], wq.clone()) for i in range(1, nset)]
+
+        def dyn():
+            x_, wq_ = dsets[ctr[0] % nset]
+            ctr[0] += 1
+            st = L.fp8q_linear_w8a8_dynamic(ptr(x_), m, k, k, ptr(wq_), n, wq_.stride(0), ptr(ws),
+                                            ptr(y), n, None, ptr(dws), dws_n, None, stream())
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+        ms = time_eager(torch, dyn, iters)
+        tf = flops / (ms * 1e-3) / 1e12
+        rows[f"a3a7_w8a8_dynamic_{key}"] = {
+            "shape": f"M={m} N={n} K={k}", "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+            "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4), "input_sets_rotated": nset,
+            "note": "fp8q_linear_w8a8_dynamic from bf16 X: absmax + cast + FP8 MFMA GEMM (3 kernels)"}
+        log(key, rows[f"a3a7_w8a8_dynamic_{key}"])
+        del dsets, dws
 
         # held (static) and EMA scales: one read of X per call
         held = xsc.clone()
@@ -561,13 +747,17 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
             raise RuntimeError(fq._lib.last_error())
 
         def actq_static():
-            st = L.fp8q_quantize_act_static(ptr(x), m, k, k, ptr(held), ptr(xq), xq.stride(0),
+            x_, q_ = asets[ctr[0] % aset]
+            ctr[0] += 1
+            st = L.fp8q_quantize_act_static(ptr(x_), m, k, k, ptr(held), ptr(q_), q_.stride(0),
                                             None, stream())
             if st != 0:
                 raise RuntimeError(fq._lib.last_error())
 
         def actq_ema():
-            st = L.fp8q_quantize_act_ema(ptr(x), m, k, k, ptr(xq), xq.stride(0), ptr(xsc),
+            x_, q_ = asets[ctr[0] % aset]
+            ctr[0] += 1
+            st = L.fp8q_quantize_act_ema(ptr(x_), m, k, k, ptr(q_), q_.stride(0), ptr(xsc),
                                          ptr(state), 0.9999, 0.1, 0, ptr(aws), aws_n, None,
                                          stream())
             if st != 0:
@@ -581,18 +771,54 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
             rows[f"f2_quantize_act_{name}_{key}"] = {
                 "shape": f"M={m} K={k}", "us": round(ms * 1e3, 2),
                 "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
-                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "note": note}
+                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "input_sets_rotated": aset, "note": note}
             log(key, rows[f"f2_quantize_act_{name}_{key}"])
-        del w, x, wq, ws, xq, y
+        del x, wq, ws, xq, y, asets
         torch.cuda.empty_cache()
 
+    if "layer" in sections:
+        rows.update(layer_rows(fq, L, up_bf16, ptr, workloads, torch, dev, cpu, iters, stream))
+    if "kv" in sections:
+        rows.update(kv_rows(fq, L, up_bf16, ptr, workloads, np, torch, dev, iters, stream))
+    return rows
+
+
+def layer_rows(fq, L, up_bf16, ptr, workloads, torch, dev, cpu, iters, stream) -> dict:
+    """The Llama-3-70B decoder layer's seven linears at decode M = 12
+    (W8A16), unfused, fused and with per-group scales, and the weight
+    quantization of its matrices."""
+    rows = {}
     # 70B decoder layer at decode M = 12 (W8A16), plus weight quantization of gate_proj
     wl = workloads.WORKLOADS["layer_decode_70b"]
     m = wl.ms[0]
     t0 = time.time()
     layer = []
+    wq_us = 0.0
+    cpu_layer = {"quantize_weight_s": 0.0, "gemm_s": 0.0} if cpu is not None else None
     for lin in wl.linears:
-        w = up_bf16(workloads.weight(wl, lin))
+        w_bits = workloads.weight(wl, lin)
+        x_bits = workloads.activation(wl, m, lin.k)
+        if cpu_layer is not None:
+            import oracle
+            oracle.build()
+            oq = {}
+            cpu_layer["quantize_weight_s"] += cpu_time(
+                lambda: oq.update(zip(("q", "s", "f"), oracle.quantize_weight(w_bits))), min_s=0.0)
+            cpu_layer["gemm_s"] += cpu_time(lambda: oracle.linear(0, x_bits, oq["q"], oq["s"]),
+                                            min_s=0.0)
+            del oq
+        w = up_bf16(w_bits)
+        del w_bits
+        qb = torch.empty((lin.n, lin.k), dtype=torch.uint8, device=dev)
+        sb = torch.empty(lin.n, dtype=torch.float32, device=dev)
+
+        def wq_one(w=w, q=qb, s=sb, lin=lin):
+            st = L.fp8q_quantize_weight(ptr(w), lin.n, lin.k, lin.k, ptr(q), lin.k, ptr(s), None, stream())
+            if st != 0:
+                raise RuntimeError(fq._lib.last_error())
+        wq_us += time_eager(torch, wq_one, 3) * 1e3
+        del qb, sb
         if lin.name == "gate_proj":
             q = torch.empty((lin.n, lin.k), dtype=torch.uint8, device=dev)
             s = torch.empty(lin.n, dtype=torch.float32, device=dev)
@@ -625,13 +851,24 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
             del sg_
         wq, ws = fq.quantize_weight(w)
         del w
-        x = up_bf16(workloads.activation(wl, m, lin.k))
+        x = up_bf16(x_bits)
+        del x_bits
         y = torch.empty((m, lin.n), dtype=torch.bfloat16, device=dev)
         nws = L.fp8q_linear_workspace_size(0, m, lin.n, lin.k)
         wsb = torch.zeros(nws, dtype=torch.uint8, device=dev) if nws else None
         layer.append((lin, wq, ws, x, y, wsb, nws))
     log(f"prepared 70B layer in {time.time() - t0:.1f}s")
     torch.cuda.empty_cache()
+    nel = sum(lin.n * lin.k for lin in wl.linears)
+    rows["a1a2_quantize_weight_layer_70b"] = {
+        "shape": "7 matrices, 855,638,016 weights", "us": round(wq_us, 2),
+        "GB/s": round((3.0 * nel) / (wq_us * 1e-6) / 1e9, 1),
+        "frac_hbm": round((3.0 * nel) / (wq_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "note": "sum of the seven matrices' quantization times"}
+    log(rows["a1a2_quantize_weight_layer_70b"])
+    if cpu_layer is not None:
+        cpu_layer["gpu_us"] = None       # filled in below from the layer step
+        cpu["layer_decode_70b"] = cpu_layer
 
     def layer_step(h):
         for lin, wq, ws, x, y, wsb, nws in layer:
@@ -734,11 +971,22 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev) -> dict:
     rows["a5_layer_decode_70b"] = {
         "shape": "7 linears, M=12", "weight_MB": round(b / 1e6, 1), "us": round(ms * 1e3, 2),
         "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "timing": "one HIP graph per layer step", "per_linear_eager": per}
+        "timing": "one HIP graph per layer step (856 MB of weights: no Infinity Cache reuse)",
+        "kernels": {lin.name: fq.describe_linear(0, m, lin.n, lin.k) for lin, *_ in layer},
+        "per_linear_eager": per,
+        "per_linear_eager_note": "one eager call after another on the same weights: host call "
+                                 "overhead included, and weights under 256 MB may be served "
+                                 "from the Infinity Cache (a latency figure, not an HBM one)"}
     log(rows["a5_layer_decode_70b"])
+    if cpu is not None and "layer_decode_70b" in cpu:
+        c = cpu["layer_decode_70b"]
+        c["gpu_us"] = {"gemm_step": round(ms * 1e3, 2), "quantize_weight": round(wq_us, 2)}
+        c["speedup_gemm"] = round(c["gemm_s"] * 1e6 / (ms * 1e3), 1)
+        c["quantize_weight_s"] = round(c["quantize_weight_s"], 3)
+        c["gemm_s"] = round(c["gemm_s"], 3)
+        c["sample"] = "all 7 matrices in full: quantization, and the fp64 GEMM at M=12"
     del layer
     torch.cuda.empty_cache()
-    rows.update(kv_rows(fq, L, up_bf16, ptr, workloads, np, torch, dev, iters, stream))
     return rows
 
 
@@ -815,32 +1063,100 @@ def kv_rows(fq, L, up_bf16, ptr, workloads, np, torch, dev, iters, stream) -> di
     return rows
 
 
-def cpu_baseline(wl, lin, w_bits, xs_bits, step_bytes) -> dict:
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, lin, w_bits, xs_bits, step_bytes, seconds: float = 10.0) -> dict:
     """The CPU oracle (unchanged, fp64) on one full decode step: the four
     q_proj calls M = 1, 8, 32, 64 on the oracle-quantized weight."""
     import oracle
     oracle.build()
+    t0 = time.perf_counter()
     wq, ws, _ = oracle.quantize_weight(w_bits)
+    tq = time.perf_counter() - t0
     reps = 0
     t0 = time.perf_counter()
-    while True:                         # repeat whole steps for about 10 s of CPU work
+    while True:                         # repeat whole steps for about `seconds` of CPU work
         for m in DECODE_MS:
             oracle.linear(0, xs_bits[m], wq, ws)
         reps += 1
-        if time.perf_counter() - t0 >= 10.0:
+        if time.perf_counter() - t0 >= seconds:
             break
     dt = (time.perf_counter() - t0) / reps
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    omp = os.environ.get("OMP_NUM_THREADS")
-    if omp and omp.isdigit():
-        cores = min(cores, int(omp))
-    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle", "seconds_per_step": round(dt, 3), "steps_timed": reps,
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle", "cpu_model": cpu_model(), "seconds_per_step": round(dt, 4),
+            "steps_timed": reps, "quantize_weight_s": round(tq, 4),
             "sample": f"{reps} full decode steps (q_proj W[4096,4096], M=1,8,32,64), fp64 oracle "
-                      "GEMM; weight quantization excluded as on the GPU side"}
+                      "GEMM; weight quantization timed once, apart"}
+
+
+def cpu_prefill(key, w_bits, x_bits, m, n, k) -> dict:
+    """The oracle on a prefill workload: weight and activation quantization in
+    full, and the fp64 W8A8 GEMM on 64 seeded rows x all N columns, with its
+    linear extrapolation to all M rows (labelled as such)."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    oq = {}
+    tw = cpu_time(lambda: oq.update(w=oracle.quantize_weight(w_bits)), min_s=0.0)
+    tx = cpu_time(lambda: oq.update(x=oracle.quantize_act(x_bits)), min_s=0.0)
+    rows = np.sort(np.random.default_rng(64).choice(m, 64, replace=False))
+    wq, ws, _ = oq["w"]
+    xq, xs, _ = oq["x"]
+    tg = cpu_time(lambda: oracle.linear(1, xq, wq, ws, xs, rows=rows), min_s=0.0)
+    return {"quantize_weight_s": round(tw, 3), "quantize_act_s": round(tx, 3),
+            "gemm_64_rows_s": round(tg, 3),
+            "gemm_full_s_extrapolated": round(tg * m / 64, 2),
+            "sample": f"M={m} N={n} K={k}: quantizers in full; GEMM measured on 64 seeded rows, "
+                      "full size extrapolated linearly in M"}
+
+
+def tiny_rows(fq, L, up_bf16, ptr, workloads, torch, dev, cpu) -> dict:
+    """The Tiny workload (W [256, 512], X [16, 512], seed 0): weight
+    quantization and the W8A16 linear, each as a HIP graph of 64 calls (both
+    are launch-bound), and the oracle on the same inputs."""
+    wl = workloads.WORKLOADS["tiny"]
+    lin = wl.linears[0]
+    m, n, k = wl.ms[0], lin.n, lin.k
+    w_bits = workloads.weight(wl, lin)
+    x_bits = workloads.activation(wl, m, k)
+    w, x = up_bf16(w_bits), up_bf16(x_bits)
+    q = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    sc = torch.empty(n, dtype=torch.float32, device=dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+    def tq(h):
+        if L.fp8q_quantize_weight(ptr(w), n, k, k, ptr(q), k, ptr(sc), None, h) != 0:
+            raise RuntimeError(fq._lib.last_error())
+
+    def tl(h):
+        if L.fp8q_linear(0, ptr(x), m, k, k, None, ptr(q), n, k, ptr(sc), ptr(y), n, None, 0, h) != 0:
+            raise RuntimeError(fq._lib.last_error())
+    tq(torch.cuda.current_stream(dev).cuda_stream)
+    us_q = time_graph(torch, dev, [tq] * 64)
+    us_l = time_graph(torch, dev, [tl] * 64)
+    row = {"shape": f"W[{n},{k}] X[{m},{k}] seed 0", "quantize_weight_us": round(us_q, 3),
+           "linear_us": round(us_l, 3), "linear_kernel": fq.describe_linear(0, m, n, k),
+           "timing": "HIP graph of 64 calls each; launch-bound (0.16 MB of data)"}
+    log("tiny", row)
+    if cpu is not None:
+        import oracle
+        oracle.build()
+        oq = {}
+        cq = cpu_time(lambda: oq.update(w=oracle.quantize_weight(w_bits)))
+        cl = cpu_time(lambda: oracle.linear(0, x_bits, oq["w"][0], oq["w"][1]))
+        cpu["tiny"] = {"quantize_weight_s": round(cq, 6), "gemm_s": round(cl, 6),
+                       "gpu_us": {"quantize_weight": row["quantize_weight_us"],
+                                  "gemm": row["linear_us"]},
+                       "sample": "the whole workload, repeated for at least 0.3 s"}
+    return {"tiny": row}
 
 
 if __name__ == "__main__":
