@@ -350,9 +350,10 @@ def main() -> int:
                 "shape": "N=K=4096, M=1,8,32,64 per step", "us_per_step": round(usd, 3),
                 "GB/s": round(bytesd / (usd * 1e-6) / 1e9, 1),
                 "frac_hbm": round(bytesd / (usd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "mode": "fp8_w_fp8_a from bf16 X (fp8q_linear_w8a8_dynamic): absmax kernel, then the "
-                        "decode GEMM casting X to E4M3 in registers; 2 launches per call",
-                "kernels": {str(m): fq.describe_linear(0, m, N, K) for m in DECODE_MS}}
+                "mode": "fp8_w_fp8_a from bf16 X (fp8q_linear_w8a8_dynamic): up to 16 rows the "
+                        "absmax kernel, then the decode GEMM casting X to E4M3 in registers (2 "
+                        "launches); 17-64 rows the quantizer, then the GEMM on the codes",
+                "kernels": {str(m): fq.describe_linear(1, m, N, K, dynamic=True) for m in DECODE_MS}}
             log(rows["f1_w8a8_dynamic_q_proj_decode"])
             del wspd
 

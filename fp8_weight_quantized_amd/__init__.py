@@ -331,9 +331,14 @@ def cast_f32_to_e4m3(x: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def describe_linear(mode: int, m: int, n: int, k: int, group: int | None = None) -> str:
+def describe_linear(mode: int, m: int, n: int, k: int, group: int | None = None,
+                    dynamic: bool = False) -> str:
+    """The kernels a linear call of these sizes launches (dynamic=True: the
+    fp8_w_fp8_a entry point that quantizes bf16 activations itself)."""
     buf = ctypes.create_string_buffer(256)
-    if group is None:
+    if dynamic:
+        check(_lib.lib().fp8q_linear_w8a8_dynamic_describe(m, n, k, buf, 256))
+    elif group is None:
         check(_lib.lib().fp8q_linear_describe(mode, m, n, k, buf, 256))
     else:
         check(_lib.lib().fp8q_linear_grouped_describe(mode, m, n, k, group, buf, 256))

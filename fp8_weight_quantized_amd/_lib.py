@@ -58,6 +58,7 @@ SIGNATURES = {
     "fp8q_linear_w8a8_dynamic_workspace_size": (SZ, [I64, I64, I64]),
     "fp8q_linear_w8a8_dynamic": (ST, [P, I64, I64, I64, P, I64, I64, P, P, I64, P, P, SZ, P, P]),
     "fp8q_linear_describe": (ST, [ST, I64, I64, I64, ctypes.c_char_p, SZ]),
+    "fp8q_linear_w8a8_dynamic_describe": (ST, [I64, I64, I64, ctypes.c_char_p, SZ]),
     "fp8q_linear_grouped_describe": (ST, [ST, I64, I64, I64, I64, ctypes.c_char_p, SZ]),
 }
 

@@ -564,13 +564,21 @@ fp8q_status fp8q_linear(fp8q_mode mode,
 
 namespace {
 
+// Up to this many rows fp8q_linear_w8a8_dynamic casts the activations inside
+// the GEMM.  Every workgroup casts the activation rows it reads, and with 17..64
+// rows each row is read by a whole column of 128-256 workgroups: one separate
+// cast is then cheaper (measured on MI355X, Llama-3-8B q_proj in graphs: M = 32
+// 36 us cast in the GEMM against 20 us for the quantizer + the GEMM on codes).
+constexpr int64_t kDynamicFusedMaxM = 16;
+
 // Workspace of fp8q_linear_w8a8_dynamic: [0, 256) the scale slot (used when the
-// caller passes no x_scale_out), then the absmax pass's maxima, then either
-// the decode plan's partial tiles (m <= 64) or the E4M3 codes [m, ldq] of the
-// activations (m > 64).
+// caller passes no x_scale_out), then the absmax pass's maxima, then the
+// decode plan's partial tiles (m <= 16), or the E4M3 codes [m, ldq] of the
+// activations followed by the GEMM's scratch.
 struct DynLayout {
-    size_t part_off, part_bytes, rest_off, total;
+    size_t part_off, part_bytes, rest_off, total, codes_bytes;
     int64_t ldq;
+    bool fused;
 };
 
 DynLayout dyn_layout(int64_t m, int64_t n, int64_t k)
@@ -580,12 +588,18 @@ DynLayout dyn_layout(int64_t m, int64_t n, int64_t k)
     l.part_bytes = round_up((size_t)fp8q::launch::act_blocks(m, k) * sizeof(uint32_t), 256);
     l.rest_off = l.part_off + l.part_bytes;
     l.ldq = (k + 15) / 16 * 16;
+    l.fused = m <= kDynamicFusedMaxM;
     size_t rest;
-    if (m <= kW8A8DecodeMaxM)
+    if (l.fused) {
         rest = round_up(fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActQ).workspace, 256);
-    else
-        rest = round_up((size_t)m * (size_t)l.ldq, 256) +
-               round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
+    } else {
+        l.codes_bytes = round_up((size_t)m * (size_t)l.ldq, 256);
+        rest = l.codes_bytes +
+               round_up(m <= kW8A8DecodeMaxM
+                            ? fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActF8).workspace
+                            : fp8q::launch::plan_w8a8(m, n, k).workspace,
+                        256);
+    }
     l.total = l.rest_off + rest;
     return l;
 }
@@ -651,7 +665,7 @@ fp8q_status fp8q_linear_w8a8_dynamic(const uint16_t *x_bf16, int64_t m, int64_t 
     uint32_t *part = reinterpret_cast<uint32_t *>(ws + lay.part_off);
     void *rest = ws + lay.rest_off;
     hipError_t e;
-    if (m <= kW8A8DecodeMaxM) {
+    if (lay.fused) {
         e = fp8q::launch::act_amax(x_bf16, m, k, ld_x, part, stream);
         if (e == hipSuccess)
             e = fp8q::launch::w8a16_quant_act(
@@ -660,9 +674,14 @@ fp8q_status fp8q_linear_w8a8_dynamic(const uint16_t *x_bf16, int64_t m, int64_t 
                 w_scale, y_bf16, ld_y, rest, stream);
     } else {
         uint8_t *codes = static_cast<uint8_t *>(rest);
+        void *gemm_ws = static_cast<uint8_t *>(rest) + lay.codes_bytes;
         e = fp8q::launch::quantize_act(x_bf16, m, k, ld_x, codes, lay.ldq, scale, part,
                                        nonfinite_flag, stream);
-        if (e == hipSuccess)
+        if (e == hipSuccess && m <= kW8A8DecodeMaxM)
+            e = fp8q::launch::w8a16(fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActF8),
+                                    fp8q::launch::kW8A16ActF8, codes, m, k, lay.ldq, scale, w_fp8,
+                                    n, ld_w, w_scale, y_bf16, ld_y, gemm_ws, stream);
+        else if (e == hipSuccess)
             e = fp8q::launch::w8a8(fp8q::launch::plan_w8a8(m, n, k), codes, m, k, lay.ldq, scale,
                                    w_fp8, n, ld_w, w_scale, y_bf16, ld_y, stream);
     }
@@ -784,9 +803,10 @@ void describe_w8a16(const fp8q::launch::W8A16Plan &p, char *buf, size_t len)
     if (p.group > 0)
         std::snprintf(spg, sizeof spg, ", %lld", (long long)(p.group / 64));
     if (p.kind == fp8q::launch::W8A16Plan::kPanel)
-        std::snprintf(buf, len, "k_w8a16_panel<%d, %d, %d, %d, %d> grid=(%lld,%lld) block=%d splits=1",
+        std::snprintf(buf, len,
+                      "k_w8a16_panel<%d, %d, %d, %d, %d> grid=(%lld,%lld) block=%d staged_rows=%d splits=1",
                       p.af, p.mb, p.steps, p.depth, p.waves, (long long)p.grid_n,
-                      (long long)p.grid_m, 64 * p.waves);
+                      (long long)p.grid_m, 64 * p.waves, p.xd);
     else if (p.kind == fp8q::launch::W8A16Plan::kRows)
         std::snprintf(buf, len,
                       "k_w8a16_rows<%d, %d, %d, %d%s> rows=%d grid=(%lld,%lld,%lld) block=%d "
@@ -828,6 +848,29 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
         describe_w8a8(m, n, k, false, buf, len);
     else
         describe_w8a16(fp8q::launch::plan_w8a16(m, n, k, act_type(mode)), buf, len);
+    return ok();
+}
+
+fp8q_status fp8q_linear_w8a8_dynamic_describe(int64_t m, int64_t n, int64_t k, char *buf,
+                                              size_t len)
+{
+    if (buf == nullptr || len == 0)
+        return fail(FP8Q_ERR_INVALID_ARG, "buf is NULL or empty");
+    if (m < 0 || n < 0 || k < 1)
+        return fail(FP8Q_ERR_INVALID_ARG, "bad sizes");
+    if (m > kW8A8DecodeMaxM) {
+        char g[192];
+        describe_w8a8(m, n, k, false, g, sizeof g);
+        std::snprintf(buf, len, "k_act_amax + k_act_cast<0> + %s", g);
+    } else if (m > kDynamicFusedMaxM) {
+        char g[224];
+        describe_w8a16(fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActF8), g, sizeof g);
+        std::snprintf(buf, len, "k_act_amax + k_act_cast<0> + %s (E4M3 codes)", g);
+    } else {
+        char g[224];
+        describe_w8a16(fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActQ), g, sizeof g);
+        std::snprintf(buf, len, "k_act_amax + %s (activations cast in registers)", g);
+    }
     return ok();
 }
 

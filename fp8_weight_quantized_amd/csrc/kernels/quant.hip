@@ -545,10 +545,13 @@ hipError_t quantize_weight_grouped(const uint16_t *w, int64_t n, int64_t k, int6
     return hipGetLastError();
 }
 
+// Blocks of the activation passes: about two 16-byte chunks per thread up to
+// kActMaxBlocks blocks (a decode-sized tensor then spreads over tens of CUs
+// instead of one or two), more per thread beyond.
 int act_blocks(int64_t m, int64_t k)
 {
     const int64_t chunks = m * div_up(k, 8);
-    int64_t g = div_up(chunks, (int64_t)kThreads * 8);
+    int64_t g = div_up(chunks, (int64_t)kThreads * 2);
     if (g < 1)
         g = 1;
     if (g > kActMaxBlocks)

@@ -902,21 +902,34 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 // this kernel only for K a multiple of NWV * 64 * CS with at least D chunks
 // per wave.  Rows past N or M are clamped to a valid row when loading and their
 // outputs are never stored.
-template <int AF, int MB, int CS, int D, int NWV, int AT>
+//
+// XS: activation rows staged per chunk (the panel's first XS rows; the host
+// plans XS >= the rows that exist).  Staging fewer rows than the panel has
+// saves loads and, with activations quantized on the fly, the casts of rows
+// that only feed output columns that are never stored; the LDS rows past XS
+// are zeroed once.
+//
+// E4M3 activation codes (kActF8) are loaded 16 codes per lane and widened
+// exactly to bf16 as they are written to LDS (each loaded unit fills two
+// staged units); x_scale is then the activation scale.
+template <int AF, int MB, int CS, int D, int NWV, int AT, int XS = 16 * MB>
 __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const void *__restrict__ xv, int64_t m, int64_t k, int64_t ld_x,
+    const float *__restrict__ x_scale,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y, QuantArgs qa)
 {
-    static_assert(AT == kActBF16 || AT == kActF16 || AT == kActQ, "16-bit activations in memory");
+    constexpr bool F8 = AT == kActF8;
     constexpr int CT = compute_type<AT>();
+    constexpr int ES = F8 ? 1 : 2;              // bytes per activation value in memory
     constexpr int XR = 16 * MB;                 // activation rows of the panel
     constexpr int CK = 64 * CS;                 // k per chunk
-    constexpr int RU = CK * 2 / 16;             // 16-byte units of a staged row segment
+    constexpr int RU = CK * 2 / 16;             // 16-byte units of a staged (bf16) row segment
     constexpr int RB = 16 * RU;                 // bytes of a staged row segment
-    constexpr int NI = XR * RU / kWave;         // activation loads per lane per chunk
+    constexpr int XU = CK * ES / 16;            // 16-byte units loaded per row segment
+    constexpr int NI = XS * XU / kWave;         // activation loads per lane per chunk
     constexpr int LC = NI + CS * AF;            // loads per lane per chunk
-    static_assert(RU % 16 == 0 && (XR * RU) % kWave == 0, "chunk shape");
+    static_assert(RU % 16 == 0 && (XS * XU) % kWave == 0 && XS <= XR && XS > 0, "chunk shape");
     static_assert(D >= 1 && D <= 4, "chunks in flight");
     // the waves' staging slots; after the K loop the same bytes hold the
     // waves' fp32 panels for the reduction
@@ -934,7 +947,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const int64_t kb = (int64_t)wave * kq;
     const int nch = (int)(kq / CK);
     uint8_t *slot = xl + wave * SLOT;
-    const float xs = act_scale<AT>(nullptr, qa);
+    const float xs = act_scale<AT>(x_scale, qa);
     const E4M3Div div(AT == kActQ ? xs : 1.0f);
 
     const uint8_t *wp[AF];
@@ -942,16 +955,25 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     for (int a = 0; a < AF; ++a)
         wp[a] = w + min(n0 + 16 * a + r, n - 1) * ld_w + kb + 16 * g;
     // activation load i of a chunk: unit f = 64 i + lane of the chunk's
-    // XR x RU units, i.e. row f / RU, 16-byte unit f % RU of that row
+    // XS x XU loaded units, i.e. row f / XU, 16-byte unit f % XU of that row;
+    // its staged (bf16) unit is the same one, or units 2u and 2u + 1 for codes
     const uint8_t *x8 = static_cast<const uint8_t *>(xv);
     const uint8_t *xp[NI];
-    int xo[NI];                       // LDS byte offset of that unit, swizzled
+    int xo[NI], xo2[NI];              // LDS byte offsets of the staged unit(s), swizzled
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int f = kWave * i + lane;
-        const int rho = f / RU, u = f % RU;
-        xp[i] = x8 + (min(m0 + rho, m - 1) * ld_x + kb) * 2 + 16 * u;
-        xo[i] = rho * RB + 16 * (u ^ (rho & 15));
+        const int rho = f / XU, u = f % XU;
+        xp[i] = x8 + (min(m0 + rho, m - 1) * ld_x + kb) * ES + 16 * u;
+        const int su = F8 ? 2 * u : u;
+        xo[i] = rho * RB + 16 * (su ^ (rho & 15));
+        xo2[i] = rho * RB + 16 * ((su + 1) ^ (rho & 15));
+    }
+
+    if constexpr (XS < XR) {
+#pragma unroll
+        for (int o = XS * RB + 16 * lane; o < XR * RB; o += 16 * kWave)
+            *reinterpret_cast<v4u *>(slot + o) = v4u{0u, 0u, 0u, 0u};
     }
 
     v4u xr[D][NI];
@@ -966,7 +988,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     auto issue_x = [&](int u, int c) {
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            xr[u][i] = ldg(xp[i] + (int64_t)c * CK * 2);
+            xr[u][i] = ldg(xp[i] + (int64_t)c * CK * ES);
     };
     auto issue_w = [&](int u, int c) {
 #pragma unroll
@@ -1023,9 +1045,18 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
                 // this wave's slot: the previous chunk's reads were consumed
                 // by its MFMAs; LDS operations of one wave run in order
 #pragma unroll
-                for (int i = 0; i < NI; ++i)
-                    *reinterpret_cast<v4u *>(slot + xo[i]) =
-                        AT == kActQ ? qdq8(xr[u][i], div) : xr[u][i];
+                for (int i = 0; i < NI; ++i) {
+                    if constexpr (F8) {
+                        const v4u c = xr[u][i];
+                        const uint2 p0 = e4m3x4_to_bf16(c.x), p1 = e4m3x4_to_bf16(c.y);
+                        const uint2 p2 = e4m3x4_to_bf16(c.z), p3 = e4m3x4_to_bf16(c.w);
+                        *reinterpret_cast<v4u *>(slot + xo[i]) = v4u{p0.x, p0.y, p1.x, p1.y};
+                        *reinterpret_cast<v4u *>(slot + xo2[i]) = v4u{p2.x, p2.y, p3.x, p3.y};
+                    } else {
+                        *reinterpret_cast<v4u *>(slot + xo[i]) =
+                            AT == kActQ ? qdq8(xr[u][i], div) : xr[u][i];
+                    }
+                }
                 const bool more = c + D < nch;
                 if (more)
                     issue_x(u, c + D);
@@ -1202,13 +1233,6 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
     p.splits = 1;
     p.workspace = 0;
     p.ldp = div_up(n, 4) * 4;
-    // 17..64 activation rows with 16-bit activations in memory: one launch
-    // of k_w8a16_panel (panels of 32 activation rows x 16 weight rows, or
-    // x 32 above 32 activation rows, whole K per workgroup, no partial sums)
-    // where that makes about one workgroup per CU.  Measured on MI355X on the
-    // Llama-3-8B q_proj (N = K = 4096), in graphs: M = 32 9.9 us against
-    // 10.3 us for the split tile kernel + reduce, M = 64 11.9 us against
-    // 13.7 us.
     // Up to 16 activation rows on a wide weight (N >= 8192) with K < 16K: the
     // panel kernel with one activation group and AF = 2, 3, 4 or 7 weight
     // fragments per workgroup, the AF whose grid is closest to whole waves of
@@ -1220,6 +1244,27 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
     // gate_up [28672, 4096] 26.2 against 28.9 us; AF = 8 (224 workgroups)
     // measured 53.1 us on gate/up.  A long K (the 70B down_proj, 28672)
     // stays on the split tile kernel (51.4 us against 57.7 us).
+    // bf16 activations cast to E4M3 on the fly, up to 16 rows on a weight of
+    // 2048..8191 rows: the panel kernel with one weight fragment, staging (and
+    // casting) only the rows that exist.  Every workgroup casts the
+    // activations it reads, so the rows kernel -- which loads 16 rows per
+    // MFMA operand whatever M is -- would cast up to 16 times more values.
+    if (act == kW8A16ActQ && m <= 16 && n >= 2048 && n < 8192 && k % 512 == 0 && k >= 2048 &&
+        k < 16384) {
+        p.kind = W8A16Plan::kPanel;
+        p.af = 1;
+        p.mb = 1;
+        p.xd = m <= 4 ? 4 : m <= 8 ? 8 : 16;
+        p.rows = 16;
+        p.waves = 4;
+        p.steps = 2;
+        p.depth = 3;
+        p.grid_n = div_up(n, 16);
+        p.grid_m = 1;
+        p.kper = k;
+        p.kchunk = k / 4;
+        return p;
+    }
     if (act != kW8A16ActF8 && m <= 16 && n >= 8192 && k % 512 == 0 && k >= 2048 && k < 16384) {
         static const int kAf[4] = {2, 3, 4, 7};
         int best = 0;
@@ -1239,19 +1284,29 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
         p.waves = 4;
         p.steps = 2;
         p.depth = 3;
+        // activations cast on the fly: stage only the rows that exist (4, 8 or 16)
+        p.xd = act == kW8A16ActQ ? (m <= 4 ? 4 : m <= 8 ? 8 : 16) : 16;
         p.grid_n = div_up(n, 16 * p.af);
         p.grid_m = 1;
         p.kper = k;
         p.kchunk = k / 4;
         return p;
     }
-    if (act != kW8A16ActF8 && m > 16 && m <= 64 && k % 1024 == 0 && k >= 2048) {
+    // 17..64 activation rows: one launch of k_w8a16_panel (panels of 32
+    // activation rows x 16 weight rows, or x 32 above 32 activation rows,
+    // whole K per workgroup, no partial sums) where that makes about one
+    // workgroup per CU.  Measured on MI355X on the Llama-3-8B q_proj (N = K =
+    // 4096), in graphs: M = 32 9.9 us against 10.3 us for the split tile
+    // kernel + reduce, M = 64 11.9 us against 13.7 us.  E4M3 activation codes
+    // take it too (widened to bf16 as they are staged).
+    if (m > 16 && m <= 64 && k % 1024 == 0 && k >= 2048) {
         const int af = m > 32 ? 2 : 1;
         const int64_t gn = div_up(n, 16 * af), gm = div_up(m, 32);
         if (gn * gm >= 192 && gn * gm <= 320) {
             p.kind = W8A16Plan::kPanel;
             p.af = af;
             p.mb = 2;
+            p.xd = 32;
             p.rows = 16 * af;
             p.waves = 4;
             p.steps = 4;
@@ -1430,14 +1485,15 @@ static void launch_tile(const W8A16Plan &p, const void *x, int64_t m, int64_t k,
 // k_w8a16_panel, 4 waves.  32 activation rows: chunks of 4 x 64 k, 2 in
 // flight (the measured best on the Llama-3-8B q_proj decode shapes); 16
 // activation rows: chunks of 2 x 64 k, 3 in flight (Llama-3-70B shapes).
-template <int AF, int MB, int CS, int D, int AT>
+template <int AF, int MB, int CS, int D, int AT, int XS = 16 * MB>
 static void launch_panel(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
-                         const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
-                         uint16_t *y, int64_t ld_y, const QuantArgs &qa, hipStream_t stream)
+                         const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
+                         const float *w_scale, uint16_t *y, int64_t ld_y, const QuantArgs &qa,
+                         hipStream_t stream)
 {
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
-    hipLaunchKernelGGL((k_w8a16_panel<AF, MB, CS, D, 4, AT>), grid, dim3(4 * kWave), 0, stream, x,
-                       m, k, ld_x, w, n, ld_w, w_scale, y, ld_y, qa);
+    hipLaunchKernelGGL((k_w8a16_panel<AF, MB, CS, D, 4, AT, XS>), grid, dim3(4 * kWave), 0, stream,
+                       x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, qa);
 }
 
 template <int AT>
@@ -1448,19 +1504,34 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
 {
     float *partial = static_cast<float *>(workspace);
     if (p.group == 0 && p.kind == W8A16Plan::kPanel) {
-        if constexpr (AT != kActF8) {
-#define FP8Q_PANEL_CASE(AF, MB, CS, D)                                                        \
-            if (p.af == AF && p.mb == MB && p.steps == CS && p.depth == D && p.waves == 4) {    \
-                launch_panel<AF, MB, CS, D, AT>(p, x, m, k, ld_x, w, n, ld_w, w_scale, y, ld_y,  \
-                                                qa, stream);                                  \
+#define FP8Q_PANEL_CASE(AF, MB, CS, D, XS)                                                    \
+            if (p.af == AF && p.mb == MB && p.steps == CS && p.depth == D && p.waves == 4 &&    \
+                p.xd == XS) {                                                                 \
+                launch_panel<AF, MB, CS, D, AT, XS>(p, x, m, k, ld_x, x_scale, w, n, ld_w,       \
+                                                    w_scale, y, ld_y, qa, stream);            \
                 return hipGetLastError();                                                     \
             }
-            FP8Q_PANEL_CASE(1, 2, 4, 2)
-            FP8Q_PANEL_CASE(2, 2, 4, 2)
-            FP8Q_PANEL_CASE(2, 1, 2, 3)
-            FP8Q_PANEL_CASE(3, 1, 2, 3)
-            FP8Q_PANEL_CASE(4, 1, 2, 3)
-            FP8Q_PANEL_CASE(7, 1, 2, 3)
+        FP8Q_PANEL_CASE(1, 2, 4, 2, 32)
+        FP8Q_PANEL_CASE(2, 2, 4, 2, 32)
+        if constexpr (AT != kActF8) {
+            FP8Q_PANEL_CASE(2, 1, 2, 3, 16)
+            FP8Q_PANEL_CASE(3, 1, 2, 3, 16)
+            FP8Q_PANEL_CASE(4, 1, 2, 3, 16)
+            FP8Q_PANEL_CASE(7, 1, 2, 3, 16)
+            if constexpr (AT == kActQ) {
+                // activations cast on the fly: stage (and cast) only the rows that exist
+                FP8Q_PANEL_CASE(1, 1, 2, 3, 4)
+                FP8Q_PANEL_CASE(1, 1, 2, 3, 8)
+                FP8Q_PANEL_CASE(1, 1, 2, 3, 16)
+                FP8Q_PANEL_CASE(2, 1, 2, 3, 4)
+                FP8Q_PANEL_CASE(2, 1, 2, 3, 8)
+                FP8Q_PANEL_CASE(3, 1, 2, 3, 4)
+                FP8Q_PANEL_CASE(3, 1, 2, 3, 8)
+                FP8Q_PANEL_CASE(4, 1, 2, 3, 4)
+                FP8Q_PANEL_CASE(4, 1, 2, 3, 8)
+                FP8Q_PANEL_CASE(7, 1, 2, 3, 4)
+                FP8Q_PANEL_CASE(7, 1, 2, 3, 8)
+            }
 #undef FP8Q_PANEL_CASE
         }
     } else if (p.group == 0 && p.kind == W8A16Plan::kRows) {

@@ -305,11 +305,13 @@ fp8q_status fp8q_linear_noalloc(fp8q_mode mode,
  * i.e. fp8q_quantize_act followed by fp8q_linear(FP8Q_W8A8, ...): the codes and
  * the scale are bit for bit those of fp8q_quantize_act, the sums are exact
  * products accumulated in fp32 (tolerance and determinism as fp8q_linear).
- * Up to 64 activation rows (decode) this is two kernels: the absmax pass, then
+ * Up to 16 activation rows (decode) this is two kernels: the absmax pass, then
  * the decode GEMM, whose workgroups fold the pass's maxima into s_x and cast
  * the activations they load in registers, so the E4M3 activations never go
- * through memory.  More rows run fp8q_quantize_act into the workspace and the
- * FP8 MFMA GEMM (three kernels).
+ * through memory.  More rows run fp8q_quantize_act into the workspace, then
+ * the GEMM on the codes (the decode kernels up to 64 rows, the FP8 MFMA GEMM
+ * beyond): every GEMM workgroup casts the rows it reads, and from 17 rows on
+ * a whole column of workgroups reads each row, so one separate cast is cheaper.
  *
  *   x_bf16       [m, k] bf16, ld_x >= k, ld_x % 8 == 0, 16-byte aligned
  *   w_fp8, w_scale, y_bf16, ld_*   as fp8q_linear
@@ -370,6 +372,14 @@ fp8q_status fp8q_cast_f32_to_e4m3(const float *x, int64_t count, uint8_t *out, h
  */
 fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
                                  char *buf, size_t len);
+
+/*
+ * The same for fp8q_linear_w8a8_dynamic (the absmax pass, then the GEMM that
+ * casts the activations, or the quantizer and the FP8 MFMA GEMM above 64
+ * rows).  Host-only; launches nothing.
+ */
+fp8q_status fp8q_linear_w8a8_dynamic_describe(int64_t m, int64_t n, int64_t k, char *buf,
+                                              size_t len);
 
 /*
  * The same for fp8q_linear_grouped with this group (64, 128, 256 or 512; any

@@ -53,7 +53,8 @@ def test_workspace_queries(L):
     # rows W8A8 runs the decode kernels and their K-split scratch
     assert L.fp8q_linear_workspace_size(1, 8192, 28672, 4096) == 0
     assert L.fp8q_linear_workspace_size(1, 65, 4096, 4096) == 0
-    assert L.fp8q_linear_workspace_size(1, 64, 4096, 4096) == 4 * 64 * 4096 * 4
+    assert L.fp8q_linear_workspace_size(1, 64, 4096, 4096) == 0         # the panel kernel
+    assert L.fp8q_linear_workspace_size(1, 64, 1024, 4096) == 4 * 64 * 1024 * 4
     assert L.fp8q_linear_workspace_size(1, 1, 4096, 4096) == 0
     # W8A16, up to 16 activation rows on a weight of up to 4096 rows: the rows
     # kernel, one launch, no scratch
@@ -89,7 +90,8 @@ def test_workspace_queries(L):
     # dynamic W8A8: a 256-byte scale slot, the absmax maxima (rounded to 256
     # bytes), then the decode plan's partial tiles, or the E4M3 codes above 64 rows
     assert L.fp8q_linear_w8a8_dynamic_workspace_size(1, 4096, 4096) == 256 + 256
-    assert L.fp8q_linear_w8a8_dynamic_workspace_size(64, 4096, 4096) == 256 + 256
+    # 17..64 rows: the codes [m, k rounded to 16] and the panel GEMM (no scratch)
+    assert L.fp8q_linear_w8a8_dynamic_workspace_size(64, 4096, 4096) == 256 + 256 + 64 * 4096
     assert L.fp8q_linear_w8a8_dynamic_workspace_size(12, 1022, 8192) == 256 + 256 + 4 * 12 * 1024 * 4
     assert L.fp8q_linear_w8a8_dynamic_workspace_size(8192, 28672, 4096) == 256 + 4096 + 8192 * 4096
     assert L.fp8q_linear_w8a8_dynamic_workspace_size(100, 300, 13) == 256 + 256 + 100 * 16 + 256 - 100 * 16 % 256
@@ -133,6 +135,8 @@ def test_describe(L):
     assert L.fp8q_linear_describe(0, 32, 4096, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_panel<1, 2, 4, 2, 4>") and b"grid=(256,1)" in buf.value
     assert L.fp8q_linear_describe(1, 64, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<2, 2, 4, 2, 4>")
+    assert L.fp8q_linear_describe(1, 64, 1024, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_tile<4, 16, 8>")
     assert b"splits=4" in buf.value and b"k_w8a16_reduce" in buf.value
     assert L.fp8q_linear_describe(1, 8192, 28672, 4096, buf, 256) == 0

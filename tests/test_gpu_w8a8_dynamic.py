@@ -48,12 +48,14 @@ def run_dynamic(fq, x_bits, wq, ws):
     return host_bf16_as_f64(y), np.float32(s.cpu().numpy()[0])
 
 
-# (m, n, k, the decode kernel it takes, or None above 64 rows)
-SHAPES = [(1, 4096, 4096, "k_w8a16_rows"), (8, 4096, 4096, "k_w8a16_rows"),
+# (m, n, k, the GEMM kernel it takes after the absmax pass)
+SHAPES = [(1, 4096, 4096, "k_w8a16_panel"), (8, 4096, 4096, "k_w8a16_panel"),
           (12, 1024, 8192, "k_w8a16_rows"), (5, 256, 1000, "k_w8a16_tile"),
-          (16, 28672, 512, "k_w8a16_tile"), (32, 4096, 4096, "k_w8a16_panel"),
-          (64, 4096, 4096, "k_w8a16_panel"), (40, 300, 3000, "k_w8a16_tile"),
-          (3, 100, 13, "k_w8a16"), (65, 520, 1000, None), (300, 256, 4096, None)]
+          (16, 28672, 512, "k_w8a16_tile"), (32, 4096, 4096, "k_act_cast<0> + k_w8a16_panel"),
+          (64, 4096, 4096, "k_act_cast<0> + k_w8a16_panel"), (40, 300, 3000, "k_w8a16_tile"),
+          (3, 100, 13, "k_w8a16"), (12, 8192, 8192, "k_w8a16_panel"),
+          (2, 28672, 2048, "k_w8a16_panel"), (13, 3000, 2560, "k_w8a16_panel"),
+          (65, 520, 1000, "k_w8a8"), (300, 256, 4096, "k_w8a8")]
 
 
 @pytest.mark.parametrize("m,n,k,kern", SHAPES)
@@ -62,16 +64,19 @@ def test_dynamic_matches_quantize_then_linear(fq, orc, m, n, k, kern):
     x = workloads.outlier_act(m, k, 910 + k)
     wq, ws, _ = orc.quantize_weight(w)
     oxq, oxs, _ = orc.quantize_act(x)
-    if kern is not None:
-        assert fq.describe_linear(0, m, n, k).startswith(kern), fq.describe_linear(0, m, n, k)
-    say("w8a8 dynamic", m, n, k, kern)
+    desc = fq.describe_linear(1, m, n, k, dynamic=True)
+    assert kern in desc, desc
+    say("w8a8 dynamic", m, n, k, desc)
     y, s = run_dynamic(fq, x, wq, ws)
     assert s.view(np.uint32) == np.float32(oxs).view(np.uint32), (s, oxs)
     assert_gemm_close(y, orc.linear(1, oxq, wq, ws, oxs), f"dynamic {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m,n,k", [(4, 512, 512), (12, 1024, 8192), (5, 256, 1024),
-                                   (40, 4096, 2048), (20, 3200, 3072), (64, 4096, 4096)])
+                                   (40, 4096, 2048), (20, 3200, 3072), (64, 4096, 4096),
+                                   # the panel kernel staging 4, 8 and 16 rows
+                                   (3, 4096, 2048), (7, 2048, 2048), (12, 8192, 2048),
+                                   (2, 28672, 2048)])
 def test_dynamic_codes_exact(fq, orc, m, n, k):
     """One-hot weight rows (code 1.0 at column p_n, scale 1) make
     Y[i, n] = s_x * dec(q(X[i, p_n])); with max|X| = 448 the scale is exactly 1,
@@ -92,7 +97,7 @@ def test_dynamic_codes_exact(fq, orc, m, n, k):
     ws = np.ones(n, np.float32)
     oxq, oxs, _ = orc.quantize_act(x)
     assert oxs == np.float32(1.0)
-    say("w8a8 dynamic exact codes", m, n, k, fq.describe_linear(0, m, n, k))
+    say("w8a8 dynamic exact codes", m, n, k, fq.describe_linear(1, m, n, k, dynamic=True))
     y, s = run_dynamic(fq, x, wq, ws)
     assert s == np.float32(1.0)
     want = np.array([orc.e4m3_value(int(c)) for c in range(256)])[oxq[:, p]]
