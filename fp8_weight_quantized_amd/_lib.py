@@ -14,7 +14,9 @@ import threading
 import torch  # noqa: F401  (load order, see above)
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libfp8q.so")
+# FP8Q_LIBRARY names another build of the library to load (the test suite's
+# sanitizer build of the host code uses it); the default is the in-tree build.
+LIB_PATH = os.environ.get("FP8Q_LIBRARY") or os.path.join(PKG, "libfp8q.so")
 
 FP8Q_OK = 0
 FP8Q_ERR_INVALID_ARG = 1

@@ -56,12 +56,21 @@ def common_flags() -> list[str]:
     ]
 
 
-def _compile(src: str, asm: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", src, "-o", obj]
+# Host-code sanitizers for the test suite's sanitizer build (AddressSanitizer
+# and UndefinedBehaviorSanitizer on the host side only: each flag is scoped to
+# the host compilation, the gfx950 code is built as usual).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-g"]
+SANITIZE_DIR = os.path.join(BUILD, "sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, "libfp8q_sanitize.so")
+
+
+def _compile(src: str, asm: bool, outdir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(outdir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *common_flags(), *extra, "-c", src, "-o", obj]
     if asm:
         cmd += ["-save-temps=obj"]
-    subprocess.check_call(cmd, cwd=BUILD)
+    subprocess.check_call(cmd, cwd=outdir)
     return obj
 
 
@@ -75,6 +84,39 @@ def build(jobs: int = 4, asm: bool = False, verbose: bool = True) -> str:
     if verbose:
         print("built", LIB, file=sys.stderr)
     return LIB
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for root in (CSRC, os.path.join(ROOT, "include")):
+        for dirpath, _, files in sorted(os.walk(root)):
+            for f in sorted(files):
+                if f.endswith((".cpp", ".hip", ".hpp", ".h")):
+                    with open(os.path.join(dirpath, f), "rb") as fh:
+                        h.update(f.encode() + fh.read())
+    h.update(" ".join(SANITIZE_HOST).encode())
+    return h.hexdigest()[:16]
+
+
+def build_sanitize(jobs: int = 4) -> str:
+    """The library with host-side AddressSanitizer + UndefinedBehaviorSanitizer
+    (for CPU tests of the argument validation, loaded through FP8Q_LIBRARY
+    with the sanitizer runtime preloaded).  Rebuilt only when a source changes."""
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    stamp = os.path.join(SANITIZE_DIR, "digest")
+    digest = sources_digest()
+    if os.path.exists(SANITIZE_LIB) and os.path.exists(stamp) and open(stamp).read() == digest:
+        return SANITIZE_LIB
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, False, SANITIZE_DIR, SANITIZE_HOST), SOURCES))
+    tmp = SANITIZE_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE_HOST,
+                           *objs, "-o", tmp])
+    os.replace(tmp, SANITIZE_LIB)
+    with open(stamp, "w") as f:
+        f.write(digest)
+    return SANITIZE_LIB
 
 
 def main() -> None:

@@ -184,6 +184,7 @@ const char *fp8q_status_string(fp8q_status s)
     case FP8Q_ERR_UNSUPPORTED: return "FP8Q_ERR_UNSUPPORTED: device is not gfx950";
     case FP8Q_ERR_HIP: return "FP8Q_ERR_HIP: HIP runtime or launch error";
     case FP8Q_ERR_WORKSPACE: return "FP8Q_ERR_WORKSPACE: workspace missing or too small";
+    default: break;
     }
     return "FP8Q: unknown status";
 }

@@ -52,14 +52,21 @@ typedef enum {
                                    aliasing, wrong mode/scale combination */
     FP8Q_ERR_UNSUPPORTED = 2,   /* the stream's device is not a gfx950 GPU */
     FP8Q_ERR_HIP = 3,           /* a HIP runtime call or a kernel launch failed */
-    FP8Q_ERR_WORKSPACE = 4      /* workspace missing or smaller than the query returned */
+    FP8Q_ERR_WORKSPACE = 4,     /* workspace missing or smaller than the query returned */
+    /* range sentinels, not statuses: they make every int a value of the type,
+       so an unknown value passed through the ABI is still well defined */
+    FP8Q_STATUS_INT_MIN_ = -0x7FFFFFFF - 1,
+    FP8Q_STATUS_INT_MAX_ = 0x7FFFFFFF
 } fp8q_status;
 
 /* The FP8 MatMul modes of the write-up (§3.1 step 3). */
 typedef enum {
     FP8Q_W8A16 = 0,             /* "fp8_w_bf16_a": E4M3 weight, bf16 activation and output */
     FP8Q_W8A8 = 1,              /* "fp8_w_fp8_a":  E4M3 weight and activation, bf16 output */
-    FP8Q_W8A16_F16 = 2          /* "fp8_w_fp16_a": E4M3 weight, fp16 activation and output */
+    FP8Q_W8A16_F16 = 2,         /* "fp8_w_fp16_a": E4M3 weight, fp16 activation and output */
+    /* range sentinels, not modes (see fp8q_status) */
+    FP8Q_MODE_INT_MIN_ = -0x7FFFFFFF - 1,
+    FP8Q_MODE_INT_MAX_ = 0x7FFFFFFF
 } fp8q_mode;
 
 /* FP8Q_ABI_VERSION of the built library. */

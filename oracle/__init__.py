@@ -24,12 +24,18 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fp8q_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
 
 # -fno-fast-math / -ffp-contract=off keep every fp32 division IEEE and every
 # multiply-add unfused, which the bit-exact codes depend on.
 CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
+# ORACLE_SANITIZE=1 (the test suite's sanitizer run, with libasan preloaded)
+# builds and loads a copy with AddressSanitizer + UndefinedBehaviorSanitizer.
+SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+if SANITIZE:
+    CFLAGS = CFLAGS + ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                       "-fno-omit-frame-pointer", "-g"]
+_LIB = os.path.join(_HERE, "liboracle_sanitize.so" if SANITIZE else "liboracle.so")
 
 _lock = threading.Lock()
 _lib = None
