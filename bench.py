@@ -42,6 +42,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 / bf16 MFMA, published
 MALL_BYTES = 256 << 20         # Infinity Cache
 DECODE_MS = (1, 8, 32, 64)
 
@@ -659,7 +660,32 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev, cpu, sectio
             "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4), "kernel": fq.describe_linear(1, m, n, k),
             "input_sets_rotated": nset}
         log(key, rows[f"a6a7_w8a8_{key}"])
-        del sets
+
+        # the write-up's prefill mode, fp8_w_fp16_a: fp16 activations (the
+        # same values, rounded to fp16) on the 16-bit MFMA, and bf16 too
+        if key == "mlp_prefill":
+            for mode, dt, tag in ((2, torch.float16, "f16"), (0, torch.bfloat16, "bf16")):
+                x16 = x.to(dt)
+                y16 = torch.empty((m, n), dtype=dt, device=dev)
+                s16 = [(x16, wq)] + [(x16.clone(), sets[i][1]) for i in range(1, nset)]
+
+                def gemm16(mode=mode, s16=s16, y16=y16):
+                    x_, wq_ = s16[ctr[0] % nset]
+                    ctr[0] += 1
+                    st = L.fp8q_linear(mode, ptr(x_), m, k, k, None, ptr(wq_), n, wq_.stride(0),
+                                       ptr(ws), ptr(y16), n, None, 0, stream())
+                    if st != 0:
+                        raise RuntimeError(fq._lib.last_error())
+                ms16 = time_eager(torch, gemm16, iters)
+                tf16 = flops / (ms16 * 1e-3) / 1e12
+                rows[f"f1_w8a16_{tag}_prefill_{key}"] = {
+                    "shape": f"M={m} N={n} K={k}", "us": round(ms16 * 1e3, 2),
+                    "TFLOP/s": round(tf16, 1), "frac_16bit_peak": round(tf16 / F16_PEAK_TFLOPS, 4),
+                    "kernel": fq.describe_linear(mode, m, n, k), "input_sets_rotated": nset,
+                    "mode": ("fp8_w_fp16_a" if mode == 2 else "fp8_w_bf16_a") +
+                            ": E4M3 weights widened exactly on the 16-bit MFMA"}
+                log(key, rows[f"f1_w8a16_{tag}_prefill_{key}"])
+                del x16, y16, s16
 
         # the same GEMM with per-group weight scales (groups of 128)
         wqg, wsg = fq.quantize_weight_grouped(w, 128)
@@ -680,7 +706,7 @@ def other_rows(args, fq, L, up_bf16, ptr, workloads, np, torch, dev, cpu, sectio
             "kernel": fq.describe_linear(1, m, n, k, 128), "input_sets_rotated": nset,
             "note": "accumulators rescaled by s[g-1]/s[g] as each group opens"}
         log(key, rows[f"f4_grouped_w8a8_{key}"])
-        del wqg, wsg, gsets
+        del wqg, wsg, gsets, sets
 
         # weight quantization (offline in deployment; timed for completeness)
         wqb = torch.empty((n, k), dtype=torch.uint8, device=dev)

@@ -29,6 +29,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "quant.hip"),
     os.path.join(CSRC, "kernels", "w8a16.hip"),
     os.path.join(CSRC, "kernels", "w8a8.hip"),
+    os.path.join(CSRC, "kernels", "w8a16_gemm.hip"),
     os.path.join(CSRC, "kernels", "kv_cache.hip"),
 ]
 

@@ -455,6 +455,8 @@ size_t linear_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t
             return round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
         return round_up(fp8q::launch::plan_w8a16_grouped(m, n, k, group).workspace, 256);
     }
+    if ((mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16) && m > kW8A8DecodeMaxM)
+        return 0;                   // the 16-bit prefill GEMM needs no scratch
     if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16 ||
         (mode == FP8Q_W8A8 && m <= kW8A8DecodeMaxM))
         return round_up(fp8q::launch::plan_w8a16(m, n, k, act_type(mode)).workspace, 256);
@@ -490,6 +492,11 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
         (!fp8q::launch::w8a8_supports_ld(ld_x) || !fp8q::launch::w8a8_supports_ld(ld_w)))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_fp8_a needs ld_x and ld_w below 2^23 (got %lld, %lld)",
                     (long long)ld_x, (long long)ld_w);
+    if (a16 && group == 0 && m > kW8A8DecodeMaxM &&
+        !fp8q::launch::w8a16_gemm_supports(ld_x, ld_w))
+        return fail(FP8Q_ERR_INVALID_ARG,
+                    "above 64 rows the 16-bit activation modes need ld_x below 2^22 and ld_w "
+                    "below 2^23 (got %lld, %lld)", (long long)ld_x, (long long)ld_w);
     if ((a16 || group > 0) && (m + 63) / 64 > 65535)
         return fail(FP8Q_ERR_INVALID_ARG, "the decode kernels take at most 65535 * 64 rows");
     if (m == 0 || n == 0)
@@ -532,6 +539,9 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
         const auto plan = fp8q::launch::plan_w8a16_grouped(m, n, k, group);
         e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
                                 ld_y, workspace, stream);
+    } else if (a16 && m > kW8A8DecodeMaxM) {
+        e = fp8q::launch::w8a16_gemm(mode == FP8Q_W8A16_F16, static_cast<const uint16_t *>(x), m, k,
+                                     ld_x, w_fp8, n, ld_w, w_scale, y_bf16, ld_y, stream);
     } else if (a16 || m <= kW8A8DecodeMaxM) {
         const auto plan = fp8q::launch::plan_w8a16(m, n, k, act);
         e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
@@ -847,6 +857,11 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
         return fail(FP8Q_ERR_INVALID_ARG, "unknown mode %d", (int)mode);
     if (mode == FP8Q_W8A8 && m > kW8A8DecodeMaxM)
         describe_w8a8(m, n, k, false, buf, len);
+    else if (m > kW8A8DecodeMaxM)
+        std::snprintf(buf, len, "k_w8a16_gemm<%s> tile=256x256x64 grid=%lld (%lldx%lld) block=512",
+                      mode == FP8Q_W8A16_F16 ? "true" : "false",
+                      (long long)(((m + 255) / 256) * ((n + 255) / 256)), (long long)((m + 255) / 256),
+                      (long long)((n + 255) / 256));
     else
         describe_w8a16(fp8q::launch::plan_w8a16(m, n, k, act_type(mode)), buf, len);
     return ok();

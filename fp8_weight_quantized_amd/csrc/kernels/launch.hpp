@@ -119,6 +119,14 @@ hipError_t w8a16_quant_act(const W8A16Plan &p, const uint16_t *x, int64_t m, int
 // request for that device and kept.
 hipError_t noalloc_scratch(int device, void **ptr);
 
+// ---- prefill GEMM for 16-bit activations (fp8_w_fp16_a / fp8_w_bf16_a) ------
+// Y = X . dequant(W)^T on v_mfma_f32_32x32x16_{f16,bf16}, 256 x 256 tiles; x is
+// fp16 (f16) or bf16 [m, ld_x], y the same type.  No scratch.
+bool w8a16_gemm_supports(int64_t ld_x, int64_t ld_w);
+hipError_t w8a16_gemm(bool f16, const uint16_t *x, int64_t m, int64_t k, int64_t ld_x,
+                      const uint8_t *w, int64_t n, int64_t ld_w, const float *w_scale,
+                      uint16_t *y, int64_t ld_y, hipStream_t stream);
+
 // ---- W8A8 (fp8_w_fp8_a) GEMM on FP8 MFMA -----------------------------------
 struct W8A8Plan {
     int64_t tiles_m, tiles_n;

@@ -259,6 +259,12 @@ fp8q_status fp8q_kv_cache_write(const uint16_t *k_bf16, const uint16_t *v_bf16, 
  *               bf16 (E4M3 values are exact in fp16; |Y| must stay below 65504).
  * Products are exact and sums are accumulated in fp32; the result is within
  * 5e-3 relative Frobenius error of the exact value (see the tests).
+ * Above 64 activation rows the 16-bit modes run a prefill GEMM on the 16-bit
+ * MFMA (weights widened exactly to the activation type; it needs ld_x below
+ * 2^22 and ld_w below 2^23).
+ * Above 64 activation rows the 16-bit modes run a prefill GEMM on the 16-bit
+ * MFMA (weights widened exactly to the activation type; ld_x below 2^22 and
+ * ld_w below 2^23 there).
  *
  *   w_fp8   [n, k] E4M3 codes, ld_w >= k, ld_w % 16 == 0, 16-byte aligned
  *   w_scale [n] fp32

@@ -155,6 +155,61 @@ def test_w8a8_exact_every_code(fq, orc, m, n, k):
     assert (y == ref).all(), np.argwhere(y != ref)[:5]
 
 
+# the prefill GEMM of the 16-bit activation modes (more than 64 rows): K a
+# multiple of its 64-value stage or not (a zero-filled tail stage), ragged M and
+# N around the 256 x 256 tile, and more than 8 tile-rows
+PREFILL16 = [(65, 300, 640), (256, 256, 64), (513, 257, 200), (300, 520, 1000), (129, 200, 96),
+             (777, 64, 2048), (1000, 1000, 1280), (2305, 2048, 640), (100, 96, 4104), (257, 33, 13)]
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("m,n,k", PREFILL16[:6])
+def test_prefill16_exact_every_code(fq, orc, mode, m, n, k):
+    """One-hot 16-bit rows through k_w8a16_gemm: every E4M3 code widened
+    exactly, the tile layouts and the zero-filled K tail bit for bit."""
+    assert fq.describe_linear(mode, m, n, k).startswith("k_w8a16_gemm")
+    wq = all_codes_weight(n, k)
+    x = np.zeros((m, k), np.uint16)
+    pos = (np.arange(m) * (k - 1)) // max(m - 1, 1)
+    x[np.arange(m), pos] = 0x3F80 if mode == 0 else 0x3C00      # 1.0
+    ws = np.ones(n, np.float32)
+    say("prefill16 exact", mode, m, n, k)
+    y = run_w8a16(fq, x, wq, ws) if mode == 0 else run_w8a16_f16(fq, x, wq, ws)
+    ref = orc.linear(mode, x, wq, ws)
+    assert (y == ref).all(), np.argwhere(y != ref)[:5]
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("m,n,k", PREFILL16)
+def test_prefill16_ragged(fq, orc, mode, m, n, k):
+    w = workloads.heavy_tail_weight(n, k, m + n + 5)
+    wq, ws, _ = orc.quantize_weight(w)
+    x = workloads.normal_act(m, k, k + 3) if mode == 0 else f16_act(m, k, k + 3)
+    say("prefill16", mode, m, n, k, fq.describe_linear(mode, m, n, k))
+    y = run_w8a16(fq, x, wq, ws) if mode == 0 else run_w8a16_f16(fq, x, wq, ws)
+    assert_gemm_close(y, orc.linear(mode, x, wq, ws), f"prefill16 mode {mode} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("mode", [2, 0])
+def test_prefill16_mlp_full_size_sampled(fq, orc, mode):
+    """Llama-3-8B gate+up prefill (M=8192, N=28672, K=4096) with fp16 (the
+    write-up's prefill mode) or bf16 activations, as the benchmark launches it:
+    seeded rows in every 256-row band x all columns, so every output tile."""
+    wl = workloads.WORKLOADS["mlp_prefill"]
+    lin = wl.linears[0]
+    m = wl.ms[0]
+    wq, ws, _ = orc.quantize_weight(workloads.weight(wl, lin))
+    xb = workloads.activation(wl, m, lin.k)
+    x = xb if mode == 0 else workloads.bf16_bits_to_f32(xb).astype(np.float16).view(np.uint16)
+    say("prefill16 full", mode, fq.describe_linear(mode, m, lin.n, lin.k))
+    xd = dev_bf16(x) if mode == 0 else torch.from_numpy(np.ascontiguousarray(x).view(np.float16)).cuda()
+    y = fq.linear(xd, dev_u8(wq), torch.from_numpy(ws).cuda())
+    torch.cuda.synchronize()
+    rows = rows_every_tile(m, 13)
+    got = y[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    assert_gemm_close(got, orc.linear(mode, x, wq, ws, rows=rows), f"prefill16 full mode {mode}")
+
+
 def test_tiny(fq, orc):
     wl = workloads.WORKLOADS["tiny"]
     lin = wl.linears[0]
@@ -373,7 +428,7 @@ def test_host_pointer_and_device_checks(fq):
 
 @pytest.mark.parametrize("mode,m,n,k", [(1, 300, 300, 256), (1, 520, 1000, 384), (1, 300, 300, 200),
                                         (1, 257, 9, 128), (0, 12, 300, 8192), (0, 64, 1000, 4096),
-                                        (0, 48, 4000, 2048)])
+                                        (0, 48, 4000, 2048), (0, 300, 300, 200), (0, 520, 1000, 384)])
 def test_output_stride_guard(fq, orc, mode, m, n, k):
     """Y written into a wider buffer (ld_y = n rounded up to 8, plus 24) with
     rows to spare: every element past column n or row m keeps its sentinel,
