@@ -488,6 +488,9 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
     FP8Q_TRY(check_ld(ld_x, k, a16 ? 8 : 16, "ld_x"));
     FP8Q_TRY(check_ld(ld_w, k, 16, "ld_w"));
     FP8Q_TRY(check_ld(ld_y, n, 8, "ld_y"));
+    if (!fp8q::launch::w8a16_supports_ld(ld_x, ld_w))
+        return fail(FP8Q_ERR_INVALID_ARG, "ld_x and ld_w must be below 2^28 (got %lld, %lld)",
+                    (long long)ld_x, (long long)ld_w);
     if (mode == FP8Q_W8A8 &&
         (!fp8q::launch::w8a8_supports_ld(ld_x) || !fp8q::launch::w8a8_supports_ld(ld_w)))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_fp8_a needs ld_x and ld_w below 2^23 (got %lld, %lld)",

@@ -169,5 +169,25 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red)
     return r;
 }
 
+// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at LDS address lds + 16 * l.  `base` is wave-uniform (an
+// SGPR pair), `off` the lane's 32-bit byte offset from it, `lds` a
+// wave-uniform LDS byte address.  The instruction takes its LDS address from
+// M0, which the asm sets; no other code in these kernels uses M0 (gfx950 LDS
+// instructions do not), so the clobber is harmless and the compiler's warning
+// about clobbering a reserved register is silenced.  The load counts in
+// vmcnt like any other; once vmcnt has dropped past it, its bytes are in LDS.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 }  // namespace dev
 }  // namespace fp8q

@@ -99,6 +99,12 @@ W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group);
 // 3: bf16 activations quantized per tensor on the fly (fp8_w_fp8_a with the
 // dynamic activation quantization folded in): see w8a16_quant_act.
 constexpr int kW8A16ActBF16 = 0, kW8A16ActF16 = 1, kW8A16ActF8 = 2, kW8A16ActQ = 3;
+// Row strides the decode kernels take (elements of x, bytes of w): a load
+// instruction addresses a few rows from one base with 32-bit lane offsets.
+inline bool w8a16_supports_ld(int64_t ld_x, int64_t ld_w)
+{
+    return ld_x < ((int64_t)1 << 28) && ld_w < ((int64_t)1 << 28);
+}
 hipError_t w8a16(const W8A16Plan &p, int act, const void *x, int64_t m, int64_t k, int64_t ld_x,
                  const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
                  const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,

@@ -887,21 +887,23 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 // is a single launch.  The NWV waves take 1/NWV of K each; their fp32 panels
 // are added through LDS in wave order at the end.
 //
-// The activation panel is re-read by every workgroup of its column of
-// panels, from L2.  Loaded in the MFMA operand layout (16 rows x 32 bytes per
-// load instruction) those reads run at about half the rate of plain
-// coalesced loads, so here every load instruction reads 1 KB of whole
-// 512-byte row segments, D chunks ahead, into registers.  Each wave then
-// writes its chunk into its own LDS slot and reads it back in the B layout;
-// the 16-byte units of a staged row are XOR-swizzled by the row's low 4 bits,
-// so both the row-wise writes and the 16-row operand reads are free of bank
-// conflicts.  Weights stream straight into registers (non-temporal), one
-// 16-byte load per lane per fragment and 64-k step, as in the other kernels.
+// Both operands reach the MFMAs through LDS.  Each wave owns a ring of D
+// chunk slots (CS 64-k steps per chunk) and fills them with direct
+// global->LDS loads (global_load_lds_dwordx4): every load instruction moves
+// 1 KB of whole row segments -- whole 128-byte lines -- and needs no
+// registers, so D chunks stay in flight while the MFMAs consume an earlier
+// one.  Loaded straight in the MFMA operand layout instead (16 rows x 64
+// bytes per instruction), the weight stream touched twice as many cache lines
+// per instruction and measured about 2 us slower per call on the Llama-3-8B
+// q_proj at M = 32..64 (MI355X).  The 16-byte units of a staged row are
+// XOR-swizzled by the row's low bits (global side: a lane fetches the unit
+// that belongs at its LDS position), so the 16-row operand reads are free of
+// bank conflicts.
 //
-// CS: 64-k steps per chunk.  D: chunks in flight per wave.  The host plans
-// this kernel only for K a multiple of NWV * 64 * CS with at least D chunks
-// per wave.  Rows past N or M are clamped to a valid row when loading and their
-// outputs are never stored.
+// Activation types that are converted on the way -- E4M3 codes widened to
+// bf16 (kActF8), bf16 cast to E4M3 and back (kActQ) -- load into registers
+// instead, D chunks ahead, and each wave writes its converted chunk into a
+// single LDS slot before its MFMAs read it.
 //
 // XS: activation rows staged per chunk (the panel's first XS rows; the host
 // plans XS >= the rows that exist).  Staging fewer rows than the panel has
@@ -909,9 +911,12 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 // that only feed output columns that are never stored; the LDS rows past XS
 // are zeroed once.
 //
-// E4M3 activation codes (kActF8) are loaded 16 codes per lane and widened
-// exactly to bf16 as they are written to LDS (each loaded unit fills two
-// staged units); x_scale is then the activation scale.
+// The host plans this kernel only for K a multiple of NWV * 64 * CS with at
+// least D chunks per wave.  Rows past N or M are clamped to a valid row when
+// loading and their outputs are never stored.  A load instruction covers at
+// most 8 weight rows or 4 activation rows, addressed from that group's first
+// row, so the per-lane 32-bit offsets hold for row strides below 2^28 bytes
+// (checked by the host).
 template <int AF, int MB, int CS, int D, int NWV, int AT, int XS = 16 * MB>
 __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const void *__restrict__ xv, int64_t m, int64_t k, int64_t ld_x,
@@ -920,64 +925,100 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y, QuantArgs qa)
 {
     constexpr bool F8 = AT == kActF8;
+    constexpr bool XD = AT == kActBF16 || AT == kActF16;   // activations by direct loads
     constexpr int CT = compute_type<AT>();
     constexpr int ES = F8 ? 1 : 2;              // bytes per activation value in memory
     constexpr int XR = 16 * MB;                 // activation rows of the panel
+    constexpr int WR = 16 * AF;                 // weight rows of the panel
     constexpr int CK = 64 * CS;                 // k per chunk
     constexpr int RU = CK * 2 / 16;             // 16-byte units of a staged (bf16) row segment
-    constexpr int RB = 16 * RU;                 // bytes of a staged row segment
-    constexpr int XU = CK * ES / 16;            // 16-byte units loaded per row segment
+    constexpr int RB = 16 * RU;                 // bytes of a staged activation row segment
+    constexpr int XU = CK * ES / 16;            // 16-byte units loaded per activation row segment
     constexpr int NI = XS * XU / kWave;         // activation loads per lane per chunk
-    constexpr int LC = NI + CS * AF;            // loads per lane per chunk
-    static_assert(RU % 16 == 0 && (XS * XU) % kWave == 0 && XS <= XR && XS > 0, "chunk shape");
-    static_assert(D >= 1 && D <= 4, "chunks in flight");
-    // the waves' staging slots; after the K loop the same bytes hold the
-    // waves' fp32 panels for the reduction
-    constexpr int SLOT = XR * RB;
+    constexpr int WU = CK / 16;                 // 16-byte units of a weight row segment
+    constexpr int NW = WR * WU / kWave;         // weight loads per lane per chunk
+    constexpr int LC = NI + NW;                 // loads per lane per chunk
+    constexpr int WSW = WU >= 16 ? 15 : WU - 1; // weight unit swizzle mask
+    constexpr int XSLOT = XR * RB, WSLOT = WR * CK;
+    constexpr int XSLOTS = XD ? D : 1;
+    constexpr int SLOT = XSLOTS * XSLOT + D * WSLOT;
     constexpr int RED = (int)sizeof(v4f) * NWV * AF * MB * kWave;
+    static_assert(RU % 16 == 0 && (XS * XU) % kWave == 0 && XS <= XR && XS > 0, "chunk shape");
+    static_assert((WR * WU) % kWave == 0 && (WU & (WU - 1)) == 0, "weight chunk shape");
+    static_assert(D >= 1 && D <= 4, "chunks in flight");
+    // the waves' slots; after the K loop the same bytes hold the waves' fp32
+    // panels for the reduction
     __shared__ __attribute__((aligned(16))) uint8_t xl[NWV * SLOT > RED ? NWV * SLOT : RED];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int r = lane & 15;          // row of the A (weight) / B (activation) operand
     const int g = lane >> 4;          // which 16 k-values of a 64-k step this lane holds
-    const int64_t n0 = (int64_t)blockIdx.x * 16 * AF;
+    const int64_t n0 = (int64_t)blockIdx.x * WR;
     const int64_t m0 = (int64_t)blockIdx.y * XR;
     const int64_t kq = k / NWV;
     const int64_t kb = (int64_t)wave * kq;
     const int nch = (int)(kq / CK);
-    uint8_t *slot = xl + wave * SLOT;
+    uint8_t *xslot = xl + wave * SLOT;                  // XSLOTS activation slots
+    uint8_t *wslot = xslot + XSLOTS * XSLOT;            // D weight slots
+    const uint32_t xslot_lds = (uint32_t)(uintptr_t)xslot;
+    const uint32_t wslot_lds = (uint32_t)(uintptr_t)wslot;
     const float xs = act_scale<AT>(x_scale, qa);
     const E4M3Div div(AT == kActQ ? xs : 1.0f);
 
-    const uint8_t *wp[AF];
+    // weight load i of a chunk fills LDS bytes [1 KB i, 1 KB (i + 1)) of the
+    // slot: rows WPI * i .. WPI * (i + 1) - 1, lane l at row l / WU, position
+    // l % WU, which holds global unit (l % WU) ^ swizzle(row)
+    constexpr int WPI = kWave / WU;
+    uint32_t woff[NW];
 #pragma unroll
-    for (int a = 0; a < AF; ++a)
-        wp[a] = w + min(n0 + 16 * a + r, n - 1) * ld_w + kb + 16 * g;
-    // activation load i of a chunk: unit f = 64 i + lane of the chunk's
-    // XS x XU loaded units, i.e. row f / XU, 16-byte unit f % XU of that row;
-    // its staged (bf16) unit is the same one, or units 2u and 2u + 1 for codes
-    const uint8_t *x8 = static_cast<const uint8_t *>(xv);
-    const uint8_t *xp[NI];
-    int xo[NI], xo2[NI];              // LDS byte offsets of the staged unit(s), swizzled
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int f = kWave * i + lane;
-        const int rho = f / XU, u = f % XU;
-        xp[i] = x8 + (min(m0 + rho, m - 1) * ld_x + kb) * ES + 16 * u;
-        const int su = F8 ? 2 * u : u;
-        xo[i] = rho * RB + 16 * (su ^ (rho & 15));
-        xo2[i] = rho * RB + 16 * ((su + 1) ^ (rho & 15));
+    for (int i = 0; i < NW; ++i) {
+        const int rho = WPI * i + lane / WU, q = lane % WU;
+        const int64_t row0 = min(n0 + WPI * i, n - 1);
+        woff[i] = (uint32_t)((min(n0 + rho, n - 1) - row0) * ld_w + 16 * (q ^ (rho & WSW)));
     }
+    auto wbase = [&](int i, int c) {
+        return w + min(n0 + WPI * i, n - 1) * ld_w + kb + (int64_t)c * CK;
+    };
+    // activation load i of a chunk: unit f = 64 i + lane of the chunk's
+    // XS x XU loaded units, i.e. row f / XU, unit f % XU of that row
+    const uint8_t *x8 = static_cast<const uint8_t *>(xv);
+    constexpr int XPI = kWave / XU;             // rows per activation load (direct loads)
+    uint32_t xoff[XD ? NI : 1];
+    const uint8_t *xp[XD ? 1 : NI];
+    int xo[XD ? 1 : NI], xo2[XD ? 1 : NI];      // LDS byte offsets of the staged unit(s)
+    if constexpr (XD) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int rho = XPI * i + lane / XU, q = lane % XU;
+            const int64_t row0 = min(m0 + XPI * i, m - 1);
+            xoff[i] = (uint32_t)((min(m0 + rho, m - 1) - row0) * ld_x * ES + 16 * (q ^ (rho & 15)));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int f = kWave * i + lane;
+            const int rho = f / XU, u = f % XU;
+            xp[i] = x8 + (min(m0 + rho, m - 1) * ld_x + kb) * ES + 16 * u;
+            // its staged (bf16) unit is the same one, or units 2u and 2u + 1 for codes
+            const int su = F8 ? 2 * u : u;
+            xo[i] = rho * RB + 16 * (su ^ (rho & 15));
+            xo2[i] = rho * RB + 16 * ((su + 1) ^ (rho & 15));
+        }
+    }
+    auto xbase = [&](int i, int c) {
+        return x8 + (min(m0 + XPI * i, m - 1) * ld_x + kb + (int64_t)c * CK) * ES;
+    };
 
     if constexpr (XS < XR) {
 #pragma unroll
-        for (int o = XS * RB + 16 * lane; o < XR * RB; o += 16 * kWave)
-            *reinterpret_cast<v4u *>(slot + o) = v4u{0u, 0u, 0u, 0u};
+        for (int u = 0; u < XSLOTS; ++u)
+#pragma unroll
+            for (int o = XS * RB + 16 * lane; o < XR * RB; o += 16 * kWave)
+                *reinterpret_cast<v4u *>(xslot + u * XSLOT + o) = v4u{0u, 0u, 0u, 0u};
     }
 
-    v4u xr[D][NI];
-    v4u wr[D][CS][AF];
+    v4u xr[XD ? 1 : D][XD ? 1 : NI];
     v4f acc[AF][MB];
 #pragma unroll
     for (int a = 0; a < AF; ++a)
@@ -986,16 +1027,20 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
             acc[a][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     auto issue_x = [&](int u, int c) {
+        if constexpr (XD) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-            xr[u][i] = ldg(xp[i] + (int64_t)c * CK * ES);
+            for (int i = 0; i < NI; ++i)
+                dma16(xbase(i, c), xoff[i], xslot_lds + u * XSLOT + 1024 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                xr[u][i] = ldg(xp[i] + (int64_t)c * CK * ES);
+        }
     };
     auto issue_w = [&](int u, int c) {
 #pragma unroll
-        for (int s = 0; s < CS; ++s)
-#pragma unroll
-            for (int a = 0; a < AF; ++a)
-                wr[u][s][a] = ldg_nt(wp[a] + (int64_t)c * CK + 64 * s);
+        for (int i = 0; i < NW; ++i)
+            dma16(wbase(i, c), woff[i], wslot_lds + u * WSLOT + 1024 * i);
     };
     // the wait for chunk c: loads retire in order, and the chunks issued after
     // it are min(D - 1, nch - 1 - c) whole chunks of LC loads each
@@ -1008,18 +1053,23 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
         });
     };
     auto compute = [&](int u) {
+        const uint8_t *xs_ = xslot + (XD ? u : 0) * XSLOT;
+        const uint8_t *ws_ = wslot + u * WSLOT;
 #pragma unroll
         for (int s = 0; s < CS; ++s) {
             typename Act<CT>::frag a0[AF], a1[AF];
 #pragma unroll
-            for (int a = 0; a < AF; ++a)
-                widen<CT>(wr[u][s][a], a0[a], a1[a]);
+            for (int a = 0; a < AF; ++a) {
+                const int rho = 16 * a + r;
+                const v4u wv = *reinterpret_cast<const v4u *>(ws_ + rho * CK + 16 * ((4 * s + g) ^ (rho & WSW)));
+                widen<CT>(wv, a0[a], a1[a]);
+            }
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
                 const int rho = 16 * j + r;
                 const int u0 = 8 * s + 2 * g;
-                const v4u b0 = *reinterpret_cast<const v4u *>(slot + rho * RB + 16 * (u0 ^ (rho & 15)));
-                const v4u b1 = *reinterpret_cast<const v4u *>(slot + rho * RB + 16 * ((u0 + 1) ^ (rho & 15)));
+                const v4u b0 = *reinterpret_cast<const v4u *>(xs_ + rho * RB + 16 * (u0 ^ (rho & 15)));
+                const v4u b1 = *reinterpret_cast<const v4u *>(xs_ + rho * RB + 16 * ((u0 + 1) ^ (rho & 15)));
 #pragma unroll
                 for (int a = 0; a < AF; ++a) {
                     acc[a][j] = Act<CT>::mfma(a0[a], Act<CT>::cast(b0), acc[a][j]);
@@ -1042,29 +1092,35 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
             if (c < nch) {
                 wait_chunk(c);
                 __builtin_amdgcn_sched_barrier(0);
-                // this wave's slot: the previous chunk's reads were consumed
-                // by its MFMAs; LDS operations of one wave run in order
-#pragma unroll
-                for (int i = 0; i < NI; ++i) {
-                    if constexpr (F8) {
-                        const v4u c = xr[u][i];
-                        const uint2 p0 = e4m3x4_to_bf16(c.x), p1 = e4m3x4_to_bf16(c.y);
-                        const uint2 p2 = e4m3x4_to_bf16(c.z), p3 = e4m3x4_to_bf16(c.w);
-                        *reinterpret_cast<v4u *>(slot + xo[i]) = v4u{p0.x, p0.y, p1.x, p1.y};
-                        *reinterpret_cast<v4u *>(slot + xo2[i]) = v4u{p2.x, p2.y, p3.x, p3.y};
-                    } else {
-                        *reinterpret_cast<v4u *>(slot + xo[i]) =
-                            AT == kActQ ? qdq8(xr[u][i], div) : xr[u][i];
-                    }
-                }
                 const bool more = c + D < nch;
-                if (more)
-                    issue_x(u, c + D);
+                if constexpr (!XD) {
+                    // this wave's single activation slot: the previous chunk's
+                    // reads were consumed by its MFMAs; LDS operations of one
+                    // wave run in order
+#pragma unroll
+                    for (int i = 0; i < NI; ++i) {
+                        if constexpr (F8) {
+                            const v4u cv = xr[u][i];
+                            const uint2 p0 = e4m3x4_to_bf16(cv.x), p1 = e4m3x4_to_bf16(cv.y);
+                            const uint2 p2 = e4m3x4_to_bf16(cv.z), p3 = e4m3x4_to_bf16(cv.w);
+                            *reinterpret_cast<v4u *>(xslot + xo[i]) = v4u{p0.x, p0.y, p1.x, p1.y};
+                            *reinterpret_cast<v4u *>(xslot + xo2[i]) = v4u{p2.x, p2.y, p3.x, p3.y};
+                        } else {
+                            *reinterpret_cast<v4u *>(xslot + xo[i]) = qdq8(xr[u][i], div);
+                        }
+                    }
+                    if (more)
+                        issue_x(u, c + D);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 compute(u);
                 __builtin_amdgcn_sched_barrier(0);
-                if (more)
+                // slot u is free again: its operand reads fed the MFMAs above
+                if (more) {
+                    if constexpr (XD)
+                        issue_x(u, c + D);
                     issue_w(u, c + D);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
@@ -1223,7 +1279,85 @@ static void plan_tile(W8A16Plan &p, int64_t m, int64_t k, int steps_mb1)
     p.grid_n = p.tiles_n * p.splits;
 }
 
-W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
+// The panel kernel's plans (one launch, whole K per workgroup, no partial
+// sums).  Measured on MI355X in graphs, weights rotating through 2 GiB:
+//  - up to 16 activation rows, one activation group (MB = 1): AF weight
+//    fragments per workgroup, AF in {1, 2, 3, 4, 7}, the AF whose grid wastes
+//    the least of whole rounds of 256 workgroups (ties to the larger AF).
+//    Llama-3-8B q_proj (4096 x 4096): M = 1 5.7 us, M = 8 5.9 us, M = 16
+//    6.7 us against 5.8 / 7.0 / 8.3 us for the rows kernel; Llama-3-70B at
+//    M = 12: q/o (8192 x 8192) 14.1 us, gate/up (28672 x 8192) 42.6 us,
+//    down (8192 x 28672) 43.4 us against 51.1 us for the split tile kernel +
+//    reduce; Llama-3-8B k/v (1024 x 4096) at M = 8 4.9 us on 64 workgroups
+//    against 6.8 us for the split rows kernel + reduce (but 8.4 against 7.4
+//    us for the 70B k/v, K = 8192).
+//  - 17..32 activation rows: two activation groups of 16 rows along the grid
+//    (MB = 1, AF = 2); 33..64 rows: 32-row groups (MB = 2, AF = 2); both only
+//    where that makes 192..320 workgroups.  q_proj M = 24 7.2 us, M = 32 7.9
+//    us, M = 64 9.6 us (12.0 us with the weights loaded straight into
+//    registers).  E4M3 activation codes take chunks of 4 x 64 k (their
+//    staging goes through registers).
+// Activations cast on the fly (kActQ) stage only the rows that exist (4, 8 or
+// 16).  Chunks of CS x 64 k, D of them in flight: the LDS of 4 waves' rings
+// bounds CS * D * (activation + weight row bytes).
+static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act)
+{
+    const bool f8 = act == kW8A16ActF8, q = act == kW8A16ActQ;
+    if (m < 1 || m > 64 || n < 1 || k % 512 != 0 || k < 2048)
+        return false;
+    W8A16Plan p = out;
+    p.kind = W8A16Plan::kPanel;
+    p.waves = 4;
+    p.splits = 1;
+    p.workspace = 0;
+    p.kper = k;
+    p.kchunk = k / 4;
+    if (m <= 16) {
+        if (f8 || n < 1024)
+            return false;
+        static const int kAf[5] = {1, 2, 3, 4, 7};
+        int best = 0;
+        int64_t best_cost = 0;
+        for (int i = 0; i < 5; ++i) {
+            const int64_t cost = div_up(div_up(n, 16 * kAf[i]), 256) * kAf[i];
+            if (i == 0 || cost < best_cost || (cost == best_cost && kAf[i] > kAf[best])) {
+                best = i;
+                best_cost = cost;
+            }
+        }
+        // fewer than 96 workgroups on a long K: the split rows kernel + reduce
+        // (Llama-3-70B k/v, 1024 x 8192, at M = 12: 7.4 us against 8.4 us);
+        // casting the activations on the fly needs more workgroups still
+        // (1024 x 8192: 24 us on 64 workgroups)
+        if ((div_up(n, 16 * kAf[best]) < 96 && k > 4096) || (q && n < 2048))
+            return false;
+        p.af = kAf[best];
+        p.mb = 1;
+        p.steps = 2;
+        p.depth = p.af == 7 ? 2 : (p.af > 2 || q) ? 3 : 4;
+        p.xd = q ? (m <= 4 ? 4 : m <= 8 ? 8 : 16) : 16;
+    } else {
+        if (q)
+            return false;
+        p.af = 2;
+        p.mb = m > 32 ? 2 : 1;
+        p.steps = f8 ? 4 : 2;
+        // E4M3 codes at 17..32 rows: 3 chunks in flight where K has them
+        p.depth = m > 32 || (f8 && k < 3 * 4 * 64 * p.steps) ? 2 : 3;
+        p.xd = 16 * p.mb;
+        const int64_t wgs = div_up(n, 32) * div_up(m, 16 * p.mb);
+        if (wgs < 192 || wgs > 320 || k % (4 * 64 * p.steps) != 0 || k / (4 * 64 * p.steps) < p.depth)
+            return false;
+    }
+    p.rows = 16 * p.af;
+    p.grid_n = div_up(n, 16 * p.af);
+    p.grid_m = div_up(m, 16 * p.mb);
+    out = p;
+    return true;
+}
+
+// The rows / tile kernels' plans (the per-group weight scales use these too).
+static W8A16Plan plan_rows_tile(int64_t m, int64_t n, int64_t k)
 {
     W8A16Plan p{};
     const int64_t mgroups = div_up(m, 16);
@@ -1233,91 +1367,6 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
     p.splits = 1;
     p.workspace = 0;
     p.ldp = div_up(n, 4) * 4;
-    // Up to 16 activation rows on a wide weight (N >= 8192) with K < 16K: the
-    // panel kernel with one activation group and AF = 2, 3, 4 or 7 weight
-    // fragments per workgroup, the AF whose grid is closest to whole waves of
-    // 256 workgroups (least rows per CU: rounds of 256 workgroups x 16 AF).
-    // Measured on MI355X at M = 12 (graphs): Llama-3-70B gate/up [28672,
-    // 8192] 47.7 us (AF = 7, 256 workgroups) against 53.3 us for the 4-way
-    // split tile kernel + reduce, q/o [8192, 8192] 18.3-18.7 us against
-    // 19.1 us, fused gate_up [57344, 8192] 92.6 against 102.6 us, Llama-3-8B
-    // gate_up [28672, 4096] 26.2 against 28.9 us; AF = 8 (224 workgroups)
-    // measured 53.1 us on gate/up.  A long K (the 70B down_proj, 28672)
-    // stays on the split tile kernel (51.4 us against 57.7 us).
-    // bf16 activations cast to E4M3 on the fly, up to 16 rows on a weight of
-    // 2048..8191 rows: the panel kernel with one weight fragment, staging (and
-    // casting) only the rows that exist.  Every workgroup casts the
-    // activations it reads, so the rows kernel -- which loads 16 rows per
-    // MFMA operand whatever M is -- would cast up to 16 times more values.
-    if (act == kW8A16ActQ && m <= 16 && n >= 2048 && n < 8192 && k % 512 == 0 && k >= 2048 &&
-        k < 16384) {
-        p.kind = W8A16Plan::kPanel;
-        p.af = 1;
-        p.mb = 1;
-        p.xd = m <= 4 ? 4 : m <= 8 ? 8 : 16;
-        p.rows = 16;
-        p.waves = 4;
-        p.steps = 2;
-        p.depth = 3;
-        p.grid_n = div_up(n, 16);
-        p.grid_m = 1;
-        p.kper = k;
-        p.kchunk = k / 4;
-        return p;
-    }
-    if (act != kW8A16ActF8 && m <= 16 && n >= 8192 && k % 512 == 0 && k >= 2048 && k < 16384) {
-        static const int kAf[4] = {2, 3, 4, 7};
-        int best = 0;
-        int64_t best_cost = 0;
-        for (int i = 0; i < 4; ++i) {
-            const int64_t wgs = div_up(n, 16 * kAf[i]);
-            const int64_t cost = div_up(wgs, 256) * kAf[i];
-            if (i == 0 || cost < best_cost || (cost == best_cost && kAf[i] > kAf[best])) {
-                best = i;
-                best_cost = cost;
-            }
-        }
-        p.kind = W8A16Plan::kPanel;
-        p.af = kAf[best];
-        p.mb = 1;
-        p.rows = 16 * p.af;
-        p.waves = 4;
-        p.steps = 2;
-        p.depth = 3;
-        // activations cast on the fly: stage only the rows that exist (4, 8 or 16)
-        p.xd = act == kW8A16ActQ ? (m <= 4 ? 4 : m <= 8 ? 8 : 16) : 16;
-        p.grid_n = div_up(n, 16 * p.af);
-        p.grid_m = 1;
-        p.kper = k;
-        p.kchunk = k / 4;
-        return p;
-    }
-    // 17..64 activation rows: one launch of k_w8a16_panel (panels of 32
-    // activation rows x 16 weight rows, or x 32 above 32 activation rows,
-    // whole K per workgroup, no partial sums) where that makes about one
-    // workgroup per CU.  Measured on MI355X on the Llama-3-8B q_proj (N = K =
-    // 4096), in graphs: M = 32 9.9 us against 10.3 us for the split tile
-    // kernel + reduce, M = 64 11.9 us against 13.7 us.  E4M3 activation codes
-    // take it too (widened to bf16 as they are staged).
-    if (m > 16 && m <= 64 && k % 1024 == 0 && k >= 2048) {
-        const int af = m > 32 ? 2 : 1;
-        const int64_t gn = div_up(n, 16 * af), gm = div_up(m, 32);
-        if (gn * gm >= 192 && gn * gm <= 320) {
-            p.kind = W8A16Plan::kPanel;
-            p.af = af;
-            p.mb = 2;
-            p.xd = 32;
-            p.rows = 16 * af;
-            p.waves = 4;
-            p.steps = 4;
-            p.depth = 2;
-            p.grid_n = gn;
-            p.grid_m = gm;
-            p.kper = k;
-            p.kchunk = k / 4;
-            return p;
-        }
-    }
     // The rows kernel wins for up to 16 activation rows on a weight of up to
     // 4096 rows with K < 16K; a wider weight takes the split tile kernel
     // below, a long K, a small N or more activation rows the tile kernel
@@ -1394,6 +1443,13 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
     return p;
 }
 
+W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
+{
+    W8A16Plan p = plan_rows_tile(m, n, k);
+    plan_panel(p, m, n, k, act);
+    return p;
+}
+
 W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group)
 {
     // where the per-channel plan takes the rows kernel, so does the grouped
@@ -1402,7 +1458,7 @@ W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group)
     // K into multiples of 4 waves x 512 k; unsplit, the wave ranges are
     // rounded up to 512 k.
     {
-        W8A16Plan r = plan_w8a16(m, n, k);
+        W8A16Plan r = plan_rows_tile(m, n, k);
         if (r.kind == W8A16Plan::kRows && r.mb == 1 && r.depth == 8) {
             if (r.splits == 1) {
                 r.kchunk = div_up(div_up(k, r.waves), 512) * 512;
@@ -1482,9 +1538,7 @@ static void launch_tile(const W8A16Plan &p, const void *x, int64_t m, int64_t k,
     }
 }
 
-// k_w8a16_panel, 4 waves.  32 activation rows: chunks of 4 x 64 k, 2 in
-// flight (the measured best on the Llama-3-8B q_proj decode shapes); 16
-// activation rows: chunks of 2 x 64 k, 3 in flight (Llama-3-70B shapes).
+// k_w8a16_panel, 4 waves (the configurations plan_panel picks).
 template <int AF, int MB, int CS, int D, int AT, int XS = 16 * MB>
 static void launch_panel(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
                          const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
@@ -1511,29 +1565,25 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
                                                     w_scale, y, ld_y, qa, stream);            \
                 return hipGetLastError();                                                     \
             }
-        FP8Q_PANEL_CASE(1, 2, 4, 2, 32)
-        FP8Q_PANEL_CASE(2, 2, 4, 2, 32)
-        if constexpr (AT != kActF8) {
+#define FP8Q_PANEL_MB1(XS)                                                                    \
+            FP8Q_PANEL_CASE(3, 1, 2, 3, XS) FP8Q_PANEL_CASE(4, 1, 2, 3, XS)                   \
+            FP8Q_PANEL_CASE(7, 1, 2, 2, XS)
+        if constexpr (AT == kActF8) {
+            FP8Q_PANEL_CASE(2, 1, 4, 3, 16)
+            FP8Q_PANEL_CASE(2, 1, 4, 2, 16)
+            FP8Q_PANEL_CASE(2, 2, 4, 2, 32)
+        } else if constexpr (AT == kActQ) {
+            // activations cast on the fly: stage (and cast) only the rows that exist
+            FP8Q_PANEL_CASE(1, 1, 2, 3, 4) FP8Q_PANEL_CASE(2, 1, 2, 3, 4) FP8Q_PANEL_MB1(4)
+            FP8Q_PANEL_CASE(1, 1, 2, 3, 8) FP8Q_PANEL_CASE(2, 1, 2, 3, 8) FP8Q_PANEL_MB1(8)
+            FP8Q_PANEL_CASE(1, 1, 2, 3, 16) FP8Q_PANEL_CASE(2, 1, 2, 3, 16) FP8Q_PANEL_MB1(16)
+        } else {
+            FP8Q_PANEL_CASE(1, 1, 2, 4, 16) FP8Q_PANEL_CASE(2, 1, 2, 4, 16) FP8Q_PANEL_MB1(16)
             FP8Q_PANEL_CASE(2, 1, 2, 3, 16)
-            FP8Q_PANEL_CASE(3, 1, 2, 3, 16)
-            FP8Q_PANEL_CASE(4, 1, 2, 3, 16)
-            FP8Q_PANEL_CASE(7, 1, 2, 3, 16)
-            if constexpr (AT == kActQ) {
-                // activations cast on the fly: stage (and cast) only the rows that exist
-                FP8Q_PANEL_CASE(1, 1, 2, 3, 4)
-                FP8Q_PANEL_CASE(1, 1, 2, 3, 8)
-                FP8Q_PANEL_CASE(1, 1, 2, 3, 16)
-                FP8Q_PANEL_CASE(2, 1, 2, 3, 4)
-                FP8Q_PANEL_CASE(2, 1, 2, 3, 8)
-                FP8Q_PANEL_CASE(3, 1, 2, 3, 4)
-                FP8Q_PANEL_CASE(3, 1, 2, 3, 8)
-                FP8Q_PANEL_CASE(4, 1, 2, 3, 4)
-                FP8Q_PANEL_CASE(4, 1, 2, 3, 8)
-                FP8Q_PANEL_CASE(7, 1, 2, 3, 4)
-                FP8Q_PANEL_CASE(7, 1, 2, 3, 8)
-            }
-#undef FP8Q_PANEL_CASE
+            FP8Q_PANEL_CASE(2, 2, 2, 2, 32)
         }
+#undef FP8Q_PANEL_MB1
+#undef FP8Q_PANEL_CASE
     } else if (p.group == 0 && p.kind == W8A16Plan::kRows) {
 #define FP8Q_ROWS_CASE(AF, MB, P, NW)                                                         \
         if (p.af == AF && p.mb == MB && p.depth == P && p.waves == NW) {                      \

@@ -71,22 +71,6 @@ __device__ __forceinline__ int swz(int r)
         return (r >> 2) & 3;
 }
 
-// Direct global->LDS load of 16 bytes per lane (lane l lands at lds + 16 l):
-// `base` is wave-uniform, `off` the lane's byte offset from it.  M0 carries
-// the LDS address; nothing else here uses M0 (gfx950 LDS instructions do
-// not), so the clobber is harmless and its warning is silenced.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t off, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %2\n\t"
-                 "global_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(off), "s"(base), "s"(lds)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 // One operand's per-lane share of a stage: RB-byte tile rows, ES bytes per
 // value.  A wave instruction fills 1 KB of LDS (1024 / RB rows); lane l
 // writes slot l, i.e. row l / (RB / 16) at chunk position l % (RB / 16), so it

@@ -94,25 +94,6 @@ __device__ __forceinline__ uint4 tail16(const uint8_t *rowp, int64_t kc, int64_t
     return make_uint4(d[0], d[1], d[2], d[3]);
 }
 
-// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at
-// LDS address lds + 16 * l.  `base` is wave-uniform (an SGPR pair), `off`
-// the lane's 32-bit byte offset from it, `lds` a wave-uniform LDS address.
-// The instruction takes its LDS address from M0, which the asm sets; nothing
-// else in this kernel uses M0 (gfx950 LDS instructions do not), which keeps
-// the clobber harmless -- the compiler warns about clobbering a reserved
-// register, so the warning is silenced here.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t off, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %2\n\t"
-                 "global_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(off), "s"(base), "s"(lds)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 // One operand's per-lane share of a stage load.  The wave fills 1 KB blocks
 // (16 rows x 64 bytes) of the stage tile; lane l writes LDS slot l of a block,
 // i.e. row l / 4 at chunk position l % 4, so it fetches logical chunk

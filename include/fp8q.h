@@ -261,10 +261,9 @@ fp8q_status fp8q_kv_cache_write(const uint16_t *k_bf16, const uint16_t *v_bf16, 
  * 5e-3 relative Frobenius error of the exact value (see the tests).
  * Above 64 activation rows the 16-bit modes run a prefill GEMM on the 16-bit
  * MFMA (weights widened exactly to the activation type; it needs ld_x below
- * 2^22 and ld_w below 2^23).
- * Above 64 activation rows the 16-bit modes run a prefill GEMM on the 16-bit
- * MFMA (weights widened exactly to the activation type; ld_x below 2^22 and
- * ld_w below 2^23 there).
+ * 2^22 and ld_w below 2^23).  In every mode ld_x and ld_w must be below 2^28
+ * (the decode kernels address a few rows per load with 32-bit offsets);
+ * larger strides return FP8Q_ERR_INVALID_ARG.
  *
  *   w_fp8   [n, k] E4M3 codes, ld_w >= k, ld_w % 16 == 0, 16-byte aligned
  *   w_scale [n] fp32

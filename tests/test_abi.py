@@ -56,22 +56,20 @@ def test_workspace_queries(L):
     assert L.fp8q_linear_workspace_size(1, 64, 4096, 4096) == 0         # the panel kernel
     assert L.fp8q_linear_workspace_size(1, 64, 1024, 4096) == 4 * 64 * 1024 * 4
     assert L.fp8q_linear_workspace_size(1, 1, 4096, 4096) == 0
-    # W8A16, up to 16 activation rows on a weight of up to 4096 rows: the rows
-    # kernel, one launch, no scratch
-    assert L.fp8q_linear_workspace_size(0, 1, 4096, 4096) == 0
-    # wider weights (N >= 8192) at up to 16 rows with K < 16K: the panel
-    # kernel, whole K per workgroup, no scratch; E4M3 codes at 8K <= K < 16K
-    # take the tile kernel with K split 4 ways
+    # W8A16 / fp16 up to 16 activation rows, N >= 1024, K a multiple of 512
+    # from 2048 on: the panel kernel, whole K per workgroup, no scratch; E4M3
+    # codes at 8K <= K < 16K take the tile kernel with K split 4 ways
     assert L.fp8q_linear_workspace_size(0, 12, 8192, 8192) == 0
     assert L.fp8q_linear_workspace_size(0, 12, 28672, 8192) == 0
     assert L.fp8q_linear_workspace_size(0, 12, 28672, 4096) == 0
+    assert L.fp8q_linear_workspace_size(0, 1, 4096, 4096) == 0
+    assert L.fp8q_linear_workspace_size(0, 12, 8192, 28672) == 0
     assert L.fp8q_linear_workspace_size(1, 12, 8192, 8192) == 4 * 12 * 8192 * 4
     assert L.fp8q_linear_workspace_size(1, 12, 28672, 8192) == 4 * 12 * 28672 * 4
     # a small N on a short K: 64-row tiles, no split (K under two chunks)
     assert L.fp8q_linear_workspace_size(0, 4, 64, 500) == 0
     # 17..64 rows with about one workgroup per CU: the panel kernel, whole K
-    # per workgroup, one launch, no scratch (bf16 and fp16 activations; E4M3
-    # codes keep the split tile kernel)
+    # per workgroup, one launch, no scratch
     assert L.fp8q_linear_workspace_size(0, 64, 4096, 4096) == 0
     assert L.fp8q_linear_workspace_size(2, 32, 4096, 4096) == 0
     # otherwise K splits towards 256 workgroups (at least two chunks each),
@@ -82,8 +80,8 @@ def test_workspace_queries(L):
     #   ranges of 2048 (4 waves x 512): N=1022, K=8192 -> 64 x 4 workgroups,
     #   partial rows padded to 1024
     assert L.fp8q_linear_workspace_size(0, 12, 1022, 8192) == 4 * 12 * 1024 * 4
-    #   M=12, N=8192, K=28672 (16-step chunks of 1024): 2 splits
-    assert L.fp8q_linear_workspace_size(0, 12, 8192, 28672) == 2 * 12 * 8192 * 4
+    #   E4M3 codes, M=12, N=8192, K=28672 (16-step chunks of 1024): 2 splits
+    assert L.fp8q_linear_workspace_size(1, 12, 8192, 28672) == 2 * 12 * 8192 * 4
     #   M=40, N=100, K=3000: 2 tiles, at most 2 splits of whole 512-k chunks
     assert L.fp8q_linear_workspace_size(0, 40, 100, 3000) == 2 * 40 * 100 * 4
     assert L.fp8q_linear_workspace_size(0, 0, 4096, 4096) == 0
@@ -129,11 +127,15 @@ def test_dynamic_host_validation(L):
 def test_describe(L):
     buf = ctypes.create_string_buffer(256)
     assert L.fp8q_linear_describe(0, 1, 4096, 4096, buf, 256) == 0
-    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
+    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 4, 4>") and b"grid=(256,1)" in buf.value
     assert L.fp8q_linear_describe(0, 64, 4096, 4096, buf, 256) == 0
-    assert buf.value.startswith(b"k_w8a16_panel<2, 2, 4, 2, 4>") and b"grid=(128,2)" in buf.value
+    assert buf.value.startswith(b"k_w8a16_panel<2, 2, 2, 2, 4>") and b"grid=(128,2)" in buf.value
     assert L.fp8q_linear_describe(0, 32, 4096, 4096, buf, 256) == 0
-    assert buf.value.startswith(b"k_w8a16_panel<1, 2, 4, 2, 4>") and b"grid=(256,1)" in buf.value
+    assert buf.value.startswith(b"k_w8a16_panel<2, 1, 2, 3, 4>") and b"grid=(128,2)" in buf.value
+    assert L.fp8q_linear_describe(0, 12, 28672, 8192, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<7, 1, 2, 2, 4>") and b"grid=(256,1)" in buf.value
+    assert L.fp8q_linear_describe(1, 32, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<2, 1, 4, 3, 4>")
     assert L.fp8q_linear_describe(1, 64, 4096, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_panel<2, 2, 4, 2, 4>")
     assert L.fp8q_linear_describe(1, 64, 1024, 4096, buf, 256) == 0
@@ -144,6 +146,14 @@ def test_describe(L):
     assert L.fp8q_linear_describe(1, 8, 4096, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
     assert L.fp8q_linear_describe(2, 1, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 4, 4>")
+    # fewer than 96 workgroups on K > 4096 (the 70B k/v): the split rows kernel
+    assert L.fp8q_linear_describe(0, 12, 1024, 8192, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>") and b"splits=4" in buf.value
+    assert L.fp8q_linear_describe(0, 8, 1024, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 4, 4>") and b"grid=(64,1)" in buf.value
+    # a K that is not a multiple of 512: the rows kernel
+    assert L.fp8q_linear_describe(0, 1, 4096, 4000, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
     assert L.fp8q_linear_workspace_size(2, 64, 4096, 4096) == L.fp8q_linear_workspace_size(0, 64, 4096, 4096)
     assert L.fp8q_linear_describe(7, 1, 1, 1, buf, 256) == 1
@@ -194,6 +204,8 @@ def test_linear_host_validation(L):
         ((1, 1, 64, 64, NULL, 16, 64, 16), 1),          # x_scale missing in W8A8
         ((0, 0, 64, 64, NULL, 16, 64, 16), 0),          # empty M: no-op
         ((1, 4, 64, 64, fake, 0, 64, 16), 0),           # empty N: no-op
+        ((0, 1, 64, 1 << 28, NULL, 16, 64, 16), 1),     # ld_x >= 2^28
+        ((2, 1, 64, 64, NULL, 16, 1 << 28, 16), 1),     # ld_w >= 2^28
     ]
     for (mode, m, k, ldx, xs, n, ldw, ldy), want in cases:
         got = L.fp8q_linear(mode, NULL, m, k, ldx, xs, NULL, n, ldw, NULL, NULL, ldy, NULL, 0, NULL)

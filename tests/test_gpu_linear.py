@@ -61,14 +61,15 @@ def all_codes_weight(n: int, k: int) -> np.ndarray:
     return w
 
 
-# shapes that take k_w8a16_panel (17..64 rows, K a multiple of 1024, about one
-# workgroup per CU), including a ragged last panel of weight rows and of
-# activation rows
+# shapes that take k_w8a16_panel (K a multiple of 512 from 2048 on; 17..64
+# rows where that makes about one workgroup per CU), including a ragged last
+# panel of weight rows and of activation rows
 PANEL_SHAPES = [(40, 4096, 2048), (20, 3200, 3072), (33, 4000, 2048), (64, 4096, 4096),
                 (17, 4096, 2048), (64, 3584, 8192),
-                # up to 16 rows on a wide weight: 2, 3, 4 or 7 weight fragments
+                # up to 16 rows: 1, 2, 3, 4 or 7 weight fragments per workgroup
                 (12, 8192, 2048), (5, 10240, 2048), (16, 28672, 2048), (1, 16384, 3072),
-                (7, 9000, 2560)]
+                (7, 9000, 2560), (3, 4096, 2048), (16, 2048, 2560), (8, 1024, 2048),
+                (9, 12288, 2048), (4, 1536, 14336)]
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 64), (1, 256, 64), (64, 272, 64), (12, 256, 64),

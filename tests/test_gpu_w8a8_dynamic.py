@@ -50,7 +50,7 @@ def run_dynamic(fq, x_bits, wq, ws):
 
 # (m, n, k, the GEMM kernel it takes after the absmax pass)
 SHAPES = [(1, 4096, 4096, "k_w8a16_panel"), (8, 4096, 4096, "k_w8a16_panel"),
-          (12, 1024, 8192, "k_w8a16_rows"), (5, 256, 1000, "k_w8a16_tile"),
+          (12, 1024, 8192, "k_w8a16_rows"), (12, 2048, 4096, "k_w8a16_panel"), (5, 256, 1000, "k_w8a16_tile"),
           (16, 28672, 512, "k_w8a16_tile"), (32, 4096, 4096, "k_act_cast<0> + k_w8a16_panel"),
           (64, 4096, 4096, "k_act_cast<0> + k_w8a16_panel"), (40, 300, 3000, "k_w8a16_tile"),
           (3, 100, 13, "k_w8a16"), (12, 8192, 8192, "k_w8a16_panel"),
