@@ -914,10 +914,13 @@ def layer_rows(fq, L, up_bf16, ptr, workloads, torch, dev, cpu, iters, stream) -
     b = sum(lin.n * lin.k + 4 * lin.n + 2 * m * lin.k + 2 * m * lin.n for lin, *_ in layer)
     per = {}
     for lin, wq, ws, x, y, wsb, nws in layer:
-        def one(lin=lin, wq=wq, ws=ws, x=x, y=y, wsb=wsb, nws=nws):
-            st = L.fp8q_linear(0, ptr(x), m, lin.k, lin.k, None, ptr(wq), lin.n, wq.stride(0), ptr(ws),
-                               ptr(y), lin.n, ptr(wsb), nws, stream())
-            if st != 0:
+        # the C call as a caller holding raw pointers makes it: arguments
+        # marshalled once, so the time is the library's host path + the GPU's
+        args = (0, ptr(x), m, lin.k, lin.k, None, ptr(wq), lin.n, wq.stride(0), ptr(ws), ptr(y),
+                lin.n, ptr(wsb), nws, stream())
+
+        def one(args=args):
+            if L.fp8q_linear(*args) != 0:
                 raise RuntimeError(fq._lib.last_error())
         mso = time_eager(torch, one, iters)
         bb = lin.n * lin.k + 4 * lin.n + 2 * m * lin.k + 2 * m * lin.n
@@ -1001,9 +1004,10 @@ def layer_rows(fq, L, up_bf16, ptr, workloads, torch, dev, cpu, iters, stream) -
         "timing": "one HIP graph per layer step (856 MB of weights: no Infinity Cache reuse)",
         "kernels": {lin.name: fq.describe_linear(0, m, lin.n, lin.k) for lin, *_ in layer},
         "per_linear_eager": per,
-        "per_linear_eager_note": "one eager call after another on the same weights: host call "
-                                 "overhead included, and weights under 256 MB may be served "
-                                 "from the Infinity Cache (a latency figure, not an HBM one)"}
+        "per_linear_eager_note": "one eager C call after another on the same weights (arguments "
+                                 "marshalled once): the library's host path included, and weights "
+                                 "under 256 MB may be served from the Infinity Cache (a latency "
+                                 "figure, not an HBM one)"}
     log(rows["a5_layer_decode_70b"])
     if cpu is not None and "layer_decode_70b" in cpu:
         c = cpu["layer_decode_70b"]

@@ -8,6 +8,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -91,6 +92,54 @@ fp8q_status prepare(hipStream_t stream, int *dev)
     return check_device(*dev);
 }
 
+// Device allocations this thread has already validated.  A pointer inside
+// one of them skips the runtime query: hipPointerGetAttributes looks the
+// address up among all of the process's allocations, which costs
+// microseconds per pointer once a process holds many of them.  The last
+// kKnownRanges allocations are remembered, replaced in turn.
+// FP8Q_POINTER_CACHE=0 turns the memory off.  Not detected while a range is
+// remembered: an allocation that is freed and whose address range is handed
+// to host memory afterwards.
+struct KnownRange {
+    uintptr_t lo = 0, hi = 0;
+    int dev = -1;
+};
+constexpr int kKnownRanges = 32;
+thread_local KnownRange t_known[kKnownRanges];
+thread_local int t_known_next = 0;
+
+bool pointer_cache_on()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("FP8Q_POINTER_CACHE");
+        return !(e != nullptr && std::strcmp(e, "0") == 0);
+    }();
+    return on;
+}
+
+bool known_device_pointer(uintptr_t q, int dev)
+{
+    for (const KnownRange &r : t_known)
+        if (r.dev == dev && q >= r.lo && q < r.hi)
+            return true;
+    return false;
+}
+
+void remember_allocation(const void *p, int dev)
+{
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) != hipSuccess || size == 0) {
+        (void)hipGetLastError();
+        return;
+    }
+    KnownRange &r = t_known[t_known_next];
+    r.lo = reinterpret_cast<uintptr_t>(base);
+    r.hi = r.lo + size;
+    r.dev = dev;
+    t_known_next = (t_known_next + 1) % kKnownRanges;
+}
+
 // A pointer the kernels will dereference: non-null, aligned, device memory
 // on the stream's device.
 fp8q_status check_ptr(const void *p, const char *name, int dev, size_t align)
@@ -99,6 +148,9 @@ fp8q_status check_ptr(const void *p, const char *name, int dev, size_t align)
         return fail(FP8Q_ERR_INVALID_ARG, "%s is NULL", name);
     if (align > 1 && (reinterpret_cast<uintptr_t>(p) % align) != 0)
         return fail(FP8Q_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+    const bool cache = pointer_cache_on();
+    if (cache && known_device_pointer(reinterpret_cast<uintptr_t>(p), dev))
+        return FP8Q_OK;
     hipPointerAttribute_t attr;
     std::memset(&attr, 0, sizeof(attr));
     hipError_t e = hipPointerGetAttributes(&attr, p);
@@ -112,6 +164,8 @@ fp8q_status check_ptr(const void *p, const char *name, int dev, size_t align)
     if (attr.device != dev)
         return fail(FP8Q_ERR_INVALID_ARG, "%s lives on device %d but the stream is on device %d",
                     name, attr.device, dev);
+    if (cache)
+        remember_allocation(p, dev);
     return FP8Q_OK;
 }
 
@@ -818,9 +872,10 @@ void describe_w8a16(const fp8q::launch::W8A16Plan &p, char *buf, size_t len)
         std::snprintf(spg, sizeof spg, ", %lld", (long long)(p.group / 64));
     if (p.kind == fp8q::launch::W8A16Plan::kPanel)
         std::snprintf(buf, len,
-                      "k_w8a16_panel<%d, %d, %d, %d, %d> grid=(%lld,%lld) block=%d staged_rows=%d splits=1",
+                      "k_w8a16_panel<%d, %d, %d, %d, %d> grid=(%lld,%lld) block=%d staged_rows=%d "
+                      "rows_per_workgroup=%d splits=1",
                       p.af, p.mb, p.steps, p.depth, p.waves, (long long)p.grid_n,
-                      (long long)p.grid_m, 64 * p.waves, p.xd);
+                      (long long)p.grid_m, 64 * p.waves, p.xd, p.rpw > 0 ? p.rpw : 16 * p.mb);
     else if (p.kind == fp8q::launch::W8A16Plan::kRows)
         std::snprintf(buf, len,
                       "k_w8a16_rows<%d, %d, %d, %d%s> rows=%d grid=(%lld,%lld,%lld) block=%d "

@@ -86,9 +86,9 @@ struct W8A16Plan {
     int64_t ldp;       // row stride of the fp32 partial tiles (n rounded up to 4)
     size_t workspace;  // scratch bytes: the partial tiles [splits][m][ldp] (0 if no split)
     int64_t group;     // 0: one weight scale per row; else k per weight-scale group
+    int rpw;           // k_w8a16_panel: activation rows per workgroup (0: 16 * mb)
 };
-// act: the activation type (kW8A16Act* below); E4M3 codes cannot take the
-// panel kernel, which stages 16-bit rows.
+// act: the activation type (kW8A16Act* below).
 W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act = 0);
 // Per-group weight scales (w_scale [n, ceil(k / group)]); group is 64, 128,
 // 256 or 512.  The tile kernel serves every activation type and M.

@@ -911,13 +911,19 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 // that only feed output columns that are never stored; the LDS rows past XS
 // are zeroed once.
 //
+// RPW: activation rows per workgroup along the grid's y (16 * MB unless a
+// small weight needs more workgroups: the activation rows are then spread
+// over more of them, each reading the same weight panel, which the other
+// workgroups of its column find in L2).  Panel rows past RPW feed outputs
+// that are never stored.
+//
 // The host plans this kernel only for K a multiple of NWV * 64 * CS with at
 // least D chunks per wave.  Rows past N or M are clamped to a valid row when
 // loading and their outputs are never stored.  A load instruction covers at
 // most 8 weight rows or 4 activation rows, addressed from that group's first
 // row, so the per-lane 32-bit offsets hold for row strides below 2^28 bytes
 // (checked by the host).
-template <int AF, int MB, int CS, int D, int NWV, int AT, int XS = 16 * MB>
+template <int AF, int MB, int CS, int D, int NWV, int AT, int XS = 16 * MB, int RPW = 16 * MB>
 __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const void *__restrict__ xv, int64_t m, int64_t k, int64_t ld_x,
     const float *__restrict__ x_scale,
@@ -944,6 +950,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     constexpr int SLOT = XSLOTS * XSLOT + D * WSLOT;
     constexpr int RED = (int)sizeof(v4f) * NWV * AF * MB * kWave;
     static_assert(RU % 16 == 0 && (XS * XU) % kWave == 0 && XS <= XR && XS > 0, "chunk shape");
+    static_assert(RPW > 0 && RPW <= XR, "activation rows per workgroup");
     static_assert((WR * WU) % kWave == 0 && (WU & (WU - 1)) == 0, "weight chunk shape");
     static_assert(D >= 1 && D <= 4, "chunks in flight");
     // the waves' slots; after the K loop the same bytes hold the waves' fp32
@@ -955,7 +962,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const int r = lane & 15;          // row of the A (weight) / B (activation) operand
     const int g = lane >> 4;          // which 16 k-values of a 64-k step this lane holds
     const int64_t n0 = (int64_t)blockIdx.x * WR;
-    const int64_t m0 = (int64_t)blockIdx.y * XR;
+    const int64_t m0 = (int64_t)blockIdx.y * RPW;
     const int64_t kq = k / NWV;
     const int64_t kb = (int64_t)wave * kq;
     const int nch = (int)(kq / CK);
@@ -1144,7 +1151,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
         const int j = f % MB;
         const int64_t mr = m0 + 16 * j + (ln & 15);
         const int64_t nb = n0 + 16 * a + 4 * (ln >> 4);
-        if (mr >= m || nb >= n)
+        if (mr >= m || nb >= n || 16 * j + (ln & 15) >= RPW)
             continue;
         v4f sum = red[f * kWave + ln];
 #pragma unroll
@@ -1283,7 +1290,8 @@ static void plan_tile(W8A16Plan &p, int64_t m, int64_t k, int steps_mb1)
 // sums).  Measured on MI355X in graphs, weights rotating through 2 GiB:
 //  - up to 16 activation rows, one activation group (MB = 1): AF weight
 //    fragments per workgroup, AF in {1, 2, 3, 4, 7}, the AF whose grid wastes
-//    the least of whole rounds of 256 workgroups (ties to the larger AF).
+//    the least of whole rounds of 256 workgroups (ties to the larger AF);
+//    a weight of 256..1535 rows spreads the activation rows 4 per workgroup.
 //    Llama-3-8B q_proj (4096 x 4096): M = 1 5.7 us, M = 8 5.9 us, M = 16
 //    6.7 us against 5.8 / 7.0 / 8.3 us for the rows kernel; Llama-3-70B at
 //    M = 12: q/o (8192 x 8192) 14.1 us, gate/up (28672 x 8192) 42.6 us,
@@ -1310,10 +1318,11 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act)
     p.waves = 4;
     p.splits = 1;
     p.workspace = 0;
+    p.rpw = 0;
     p.kper = k;
     p.kchunk = k / 4;
     if (m <= 16) {
-        if (f8 || n < 1024)
+        if (f8 || n < 256)
             return false;
         static const int kAf[5] = {1, 2, 3, 4, 7};
         int best = 0;
@@ -1325,12 +1334,32 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act)
                 best_cost = cost;
             }
         }
-        // fewer than 96 workgroups on a long K: the split rows kernel + reduce
-        // (Llama-3-70B k/v, 1024 x 8192, at M = 12: 7.4 us against 8.4 us);
-        // casting the activations on the fly needs more workgroups still
-        // (1024 x 8192: 24 us on 64 workgroups)
-        if ((div_up(n, 16 * kAf[best]) < 96 && k > 4096) || (q && n < 2048))
+        // casting the activations on the fly needs many workgroups (1024 x
+        // 8192: 24 us on 64 workgroups against 7.4 us for the split rows
+        // kernel + reduce on bf16)
+        if (q && n < 2048)
             return false;
+        if (div_up(n, 16) < 96 && !q) {
+            // a small weight (Llama-3 k/v, 1024 rows): 16-row panels, the
+            // activation rows spread 4 per workgroup (each weight panel read
+            // by div_up(m, 4) workgroups, from L2 after the first).  At M =
+            // 12: 70B k/v (1024 x 8192) 6.8 us against 7.4 us for the split
+            // rows kernel + reduce and 8.4 us for one workgroup per panel;
+            // 8B k/v (1024 x 4096) 4.6 against 4.8 us.
+            if (k % 1024 != 0)
+                return false;
+            p.af = 1;
+            p.mb = 1;
+            p.rpw = 4;
+            p.steps = 4;
+            p.depth = 2;
+            p.xd = 4;
+            p.rows = 16;
+            p.grid_n = div_up(n, 16);
+            p.grid_m = div_up(m, 4);
+            out = p;
+            return true;
+        }
         p.af = kAf[best];
         p.mb = 1;
         p.steps = 2;
@@ -1539,15 +1568,15 @@ static void launch_tile(const W8A16Plan &p, const void *x, int64_t m, int64_t k,
 }
 
 // k_w8a16_panel, 4 waves (the configurations plan_panel picks).
-template <int AF, int MB, int CS, int D, int AT, int XS = 16 * MB>
+template <int AF, int MB, int CS, int D, int AT, int XS = 16 * MB, int RPW = 16 * MB>
 static void launch_panel(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
                          const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
                          const float *w_scale, uint16_t *y, int64_t ld_y, const QuantArgs &qa,
                          hipStream_t stream)
 {
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
-    hipLaunchKernelGGL((k_w8a16_panel<AF, MB, CS, D, 4, AT, XS>), grid, dim3(4 * kWave), 0, stream,
-                       x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, qa);
+    hipLaunchKernelGGL((k_w8a16_panel<AF, MB, CS, D, 4, AT, XS, RPW>), grid, dim3(4 * kWave), 0,
+                       stream, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, qa);
 }
 
 template <int AT>
@@ -1560,7 +1589,7 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
     if (p.group == 0 && p.kind == W8A16Plan::kPanel) {
 #define FP8Q_PANEL_CASE(AF, MB, CS, D, XS)                                                    \
             if (p.af == AF && p.mb == MB && p.steps == CS && p.depth == D && p.waves == 4 &&    \
-                p.xd == XS) {                                                                 \
+                p.xd == XS && p.rpw == 0) {                                                   \
                 launch_panel<AF, MB, CS, D, AT, XS>(p, x, m, k, ld_x, x_scale, w, n, ld_w,       \
                                                     w_scale, y, ld_y, qa, stream);            \
                 return hipGetLastError();                                                     \
@@ -1581,6 +1610,13 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
             FP8Q_PANEL_CASE(1, 1, 2, 4, 16) FP8Q_PANEL_CASE(2, 1, 2, 4, 16) FP8Q_PANEL_MB1(16)
             FP8Q_PANEL_CASE(2, 1, 2, 3, 16)
             FP8Q_PANEL_CASE(2, 2, 2, 2, 32)
+            // a small weight: 4 activation rows per workgroup
+            if (p.af == 1 && p.mb == 1 && p.steps == 4 && p.depth == 2 && p.waves == 4 &&
+                p.xd == 4 && p.rpw == 4) {
+                launch_panel<1, 1, 4, 2, AT, 4, 4>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale,
+                                                   y, ld_y, qa, stream);
+                return hipGetLastError();
+            }
         }
 #undef FP8Q_PANEL_MB1
 #undef FP8Q_PANEL_CASE

@@ -29,9 +29,18 @@
  * are reported through an optional device flag (set to 1, never cleared by
  * the library), and the codes they produce are unspecified.
  *
- * Threading.  Calls are thread-safe; the only shared state is a per-device
- * cache of device properties.  Two calls that share a workspace must be
- * ordered on one stream.
+ * Pointer checks.  Every pointer a kernel dereferences is checked to be
+ * device memory on the stream's device (hipPointerGetAttributes).  Each
+ * thread remembers the last 32 device allocations it has checked, and a
+ * pointer inside one of them is not queried again (the query costs
+ * microseconds per pointer in a process with many allocations).  Not
+ * detected while an allocation is remembered: freeing it and handing its
+ * address range to host memory.  Setting the environment variable
+ * FP8Q_POINTER_CACHE=0 turns the memory off.
+ *
+ * Threading.  Calls are thread-safe; the shared state is a per-device cache
+ * of device properties (the pointer memory above is per thread).  Two calls
+ * that share a workspace must be ordered on one stream.
  */
 #ifndef FP8Q_H
 #define FP8Q_H

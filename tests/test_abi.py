@@ -76,10 +76,13 @@ def test_workspace_queries(L):
     # with fp32 partial tiles [splits][m][n rounded up to 4]
     #   M=64, N=1024, K=4096: 16 tiles -> 4 splits of 1024
     assert L.fp8q_linear_workspace_size(0, 64, 1024, 4096) == 4 * 64 * 1024 * 4
-    #   a small N on a long K (k/v projections): 16-row workgroups, K split in
-    #   ranges of 2048 (4 waves x 512): N=1022, K=8192 -> 64 x 4 workgroups,
-    #   partial rows padded to 1024
-    assert L.fp8q_linear_workspace_size(0, 12, 1022, 8192) == 4 * 12 * 1024 * 4
+    #   a small N on a long K (k/v projections) with K not a multiple of 512:
+    #   16-row workgroups, K split in whole ranges of 2048 (4 waves x 512):
+    #   N=1022, K=7000 -> 2 splits of 4096, partial rows padded to 1024
+    assert L.fp8q_linear_workspace_size(0, 12, 1022, 7000) == 2 * 12 * 1024 * 4
+    #   with K a multiple of 1024 the panel kernel spreads the activation rows
+    #   4 per workgroup instead: no scratch
+    assert L.fp8q_linear_workspace_size(0, 12, 1022, 8192) == 0
     #   E4M3 codes, M=12, N=8192, K=28672 (16-step chunks of 1024): 2 splits
     assert L.fp8q_linear_workspace_size(1, 12, 8192, 28672) == 2 * 12 * 8192 * 4
     #   M=40, N=100, K=3000: 2 tiles, at most 2 splits of whole 512-k chunks
@@ -147,11 +150,16 @@ def test_describe(L):
     assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
     assert L.fp8q_linear_describe(2, 1, 4096, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 4, 4>")
-    # fewer than 96 workgroups on K > 4096 (the 70B k/v): the split rows kernel
+    # a weight of under 96 16-row panels (the Llama-3 k/v): 4 activation rows
+    # per workgroup
     assert L.fp8q_linear_describe(0, 12, 1024, 8192, buf, 256) == 0
-    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>") and b"splits=4" in buf.value
+    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 4, 2, 4>") and b"grid=(64,3)" in buf.value
+    assert b"rows_per_workgroup=4" in buf.value
     assert L.fp8q_linear_describe(0, 8, 1024, 4096, buf, 256) == 0
-    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 4, 4>") and b"grid=(64,1)" in buf.value
+    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 4, 2, 4>") and b"grid=(64,2)" in buf.value
+    # on the fly quantized activations keep the split rows kernel there
+    assert L.fp8q_linear_w8a8_dynamic_describe(12, 1024, 8192, buf, 256) == 0
+    assert b"k_w8a16_rows<1, 1, 8, 4>" in buf.value and b"splits=4" in buf.value
     # a K that is not a multiple of 512: the rows kernel
     assert L.fp8q_linear_describe(0, 1, 4096, 4000, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")

@@ -69,7 +69,10 @@ PANEL_SHAPES = [(40, 4096, 2048), (20, 3200, 3072), (33, 4000, 2048), (64, 4096,
                 # up to 16 rows: 1, 2, 3, 4 or 7 weight fragments per workgroup
                 (12, 8192, 2048), (5, 10240, 2048), (16, 28672, 2048), (1, 16384, 3072),
                 (7, 9000, 2560), (3, 4096, 2048), (16, 2048, 2560), (8, 1024, 2048),
-                (9, 12288, 2048), (4, 1536, 14336)]
+                (9, 12288, 2048), (4, 1536, 14336),
+                # a weight of under 96 16-row panels: 4 activation rows per
+                # workgroup (ragged last row group and weight panel)
+                (13, 1000, 4096), (16, 1024, 8192)]
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 64), (1, 256, 64), (64, 272, 64), (12, 256, 64),
@@ -425,6 +428,11 @@ def test_host_pointer_and_device_checks(fq):
     assert st == 0, L.fp8q_last_error()
     torch.cuda.synchronize()
     assert (y.float() == 0).all()
+    # the allocations remembered by the valid call admit no host memory
+    for hp in (host.data_ptr(), buf.ctypes.data):
+        st = L.fp8q_linear(0, x.data_ptr(), 4, 64, 64, None, hp, 16, 64,
+                           ws.data_ptr(), y.data_ptr(), 16, None, 0, stream)
+        assert st == 1, L.fp8q_last_error()
 
 
 @pytest.mark.parametrize("mode,m,n,k", [(1, 300, 300, 256), (1, 520, 1000, 384), (1, 300, 300, 200),
