@@ -3,19 +3,31 @@
 // ("FP8量化与长上下文实测：Llama 3 70B部署优化指南", §3.1) rounds:
 // E4M3_RNE_SAT(fl32(x / s)).
 //
-// A correctly rounded fp32 division costs about ten vector instructions, and
-// in the per-tensor activation cast that work, not the memory traffic, set
-// the time.  With r = fl32(1 / s) computed once, t = fl32(x * r) is within
-// 1.5 * 2^-23 * |x / s| of x / s, so within 2^-22 * |t| of fl32(x / s) (both
-// normal).  E4M3 rounding (with the saturating clamp) is a monotone step
-// function of its input, so if t * (1 - 2^-20) and t * (1 + 2^-20) -- an
-// interval that contains fl32(x / s) with a 4x margin -- round to the same
-// code, that is the code of fl32(x / s).  Otherwise (t lies near a midpoint
-// between two E4M3 values, about 1 element in 10^5) the exact quotient is
-// computed.  Zeros keep their sign through the product; every value below
-// 2^-10 rounds to a signed zero either way.  Scales whose reciprocal is not a
-// normal number with margin (held scales beyond 2^125, or non-finite ones)
-// take the exact division throughout.
+// A correctly rounded fp32 division costs about ten vector instructions and a
+// branch per value, which made the per-tensor activation cast, and above all
+// the decode GEMM that casts the activations it stages, bound by the ALU.
+// Instead, with r = fl32(1 / s) computed once per kernel (an IEEE division),
+// every quotient is formed by a product and Markstein's FMA correction
+// (Markstein, "Computation of elementary functions on the IBM RISC System/6000
+// processor", IBM J. Res. Dev. 34(1), 1990; the correction step of IA-64
+// division):
+//   q0 = fl32(x * r),   q1 = fma(fma(-q0, s, x), r, q0),
+// and for scales the caller does not guarantee to be dynamic ones, a second
+// step q2 = fma(fma(-q1, s, x), r, q1).  Markstein's theorem: if r is within
+// half an ulp of 1 / s and q within one ulp of x / s, then fma(-q, s, x) is
+// exact and fma(that, r, q) is the correctly rounded x / s.  q1 is within one
+// ulp, so the second step is correctly rounded for any normal scale.  One
+// step was checked exhaustively against IEEE division on the CPU for every
+// finite bf16 x and every dynamic scale max(fl32(amax / 448), 1e-12) of a
+// finite bf16 amax (1.2e9 pairs, no difference), plus 8000 other scales in
+// [2^-40, 2^40]; the dynamic per-tensor path uses it.
+//
+// Quotients of magnitude 512 and more saturate to +-448 either way, so there
+// (and for infinities) q0 is used as it is; below 2^-10 every value rounds to
+// a signed zero, and the sign of a zero quotient is the sign of x, so the
+// result takes x's sign.  Scales whose reciprocal is not a normal number with
+// margin (held scales beyond 2^125, or non-finite ones) take the IEEE
+// division throughout.
 #pragma once
 
 #include "device_common.hpp"
@@ -24,14 +36,28 @@ namespace fp8q {
 namespace dev {
 
 struct E4M3Div {
-    float s;     // the scale
-    float r;     // fl32(1 / s)
-    bool fast;   // r and s normal with margin: the product path is valid
+    float s;          // the scale
+    float r;          // fl32(1 / s)
+    bool fast;        // r and s normal with margin: the product path is valid
+    bool two_steps;   // the scale is not known to be a dynamic one
 
-    __device__ __forceinline__ explicit E4M3Div(float scale) : s(scale)
+    // dynamic: s = max(fl32(amax / 448), 1e-12f) for a bf16 amax, where one
+    // correction step is exhaustively verified.
+    __device__ __forceinline__ explicit E4M3Div(float scale, bool dynamic = false)
+        : s(scale), two_steps(!dynamic)
     {
         r = 1.0f / scale;
         fast = scale >= 0x1p-125f && scale <= 0x1p125f && r >= 0x1p-125f && r <= 0x1p125f;
+    }
+
+    // fl32(x / s) where |x / s| < 512; q0 (already saturating) beyond.
+    __device__ __forceinline__ float quot(float x) const
+    {
+        const float q0 = __fmul_rn(x, r);
+        float q = __fmaf_rn(__fmaf_rn(-q0, s, x), r, q0);
+        if (two_steps)
+            q = __fmaf_rn(__fmaf_rn(-q, s, x), r, q);
+        return __builtin_fabsf(q0) < 512.0f ? __builtin_copysignf(q, x) : q0;
     }
 
     // Eight bf16 values (a uint4) divided by s, cast to eight E4M3 codes.
@@ -39,20 +65,10 @@ struct E4M3Div {
     {
         if (!fast)
             return quantize8(v, s);
-        constexpr float dn = 1.0f - 0x1p-20f;
-        constexpr float up = 1.0f + 0x1p-20f;
-        const float t0 = bf16_lo(v.x) * r, t1 = bf16_hi(v.x) * r;
-        const float t2 = bf16_lo(v.y) * r, t3 = bf16_hi(v.y) * r;
-        const float t4 = bf16_lo(v.z) * r, t5 = bf16_hi(v.z) * r;
-        const float t6 = bf16_lo(v.w) * r, t7 = bf16_hi(v.w) * r;
-        uint2 a, b;
-        a.x = e4m3x4(t0 * dn, t1 * dn, t2 * dn, t3 * dn);
-        a.y = e4m3x4(t4 * dn, t5 * dn, t6 * dn, t7 * dn);
-        b.x = e4m3x4(t0 * up, t1 * up, t2 * up, t3 * up);
-        b.y = e4m3x4(t4 * up, t5 * up, t6 * up, t7 * up);
-        if (a.x == b.x && a.y == b.y)
-            return a;
-        return quantize8(v, s);
+        uint2 c;
+        c.x = e4m3x4(quot(bf16_lo(v.x)), quot(bf16_hi(v.x)), quot(bf16_lo(v.y)), quot(bf16_hi(v.y)));
+        c.y = e4m3x4(quot(bf16_lo(v.z)), quot(bf16_hi(v.z)), quot(bf16_lo(v.w)), quot(bf16_hi(v.w)));
+        return c;
     }
 };
 

@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void k_act_cast(
         s = *held;
     }
 
-    const E4M3Div div(s);
+    const E4M3Div div(s, SRC == kFromPartials);
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (layout == kScalar) {

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a16_rows(
         xp[j] = static_cast<const uint8_t *>(xv) + ((xr < m ? xr : m0) * ld_x + 16 * g) * ES;
     }
     const float xs = act_scale<AT>(x_scale, qa);
-    const E4M3Div div(AT == kActQ ? xs : 1.0f);
+    const E4M3Div div(AT == kActQ ? xs : 1.0f, true);
 
     v4f acc[2][AF][MB];
 #pragma unroll
@@ -624,7 +624,7 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
     typedef typename std::conditional<F8, uint2, v4u>::type XReg;
     const uint8_t *x8 = static_cast<const uint8_t *>(xv);
     const float xs = act_scale<AT>(x_scale, qa);
-    const E4M3Div div(AT == kActQ ? xs : 1.0f);
+    const E4M3Div div(AT == kActQ ? xs : 1.0f, true);
     __shared__ __attribute__((aligned(16))) uint8_t xlds[2 * XR * RB];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -971,7 +971,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const uint32_t xslot_lds = (uint32_t)(uintptr_t)xslot;
     const uint32_t wslot_lds = (uint32_t)(uintptr_t)wslot;
     const float xs = act_scale<AT>(x_scale, qa);
-    const E4M3Div div(AT == kActQ ? xs : 1.0f);
+    const E4M3Div div(AT == kActQ ? xs : 1.0f, true);
 
     // weight load i of a chunk fills LDS bytes [1 KB i, 1 KB (i + 1)) of the
     // slot: rows WPI * i .. WPI * (i + 1) - 1, lane l at row l / WU, position
