@@ -20,6 +20,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -91,20 +92,17 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t codes)
     return r;
 }
 
-// fp32 -> bf16 bit pattern, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return 0x7FC0u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
+// Two fp32 values -> two bf16 bit patterns (lo in bits 15:0), round to
+// nearest even: one v_cvt_pk_bf16_f32 (gfx950), where the integer rounding it
+// replaced took about five instructions per value -- enough to show in the
+// epilogues of the GEMMs (a 256 x 256 tile is 128 values per lane).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
 }
+
+// fp32 -> bf16 bit pattern, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 
 // Wave-wide unsigned max (64 lanes).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
