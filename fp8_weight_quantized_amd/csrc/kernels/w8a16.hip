@@ -900,10 +900,17 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 // that belongs at its LDS position), so the 16-row operand reads are free of
 // bank conflicts.
 //
-// Activation types that are converted on the way -- E4M3 codes widened to
-// bf16 (kActF8), bf16 cast to E4M3 and back (kActQ) -- load into registers
-// instead, D chunks ahead, and each wave writes its converted chunk into a
-// single LDS slot before its MFMAs read it.
+// Every activation type arrives the same way.  16-bit activations are
+// staged as they are; bf16 activations quantized on the fly (kActQ) are cast
+// to E4M3 and widened back to bf16 in place in their slot (one read and one
+// write per staged unit, by the wave that owns the slot) before the MFMAs
+// read them; E4M3 activation codes (kActF8) are staged as codes and widened
+// to bf16 after the operand read, as the weights are.  No value of the
+// pipeline passes through a compiler-visible load: loaded into registers
+// instead, the compiler guarded each use with its own vmcnt wait, counting
+// only the loads it could see, and so waited for direct loads of later
+// chunks too (the E4M3 decode took 8.6 us at M = 1 on q_proj against 5.7 us
+// for bf16).
 //
 // XS: activation rows staged per chunk (the panel's first XS rows; the host
 // plans XS >= the rows that exist).  Staging fewer rows than the panel has
@@ -930,30 +937,29 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y, QuantArgs qa)
 {
-    constexpr bool F8 = AT == kActF8;
-    constexpr bool XD = AT == kActBF16 || AT == kActF16;   // activations by direct loads
+    constexpr bool F8 = AT == kActF8;           // activations staged as E4M3 codes
     constexpr int CT = compute_type<AT>();
-    constexpr int ES = F8 ? 1 : 2;              // bytes per activation value in memory
+    constexpr int ES = F8 ? 1 : 2;              // bytes per activation value in memory and in LDS
     constexpr int XR = 16 * MB;                 // activation rows of the panel
     constexpr int WR = 16 * AF;                 // weight rows of the panel
     constexpr int CK = 64 * CS;                 // k per chunk
-    constexpr int RU = CK * 2 / 16;             // 16-byte units of a staged (bf16) row segment
-    constexpr int RB = 16 * RU;                 // bytes of a staged activation row segment
-    constexpr int XU = CK * ES / 16;            // 16-byte units loaded per activation row segment
+    constexpr int XU = CK * ES / 16;            // 16-byte units of an activation row segment
+    constexpr int XRB = 16 * XU;                // bytes of a staged activation row segment
     constexpr int NI = XS * XU / kWave;         // activation loads per lane per chunk
+    constexpr int XSW = XU >= 16 ? 15 : XU - 1; // activation unit swizzle mask
     constexpr int WU = CK / 16;                 // 16-byte units of a weight row segment
     constexpr int NW = WR * WU / kWave;         // weight loads per lane per chunk
     constexpr int LC = NI + NW;                 // loads per lane per chunk
     constexpr int WSW = WU >= 16 ? 15 : WU - 1; // weight unit swizzle mask
-    constexpr int XSLOT = XR * RB, WSLOT = WR * CK;
-    constexpr int XSLOTS = XD ? D : 1;
-    constexpr int SLOT = XSLOTS * XSLOT + D * WSLOT;
+    constexpr int XSLOT = XR * XRB, WSLOT = WR * CK;
+    constexpr int SLOT = D * (XSLOT + WSLOT);
     constexpr int RED = (int)sizeof(v4f) * NWV * AF * MB * kWave;
-    static_assert(RU % 16 == 0 && (XS * XU) % kWave == 0 && XS <= XR && XS > 0, "chunk shape");
-    static_assert(RPW > 0 && RPW <= XR, "activation rows per workgroup");
+    static_assert((XS * XU) % kWave == 0 && XS <= XR && XS > 0 && (XU & (XU - 1)) == 0,
+                  "chunk shape");
     static_assert((WR * WU) % kWave == 0 && (WU & (WU - 1)) == 0, "weight chunk shape");
+    static_assert(RPW > 0 && RPW <= XR, "activation rows per workgroup");
     static_assert(D >= 1 && D <= 4, "chunks in flight");
-    // the waves' slots; after the K loop the same bytes hold the waves' fp32
+    // the waves' rings; after the K loop the same bytes hold the waves' fp32
     // panels for the reduction
     __shared__ __attribute__((aligned(16))) uint8_t xl[NWV * SLOT > RED ? NWV * SLOT : RED];
 
@@ -966,16 +972,16 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const int64_t kq = k / NWV;
     const int64_t kb = (int64_t)wave * kq;
     const int nch = (int)(kq / CK);
-    uint8_t *xslot = xl + wave * SLOT;                  // XSLOTS activation slots
-    uint8_t *wslot = xslot + XSLOTS * XSLOT;            // D weight slots
+    uint8_t *xslot = xl + wave * SLOT;                  // D activation slots
+    uint8_t *wslot = xslot + D * XSLOT;                 // D weight slots
     const uint32_t xslot_lds = (uint32_t)(uintptr_t)xslot;
     const uint32_t wslot_lds = (uint32_t)(uintptr_t)wslot;
     const float xs = act_scale<AT>(x_scale, qa);
     const E4M3Div div(AT == kActQ ? xs : 1.0f, true);
 
-    // weight load i of a chunk fills LDS bytes [1 KB i, 1 KB (i + 1)) of the
-    // slot: rows WPI * i .. WPI * (i + 1) - 1, lane l at row l / WU, position
-    // l % WU, which holds global unit (l % WU) ^ swizzle(row)
+    // load i of a chunk fills LDS bytes [1 KB i, 1 KB (i + 1)) of the slot:
+    // for an operand of U units per row segment, rows (64 / U) i .. , lane l
+    // at row l / U, position l % U, which holds global unit (l % U) ^ swizzle(row)
     constexpr int WPI = kWave / WU;
     uint32_t woff[NW];
 #pragma unroll
@@ -987,31 +993,14 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     auto wbase = [&](int i, int c) {
         return w + min(n0 + WPI * i, n - 1) * ld_w + kb + (int64_t)c * CK;
     };
-    // activation load i of a chunk: unit f = 64 i + lane of the chunk's
-    // XS x XU loaded units, i.e. row f / XU, unit f % XU of that row
     const uint8_t *x8 = static_cast<const uint8_t *>(xv);
-    constexpr int XPI = kWave / XU;             // rows per activation load (direct loads)
-    uint32_t xoff[XD ? NI : 1];
-    const uint8_t *xp[XD ? 1 : NI];
-    int xo[XD ? 1 : NI], xo2[XD ? 1 : NI];      // LDS byte offsets of the staged unit(s)
-    if constexpr (XD) {
+    constexpr int XPI = kWave / XU;
+    uint32_t xoff[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int rho = XPI * i + lane / XU, q = lane % XU;
-            const int64_t row0 = min(m0 + XPI * i, m - 1);
-            xoff[i] = (uint32_t)((min(m0 + rho, m - 1) - row0) * ld_x * ES + 16 * (q ^ (rho & 15)));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int f = kWave * i + lane;
-            const int rho = f / XU, u = f % XU;
-            xp[i] = x8 + (min(m0 + rho, m - 1) * ld_x + kb) * ES + 16 * u;
-            // its staged (bf16) unit is the same one, or units 2u and 2u + 1 for codes
-            const int su = F8 ? 2 * u : u;
-            xo[i] = rho * RB + 16 * (su ^ (rho & 15));
-            xo2[i] = rho * RB + 16 * ((su + 1) ^ (rho & 15));
-        }
+    for (int i = 0; i < NI; ++i) {
+        const int rho = XPI * i + lane / XU, q = lane % XU;
+        const int64_t row0 = min(m0 + XPI * i, m - 1);
+        xoff[i] = (uint32_t)((min(m0 + rho, m - 1) - row0) * ld_x * ES + 16 * (q ^ (rho & XSW)));
     }
     auto xbase = [&](int i, int c) {
         return x8 + (min(m0 + XPI * i, m - 1) * ld_x + kb + (int64_t)c * CK) * ES;
@@ -1019,13 +1008,12 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
 
     if constexpr (XS < XR) {
 #pragma unroll
-        for (int u = 0; u < XSLOTS; ++u)
+        for (int u = 0; u < D; ++u)
 #pragma unroll
-            for (int o = XS * RB + 16 * lane; o < XR * RB; o += 16 * kWave)
+            for (int o = XS * XRB + 16 * lane; o < XR * XRB; o += 16 * kWave)
                 *reinterpret_cast<v4u *>(xslot + u * XSLOT + o) = v4u{0u, 0u, 0u, 0u};
     }
 
-    v4u xr[XD ? 1 : D][XD ? 1 : NI];
     v4f acc[AF][MB];
 #pragma unroll
     for (int a = 0; a < AF; ++a)
@@ -1033,18 +1021,10 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
         for (int j = 0; j < MB; ++j)
             acc[a][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    auto issue_x = [&](int u, int c) {
-        if constexpr (XD) {
+    auto issue = [&](int u, int c) {
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
-                dma16(xbase(i, c), xoff[i], xslot_lds + u * XSLOT + 1024 * i);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-                xr[u][i] = ldg(xp[i] + (int64_t)c * CK * ES);
-        }
-    };
-    auto issue_w = [&](int u, int c) {
+        for (int i = 0; i < NI; ++i)
+            dma16(xbase(i, c), xoff[i], xslot_lds + u * XSLOT + 1024 * i);
 #pragma unroll
         for (int i = 0; i < NW; ++i)
             dma16(wbase(i, c), woff[i], wslot_lds + u * WSLOT + 1024 * i);
@@ -1059,8 +1039,19 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
                 wait_vmcnt<j * LC>();
         });
     };
+    // kActQ: the staged bf16 units of slot u cast to E4M3 and widened back,
+    // in place (elementwise, so the units' swizzled positions do not matter)
+    auto quantize_slot = [&](int u) {
+        if constexpr (AT == kActQ) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                v4u *p = reinterpret_cast<v4u *>(xslot + u * XSLOT + 1024 * i + 16 * lane);
+                *p = qdq8(*p, div);
+            }
+        }
+    };
     auto compute = [&](int u) {
-        const uint8_t *xs_ = xslot + (XD ? u : 0) * XSLOT;
+        const uint8_t *xs_ = xslot + u * XSLOT;
         const uint8_t *ws_ = wslot + u * WSLOT;
 #pragma unroll
         for (int s = 0; s < CS; ++s) {
@@ -1074,13 +1065,20 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
 #pragma unroll
             for (int j = 0; j < MB; ++j) {
                 const int rho = 16 * j + r;
-                const int u0 = 8 * s + 2 * g;
-                const v4u b0 = *reinterpret_cast<const v4u *>(xs_ + rho * RB + 16 * (u0 ^ (rho & 15)));
-                const v4u b1 = *reinterpret_cast<const v4u *>(xs_ + rho * RB + 16 * ((u0 + 1) ^ (rho & 15)));
+                typename Act<CT>::frag b0, b1;
+                if constexpr (F8) {
+                    // 16 codes: k = 64 s + 16 g .. + 15 of this row
+                    const v4u cv = *reinterpret_cast<const v4u *>(xs_ + rho * XRB + 16 * ((4 * s + g) ^ (rho & XSW)));
+                    widen<CT>(cv, b0, b1);
+                } else {
+                    const int u0 = 8 * s + 2 * g;
+                    b0 = Act<CT>::cast(*reinterpret_cast<const v4u *>(xs_ + rho * XRB + 16 * (u0 ^ (rho & XSW))));
+                    b1 = Act<CT>::cast(*reinterpret_cast<const v4u *>(xs_ + rho * XRB + 16 * ((u0 + 1) ^ (rho & XSW))));
+                }
 #pragma unroll
                 for (int a = 0; a < AF; ++a) {
-                    acc[a][j] = Act<CT>::mfma(a0[a], Act<CT>::cast(b0), acc[a][j]);
-                    acc[a][j] = Act<CT>::mfma(a1[a], Act<CT>::cast(b1), acc[a][j]);
+                    acc[a][j] = Act<CT>::mfma(a0[a], b0, acc[a][j]);
+                    acc[a][j] = Act<CT>::mfma(a1[a], b1, acc[a][j]);
                 }
             }
         }
@@ -1089,8 +1087,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     // prologue: the first D chunks (nch >= D)
     static_for<0, D>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
-        issue_x(u, u);
-        issue_w(u, u);
+        issue(u, u);
     });
     for (int c0 = 0; c0 < nch; c0 += D) {
         static_for<0, D>([&](auto uc) {
@@ -1099,35 +1096,12 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
             if (c < nch) {
                 wait_chunk(c);
                 __builtin_amdgcn_sched_barrier(0);
-                const bool more = c + D < nch;
-                if constexpr (!XD) {
-                    // this wave's single activation slot: the previous chunk's
-                    // reads were consumed by its MFMAs; LDS operations of one
-                    // wave run in order
-#pragma unroll
-                    for (int i = 0; i < NI; ++i) {
-                        if constexpr (F8) {
-                            const v4u cv = xr[u][i];
-                            const uint2 p0 = e4m3x4_to_bf16(cv.x), p1 = e4m3x4_to_bf16(cv.y);
-                            const uint2 p2 = e4m3x4_to_bf16(cv.z), p3 = e4m3x4_to_bf16(cv.w);
-                            *reinterpret_cast<v4u *>(xslot + xo[i]) = v4u{p0.x, p0.y, p1.x, p1.y};
-                            *reinterpret_cast<v4u *>(xslot + xo2[i]) = v4u{p2.x, p2.y, p3.x, p3.y};
-                        } else {
-                            *reinterpret_cast<v4u *>(xslot + xo[i]) = qdq8(xr[u][i], div);
-                        }
-                    }
-                    if (more)
-                        issue_x(u, c + D);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                quantize_slot(u);
                 compute(u);
                 __builtin_amdgcn_sched_barrier(0);
                 // slot u is free again: its operand reads fed the MFMAs above
-                if (more) {
-                    if constexpr (XD)
-                        issue_x(u, c + D);
-                    issue_w(u, c + D);
-                }
+                if (c + D < nch)
+                    issue(u, c + D);
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
@@ -1303,8 +1277,9 @@ static void plan_tile(W8A16Plan &p, int64_t m, int64_t k, int steps_mb1)
 //    (MB = 1, AF = 2); 33..64 rows: 32-row groups (MB = 2, AF = 2); both only
 //    where that makes 192..320 workgroups.  q_proj M = 24 7.2 us, M = 32 7.9
 //    us, M = 64 9.6 us (12.0 us with the weights loaded straight into
-//    registers).  E4M3 activation codes take chunks of 4 x 64 k (their
-//    staging goes through registers).
+//    registers).  E4M3 activation codes take chunks of 4 x 64 k there.
+//  - E4M3 activation codes up to 16 rows: as 16-bit activations, 3 chunks
+//    in flight (q_proj M = 1: 5.5 us; half the activation bytes).
 // Activations cast on the fly (kActQ) stage only the rows that exist (4, 8 or
 // 16).  Chunks of CS x 64 k, D of them in flight: the LDS of 4 waves' rings
 // bounds CS * D * (activation + weight row bytes).
@@ -1322,7 +1297,7 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act)
     p.kper = k;
     p.kchunk = k / 4;
     if (m <= 16) {
-        if (f8 || n < 256)
+        if (n < 256)
             return false;
         static const int kAf[5] = {1, 2, 3, 4, 7};
         int best = 0;
@@ -1363,7 +1338,7 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act)
         p.af = kAf[best];
         p.mb = 1;
         p.steps = 2;
-        p.depth = p.af == 7 ? 2 : (p.af > 2 || q) ? 3 : 4;
+        p.depth = p.af == 7 ? 2 : (p.af > 2 || q || f8) ? 3 : 4;
         p.xd = q ? (m <= 4 ? 4 : m <= 8 ? 8 : 16) : 16;
     } else {
         if (q)
@@ -1598,6 +1573,7 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
             FP8Q_PANEL_CASE(3, 1, 2, 3, XS) FP8Q_PANEL_CASE(4, 1, 2, 3, XS)                   \
             FP8Q_PANEL_CASE(7, 1, 2, 2, XS)
         if constexpr (AT == kActF8) {
+            FP8Q_PANEL_CASE(1, 1, 2, 3, 16) FP8Q_PANEL_CASE(2, 1, 2, 3, 16) FP8Q_PANEL_MB1(16)
             FP8Q_PANEL_CASE(2, 1, 4, 3, 16)
             FP8Q_PANEL_CASE(2, 1, 4, 2, 16)
             FP8Q_PANEL_CASE(2, 2, 4, 2, 32)
@@ -1610,6 +1586,8 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
             FP8Q_PANEL_CASE(1, 1, 2, 4, 16) FP8Q_PANEL_CASE(2, 1, 2, 4, 16) FP8Q_PANEL_MB1(16)
             FP8Q_PANEL_CASE(2, 1, 2, 3, 16)
             FP8Q_PANEL_CASE(2, 2, 2, 2, 32)
+        }
+        if constexpr (AT != kActQ) {
             // a small weight: 4 activation rows per workgroup
             if (p.af == 1 && p.mb == 1 && p.steps == 4 && p.depth == 2 && p.waves == 4 &&
                 p.xd == 4 && p.rpw == 4) {

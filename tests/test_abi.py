@@ -56,16 +56,18 @@ def test_workspace_queries(L):
     assert L.fp8q_linear_workspace_size(1, 64, 4096, 4096) == 0         # the panel kernel
     assert L.fp8q_linear_workspace_size(1, 64, 1024, 4096) == 4 * 64 * 1024 * 4
     assert L.fp8q_linear_workspace_size(1, 1, 4096, 4096) == 0
-    # W8A16 / fp16 up to 16 activation rows, N >= 1024, K a multiple of 512
-    # from 2048 on: the panel kernel, whole K per workgroup, no scratch; E4M3
-    # codes at 8K <= K < 16K take the tile kernel with K split 4 ways
+    # up to 16 activation rows, K a multiple of 512 from 2048 on: the panel
+    # kernel, whole K per workgroup, no scratch (every activation type); E4M3
+    # codes with K not a multiple of 512 at 8K <= K < 16K take the tile
+    # kernel with K split towards 4 ways (whole 1024-k chunks: 3 here)
     assert L.fp8q_linear_workspace_size(0, 12, 8192, 8192) == 0
     assert L.fp8q_linear_workspace_size(0, 12, 28672, 8192) == 0
     assert L.fp8q_linear_workspace_size(0, 12, 28672, 4096) == 0
     assert L.fp8q_linear_workspace_size(0, 1, 4096, 4096) == 0
     assert L.fp8q_linear_workspace_size(0, 12, 8192, 28672) == 0
-    assert L.fp8q_linear_workspace_size(1, 12, 8192, 8192) == 4 * 12 * 8192 * 4
-    assert L.fp8q_linear_workspace_size(1, 12, 28672, 8192) == 4 * 12 * 28672 * 4
+    assert L.fp8q_linear_workspace_size(1, 12, 8192, 8192) == 0
+    assert L.fp8q_linear_workspace_size(1, 12, 28672, 8192) == 0
+    assert L.fp8q_linear_workspace_size(1, 12, 28672, 8208) == 3 * 12 * 28672 * 4
     # a small N on a short K: 64-row tiles, no split (K under two chunks)
     assert L.fp8q_linear_workspace_size(0, 4, 64, 500) == 0
     # 17..64 rows with about one workgroup per CU: the panel kernel, whole K
@@ -83,8 +85,8 @@ def test_workspace_queries(L):
     #   with K a multiple of 1024 the panel kernel spreads the activation rows
     #   4 per workgroup instead: no scratch
     assert L.fp8q_linear_workspace_size(0, 12, 1022, 8192) == 0
-    #   E4M3 codes, M=12, N=8192, K=28672 (16-step chunks of 1024): 2 splits
-    assert L.fp8q_linear_workspace_size(1, 12, 8192, 28672) == 2 * 12 * 8192 * 4
+    #   E4M3 codes, M=12, N=8192, K=28688 (16-step chunks of 1024): 2 splits
+    assert L.fp8q_linear_workspace_size(1, 12, 8192, 28688) == 2 * 12 * 8192 * 4
     #   M=40, N=100, K=3000: 2 tiles, at most 2 splits of whole 512-k chunks
     assert L.fp8q_linear_workspace_size(0, 40, 100, 3000) == 2 * 40 * 100 * 4
     assert L.fp8q_linear_workspace_size(0, 0, 4096, 4096) == 0
@@ -147,7 +149,7 @@ def test_describe(L):
     assert L.fp8q_linear_describe(1, 8192, 28672, 4096, buf, 256) == 0
     assert b"32x112" in buf.value
     assert L.fp8q_linear_describe(1, 8, 4096, 4096, buf, 256) == 0
-    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")
+    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 3, 4>")
     assert L.fp8q_linear_describe(2, 1, 4096, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 4, 4>")
     # a weight of under 96 16-row panels (the Llama-3 k/v): 4 activation rows
@@ -226,7 +228,7 @@ def test_linear_overlap_rejected_on_host(L):
     """Aliasing is refused from the pointer values alone, before any device
     query: here an activation scale placed inside the K-split workspace, which
     the split GEMM would overwrite before the reduction reads the scale."""
-    m, n, k = 12, 1024, 8192          # a K-split decode plan
+    m, n, k = 12, 1024, 8208          # a K-split decode plan (K not a multiple of 512)
     need = L.fp8q_linear_workspace_size(1, m, n, k)
     assert need > 0
     base = 0x10000000

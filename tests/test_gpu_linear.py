@@ -145,7 +145,7 @@ def test_w8a16_f16_ragged(fq, orc, m, n, k):
 
 @pytest.mark.parametrize("m,n,k", [(256, 256, 64), (300, 260, 128), (33, 512, 64), (8, 300, 1100),
                                    (64, 272, 1600), (1, 4096, 640), (16, 512, 4160), (520, 300, 640)]
-                         + [s for s in PANEL_SHAPES if s[0] > 16])
+                         + PANEL_SHAPES)
 def test_w8a8_exact_every_code(fq, orc, m, n, k):
     """One-hot E4M3 rows (spread over K) pick weight columns exactly; up to 64
     rows this is the decode path, beyond it the FP8 MFMA GEMM."""
@@ -250,7 +250,7 @@ MANY_TILE_ROWS = [(2305, 2048, 640), (4100, 600, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", RAGGED + [(300, 520, 1000), (256, 256, 4096), (513, 257, 200)] + WHOLE_STAGES
-                         + MANY_TILE_ROWS + [s for s in PANEL_SHAPES if s[0] > 16])
+                         + MANY_TILE_ROWS + PANEL_SHAPES)
 def test_w8a8_ragged(fq, orc, m, n, k):
     w = workloads.heavy_tail_weight(n, k, m + n)
     x = workloads.outlier_act(m, k, k)
@@ -362,12 +362,11 @@ def test_w8a16_split_workspace_reuse(fq, orc, shapes):
 
 
 def test_panel_plans_are_taken(fq):
-    """The panel shapes above run k_w8a16_panel (so their parity tests cover
-    it); E4M3 codes take it from 17 rows on."""
+    """The panel shapes above run k_w8a16_panel in every mode (so their parity
+    tests cover it)."""
     for m, n, k in PANEL_SHAPES:
-        assert fq.describe_linear(0, m, n, k).startswith("k_w8a16_panel"), (m, n, k)
-        assert fq.describe_linear(2, m, n, k).startswith("k_w8a16_panel"), (m, n, k)
-        assert fq.describe_linear(1, m, n, k).startswith("k_w8a16_panel") == (m > 16), (m, n, k)
+        for mode in (0, 1, 2):
+            assert fq.describe_linear(mode, m, n, k).startswith("k_w8a16_panel"), (mode, m, n, k)
 
 
 def test_deterministic(fq, orc):

@@ -57,7 +57,7 @@ def _call(L, fn, mode, xd, xsd, m, k, wd, n, wsd, y, extra):
 
 # (mode, m, n, k): the first call of each pair is the larger one; every shape
 # splits K (so the scratch carries partial tiles between two kernels)
-PAIRS = [[(1, 12, 28672, 8192), (0, 12, 1022, 7000)],
+PAIRS = [[(1, 12, 28672, 8208), (0, 12, 1022, 7000)],
          [(1, 64, 1024, 4096), (1, 24, 1024, 8192)],
          [(0, 40, 300, 3000), (0, 12, 1000, 6000)]]
 
@@ -98,12 +98,12 @@ def test_noalloc_without_split_and_refusal(L, orc):
     assert_gemm_close(host_bf16_as_f64(y), ref, "noalloc no split")
     # a K-split scratch above the maximum: refused, nothing launched (the
     # output keeps its sentinel).  16 rows of E4M3 codes on a 57344-row weight
-    # (the Llama-3-70B fused gate_up) split K 4 ways: 4 * 16 * 57344 * 4
-    # bytes.  Every buffer has its full size, so nothing could be read out of
-    # bounds.
-    mode, m, n, k = 1, 16, 57344, 8192
+    # (the Llama-3-70B fused gate_up) with K = 8208 (not a multiple of 512, so
+    # the tile kernel) split K 3 ways: 3 * 16 * 57344 * 4 bytes.  Every buffer
+    # has its full size, so nothing could be read out of bounds.
+    mode, m, n, k = 1, 16, 57344, 8208
     need = L.fp8q_linear_workspace_size(mode, m, n, k)
-    assert need == 4 * 16 * 57344 * 4 > SCRATCH_BYTES
+    assert need == 3 * 16 * 57344 * 4 > SCRATCH_BYTES
     xb = torch.zeros((m, k), dtype=torch.uint8, device="cuda")
     xs1 = torch.ones(1, dtype=torch.float32, device="cuda")
     w8 = torch.zeros((n, k), dtype=torch.uint8, device="cuda")
