@@ -507,7 +507,8 @@ size_t linear_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t
             return 0;
         if (grouped_uses_gemm(mode, m, group))
             return round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
-        return round_up(fp8q::launch::plan_w8a16_grouped(m, n, k, group).workspace, 256);
+        return round_up(fp8q::launch::plan_w8a16_grouped(m, n, k, group, act_type(mode)).workspace,
+                        256);
     }
     if ((mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16) && m > kW8A8DecodeMaxM)
         return 0;                   // the 16-bit prefill GEMM needs no scratch
@@ -593,7 +594,7 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
         e = fp8q::launch::w8a8(plan, static_cast<const uint8_t *>(x), m, k, ld_x, x_scale, w_fp8,
                                n, ld_w, w_scale, y_bf16, ld_y, stream, group);
     } else if (group > 0) {
-        const auto plan = fp8q::launch::plan_w8a16_grouped(m, n, k, group);
+        const auto plan = fp8q::launch::plan_w8a16_grouped(m, n, k, group, act);
         e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
                                 ld_y, workspace, stream);
     } else if (a16 && m > kW8A8DecodeMaxM) {
@@ -872,10 +873,12 @@ void describe_w8a16(const fp8q::launch::W8A16Plan &p, char *buf, size_t len)
         std::snprintf(spg, sizeof spg, ", %lld", (long long)(p.group / 64));
     if (p.kind == fp8q::launch::W8A16Plan::kPanel)
         std::snprintf(buf, len,
-                      "k_w8a16_panel<%d, %d, %d, %d, %d> grid=(%lld,%lld) block=%d staged_rows=%d "
-                      "rows_per_workgroup=%d splits=1",
-                      p.af, p.mb, p.steps, p.depth, p.waves, (long long)p.grid_n,
-                      (long long)p.grid_m, 64 * p.waves, p.xd, p.rpw > 0 ? p.rpw : 16 * p.mb);
+                      "k_w8a16_panel<%d, %d, %d, %d, %d%s> grid=(%lld,%lld) block=%d staged_rows=%d "
+                      "rows_per_workgroup=%d splits=1%s",
+                      p.af, p.mb, p.steps, p.depth, p.waves, spg, (long long)p.grid_n,
+                      (long long)p.grid_m, 64 * p.waves, p.xd, p.rpw > 0 ? p.rpw : 16 * p.mb,
+                      p.group == 0 ? ""
+                      : p.scale_stage == 2 ? " scales=preloaded" : " scales=per_chunk");
     else if (p.kind == fp8q::launch::W8A16Plan::kRows)
         std::snprintf(buf, len,
                       "k_w8a16_rows<%d, %d, %d, %d%s> rows=%d grid=(%lld,%lld,%lld) block=%d "
@@ -963,7 +966,7 @@ fp8q_status fp8q_linear_grouped_describe(fp8q_mode mode, int64_t m, int64_t n, i
     if (grouped_uses_gemm(mode, m, group))
         describe_w8a8(m, n, k, true, buf, len);
     else
-        describe_w8a16(fp8q::launch::plan_w8a16_grouped(m, n, k, group), buf, len);
+        describe_w8a16(fp8q::launch::plan_w8a16_grouped(m, n, k, group, act_type(mode)), buf, len);
     return ok();
 }
 

@@ -185,6 +185,24 @@ __device__ __forceinline__ void dma16(const uint8_t *base, uint32_t off, uint32_
                  : "v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
+
+// The same with 4 bytes per lane (global_load_lds_dword): lane l's dword lands
+// at LDS address lds + 4 * l.  `base` must be wave-uniform; it is read from
+// the first lane (the compiler does not always prove such an address uniform,
+// and the instruction takes it from an SGPR pair).  Each half goes through
+// uint32_t, so the signed result of readfirstlane is not sign-extended.
+__device__ __forceinline__ void dma4(const void *base, uint32_t off, uint32_t lds)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const void *ub = reinterpret_cast<const void *>(((uint64_t)hi << 32) | (uint64_t)lo);
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dword %0, %1"
+                 :
+                 : "v"(off), "s"(ub), "s"(lds)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 }  // namespace dev

@@ -87,12 +87,16 @@ struct W8A16Plan {
     size_t workspace;  // scratch bytes: the partial tiles [splits][m][ldp] (0 if no split)
     int64_t group;     // 0: one weight scale per row; else k per weight-scale group
     int rpw;           // k_w8a16_panel: activation rows per workgroup (0: 16 * mb)
+    int scale_stage;   // k_w8a16_panel with groups: 2 = each wave's group scales
+                       // preloaded into LDS, 1 = staged per chunk
 };
 // act: the activation type (kW8A16Act* below).
 W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act = 0);
 // Per-group weight scales (w_scale [n, ceil(k / group)]); group is 64, 128,
-// 256 or 512.  The tile kernel serves every activation type and M.
-W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group);
+// 256 or 512; act as for plan_w8a16 (not kW8A16ActQ).  The panel kernel where
+// the per-channel plan takes it and the groups divide the waves' K ranges,
+// else the rows or tile kernel.
+W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group, int act = 0);
 // act: the activation type -- 0 bf16 (fp8_w_bf16_a, bf16 out), 1 fp16
 // (fp8_w_fp16_a, fp16 out), 2 E4M3 codes with *x_scale (fp8_w_fp8_a at decode
 // sizes, bf16 out).  ld_x counts activation values.

@@ -924,18 +924,55 @@ __global__ __launch_bounds__(kTileThreads) void k_w8a16_tile(
 // workgroups of its column find in L2).  Panel rows past RPW feed outputs
 // that are never stored.
 //
+// GRP: per-group weight scales (the deployment guide, §4.3): w_scale [n,
+// ngroups] for groups of 2^glog k (64..512).  The MFMAs accumulate a group's
+// products on their own (accg); at the group's end the lane's 4 weight rows'
+// scales multiply them into the running total.  GRP = 2: before the K loop
+// each wave loads the scales of its whole K range, [WR rows][K range /
+// group], into LDS beside the rings, each load instruction covering runs of
+// consecutive groups of a few rows (the host plans it where that block fits).
+// GRP = 1: the scales of a chunk's groups are staged with the chunk, one
+// 4-byte direct load per row and group, which touches WR rows' cache lines
+// per instruction and costs up to a third of the kernel's time on long K.
+// The host plans either only where a wave's K range is a whole number of
+// groups.
+//
 // The host plans this kernel only for K a multiple of NWV * 64 * CS with at
 // least D chunks per wave.  Rows past N or M are clamped to a valid row when
 // loading and their outputs are never stored.  A load instruction covers at
 // most 8 weight rows or 4 activation rows, addressed from that group's first
 // row, so the per-lane 32-bit offsets hold for row strides below 2^28 bytes
 // (checked by the host).
-template <int AF, int MB, int CS, int D, int NWV, int AT, int XS = 16 * MB, int RPW = 16 * MB>
+// LDS of k_w8a16_panel's rings (NWV waves, D chunk slots each), and what a
+// wave may take beside them for preloaded group scales within gfx950's 160 KB
+// per workgroup (whole 256-byte loads).
+constexpr int kPanelLdsBytes = 160 * 1024;
+constexpr int panel_ring_bytes(int af, int mb, int cs, int d, int nwv, bool f8, bool chunk_scales)
+{
+    const int ck = 64 * cs, wr = 16 * af;
+    const int xslot = 16 * mb * ck * (f8 ? 1 : 2);
+    const int se = chunk_scales ? wr * (ck / 64) : 0;
+    return nwv * d * (xslot + wr * ck + (se + 63) / 64 * 256);
+}
+constexpr int panel_scale_bytes(int ring, int nwv)
+{
+    return ring >= kPanelLdsBytes ? 0 : ((kPanelLdsBytes - ring) / nwv) & ~255;
+}
+// Preloaded group scales: not for E4M3 codes at 17..32 rows (two fragments,
+// 4-step chunks), whose kernel then spills to scratch.
+constexpr bool panel_preload_ok(int af, int cs, bool f8)
+{
+    return !(f8 && af == 2 && cs == 4);
+}
+
+template <int AF, int MB, int CS, int D, int NWV, int AT, int XS = 16 * MB, int RPW = 16 * MB,
+          int GRP = 0>
 __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const void *__restrict__ xv, int64_t m, int64_t k, int64_t ld_x,
     const float *__restrict__ x_scale,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
-    const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y, QuantArgs qa)
+    const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
+    int glog, int64_t ngroups, QuantArgs qa)
 {
     constexpr bool F8 = AT == kActF8;           // activations staged as E4M3 codes
     constexpr int CT = compute_type<AT>();
@@ -949,11 +986,20 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     constexpr int XSW = XU >= 16 ? 15 : XU - 1; // activation unit swizzle mask
     constexpr int WU = CK / 16;                 // 16-byte units of a weight row segment
     constexpr int NW = WR * WU / kWave;         // weight loads per lane per chunk
-    constexpr int LC = NI + NW;                 // loads per lane per chunk
     constexpr int WSW = WU >= 16 ? 15 : WU - 1; // weight unit swizzle mask
-    constexpr int XSLOT = XR * XRB, WSLOT = WR * CK;
-    constexpr int SLOT = D * (XSLOT + WSLOT);
+    // group scales staged per chunk: up to CK / 64 groups x WR rows, floats
+    // [group][row], in whole 256-byte (64-lane) loads
+    constexpr int SE = GRP == 1 ? WR * (CK / 64) : 0;
+    constexpr int NS = (SE + kWave - 1) / kWave;
+    constexpr int LC = NI + NW + NS;            // loads per lane per chunk
+    constexpr int XSLOT = XR * XRB, WSLOT = WR * CK, SSLOT = NS * 4 * kWave;
+    constexpr int SLOT = D * (XSLOT + WSLOT + SSLOT);
     constexpr int RED = (int)sizeof(v4f) * NWV * AF * MB * kWave;
+    // GRP = 2: each wave's preloaded scales, in the LDS the rings leave free
+    constexpr int SAB = GRP == 2 ? panel_scale_bytes(NWV * SLOT, NWV) : 0;
+    static_assert(NWV * SLOT == panel_ring_bytes(AF, MB, CS, D, NWV, F8, GRP == 1),
+                  "ring size as the host plans it");
+    static_assert(GRP != 2 || SAB >= 256 * 4, "room for the preloaded scales");
     static_assert((XS * XU) % kWave == 0 && XS <= XR && XS > 0 && (XU & (XU - 1)) == 0,
                   "chunk shape");
     static_assert((WR * WU) % kWave == 0 && (WU & (WU - 1)) == 0, "weight chunk shape");
@@ -961,7 +1007,8 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     static_assert(D >= 1 && D <= 4, "chunks in flight");
     // the waves' rings; after the K loop the same bytes hold the waves' fp32
     // panels for the reduction
-    __shared__ __attribute__((aligned(16))) uint8_t xl[NWV * SLOT > RED ? NWV * SLOT : RED];
+    __shared__ __attribute__((aligned(16)))
+    uint8_t xl[NWV * (SLOT + SAB) > RED ? NWV * (SLOT + SAB) : RED];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
@@ -974,8 +1021,10 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const int nch = (int)(kq / CK);
     uint8_t *xslot = xl + wave * SLOT;                  // D activation slots
     uint8_t *wslot = xslot + D * XSLOT;                 // D weight slots
+    uint8_t *sslot = wslot + D * WSLOT;                 // D group-scale slots
     const uint32_t xslot_lds = (uint32_t)(uintptr_t)xslot;
     const uint32_t wslot_lds = (uint32_t)(uintptr_t)wslot;
+    const uint32_t sslot_lds = (uint32_t)(uintptr_t)sslot;
     const float xs = act_scale<AT>(x_scale, qa);
     const E4M3Div div(AT == kActQ ? xs : 1.0f, true);
 
@@ -1005,6 +1054,21 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     auto xbase = [&](int i, int c) {
         return x8 + (min(m0 + XPI * i, m - 1) * ld_x + kb + (int64_t)c * CK) * ES;
     };
+    // group-scale load i: element e = 64 i + lane is group e / WR of the
+    // chunk (clamped to the groups the chunk has), weight row e % WR
+    uint32_t soff[NS > 0 ? NS : 1];
+    if constexpr (GRP == 1) {
+        const int gpc = CK >> glog > 0 ? CK >> glog : 1;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int e = kWave * i + lane;
+            const int gi = min(e / WR, gpc - 1), row = e % WR;
+            soff[i] = (uint32_t)(((min(n0 + row, n - 1) - n0) * ngroups + gi) * 4);
+        }
+    }
+    auto sbase = [&](int c) {
+        return w_scale + n0 * ngroups + ((kb + (int64_t)c * CK) >> glog);
+    };
 
     if constexpr (XS < XR) {
 #pragma unroll
@@ -1014,12 +1078,36 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
                 *reinterpret_cast<v4u *>(xslot + u * XSLOT + o) = v4u{0u, 0u, 0u, 0u};
     }
 
-    v4f acc[AF][MB];
+    v4f acc[AF][MB], accg[GRP ? AF : 1][GRP ? MB : 1];
+    // GRP = 2: groups of the wave's K range, and its scales [WR][gw] in LDS
+    const int gw = GRP == 2 ? (int)(kq >> glog) : 0;
+    const float *sall = reinterpret_cast<const float *>(xl + NWV * SLOT + wave * SAB);
+    if constexpr (GRP == 2) {
+        // element e = row * gw + j (row of the panel, j-th group of the K
+        // range), lane l of load i holding e = 64 i + l, so a load covers
+        // 64 / gw rows' runs of consecutive groups; the lanes past the
+        // block repeat its last element into the padding
+        const uint32_t sall_lds = (uint32_t)(uintptr_t)sall;
+        const float *sb = w_scale + n0 * ngroups + (kb >> glog);
+        const int tot = WR * gw;
+        for (int i = 0; i < tot; i += kWave) {
+            const int e = min(i + lane, tot - 1);
+            const int row = e / gw, j = e - row * gw;
+            dma4(sb, (uint32_t)(((min(n0 + row, n - 1) - n0) * ngroups + j) * 4), sall_lds + 4 * i);
+        }
+    }
 #pragma unroll
     for (int a = 0; a < AF; ++a)
 #pragma unroll
         for (int j = 0; j < MB; ++j)
             acc[a][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (GRP) {
+#pragma unroll
+        for (int a = 0; a < AF; ++a)
+#pragma unroll
+            for (int j = 0; j < MB; ++j)
+                accg[a][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
 
     auto issue = [&](int u, int c) {
 #pragma unroll
@@ -1028,6 +1116,11 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
 #pragma unroll
         for (int i = 0; i < NW; ++i)
             dma16(wbase(i, c), woff[i], wslot_lds + u * WSLOT + 1024 * i);
+        if constexpr (GRP == 1) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                dma4(sbase(c), soff[i], sslot_lds + u * SSLOT + 4 * kWave * i);
+        }
     };
     // the wait for chunk c: loads retire in order, and the chunks issued after
     // it are min(D - 1, nch - 1 - c) whole chunks of LC loads each
@@ -1050,7 +1143,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
             }
         }
     };
-    auto compute = [&](int u) {
+    auto compute = [&](int u, int c) {
         const uint8_t *xs_ = xslot + u * XSLOT;
         const uint8_t *ws_ = wslot + u * WSLOT;
 #pragma unroll
@@ -1077,8 +1170,40 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
                 }
 #pragma unroll
                 for (int a = 0; a < AF; ++a) {
-                    acc[a][j] = Act<CT>::mfma(a0[a], b0, acc[a][j]);
-                    acc[a][j] = Act<CT>::mfma(a1[a], b1, acc[a][j]);
+                    if constexpr (GRP) {
+                        accg[a][j] = Act<CT>::mfma(a0[a], b0, accg[a][j]);
+                        accg[a][j] = Act<CT>::mfma(a1[a], b1, accg[a][j]);
+                    } else {
+                        acc[a][j] = Act<CT>::mfma(a0[a], b0, acc[a][j]);
+                        acc[a][j] = Act<CT>::mfma(a1[a], b1, acc[a][j]);
+                    }
+                }
+            }
+            if constexpr (GRP) {
+                // the group ends with this step: its sums, times the lane's
+                // 4 weight rows' scales, join the total
+                if ((((c * CS + s + 1) << 6) & ((1 << glog) - 1)) == 0) {
+                    const int gi = (s << 6) >> glog;
+                    const int t = (((c * CS + s + 1) << 6) >> glog) - 1;
+                    const float *sc = reinterpret_cast<const float *>(sslot + u * SSLOT) + gi * WR;
+#pragma unroll
+                    for (int a = 0; a < AF; ++a) {
+                        v4f s4;
+                        if constexpr (GRP == 2) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                s4[v] = sall[(16 * a + 4 * g + v) * gw + t];
+                        } else {
+                            s4 = *reinterpret_cast<const v4f *>(sc + 16 * a + 4 * g);
+                        }
+#pragma unroll
+                        for (int j = 0; j < MB; ++j) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                acc[a][j][v] = __builtin_fmaf(s4[v], accg[a][j][v], acc[a][j][v]);
+                            accg[a][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
                 }
             }
         }
@@ -1097,7 +1222,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
                 wait_chunk(c);
                 __builtin_amdgcn_sched_barrier(0);
                 quantize_slot(u);
-                compute(u);
+                compute(u, c);
                 __builtin_amdgcn_sched_barrier(0);
                 // slot u is free again: its operand reads fed the MFMAs above
                 if (c + D < nch)
@@ -1131,7 +1256,8 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
 #pragma unroll
         for (int wv = 1; wv < NWV; ++wv)
             sum += red[(wv * AF * MB + f) * kWave + ln];
-        store_y4<CT>(y, ld_y, w_scale, xs, mr, nb, n, sum);
+        // grouped: the group scales are in the sums already
+        store_y4<CT>(y, ld_y, GRP ? nullptr : w_scale, xs, mr, nb, n, sum);
     }
 }
 
@@ -1283,7 +1409,13 @@ static void plan_tile(W8A16Plan &p, int64_t m, int64_t k, int steps_mb1)
 // Activations cast on the fly (kActQ) stage only the rows that exist (4, 8 or
 // 16).  Chunks of CS x 64 k, D of them in flight: the LDS of 4 waves' rings
 // bounds CS * D * (activation + weight row bytes).
-static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act)
+// grouped: per-group weight scales; the kernels with the most direct-load
+// addresses (7 weight fragments; E4M3 codes at 33..64 rows) then run out of
+// scalar registers, spill to scratch, and the compiler's waits for the spill
+// loads stall the direct loads, so those shapes take at most 4 fragments or
+// the rows / tile kernels.
+static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act,
+                       bool grouped = false)
 {
     const bool f8 = act == kW8A16ActF8, q = act == kW8A16ActQ;
     if (m < 1 || m > 64 || n < 1 || k % 512 != 0 || k < 2048)
@@ -1302,8 +1434,13 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act)
         static const int kAf[5] = {1, 2, 3, 4, 7};
         int best = 0;
         int64_t best_cost = 0;
-        for (int i = 0; i < 5; ++i) {
-            const int64_t cost = div_up(div_up(n, 16 * kAf[i]), 256) * kAf[i];
+        for (int i = 0; i < (grouped ? 4 : 5); ++i) {
+            // rounds of 256 workgroups, each as long as its fragments, plus
+            // half a fragment per round for the pipeline's fill and drain
+            // (M = 8, 28672 x 4096: 1 fragment, 7 rounds 32.6 us; 4 fragments,
+            // 2 rounds 25.7 us; 7 fragments, 1 round 24.0 us)
+            const int64_t rounds = div_up(div_up(n, 16 * kAf[i]), 256);
+            const int64_t cost = rounds * (2 * kAf[i] + 1);
             if (i == 0 || cost < best_cost || (cost == best_cost && kAf[i] > kAf[best])) {
                 best = i;
                 best_cost = cost;
@@ -1341,7 +1478,7 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act)
         p.depth = p.af == 7 ? 2 : (p.af > 2 || q || f8) ? 3 : 4;
         p.xd = q ? (m <= 4 ? 4 : m <= 8 ? 8 : 16) : 16;
     } else {
-        if (q)
+        if (q || (grouped && f8 && m > 32))
             return false;
         p.af = 2;
         p.mb = m > 32 ? 2 : 1;
@@ -1454,8 +1591,25 @@ W8A16Plan plan_w8a16(int64_t m, int64_t n, int64_t k, int act)
     return p;
 }
 
-W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group)
+W8A16Plan plan_w8a16_grouped(int64_t m, int64_t n, int64_t k, int64_t group, int act)
 {
+    // the panel kernel where it takes the per-channel call and every wave's K
+    // range is a whole number of groups
+    if (act != kW8A16ActQ) {
+        W8A16Plan p = plan_rows_tile(m, n, k);
+        if (plan_panel(p, m, n, k, act, true) && (k / p.waves) % group == 0) {
+            p.group = group;
+            // the wave's [rows][groups] scales, in whole 64-element loads,
+            // beside the rings if they fit
+            const int64_t elems = div_up(16 * p.af * (k / p.waves / group), 64) * 64;
+            const int ring = panel_ring_bytes(p.af, p.mb, p.steps, p.depth, p.waves,
+                                              act == kW8A16ActF8, false);
+            p.scale_stage = panel_preload_ok(p.af, p.steps, act == kW8A16ActF8) &&
+                                    elems * 4 <= panel_scale_bytes(ring, p.waves)
+                                ? 2 : 1;
+            return p;
+        }
+    }
     // where the per-channel plan takes the rows kernel, so does the grouped
     // one, with wave K ranges in whole 512-k rounds (so groups of up to 512 k
     // never straddle a round).  A K split (small N on a long K) already cuts
@@ -1542,16 +1696,41 @@ static void launch_tile(const W8A16Plan &p, const void *x, int64_t m, int64_t k,
     }
 }
 
-// k_w8a16_panel, 4 waves (the configurations plan_panel picks).
+// k_w8a16_panel, 4 waves (the configurations plan_panel picks).  Per-group
+// weight scales are instantiated only where plan_panel takes them (not with
+// 7 weight fragments, nor with E4M3 codes at two 16-row blocks); false when
+// the plan asks for a kernel that does not exist.
 template <int AF, int MB, int CS, int D, int AT, int XS = 16 * MB, int RPW = 16 * MB>
-static void launch_panel(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
+static bool launch_panel(const W8A16Plan &p, const void *x, int64_t m, int64_t k, int64_t ld_x,
                          const float *x_scale, const uint8_t *w, int64_t n, int64_t ld_w,
                          const float *w_scale, uint16_t *y, int64_t ld_y, const QuantArgs &qa,
                          hipStream_t stream)
 {
+    constexpr bool kGrouped = AT != kActQ && AF != 7 && !(AT == kActF8 && MB == 2);
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
+    if (p.group > 0) {
+        if constexpr (kGrouped) {
+            const int glog = p.group == 64 ? 6 : p.group == 128 ? 7 : p.group == 256 ? 8 : 9;
+            if constexpr (panel_preload_ok(AF, CS, AT == kActF8)) {
+                if (p.scale_stage == 2) {
+                    hipLaunchKernelGGL((k_w8a16_panel<AF, MB, CS, D, 4, AT, XS, RPW, 2>), grid,
+                                       dim3(4 * kWave), 0, stream, x, m, k, ld_x, x_scale, w, n,
+                                       ld_w, w_scale, y, ld_y, glog, div_up(k, p.group), qa);
+                    return true;
+                }
+            }
+            if (p.scale_stage == 1)
+                hipLaunchKernelGGL((k_w8a16_panel<AF, MB, CS, D, 4, AT, XS, RPW, 1>), grid,
+                                   dim3(4 * kWave), 0, stream, x, m, k, ld_x, x_scale, w, n, ld_w,
+                                   w_scale, y, ld_y, glog, div_up(k, p.group), qa);
+            return p.scale_stage == 1;
+        }
+        return false;
+    }
     hipLaunchKernelGGL((k_w8a16_panel<AF, MB, CS, D, 4, AT, XS, RPW>), grid, dim3(4 * kWave), 0,
-                       stream, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, qa);
+                       stream, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y, 0,
+                       (int64_t)0, qa);
+    return true;
 }
 
 template <int AT>
@@ -1561,12 +1740,13 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
                            void *workspace, const QuantArgs &qa, hipStream_t stream)
 {
     float *partial = static_cast<float *>(workspace);
-    if (p.group == 0 && p.kind == W8A16Plan::kPanel) {
+    if (p.kind == W8A16Plan::kPanel && (p.group == 0 || AT != kActQ)) {
 #define FP8Q_PANEL_CASE(AF, MB, CS, D, XS)                                                    \
             if (p.af == AF && p.mb == MB && p.steps == CS && p.depth == D && p.waves == 4 &&    \
                 p.xd == XS && p.rpw == 0) {                                                   \
-                launch_panel<AF, MB, CS, D, AT, XS>(p, x, m, k, ld_x, x_scale, w, n, ld_w,       \
-                                                    w_scale, y, ld_y, qa, stream);            \
+                if (!launch_panel<AF, MB, CS, D, AT, XS>(p, x, m, k, ld_x, x_scale, w, n, ld_w,  \
+                                                         w_scale, y, ld_y, qa, stream))       \
+                    return hipErrorInvalidValue;                                              \
                 return hipGetLastError();                                                     \
             }
 #define FP8Q_PANEL_MB1(XS)                                                                    \
@@ -1591,8 +1771,9 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
             // a small weight: 4 activation rows per workgroup
             if (p.af == 1 && p.mb == 1 && p.steps == 4 && p.depth == 2 && p.waves == 4 &&
                 p.xd == 4 && p.rpw == 4) {
-                launch_panel<1, 1, 4, 2, AT, 4, 4>(p, x, m, k, ld_x, x_scale, w, n, ld_w, w_scale,
-                                                   y, ld_y, qa, stream);
+                if (!launch_panel<1, 1, 4, 2, AT, 4, 4>(p, x, m, k, ld_x, x_scale, w, n, ld_w,
+                                                        w_scale, y, ld_y, qa, stream))
+                    return hipErrorInvalidValue;
                 return hipGetLastError();
             }
         }

@@ -171,17 +171,27 @@ def test_describe(L):
 
 def test_describe_grouped(L):
     buf = ctypes.create_string_buffer(256)
-    # up to 16 rows on a 4096-row weight: the rows kernel, 1024-k wave ranges
+    # up to 16 rows on a 4096-row weight: the panel kernel with group scales
     assert L.fp8q_linear_grouped_describe(0, 1, 4096, 4096, 128, buf, 256) == 0
-    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4, 2>") and b"kchunk=1024" in buf.value
-    # K = 1000: wave ranges rounded up to one 512-k round
+    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 4, 4, 2>")
+    # 28672 rows: 4 weight fragments (7, as per channel, spill with group scales)
+    assert L.fp8q_linear_grouped_describe(0, 12, 28672, 8192, 128, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<4, 1, 2, 3, 4, 2>") and b"grid=(448,1)" in buf.value
+    # K = 1000 (not a multiple of 512): the rows kernel, wave ranges rounded up
+    # to one 512-k round
     assert L.fp8q_linear_grouped_describe(2, 12, 4096, 1000, 64, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4, 1>") and b"kchunk=512" in buf.value
-    # a small N on a long K: the rows kernel with K splits, as per channel
+    # a small N on a long K: 4 activation rows per workgroup, as per channel
     assert L.fp8q_linear_grouped_describe(0, 12, 1024, 8192, 512, buf, 256) == 0
-    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4, 8>") and b"k_w8a16_reduce" in buf.value
-    # 64 rows: the tile kernel
+    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 4, 2, 4, 8>") and b"grid=(64,3)" in buf.value
+    # a group that does not divide the waves' K ranges: the rows kernel
+    assert L.fp8q_linear_grouped_describe(0, 12, 4096, 2560, 512, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4, 8>")
+    # 64 rows: two 32-row panels for 16-bit activations; the tile kernel for
+    # E4M3 codes
     assert L.fp8q_linear_grouped_describe(0, 64, 4096, 4096, 128, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<2, 2, 2, 2, 4, 2>")
+    assert L.fp8q_linear_grouped_describe(1, 64, 4096, 4096, 128, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_tile<4, 16, 8, 2>")
     # prefill W8A8: the FP8 GEMM for groups of 128 and up, the tile kernel for 64
     assert L.fp8q_linear_grouped_describe(1, 8192, 28672, 4096, 128, buf, 256) == 0
@@ -327,10 +337,12 @@ def test_grouped_host_validation(L):
     assert L.fp8q_linear_workspace_size(0, 12, 128, 28672) == 14 * 12 * 128 * 4
     assert lg(0, NULL, 12, 28672, 28672, NULL, NULL, 128, 28672, NULL, 128, NULL, 128, NULL, 0,
               NULL) == 4
-    # up to 16 rows on a 4096-row weight: the rows kernel, unsplit, as per channel
+    # up to 16 rows on a 4096-row weight: the panel kernel, unsplit, as per channel
     assert L.fp8q_linear_grouped_workspace_size(0, 1, 4096, 4096, 128) == 0
-    # 64 rows: 64 tiles, 4 splits of 1024 k
-    assert L.fp8q_linear_grouped_workspace_size(0, 64, 4096, 4096, 128) == 4 * 64 * 4096 * 4
+    # 64 rows of 16-bit activations: two 32-row panels, unsplit
+    assert L.fp8q_linear_grouped_workspace_size(0, 64, 4096, 4096, 128) == 0
+    # 64 rows of E4M3 codes: 64 tiles, 4 splits of 1024 k
+    assert L.fp8q_linear_grouped_workspace_size(1, 64, 4096, 4096, 128) == 4 * 64 * 4096 * 4
     # 448 tiles x 128 row blocks: no split
     assert L.fp8q_linear_grouped_workspace_size(1, 8192, 28672, 4096, 128) == 0
 

@@ -128,10 +128,11 @@ def test_linear_shapes(fq, orc, mode, group, m, n, k):
                                    (3, 2100, 700), (12, 4096, 1000), (1, 2050, 520),
                                    (16, 8200, 2048), (2, 12000, 1100)])
 def test_linear_rows_kernel(fq, orc, mode, group, m, n, k):
-    """Up to 16 rows on weights of 2049 to ~16K rows (short K past 4096): the
-    rows kernel with group folds at fixed steps of its 512-k rounds.  N = 3000,
-    2100 and 2050 give 8-row workgroups, 4096 16-row ones, 8200 and 12000
-    32-row ones; K = 520 and 700 leave waves with no K range."""
+    """Up to 16 rows on weights of 2049 to ~16K rows.  K a multiple of 512 (from
+    2048): the panel kernel; short or ragged K: the rows kernel with group
+    folds at fixed steps of its 512-k rounds (N = 2100 and 2050 give 8-row
+    workgroups, 8200 and 12000 32-row ones; K = 520 and 700 leave waves with
+    no K range)."""
     run_grouped(fq, orc, mode, m, n, k, group, 4000 + m + n + k, "rows")
 
 
@@ -143,18 +144,90 @@ def test_linear_rows_kernel_k_splits(fq, orc, mode, group, m, n, k):
     """A small N on a long K: the rows kernel with K split across workgroups in
     ranges of 2048 k; each split writes its group-scaled partial sums and the
     reduce applies only the activation scale (N = 1000 and 130 leave part of
-    a workgroup's rows past N; K = 4100 ends in a partial step)."""
+    a workgroup's rows past N; K = 4100 ends in a partial step).  1024 x 8192
+    takes the panel kernel with 4 activation rows per workgroup."""
     run_grouped(fq, orc, mode, m, n, k, group, 5000 + m + n + k, "rows split")
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("group", GROUPS)
-@pytest.mark.parametrize("m,n,k", [(12, 16448, 8192), (4, 300, 20000), (16, 4160, 17000)])
+@pytest.mark.parametrize("m,n,k", [(12, 16448, 12000), (4, 300, 20000), (16, 4160, 17000)])
 def test_linear_tile_1024k_chunks(fq, orc, mode, group, m, n, k):
     """The tile kernel with 1024-k chunks (16 steps): a weight of more than 256
-    tiles with 8K <= K < 16K (K split 4 ways), or K >= 16K (K = 20000 and
-    17000 leave a ragged tail of steps after the whole chunks)."""
+    tiles with 8K <= K < 16K (K split 4 ways), or K >= 16K (K = 12000, 20000
+    and 17000 leave a ragged tail of steps after the whole chunks)."""
+    assert fq.describe_linear(mode, m, n, k, group=group).startswith("k_w8a16_tile<1, ")
     run_grouped(fq, orc, mode, m, n, k, group, 6000 + m + n + k, "tile 1024k")
+
+
+# ---- decode on the panel kernel: per-group scales folded into the fp32
+# accumulators at each group's last 64-k step (the group's scales staged by
+# direct loads beside each chunk's weights)
+
+PANEL_GROUPED = [(3, 2048, 2048, "k_w8a16_panel<1, 1,"),     # 1 weight fragment
+                 (12, 6100, 2048, "k_w8a16_panel<2, 1,"),    # 2, ragged N
+                 (9, 12288, 2048, "k_w8a16_panel<3, 1,"),    # 3
+                 (4, 14336, 2048, "k_w8a16_panel<4, 1,"),    # 4
+                 (13, 1000, 4096, "k_w8a16_panel<1, 1, 4, 2,"),  # 4 rows per workgroup
+                 (5, 3000, 4096, "k_w8a16_panel<1, 1,"),     # ragged N, 1024-k wave ranges
+                 (24, 4096, 2048, "k_w8a16_panel<2, 1,"),    # two 16-row activation groups
+                 (40, 4096, 2048, "k_w8a16_panel<2, 2,")]    # 32-row activation groups
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("group", GROUPS)
+@pytest.mark.parametrize("m,n,k,kernel", PANEL_GROUPED)
+def test_linear_panel(fq, orc, mode, group, m, n, k, kernel):
+    plan = fq.describe_linear(mode, m, n, k, group=group)
+    if mode == 1 and m > 32:
+        # E4M3 codes past 32 rows: the tile kernel (the panel's grouped
+        # variant there would spill)
+        assert plan.startswith("k_w8a16_tile"), plan
+    else:
+        assert plan.startswith(kernel), plan
+    run_grouped(fq, orc, mode, m, n, k, group, 7000 + m + n + k + group, "panel")
+
+
+# where a wave's [rows][groups] block of scales does not fit in the LDS the
+# rings leave (or for E4M3 codes at 17..32 rows), the scales are staged with
+# each chunk instead of preloaded
+PANEL_STAGES = [(12, 6100, 16896, 64, 0, "per_chunk"), (12, 6100, 16896, 64, 1, "preloaded"),
+                (12, 6100, 16896, 128, 2, "preloaded"),
+                (4, 14336, 4608, 64, 2, "per_chunk"), (4, 14336, 4608, 64, 1, "preloaded"),
+                (24, 4096, 2048, 128, 1, "per_chunk"), (24, 4096, 2048, 64, 1, "per_chunk"),
+                (24, 4096, 2048, 64, 0, "preloaded")]
+
+
+@pytest.mark.parametrize("m,n,k,group,mode,stage", PANEL_STAGES)
+def test_linear_panel_scale_stages(fq, orc, m, n, k, group, mode, stage):
+    plan = fq.describe_linear(mode, m, n, k, group=group)
+    assert plan.startswith("k_w8a16_panel") and plan.endswith("scales=" + stage), plan
+    run_grouped(fq, orc, mode, m, n, k, group, 8000 + m + n + k + group, "panel " + stage)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("group", (64, 512))
+def test_linear_panel_wide_scale_range(fq, orc, mode, group):
+    """Adjacent groups whose scales differ by many orders of magnitude on the
+    panel kernel: an all-zero group (scale at the 1e-12 floor) next to groups
+    scaled up by 1e4 and down by 1e-6."""
+    m, n, k = 8, 2048, 4096
+    w = workloads.heavy_tail_weight(n, k, 58)
+    wf = workloads.bf16_bits_to_f32(w)
+    wf[:, group:2 * group] = 0.0
+    wf[::3, 3 * group:4 * group] *= np.float32(1e4)
+    wf[1::5, :group] *= np.float32(1e-6)
+    w = workloads.f32_to_bf16_bits(wf)
+    wq, ws, _ = orc.quantize_weight_grouped(w, group)
+    assert (ws[:, 1] == np.float32(1e-12)).all()
+    x, xs = make_x(mode, m, k, 59, orc)
+    assert fq.describe_linear(mode, m, n, k, group=group).startswith("k_w8a16_panel")
+    say("grouped panel wide scale range", mode, group)
+    y = fq.linear(dev_x(mode, x), dev_u8(wq), torch.from_numpy(ws).cuda(),
+                  x_scale=None if xs is None else torch.tensor([xs], device="cuda"), group=group)
+    torch.cuda.synchronize()
+    ref = orc.linear_grouped(mode, x, wq, ws, group, x_scale=xs)
+    assert_gemm_close(host_bf16_as_f64(y), ref, f"panel wide scale range {mode} g={group}")
 
 
 @pytest.mark.parametrize("mode", [0, 1])
