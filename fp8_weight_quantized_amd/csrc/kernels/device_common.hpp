@@ -21,6 +21,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -181,6 +183,31 @@ __device__ __forceinline__ void dma16(const uint8_t *base, uint32_t off, uint32_
 {
     asm volatile("s_mov_b32 m0, %2\n\t"
                  "global_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+// 16 bytes loaded / 8 bytes stored with the non-temporal hint: for data that
+// streams through once (a weight matrix being quantized, the last read of
+// an activation tensor), so that it does not displace what is re-read.
+__device__ __forceinline__ uint4 ld_nt16(const void *p)
+{
+    const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt8(void *p, uint2 v)
+{
+    __builtin_nontemporal_store(v2u32{v.x, v.y}, reinterpret_cast<v2u32 *>(p));
+}
+
+// The same as dma16 with the non-temporal hint, for data read once (a
+// stream of weights): streaming reads this way measured about 6.0 TB/s
+// against 5.6 TB/s with the default policy on MI355X.
+__device__ __forceinline__ void dma16_nt(const uint8_t *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %0, %1 nt"
                  :
                  : "v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");

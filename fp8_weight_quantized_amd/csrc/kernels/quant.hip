@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight(
         for (int c = 0; c < CH; ++c) {
             const int64_t idx = tid + (int64_t)c * kThreads;
             if (idx < nfull) {
-                buf[c] = *reinterpret_cast<const uint4 *>(wr + idx * 8);
+                buf[c] = ld_nt16(wr + idx * 8);
                 uint32_t m01 = max(abs_key_max2(buf[c].x), abs_key_max2(buf[c].y));
                 uint32_t m23 = max(abs_key_max2(buf[c].z), abs_key_max2(buf[c].w));
                 key = max(key, max(m01, m23));
@@ -58,6 +58,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight(
         }
     } else {
         for (int64_t idx = tid; idx < nfull; idx += kThreads) {
+            // (a default load: the second pass re-reads the row from cache)
             uint4 v = *reinterpret_cast<const uint4 *>(wr + idx * 8);
             key = max(key, max(max(abs_key_max2(v.x), abs_key_max2(v.y)),
                                max(abs_key_max2(v.z), abs_key_max2(v.w))));
@@ -79,12 +80,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight(
         for (int c = 0; c < CH; ++c) {
             const int64_t idx = tid + (int64_t)c * kThreads;
             if (idx < nfull)
-                *reinterpret_cast<uint2 *>(qr + idx * 8) = quantize8(buf[c], s);
+                st_nt8(qr + idx * 8, quantize8(buf[c], s));
         }
     } else {
         for (int64_t idx = tid; idx < nfull; idx += kThreads) {
-            uint4 v = *reinterpret_cast<const uint4 *>(wr + idx * 8);
-            *reinterpret_cast<uint2 *>(qr + idx * 8) = quantize8(v, s);
+            uint4 v = ld_nt16(wr + idx * 8);
+            st_nt8(qr + idx * 8, quantize8(v, s));
         }
     }
     if (tid < tail) {
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight_scalar(
 __device__ __forceinline__ uint4 load_chunk(const uint16_t *wr, int64_t e0, int valid)
 {
     if (valid == 8)
-        return *reinterpret_cast<const uint4 *>(wr + e0);
+        return ld_nt16(wr + e0);
     uint4 v = {0u, 0u, 0u, 0u};
     if (valid > 0) {
         uint32_t h[8];
@@ -156,7 +157,7 @@ __device__ __forceinline__ void quant_chunk(uint4 v, int64_t c, int valid, uint8
     const float s = scale_from_key(key);
     const int64_t e0 = c * 8;
     if (valid == 8) {
-        *reinterpret_cast<uint2 *>(qr + e0) = quantize8(v, s);
+        st_nt8(qr + e0, quantize8(v, s));
     } else if (valid > 0) {
         const uint2 codes = quantize8(v, s);
         for (int i = 0; i < valid; ++i)

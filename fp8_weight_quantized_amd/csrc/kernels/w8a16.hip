@@ -1115,7 +1115,7 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
             dma16(xbase(i, c), xoff[i], xslot_lds + u * XSLOT + 1024 * i);
 #pragma unroll
         for (int i = 0; i < NW; ++i)
-            dma16(wbase(i, c), woff[i], wslot_lds + u * WSLOT + 1024 * i);
+            dma16_nt(wbase(i, c), woff[i], wslot_lds + u * WSLOT + 1024 * i);
         if constexpr (GRP == 1) {
 #pragma unroll
             for (int i = 0; i < NS; ++i)
