@@ -171,7 +171,7 @@ constexpr int vmcnt_lgkm0_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 // GS: per-group weight scales (the deployment guide §4.3), w_scale
-// [n, ngroups] for groups of gstages * 128 k, so a group is a whole number of
+// [n, ngroups] for groups of 128 << gshift k, so a group is a whole number of
 // stages.  The accumulators then hold the running sum in units of the
 // current group's scale: when stage ks opens group g, every accumulator of
 // weight row n is multiplied by s[n][g-1] / s[n][g] before the stage's
@@ -186,10 +186,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     const float *__restrict__ x_scale,
     const uint8_t *__restrict__ w, int64_t n, int64_t ld_w,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ld_y,
-    int tiles_m, int tiles_n, int64_t ngroups, int gstages)
+    int tiles_m, int tiles_n, int64_t ngroups, int gshift)
 {
     __shared__ __align__(16) uint8_t lds[kLdsBytes];
     __shared__ __align__(16) float gsc[GS ? 4 * BN : 4];
+    // grouped: s[n][g-1] / s[n][g] of the tile's rows, slot g & 3
+    __shared__ __align__(16) float gratio[GS ? 4 * BN : 4];
     // per-row scales: xs * w_scale[n] of the tile's 256 weight rows, fetched
     // into LDS before the main loop hides the load; read by the epilogue
     __shared__ __align__(16) float wsl[GS ? 4 : BN];
@@ -238,14 +240,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     // grouped: the scale of tile row tid (< BN) for group g, loaded into a
     // register one stage ahead and written to LDS slot g & 3 before the barrier
     // of the stage that opens group g
-    const int64_t last_stage = k / BK - (k % BK == 0 ? 1 : 0);
+    // Stage indices are 32-bit (K < 2^31) and group boundaries a shift and a
+    // mask: 64-bit divisions here cost over a hundred scalar instructions
+    // each, per stage and wave, on the scalar unit the CU's waves share.
+    const int last_stage = (int)(k / BK) - (k % BK == 0 ? 1 : 0);
+    const int gmask = (1 << gshift) - 1;
     const float *srow = w_scale + (GS ? min(n0 + tid, n - 1) * ngroups : 0);
-    float pend = 0.f;
+    float pend = 0.f, prev = 0.f;
     int pend_g = -1;
-    auto fetch_scale = [&](int64_t st) {
+    auto fetch_scale = [&](int st) {
         if constexpr (GS) {
-            if (st <= last_stage && st % gstages == 0) {
-                pend_g = (int)(st / gstages);
+            if (st <= last_stage && (st & gmask) == 0) {
+                pend_g = st >> gshift;
                 if (tid < BN)
                     pend = srow[pend_g];
             }
@@ -254,8 +260,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     auto store_scale = [&]() {
         if constexpr (GS) {
             if (pend_g >= 0) {
-                if (tid < BN)
+                if (tid < BN) {
                     gsc[(pend_g & 3) * BN + tid] = pend;
+                    // the ratio each lane holding this row multiplies by
+                    // when group pend_g opens (hardware reciprocal, ~1 ulp)
+                    gratio[(pend_g & 3) * BN + tid] = prev * __builtin_amdgcn_rcpf(pend);
+                    prev = pend;
+                }
                 pend_g = -1;
             }
             __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(63));   // lgkmcnt(0): the write is done
@@ -264,26 +275,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     // stage st opens group g > 0: bring the accumulators from units of
     // s[g-1] to units of s[g] before the stage's MFMAs.  Lane (col, h) of a
     // 32 x 32 block holds rows 8 * q + 4 * h + e (e = 0..3) of W block i, so
-    // one ratio serves the TM blocks of that row.  (Interleaving these
-    // multiplies with the stage's MFMAs measured slower: each then waits for
-    // the previous stage's last MFMA on its block, and the ratios held live
-    // cost 27 registers.)
-    auto rescale = [&](int64_t st) {
+    // one ratio serves the TM blocks of that row; the thread that stores a
+    // row's group scale also stores its ratio, once per workgroup instead of
+    // once per lane.  (Interleaving these multiplies with the stage's MFMAs
+    // measured slower: each then waits for the previous stage's last MFMA
+    // on its block, and the ratios held live cost 27 registers.)
+    auto rescale = [&](int st) {
         if constexpr (GS) {
-            if (st == 0 || st % gstages != 0)
+            if (st == 0 || (st & gmask) != 0)
                 return;
-            const int g = (int)(st / gstages);
-            const float *sp = gsc + ((g - 1) & 3) * BN;
-            const float *sc = gsc + (g & 3) * BN;
+            const int g = st >> gshift;
+            const float *rt = gratio + (g & 3) * BN;
 #pragma unroll
             for (int i = 0; i < TN; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int r = wn * WN + i * 32 + 8 * q + 4 * lh;
-                    const float4 a = *reinterpret_cast<const float4 *>(sp + r);
-                    const float4 b = *reinterpret_cast<const float4 *>(sc + r);
-                    const float ra[4] = {a.x * __builtin_amdgcn_rcpf(b.x), a.y * __builtin_amdgcn_rcpf(b.y),
-                                         a.z * __builtin_amdgcn_rcpf(b.z), a.w * __builtin_amdgcn_rcpf(b.w)};
+                    const float4 r4 = *reinterpret_cast<const float4 *>(rt + r);
+                    const float ra[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
                     for (int j = 0; j < TM; ++j)
 #pragma unroll
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
         }
     };
 
-    auto compute = [&](int64_t st) {
+    auto compute = [&](int st) {
         rescale(st);
         const uint8_t *tx = lds + (int)(st % kStages) * kStageBytes;
         const uint8_t *tw = tx + kTileBytes;
@@ -313,15 +322,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
             }
         }
     };
-    auto issue_full = [&](int64_t st) {
+    auto issue_full = [&](int st) {
         const uint32_t t = lds_base + (uint32_t)((st % kStages) * kStageBytes);
-        lx.load_full(t, st * BK);
-        lw.load_full(t + kTileBytes, st * BK);
+        lx.load_full(t, (int64_t)st * BK);
+        lw.load_full(t + kTileBytes, (int64_t)st * BK);
     };
 
     // Full stages run through the ring, loaded kStages-1 stages ahead; a
     // partial last stage (k not a multiple of BK) is peeled off after the loop.
-    const int64_t nfull = k / BK;
+    const int nfull = (int)(k / BK);
     fetch_scale(0);
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st)
@@ -334,13 +343,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
             wsl[tid] = *x_scale * w_scale[min(n0 + tid, n - 1)];
     }
 
-    for (int64_t ks = 0; ks < nfull; ++ks) {
+    for (int ks = 0; ks < nfull; ++ks) {
         // This wave's loads for stage ks have landed once no more than the
         // loads of the later stages already issued (up to kStages-2 of them,
         // exactly kOps each) are outstanding.  The barrier then makes every
         // wave's part of the stage visible, and guarantees that all waves are
         // done with stage ks-1, whose slot the next issue overwrites.
-        const int64_t later = min<int64_t>(kStages - 2, nfull - 1 - ks);
+        const int later = min(kStages - 2, nfull - 1 - ks);
         if (later >= 2)
             __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(2 * kOps));
         else if (later == 1)
@@ -363,8 +372,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
         // this barrier also covers the reads of the last full stage.
         barrier_no_fence();
         uint8_t *t = lds + (int)(nfull % kStages) * kStageBytes;
-        lx.load_tail(t, nfull * BK, k, wave, lane);
-        lw.load_tail(t + kTileBytes, nfull * BK, k, wave, lane);
+        lx.load_tail(t, (int64_t)nfull * BK, k, wave, lane);
+        lw.load_tail(t + kTileBytes, (int64_t)nfull * BK, k, wave, lane);
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
         store_scale();
         barrier_no_fence();
@@ -384,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     const float xs = *x_scale;
     // grouped: the last group's scales (every group's LDS write preceded a
     // barrier that every wave has passed)
-    const float *slast = gsc + (GS ? ((int)(last_stage / (gstages > 0 ? gstages : 1)) & 3) * BN : 0);
+    const float *slast = gsc + (GS ? ((last_stage >> gshift) & 3) * BN : 0);
     // xs * w_scale of output column nb + v
     auto wsc = [&](int64_t nb, int v) {
         if constexpr (GS)
@@ -466,13 +475,17 @@ hipError_t w8a8(const W8A8Plan &p, const uint8_t *x, int64_t m, int64_t k, int64
 {
     const int64_t blocks = p.tiles_m * p.tiles_n;
     if (group > 0) {
-        if (group % BK != 0)
+        // groups of 128 << gshift k (128, 256 or 512)
+        const int gshift = group == BK ? 0 : group == 2 * BK ? 1 : group == 4 * BK ? 2 : -1;
+        if (gshift < 0 || k >= ((int64_t)1 << 31))
             return hipErrorInvalidValue;
         const int64_t ngroups = (k + group - 1) / group;
         hipLaunchKernelGGL(k_w8a8<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                            x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,
-                           (int)p.tiles_m, (int)p.tiles_n, ngroups, (int)(group / BK));
+                           (int)p.tiles_m, (int)p.tiles_n, ngroups, gshift);
     } else {
+        if (k >= ((int64_t)1 << 31))
+            return hipErrorInvalidValue;
         hipLaunchKernelGGL(k_w8a8<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                            x, m, k, ld_x, x_scale, w, n, ld_w, w_scale, y, ld_y,
                            (int)p.tiles_m, (int)p.tiles_n, (int64_t)0, 0);
