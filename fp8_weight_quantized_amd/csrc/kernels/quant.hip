@@ -351,23 +351,25 @@ __global__ __launch_bounds__(kThreads) void k_act_cast(
             q[row * ld_q + c] = (uint8_t)(e4m3x4(t, 0.f, 0.f, 0.f) & 0xFFu);
         }
     } else if (layout == kFlat) {
+        // the tensor's last read and the codes' only write: non-temporal
         const uint4 *p = reinterpret_cast<const uint4 *>(x);
         uint2 *o = reinterpret_cast<uint2 *>(q);
         const int64_t total = m * (k >> 3);
         for (; i + 3 * stride < total; i += 4 * stride) {
-            uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+            const uint4 a = ld_nt16(p + i), b = ld_nt16(p + i + stride);
+            const uint4 c = ld_nt16(p + i + 2 * stride), d = ld_nt16(p + i + 3 * stride);
             if constexpr (kTrack)
                 key = max(key, max(max(key_max8(a), key_max8(b)), max(key_max8(c), key_max8(d))));
-            o[i] = div.codes8(a);
-            o[i + stride] = div.codes8(b);
-            o[i + 2 * stride] = div.codes8(c);
-            o[i + 3 * stride] = div.codes8(d);
+            st_nt8(o + i, div.codes8(a));
+            st_nt8(o + i + stride, div.codes8(b));
+            st_nt8(o + i + 2 * stride, div.codes8(c));
+            st_nt8(o + i + 3 * stride, div.codes8(d));
         }
         for (; i < total; i += stride) {
-            const uint4 a = p[i];
+            const uint4 a = ld_nt16(p + i);
             if constexpr (kTrack)
                 key = max(key, key_max8(a));
-            o[i] = div.codes8(a);
+            st_nt8(o + i, div.codes8(a));
         }
     } else {
         const int64_t cpr = (k + 7) >> 3;
