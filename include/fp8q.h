@@ -363,9 +363,13 @@ fp8q_status fp8q_linear_w8a8_dynamic(const uint16_t *x_bf16, int64_t m, int64_t 
  * multiplied by s[n][g-1] / s[n][g] (hardware reciprocal) as group g opens, and
  * scaled by the last group's scale at the end.  This needs adjacent group scales
  * of a row within a factor of about 1e28 of each other, which holds for weights
- * of magnitude below 1e16.  Every other case runs the decode kernels: the rows
- * kernel where fp8q_linear would, else the tile kernel (at prefill sizes with
- * group 64, W is then re-read once per 64 activation rows).
+ * of magnitude below 1e16.  Every other case runs the decode kernels: the
+ * panel kernel where fp8q_linear would and every 4-wave K range is a whole
+ * number of groups (each wave's group scales preloaded into LDS where they
+ * fit, else staged with each chunk), the rows kernel where fp8q_linear would
+ * take it, else the tile kernel (at prefill sizes with group 64, W is then
+ * re-read once per 64 activation rows).  fp8q_linear_grouped_describe names
+ * the plan.
  * Tolerance and determinism as fp8q_linear.
  */
 size_t fp8q_linear_grouped_workspace_size(fp8q_mode mode, int64_t m, int64_t n, int64_t k,
