@@ -20,7 +20,8 @@
 // step was checked exhaustively against IEEE division on the CPU for every
 // finite bf16 x and every dynamic scale max(fl32(amax / 448), 1e-12) of a
 // finite bf16 amax (1.2e9 pairs, no difference), plus 8000 other scales in
-// [2^-40, 2^40]; the dynamic per-tensor path uses it.
+// [2^-40, 2^40]; the dynamic per-tensor activation cast and the weight
+// quantizers (per row and per group, whose scales have the same form) use it.
 //
 // Quotients of magnitude 512 and more saturate to +-448 either way, so there
 // (and for infinities) q0 is used as it is; below 2^-10 every value rounds to

@@ -75,17 +75,20 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight(
             *flag = 1;
     }
 
+    // s = max(fl32(amax / 448), 1e-12) of a bf16 amax: the quotients by the
+    // product and one FMA correction equal the IEEE divisions
+    const E4M3Div div(s, true);
     if constexpr (CH > 0) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int64_t idx = tid + (int64_t)c * kThreads;
             if (idx < nfull)
-                st_nt8(qr + idx * 8, quantize8(buf[c], s));
+                st_nt8(qr + idx * 8, div.codes8(buf[c]));
         }
     } else {
         for (int64_t idx = tid; idx < nfull; idx += kThreads) {
             uint4 v = ld_nt16(wr + idx * 8);
-            st_nt8(qr + idx * 8, quantize8(v, s));
+            st_nt8(qr + idx * 8, div.codes8(v));
         }
     }
     if (tid < tail) {
@@ -156,10 +159,13 @@ __device__ __forceinline__ void quant_chunk(uint4 v, int64_t c, int valid, uint8
     const uint32_t key = group_max_u32<LPG>(key_max8(v));
     const float s = scale_from_key(key);
     const int64_t e0 = c * 8;
+    // one reciprocal per chunk; the product and one FMA correction equal the
+    // IEEE quotients for this form of scale
+    const E4M3Div div(s, true);
     if (valid == 8) {
-        st_nt8(qr + e0, quantize8(v, s));
+        st_nt8(qr + e0, div.codes8(v));
     } else if (valid > 0) {
-        const uint2 codes = quantize8(v, s);
+        const uint2 codes = div.codes8(v);
         for (int i = 0; i < valid; ++i)
             qr[e0 + i] = (uint8_t)(((i < 4 ? codes.x : codes.y) >> (8 * (i & 3))) & 0xFFu);
     }
