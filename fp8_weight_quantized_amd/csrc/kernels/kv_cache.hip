@@ -16,6 +16,7 @@
 // grid-strided index; blockIdx.y selects K (0) or V (1).  HBM-bound: 2 B in
 // and 1 B out per value, plus a second read of the batch when calibrating.
 #include "device_common.hpp"
+#include "e4m3_div.hpp"
 #include "launch.hpp"
 
 namespace fp8q {
@@ -66,7 +67,13 @@ __global__ __launch_bounds__(kThreads) void k_kv_amax(KvArgs a)
 // The cast.  CAL: fold pass 1's maxima, raise the running maximum (every
 // block computes the same value; block 0 stores it), then cast with the
 // raised scale.  !CAL: cast with the scale of the running maximum as it is.
-template <bool CAL>
+// RCP (a prefill chunk, several chunks per thread): the quotients by one
+// reciprocal and two FMA correction steps (the running maximum may have been
+// set by the caller, so the scale need not have the dynamic form; two steps
+// are exact for any normal scale, and other scales take the IEEE division),
+// the same codes as the division per value that !RCP (a decode step's few
+// tokens) does.
+template <bool CAL, bool RCP>
 __global__ __launch_bounds__(kThreads) void k_kv_cast(KvArgs a)
 {
     __shared__ uint32_t red[kThreads / kWave];
@@ -93,11 +100,11 @@ __global__ __launch_bounds__(kThreads) void k_kv_cast(KvArgs a)
             a.running[which] = r;
         a.scale_out[which] = s;
     }
-
     const uint16_t *x = which ? a.src[1] : a.src[0];
     uint8_t *cache = which ? a.cache[1] : a.cache[0];
     int32_t local = 0;
     const uint32_t stride = gridDim.x * kThreads;
+    [[maybe_unused]] const E4M3Div div(RCP ? s : 1.0f);
     for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < a.chunks; i += stride) {
         const uint32_t t = i / a.per_token;
         const uint32_t c = i - t * a.per_token;
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_kv_cast(KvArgs a)
             continue;
         }
         *reinterpret_cast<uint2 *>(cache + ((int64_t)h * a.slots + row) * a.head_dim + j * 8) =
-            quantize8(v, s);
+            RCP ? div.codes8(v) : quantize8(v, s);
     }
     if (a.flags != nullptr) {
         if (local != 0)
@@ -160,14 +167,22 @@ hipError_t kv_cache_write(const uint16_t *k, const uint16_t *v, int64_t tokens, 
     a.per_head = (uint32_t)(head_dim / 8);
     a.head_dim = (uint32_t)head_dim;
     const dim3 grid((unsigned)kv_blocks(tokens, heads, head_dim), 2), block(kThreads);
+    // at least 4 chunks per thread: the reciprocal's setup pays off
+    const bool rcp = (int64_t)a.chunks >= 4 * (int64_t)grid.x * kThreads;
     if (calibrate) {
         hipLaunchKernelGGL(k_kv_amax, grid, block, 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(k_kv_cast<true>, grid, block, 0, stream, a);
+        if (rcp)
+            hipLaunchKernelGGL((k_kv_cast<true, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_kv_cast<true, false>), grid, block, 0, stream, a);
     } else {
-        hipLaunchKernelGGL(k_kv_cast<false>, grid, block, 0, stream, a);
+        if (rcp)
+            hipLaunchKernelGGL((k_kv_cast<false, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_kv_cast<false, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }
