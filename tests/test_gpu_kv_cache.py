@@ -94,6 +94,23 @@ def test_warmup_then_decode(fq, orc):
     assert ((L.kc[:, pos:, :] & 0x7F) == 0x7E).any()     # decode saturated somewhere
 
 
+def test_held_arbitrary_running_max(fq, orc):
+    """Running maxima set by the caller to fp32 values no bf16 maximum gives
+    (so the scale r / 448 is not of the dynamic form), on a write large
+    enough (32 heads x 128, 2048 tokens: 4 chunks per thread) for the cast to
+    take one reciprocal and two FMA correction steps per value: every code
+    must still equal the oracle's, which divides."""
+    L = Layer(32, 2048, 128)
+    L.run = np.array([np.float32(2.7182817), np.float32(0.33333334)], np.float32)
+    L.run_d.copy_(torch.from_numpy(L.run.copy()))
+    k, v = kv_batch(2048, 32 * 128, 7, k_gain=0.5, v_gain=0.1)
+    L.write(fq, orc, k, v, np.arange(2048), False, "held, arbitrary running max")
+    # a calibrating write whose maxima stay below the running maxima keeps them
+    k, v = kv_batch(2048, 32 * 128, 8, k_gain=0.01, v_gain=0.001)
+    L.write(fq, orc, k, v, np.arange(2048)[::-1].copy(), True, "calibrating, maxima below")
+    assert (L.run == np.array([np.float32(2.7182817), np.float32(0.33333334)], np.float32)).all()
+
+
 @pytest.mark.parametrize("heads,head_dim", [(1, 8), (4, 64), (32, 128), (2, 136), (8, 256)])
 def test_head_shapes(fq, orc, heads, head_dim):
     L = Layer(heads, 96, head_dim)
