@@ -205,6 +205,34 @@ def test_linear_panel_scale_stages(fq, orc, m, n, k, group, mode, stage):
     run_grouped(fq, orc, mode, m, n, k, group, 8000 + m + n + k + group, "panel " + stage)
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("m,n,k,group", [(12, 2048, 4096, 128), (13, 1000, 4096, 64),
+                                         (40, 4096, 2048, 256)])
+def test_linear_panel_strided(fq, orc, mode, m, n, k, group):
+    """Activation and weight rows with strides beyond K (views into wider
+    buffers, row pitch K + 64 values and K + 128 bytes): the panel kernel's
+    per-lane offsets and the preloaded scales' addressing."""
+    w = workloads.heavy_tail_weight(n, k, 31 + m)
+    wq, ws, _ = orc.quantize_weight_grouped(w, group)
+    x, xs = make_x(mode, m, k, 32 + m, orc)
+    wbuf = torch.zeros((n, k + 128), dtype=torch.uint8, device="cuda")
+    wbuf[:, :k] = dev_u8(wq)
+    if mode == 1:
+        xbuf = torch.zeros((m, k + 64), dtype=torch.uint8, device="cuda")
+        xbuf[:, :k] = dev_u8(x)
+    else:
+        dt = torch.bfloat16 if mode == 0 else torch.float16
+        xbuf = torch.zeros((m, k + 64), dtype=dt, device="cuda")
+        xbuf[:, :k] = dev_x(mode, x)
+    plan = fq.describe_linear(mode, m, n, k, group=group)
+    say("grouped panel strided", mode, m, n, k, group, plan)
+    y = fq.linear(xbuf[:, :k], wbuf[:, :k], torch.from_numpy(ws).cuda(),
+                  x_scale=None if xs is None else torch.tensor([xs], device="cuda"), group=group)
+    torch.cuda.synchronize()
+    ref = orc.linear_grouped(mode, x, wq, ws, group, x_scale=xs)
+    assert_gemm_close(host_bf16_as_f64(y), ref, f"strided {mode} {m}x{n}x{k} g={group}")
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("group", (64, 512))
 def test_linear_panel_wide_scale_range(fq, orc, mode, group):
