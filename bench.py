@@ -75,9 +75,10 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
-            print(json.dumps({"error": "this benchmark runs on exactly one GPU; the FP8 linear "
-                              "path is measured on one MI355X (see DESIGN.md for how it would shard)",
-                              "n_gpus": args.gpus}), flush=True)
+            print(json.dumps({"error": "this benchmark runs on exactly one GPU: the FP8 linear "
+                              "path is data-parallel (each GPU would hold whole weights and take "
+                              "its own share of the tokens), so one MI355X's share is what it "
+                              "measures", "n_gpus": args.gpus}), flush=True)
         return 2
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
