@@ -639,6 +639,15 @@ namespace {
 // cast is then cheaper (measured on MI355X, Llama-3-8B q_proj in graphs: M = 32
 // 36 us cast in the GEMM against 20 us for the quantizer + the GEMM on codes).
 constexpr int64_t kDynamicFusedMaxM = 16;
+// Up to this many activation values (64 KB of bf16) the panel kernel's
+// workgroups each read the whole tensor for its maximum instead of taking the
+// maxima of an absmax launch: an L2 read per workgroup against a launch.
+constexpr int64_t kDynamicScanMaxElems = 32768;
+
+bool dynamic_scans(const fp8q::launch::W8A16Plan &plan, int64_t m, int64_t k)
+{
+    return plan.kind == fp8q::launch::W8A16Plan::kPanel && m * k <= kDynamicScanMaxElems;
+}
 
 // Workspace of fp8q_linear_w8a8_dynamic: [0, 256) the scale slot (used when the
 // caller passes no x_scale_out), then the absmax pass's maxima, then the
@@ -735,12 +744,21 @@ fp8q_status fp8q_linear_w8a8_dynamic(const uint16_t *x_bf16, int64_t m, int64_t 
     void *rest = ws + lay.rest_off;
     hipError_t e;
     if (lay.fused) {
-        e = fp8q::launch::act_amax(x_bf16, m, k, ld_x, part, stream);
-        if (e == hipSuccess)
-            e = fp8q::launch::w8a16_quant_act(
-                fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActQ), x_bf16, m, k, ld_x,
-                part, fp8q::launch::act_blocks(m, k), scale, nonfinite_flag, w_fp8, n, ld_w,
-                w_scale, y_bf16, ld_y, rest, stream);
+        const auto plan = fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActQ);
+        if (dynamic_scans(plan, m, k)) {
+            // one launch: every panel workgroup reads the whole (small) X for
+            // its maximum
+            e = fp8q::launch::w8a16_quant_act(plan, x_bf16, m, k, ld_x, nullptr, 0, scale,
+                                              nonfinite_flag, w_fp8, n, ld_w, w_scale, y_bf16,
+                                              ld_y, rest, stream);
+        } else {
+            e = fp8q::launch::act_amax(x_bf16, m, k, ld_x, part, stream);
+            if (e == hipSuccess)
+                e = fp8q::launch::w8a16_quant_act(plan, x_bf16, m, k, ld_x, part,
+                                                  fp8q::launch::act_blocks(m, k), scale,
+                                                  nonfinite_flag, w_fp8, n, ld_w, w_scale, y_bf16,
+                                                  ld_y, rest, stream);
+        }
     } else {
         uint8_t *codes = static_cast<uint8_t *>(rest);
         void *gemm_ws = static_cast<uint8_t *>(rest) + lay.codes_bytes;
@@ -945,8 +963,12 @@ fp8q_status fp8q_linear_w8a8_dynamic_describe(int64_t m, int64_t n, int64_t k, c
         std::snprintf(buf, len, "k_act_amax + k_act_cast<0> + %s (E4M3 codes)", g);
     } else {
         char g[224];
-        describe_w8a16(fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActQ), g, sizeof g);
-        std::snprintf(buf, len, "k_act_amax + %s (activations cast in registers)", g);
+        const auto plan = fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActQ);
+        describe_w8a16(plan, g, sizeof g);
+        if (dynamic_scans(plan, m, k))
+            std::snprintf(buf, len, "%s (absmax and cast in the kernel)", g);
+        else
+            std::snprintf(buf, len, "k_act_amax + %s (activations cast in registers)", g);
     }
     return ok();
 }

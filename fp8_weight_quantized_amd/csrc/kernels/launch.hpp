@@ -115,7 +115,8 @@ hipError_t w8a16(const W8A16Plan &p, int act, const void *x, int64_t m, int64_t 
                  hipStream_t stream);
 // fp8_w_fp8_a on bf16 activations, quantized per tensor inside the GEMM: the
 // plan is plan_w8a16(m, n, k, kW8A16ActQ); act_part holds the npart maxima of
-// act_amax over x.  The scale used goes to *x_scale_out (always written;
+// act_amax over x, or is null with a panel plan, whose workgroups then each
+// read all of x for its maximum (for tensors of a few tens of KB).  The scale used goes to *x_scale_out (always written;
 // the K-split reduction reads it back), a non-finite maximum raises *flag.
 // workspace: the plan's partial tiles.
 hipError_t w8a16_quant_act(const W8A16Plan &p, const uint16_t *x, int64_t m, int64_t k,

@@ -183,6 +183,33 @@ __device__ __forceinline__ float fold_act_scale(const QuantArgs &qa)
     return s;
 }
 
+// The same scale from the activations themselves, for a tensor small enough
+// that every workgroup reads all of it (at most a few tens of KB; the host
+// passes no maxima then): the maximum is exact, so the scale is the same as
+// from the absmax pass's maxima.  k is a multiple of 8 and the rows are
+// 16-byte aligned.  Contains __syncthreads; called at the start of the
+// kernel, before any direct load is in flight.
+__device__ __forceinline__ float scan_act_scale(const uint16_t *x, int64_t m, int64_t k,
+                                                int64_t ld_x, const QuantArgs &qa)
+{
+    __shared__ uint32_t red[16];
+    uint32_t key = 0;
+    const int cpr = (int)(k >> 3);
+    const int chunks = (int)m * cpr;
+    for (int i = threadIdx.x; i < chunks; i += blockDim.x) {
+        const int row = i / cpr, c = i - row * cpr;
+        key = max(key, key_max8(*reinterpret_cast<const uint4 *>(x + row * ld_x + 8 * c)));
+    }
+    key = block_max_u32(key, red);
+    const float s = scale_from_key(key);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+        *qa.scale_out = s;
+        if (qa.flag != nullptr && key >= 0x7F80u)
+            *qa.flag = 1;
+    }
+    return s;
+}
+
 // The scale the epilogue applies for activation type AT: 1 for 16-bit
 // activations, *x_scale for E4M3 codes, the folded per-tensor scale for kActQ.
 template <int AT>
@@ -1025,7 +1052,11 @@ __global__ __launch_bounds__(NWV * 64) void k_w8a16_panel(
     const uint32_t xslot_lds = (uint32_t)(uintptr_t)xslot;
     const uint32_t wslot_lds = (uint32_t)(uintptr_t)wslot;
     const uint32_t sslot_lds = (uint32_t)(uintptr_t)sslot;
-    const float xs = act_scale<AT>(x_scale, qa);
+    // kActQ without maxima from an absmax pass: the scale from the whole
+    // (small) activation tensor, before the pipeline starts
+    const float xs = AT == kActQ && qa.part == nullptr
+                         ? scan_act_scale(static_cast<const uint16_t *>(xv), m, k, ld_x, qa)
+                         : act_scale<AT>(x_scale, qa);
     const E4M3Div div(AT == kActQ ? xs : 1.0f, true);
 
     // load i of a chunk fills LDS bytes [1 KB i, 1 KB (i + 1)) of the slot:
@@ -1877,7 +1908,8 @@ hipError_t w8a16_quant_act(const W8A16Plan &p, const uint16_t *x, int64_t m, int
                            const float *w_scale, uint16_t *y, int64_t ld_y, void *workspace,
                            hipStream_t stream)
 {
-    if (p.group != 0)
+    // without maxima only the panel kernel (which scans x itself) applies
+    if (p.group != 0 || (act_part == nullptr && p.kind != W8A16Plan::kPanel))
         return hipErrorInvalidValue;
     const QuantArgs qa{act_part, npart, x_scale_out, flag};
     return dispatch<kActQ>(p, x, m, k, ld_x, nullptr, w, n, ld_w, w_scale, y, ld_y, workspace, qa,

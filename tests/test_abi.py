@@ -162,6 +162,12 @@ def test_describe(L):
     # on the fly quantized activations keep the split rows kernel there
     assert L.fp8q_linear_w8a8_dynamic_describe(12, 1024, 8192, buf, 256) == 0
     assert b"k_w8a16_rows<1, 1, 8, 4>" in buf.value and b"splits=4" in buf.value
+    # up to 32768 activation values on the panel kernel: one launch, the
+    # workgroups take the absmax themselves; above, the absmax pass first
+    assert L.fp8q_linear_w8a8_dynamic_describe(8, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 3, 4>") and b"absmax and cast in the kernel" in buf.value
+    assert L.fp8q_linear_w8a8_dynamic_describe(12, 4096, 4096, buf, 256) == 0
+    assert buf.value.startswith(b"k_act_amax + k_w8a16_panel")
     # a K that is not a multiple of 512: the rows kernel
     assert L.fp8q_linear_describe(0, 1, 4096, 4000, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_rows<1, 1, 8, 4>")

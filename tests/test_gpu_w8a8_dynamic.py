@@ -165,6 +165,30 @@ def test_dynamic_nonfinite_flag(fq):
     assert int(flag.item()) == 1
 
 
+def test_dynamic_nonfinite_flag_single_launch(fq, orc):
+    """The same flag and scale when the panel kernel's workgroups take the
+    absmax themselves (8 x 2048 activations, one launch)."""
+    m, n, k = 8, 4096, 2048
+    assert "absmax and cast in the kernel" in fq.describe_linear(1, m, n, k, dynamic=True)
+    x = workloads.outlier_act(m, k, 4)
+    wq, ws, _ = orc.quantize_weight(workloads.heavy_tail_weight(n, k, 5))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("w8a8 dynamic single launch, finite input")
+    y, s = fq.linear_w8a8_dynamic(padded_bf16(x), padded_u8(wq), torch.from_numpy(ws).cuda(),
+                                  nonfinite_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    oxq, oxs, _ = orc.quantize_act(x)
+    assert np.float32(s.cpu().numpy()[0]).view(np.uint32) == np.float32(oxs).view(np.uint32)
+    assert_gemm_close(host_bf16_as_f64(y), orc.linear(1, oxq, wq, ws, oxs), "single launch")
+    x[5, 2047] = 0xFF80                                  # -Inf
+    say("w8a8 dynamic single launch, non-finite input")
+    fq.linear_w8a8_dynamic(padded_bf16(x), padded_u8(wq), torch.from_numpy(ws).cuda(),
+                           nonfinite_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+
+
 def test_dynamic_workspace_reuse_and_stride_guard(fq, orc):
     """Calls sharing one NaN-filled workspace, Y written into a wider buffer:
     nothing past column n or row m changes, and each call is in tolerance."""
