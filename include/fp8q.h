@@ -326,10 +326,13 @@ fp8q_status fp8q_linear_noalloc(fp8q_mode mode,
  * i.e. fp8q_quantize_act followed by fp8q_linear(FP8Q_W8A8, ...): the codes and
  * the scale are bit for bit those of fp8q_quantize_act, the sums are exact
  * products accumulated in fp32 (tolerance and determinism as fp8q_linear).
- * Up to 16 activation rows (decode) this is two kernels: the absmax pass, then
- * the decode GEMM, whose workgroups fold the pass's maxima into s_x and cast
- * the activations they load in registers, so the E4M3 activations never go
- * through memory.  More rows run fp8q_quantize_act into the workspace, then
+ * Up to 16 activation rows (decode) the decode GEMM's workgroups cast the
+ * activations they load in registers, so the E4M3 activations never go
+ * through memory: with at most 32768 activation values and the panel kernel
+ * (fp8q_linear_w8a8_dynamic_describe says which) that is one kernel whose
+ * workgroups each read all of X for its maximum, otherwise the absmax pass
+ * runs first and the GEMM folds its maxima into s_x.  More rows run
+ * fp8q_quantize_act into the workspace, then
  * the GEMM on the codes (the decode kernels up to 64 rows, the FP8 MFMA GEMM
  * beyond): every GEMM workgroup casts the rows it reads, and from 17 rows on
  * a whole column of workgroups reads each row, so one separate cast is cheaper.
