@@ -1420,9 +1420,11 @@ static void plan_tile(W8A16Plan &p, int64_t m, int64_t k, int steps_mb1)
 // The panel kernel's plans (one launch, whole K per workgroup, no partial
 // sums).  Measured on MI355X in graphs, weights rotating through 2 GiB:
 //  - up to 16 activation rows, one activation group (MB = 1): AF weight
-//    fragments per workgroup, AF in {1, 2, 3, 4, 7}, the AF whose grid wastes
-//    the least of whole rounds of 256 workgroups (ties to the larger AF);
-//    a weight of 256..1535 rows spreads the activation rows 4 per workgroup.
+//    fragments per workgroup, AF in {1, 2, 3, 4, 7}, the AF with the least
+//    rounds of 256 workgroups x (2 AF + 1) (the rule below; ties to the
+//    larger AF); a weight of 256..1535 rows spreads the activation rows 4
+//    per workgroup.  (Figures below are from before the non-temporal weight
+//    loads, which took another 5-11% off.)
 //    Llama-3-8B q_proj (4096 x 4096): M = 1 5.7 us, M = 8 5.9 us, M = 16
 //    6.7 us against 5.8 / 7.0 / 8.3 us for the rows kernel; Llama-3-70B at
 //    M = 12: q/o (8192 x 8192) 14.1 us, gate/up (28672 x 8192) 42.6 us,
