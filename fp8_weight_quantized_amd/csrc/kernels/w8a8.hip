@@ -302,7 +302,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
         }
     };
 
-    auto compute = [&](int st) {
+    // after_first_reads runs once the stage's first activation fragments
+    // have been read from LDS (the grouped kernel issues the next stage's
+    // loads there)
+    auto compute = [&](int st, auto after_first_reads) {
         rescale(st);
         const uint8_t *tx = lds + (int)(st % kStages) * kStageBytes;
         const uint8_t *tw = tx + kTileBytes;
@@ -312,6 +315,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
 #pragma unroll
             for (int j = 0; j < TM; ++j)
                 xf[j] = lds_frag(tx, wm * WM + j * 32 + lr, lh, sub);
+            if (sub == 0)
+                after_first_reads();
 #pragma unroll
             for (int i = 0; i < TN; ++i) {
                 const v8i wf = lds_frag(tw, wn * WN + i * 32 + lr, lh, sub);
@@ -360,10 +365,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
         // with this wait; its LDS write goes before the barrier)
         store_scale();
         barrier_no_fence();
-        if (ks + kStages - 1 < nfull)
-            issue_full(ks + kStages - 1);
+        // grouped: the next stage's loads go out after the rescale and this
+        // stage's first fragment reads (5-6% faster with groups of 128 than
+        // issuing them first; per channel 2.5% slower, so there they go first)
+        auto issue_next = [&] {
+            if (ks + kStages - 1 < nfull)
+                issue_full(ks + kStages - 1);
+        };
+        if constexpr (!GS)
+            issue_next();
         fetch_scale(ks + 1);
-        compute(ks);
+        if constexpr (GS)
+            compute(ks, issue_next);
+        else
+            compute(ks, [] {});
     }
     if (k % BK != 0) {
         // All direct loads have landed (the last loop iteration waited for
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
         store_scale();
         barrier_no_fence();
-        compute(nfull);
+        compute(nfull, [] {});
     }
 
     // ---- epilogue.  In a 32 x 32 block, lane (col = lane % 32, h = lane / 32)
