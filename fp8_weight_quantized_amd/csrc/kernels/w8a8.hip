@@ -175,11 +175,16 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 // stages.  The accumulators then hold the running sum in units of the
 // current group's scale: when stage ks opens group g, every accumulator of
 // weight row n is multiplied by s[n][g-1] / s[n][g] before the stage's
-// MFMAs, and the epilogue multiplies by the last group's scale.  That is
+// MFMAs add to it, and the epilogue multiplies by the last group's scale.  That is
 // sum_g s_g * P_g with one accumulator set (a second set would not fit the
 // register file next to the 256 x 256 tile).  The ratios use the hardware
 // reciprocal (about 1 ulp); group scales come through a 4-slot LDS ring of
-// the tile's 256 rows, loaded one stage ahead.
+// the tile's 256 rows, loaded two stages ahead.  The two waves of a SIMD
+// (waves w and w + 4, which own different halves of the tile's M) multiply at
+// different times: the first half at the start of the stage that opens the
+// group, the second at the end of the stage before it, after its MFMAs, so
+// one wave's multiplies can overlap the other's MFMAs (2-3% faster with
+// groups of 128 than both at the start of the stage).
 template <bool GS>
 __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     const uint8_t *__restrict__ x, int64_t m, int64_t k, int64_t ld_x,
@@ -238,16 +243,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
                 acc[i][j][v] = 0.f;
 
     // grouped: the scale of tile row tid (< BN) for group g, loaded into a
-    // register one stage ahead and written to LDS slot g & 3 before the barrier
-    // of the stage that opens group g
+    // register two stages ahead and written to LDS slot g & 3 before the
+    // barrier of the stage before the one that opens group g (group 0 and the
+    // group of stage 1 are loaded before the loop and written in stage 0)
     // Stage indices are 32-bit (K < 2^31) and group boundaries a shift and a
     // mask: 64-bit divisions here cost over a hundred scalar instructions
     // each, per stage and wave, on the scalar unit the CU's waves share.
     const int last_stage = (int)(k / BK) - (k % BK == 0 ? 1 : 0);
     const int gmask = (1 << gshift) - 1;
     const float *srow = w_scale + (GS ? min(n0 + tid, n - 1) * ngroups : 0);
-    float pend = 0.f, prev = 0.f;
+    float pend = 0.f, prev = 0.f, pend0 = 0.f;
     int pend_g = -1;
+    bool have0 = false;
     auto fetch_scale = [&](int st) {
         if constexpr (GS) {
             if (st <= last_stage && (st & gmask) == 0) {
@@ -259,6 +266,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     };
     auto store_scale = [&]() {
         if constexpr (GS) {
+            if (have0) {
+                if (tid < BN) {
+                    gsc[tid] = pend0;
+                    prev = pend0;
+                }
+                have0 = false;
+            }
             if (pend_g >= 0) {
                 if (tid < BN) {
                     gsc[(pend_g & 3) * BN + tid] = pend;
@@ -306,7 +320,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     // have been read from LDS (the grouped kernel issues the next stage's
     // loads there)
     auto compute = [&](int st, auto after_first_reads) {
-        rescale(st);
+        if (!GS || wm == 0)
+            rescale(st);
         const uint8_t *tx = lds + (int)(st % kStages) * kStageBytes;
         const uint8_t *tw = tx + kTileBytes;
 #pragma unroll
@@ -326,6 +341,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
                         wf, xf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
             }
         }
+        if (GS && wm == 1 && st < last_stage)
+            rescale(st + 1);
     };
     auto issue_full = [&](int st) {
         const uint32_t t = lds_base + (uint32_t)((st % kStages) * kStageBytes);
@@ -336,7 +353,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
     // Full stages run through the ring, loaded kStages-1 stages ahead; a
     // partial last stage (k not a multiple of BK) is peeled off after the loop.
     const int nfull = (int)(k / BK);
-    fetch_scale(0);
+    if constexpr (GS) {
+        if (tid < BN)
+            pend0 = srow[0];
+        have0 = true;
+        fetch_scale(1);
+    }
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st)
         if (st < nfull)
@@ -365,16 +387,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
         // with this wait; its LDS write goes before the barrier)
         store_scale();
         barrier_no_fence();
-        // grouped: the next stage's loads go out after the rescale and this
-        // stage's first fragment reads (5-6% faster with groups of 128 than
-        // issuing them first; per channel 2.5% slower, so there they go first)
+        // grouped: the next stage's loads go out after this stage's first
+        // fragment reads, and after the rescale where it comes first (5-6%
+        // faster with groups of 128 than issuing them first; per channel 2.5%
+        // slower, so there they go first)
         auto issue_next = [&] {
             if (ks + kStages - 1 < nfull)
                 issue_full(ks + kStages - 1);
         };
         if constexpr (!GS)
             issue_next();
-        fetch_scale(ks + 1);
+        fetch_scale(ks + 2);
         if constexpr (GS)
             compute(ks, issue_next);
         else
