@@ -332,6 +332,14 @@ def test_w8a8_gemm_grouped(fq, orc, group, m, n, k):
     run_grouped(fq, orc, 1, m, n, k, group, 3000 + m + n + k, "gemm")
 
 
+# more than 8 tile-rows, so the XCD-banded tile order has a full band and a
+# partial one (80 and 51 tiles); K = 640 ends in a partial group of 256 or 512
+@pytest.mark.parametrize("group", (128, 256, 512))
+@pytest.mark.parametrize("m,n,k", [(2305, 2048, 640), (4100, 600, 256)])
+def test_w8a8_gemm_grouped_many_tile_rows(fq, orc, group, m, n, k):
+    run_grouped(fq, orc, 1, m, n, k, group, 3100 + m + n + k, "gemm, many tile-rows")
+
+
 @pytest.mark.parametrize("group", (128, 512))
 def test_w8a8_gemm_grouped_wide_scale_range(fq, orc, group):
     """Adjacent groups whose scales differ by many orders of magnitude: an
@@ -430,3 +438,32 @@ def test_grouped_output_stride_guard(fq, orc, mode, m, n, k, group):
     got = ybuf[:m, :n].view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
     ref = orc.linear_grouped(mode, x, wq, ws, group, x_scale=xs)
     assert_gemm_close(got, ref, f"grouped stride guard mode {mode} {m}x{n}x{k} g={group}")
+
+
+def test_w8a8_gemm_grouped_full_down_prefill_sampled(fq, orc):
+    """Llama-3-70B down_proj prefill, W[8192, 28672], X[4096, 28672], groups
+    of 128: 224 groups per row, so every wave pair of the GEMM passes through
+    224 rescales; codes and scales bit-exact, GEMM checked on sampled rows of
+    every 256-row tile band."""
+    wl = workloads.WORKLOADS["down_prefill_70b"]
+    lin = wl.linears[0]
+    m = wl.ms[0]
+    w = workloads.weight(wl, lin)
+    x = workloads.activation(wl, m, lin.k)
+    say("grouped down prefill quantize")
+    q, s = fq.quantize_weight_grouped(dev_bf16(w), 128)
+    xq, xs = fq.quantize_act(dev_bf16(x))
+    torch.cuda.synchronize()
+    qr, sr, _ = orc.quantize_weight_grouped(w, 128)
+    assert (host_u8(q) == qr).all()
+    assert (host_f32(s).view(np.uint32) == sr.view(np.uint32)).all()
+    del w
+    say("grouped down prefill gemm")
+    y = fq.linear(xq, q, s, x_scale=xs, group=128)
+    torch.cuda.synchronize()
+    xqr, xsr, _ = orc.quantize_act(x)
+    rows = rows_every_tile(m, 10)
+    assert rows.size >= 64 and len(set(rows // 256)) == (m + 255) // 256
+    ref = orc.linear_grouped(1, xqr, qr, sr, 128, x_scale=xsr, rows=rows)
+    got = host_bf16_as_f64(y[torch.from_numpy(rows).cuda()])
+    assert_gemm_close(got, ref, "grouped down prefill sampled rows")
