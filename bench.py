@@ -353,8 +353,9 @@ def main() -> int:
                 "GB/s": round(bytesd / (usd * 1e-6) / 1e9, 1),
                 "frac_hbm": round(bytesd / (usd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "mode": "fp8_w_fp8_a from bf16 X (fp8q_linear_w8a8_dynamic): up to 16 rows the "
-                        "absmax kernel, then the decode GEMM casting X to E4M3 in registers (2 "
-                        "launches); 17-64 rows the quantizer, then the GEMM on the codes",
+                        "decode GEMM taking the absmax and casting X to E4M3 in registers (one "
+                        "launch up to 32768 activation values, else after an absmax launch); "
+                        "17-64 rows the quantizer, then the GEMM on the codes",
                 "kernels": {str(m): fq.describe_linear(1, m, N, K, dynamic=True) for m in DECODE_MS}}
             log(rows["f1_w8a8_dynamic_q_proj_decode"])
             del wspd
