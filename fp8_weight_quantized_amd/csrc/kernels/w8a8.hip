@@ -383,8 +383,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_w8a8(
             __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kOps));
         else
             __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
-        // (grouped: the scale load issued during the previous stage has landed
-        // with this wait; its LDS write goes before the barrier)
+        // (grouped: the scale load issued one stage earlier, or before the
+        // loop, has landed with this wait; its LDS write goes before the
+        // barrier)
         store_scale();
         barrier_no_fence();
         // grouped: the next stage's loads go out after this stage's first
