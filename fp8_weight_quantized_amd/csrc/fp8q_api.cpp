@@ -497,6 +497,40 @@ int act_type(fp8q_mode mode)
                                     : fp8q::launch::kW8A16ActF8;
 }
 
+// Whether a per-channel call runs the decode kernels rather than a prefill
+// GEMM (the FP8 one for fp8_w_fp8_a, the 16-bit one for the other two modes).
+// Up to 64 rows always.  From 65 to 1024 rows a GEMM whose grid is one round
+// of a few 256 x 256 tiles keeps most CUs idle through its whole K loop,
+// while the decode kernels run the rows as 64-row groups along their grid,
+// each group streaming W (the later ones largely from L2).  The choice takes
+// the cheaper of two cost estimates in microseconds, fitted to measurements
+// on MI355X (K = 4096; N = 4096, 8192, 28672; M = 65..1024; HIP graphs with
+// the weights rotated past the Infinity Cache):
+//   decode kernels   5 + ceil(M / 64) * N * K / 3.2e6
+//   FP8 GEMM         rounds * (K / 128) * 1.45
+//   16-bit GEMM      rounds * (K / 64) * 1.4
+// where rounds = ceil(256 x 256 tiles / 256).  E.g. N = K = 4096 at 128 rows:
+// 18 us on the decode kernels against 44 us (FP8) and 85 us (16-bit) for the
+// GEMMs; N = 28672 keeps the FP8 GEMM from 65 rows on.  Plans whose K-split
+// scratch would pass 4 MiB keep the GEMM.
+constexpr int64_t kMidRowsMax = 1024;
+constexpr size_t kMidRowsMaxWorkspace = (size_t)4 << 20;
+
+bool rows_on_decode(fp8q_mode mode, int64_t m, int64_t n, int64_t k)
+{
+    if (m <= kW8A8DecodeMaxM)
+        return true;
+    if (m > kMidRowsMax)
+        return false;
+    const double tiles = (double)((m + 255) / 256) * (double)((n + 255) / 256);
+    const double rounds = (double)(int64_t)((tiles + 255.0) / 256.0);
+    const double gemm = mode == FP8Q_W8A8 ? rounds * (double)k / 128.0 * 1.45
+                                          : rounds * (double)k / 64.0 * 1.4;
+    const double decode = 5.0 + (double)((m + 63) / 64) * (double)n * (double)k / 3.2e6;
+    return decode < gemm &&
+           fp8q::launch::plan_w8a16(m, n, k, act_type(mode)).workspace <= kMidRowsMaxWorkspace;
+}
+
 // group == 0: one weight scale per output row; else per-group scales
 size_t linear_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t group)
 {
@@ -510,14 +544,13 @@ size_t linear_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t
         return round_up(fp8q::launch::plan_w8a16_grouped(m, n, k, group, act_type(mode)).workspace,
                         256);
     }
-    if ((mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16) && m > kW8A8DecodeMaxM)
-        return 0;                   // the 16-bit prefill GEMM needs no scratch
-    if (mode == FP8Q_W8A16 || mode == FP8Q_W8A16_F16 ||
-        (mode == FP8Q_W8A8 && m <= kW8A8DecodeMaxM))
+    if (mode != FP8Q_W8A16 && mode != FP8Q_W8A16_F16 && mode != FP8Q_W8A8)
+        return 0;
+    if (rows_on_decode(mode, m, n, k))
         return round_up(fp8q::launch::plan_w8a16(m, n, k, act_type(mode)).workspace, 256);
     if (mode == FP8Q_W8A8)
         return round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
-    return 0;
+    return 0;                       // the 16-bit prefill GEMM needs no scratch
 }
 
 fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int64_t ld_x,
@@ -550,7 +583,7 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
         (!fp8q::launch::w8a8_supports_ld(ld_x) || !fp8q::launch::w8a8_supports_ld(ld_w)))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_w_fp8_a needs ld_x and ld_w below 2^23 (got %lld, %lld)",
                     (long long)ld_x, (long long)ld_w);
-    if (a16 && group == 0 && m > kW8A8DecodeMaxM &&
+    if (a16 && group == 0 && !rows_on_decode(mode, m, n, k) &&
         !fp8q::launch::w8a16_gemm_supports(ld_x, ld_w))
         return fail(FP8Q_ERR_INVALID_ARG,
                     "above 64 rows the 16-bit activation modes need ld_x below 2^22 and ld_w "
@@ -597,13 +630,13 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
         const auto plan = fp8q::launch::plan_w8a16_grouped(m, n, k, group, act);
         e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
                                 ld_y, workspace, stream);
-    } else if (a16 && m > kW8A8DecodeMaxM) {
-        e = fp8q::launch::w8a16_gemm(mode == FP8Q_W8A16_F16, static_cast<const uint16_t *>(x), m, k,
-                                     ld_x, w_fp8, n, ld_w, w_scale, y_bf16, ld_y, stream);
-    } else if (a16 || m <= kW8A8DecodeMaxM) {
+    } else if (rows_on_decode(mode, m, n, k)) {
         const auto plan = fp8q::launch::plan_w8a16(m, n, k, act);
         e = fp8q::launch::w8a16(plan, act, x, m, k, ld_x, x_scale, w_fp8, n, ld_w, w_scale, y_bf16,
                                 ld_y, workspace, stream);
+    } else if (a16) {
+        e = fp8q::launch::w8a16_gemm(mode == FP8Q_W8A16_F16, static_cast<const uint16_t *>(x), m, k,
+                                     ld_x, w_fp8, n, ld_w, w_scale, y_bf16, ld_y, stream);
     } else {
         const auto plan = fp8q::launch::plan_w8a8(m, n, k);
         e = fp8q::launch::w8a8(plan, static_cast<const uint8_t *>(x), m, k, ld_x, x_scale, w_fp8,
@@ -673,7 +706,7 @@ DynLayout dyn_layout(int64_t m, int64_t n, int64_t k)
     } else {
         l.codes_bytes = round_up((size_t)m * (size_t)l.ldq, 256);
         rest = l.codes_bytes +
-               round_up(m <= kW8A8DecodeMaxM
+               round_up(rows_on_decode(FP8Q_W8A8, m, n, k)
                             ? fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActF8).workspace
                             : fp8q::launch::plan_w8a8(m, n, k).workspace,
                         256);
@@ -764,7 +797,7 @@ fp8q_status fp8q_linear_w8a8_dynamic(const uint16_t *x_bf16, int64_t m, int64_t 
         void *gemm_ws = static_cast<uint8_t *>(rest) + lay.codes_bytes;
         e = fp8q::launch::quantize_act(x_bf16, m, k, ld_x, codes, lay.ldq, scale, part,
                                        nonfinite_flag, stream);
-        if (e == hipSuccess && m <= kW8A8DecodeMaxM)
+        if (e == hipSuccess && rows_on_decode(FP8Q_W8A8, m, n, k))
             e = fp8q::launch::w8a16(fp8q::launch::plan_w8a16(m, n, k, fp8q::launch::kW8A16ActF8),
                                     fp8q::launch::kW8A16ActF8, codes, m, k, lay.ldq, scale, w_fp8,
                                     n, ld_w, w_scale, y_bf16, ld_y, gemm_ws, stream);
@@ -934,15 +967,15 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
         return fail(FP8Q_ERR_INVALID_ARG, "bad sizes");
     if (mode != FP8Q_W8A16 && mode != FP8Q_W8A16_F16 && mode != FP8Q_W8A8)
         return fail(FP8Q_ERR_INVALID_ARG, "unknown mode %d", (int)mode);
-    if (mode == FP8Q_W8A8 && m > kW8A8DecodeMaxM)
+    if (rows_on_decode(mode, m, n, k))
+        describe_w8a16(fp8q::launch::plan_w8a16(m, n, k, act_type(mode)), buf, len);
+    else if (mode == FP8Q_W8A8)
         describe_w8a8(m, n, k, false, buf, len);
-    else if (m > kW8A8DecodeMaxM)
+    else
         std::snprintf(buf, len, "k_w8a16_gemm<%s> tile=256x256x64 grid=%lld (%lldx%lld) block=512",
                       mode == FP8Q_W8A16_F16 ? "true" : "false",
                       (long long)(((m + 255) / 256) * ((n + 255) / 256)), (long long)((m + 255) / 256),
                       (long long)((n + 255) / 256));
-    else
-        describe_w8a16(fp8q::launch::plan_w8a16(m, n, k, act_type(mode)), buf, len);
     return ok();
 }
 
@@ -953,7 +986,7 @@ fp8q_status fp8q_linear_w8a8_dynamic_describe(int64_t m, int64_t n, int64_t k, c
         return fail(FP8Q_ERR_INVALID_ARG, "buf is NULL or empty");
     if (m < 0 || n < 0 || k < 1)
         return fail(FP8Q_ERR_INVALID_ARG, "bad sizes");
-    if (m > kW8A8DecodeMaxM) {
+    if (!rows_on_decode(FP8Q_W8A8, m, n, k)) {
         char g[192];
         describe_w8a8(m, n, k, false, g, sizeof g);
         std::snprintf(buf, len, "k_act_amax + k_act_cast<0> + %s", g);

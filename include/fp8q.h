@@ -263,14 +263,18 @@ fp8q_status fp8q_kv_cache_write(const uint16_t *k_bf16, const uint16_t *v_bf16, 
  *               x = E4M3 codes [m, k] (ld_x % 16 == 0); x_scale = device fp32[1];
  *               ld_x and ld_w must be below 2^23 in this mode.  Up to 64 activation
  *               rows run the decode kernels (codes widened exactly to bf16), more
- *               rows the FP8 MFMA GEMM; both compute the same sums.
+ *               rows the FP8 MFMA GEMM (but see below); both compute the same sums.
  *   FP8Q_W8A16_F16: as FP8Q_W8A16 with x = fp16 [m, k] and y fp16 (RNE) instead of
  *               bf16 (E4M3 values are exact in fp16; |Y| must stay below 65504).
  * Products are exact and sums are accumulated in fp32; the result is within
  * 5e-3 relative Frobenius error of the exact value (see the tests).
  * Above 64 activation rows the 16-bit modes run a prefill GEMM on the 16-bit
  * MFMA (weights widened exactly to the activation type; it needs ld_x below
- * 2^22 and ld_w below 2^23).  In every mode ld_x and ld_w must be below 2^28
+ * 2^22 and ld_w below 2^23).  From 65 to 1024 rows, where a GEMM's grid would
+ * be one round of a few 256 x 256 tiles (a narrow N), the decode kernels run
+ * instead, the rows in 64-row groups along their grid, when a cost estimate
+ * fitted to MI355X measurements says they are faster (fp8q_linear_describe
+ * names the kernel a shape gets).  In every mode ld_x and ld_w must be below 2^28
  * (the decode kernels address a few rows per load with 32-bit offsets);
  * larger strides return FP8Q_ERR_INVALID_ARG.
  *
@@ -333,8 +337,8 @@ fp8q_status fp8q_linear_noalloc(fp8q_mode mode,
  * workgroups each read all of X for its maximum, otherwise the absmax pass
  * runs first and the GEMM folds its maxima into s_x.  More rows run
  * fp8q_quantize_act into the workspace, then
- * the GEMM on the codes (the decode kernels up to 64 rows, the FP8 MFMA GEMM
- * beyond): every GEMM workgroup casts the rows it reads, and from 17 rows on
+ * the GEMM on the codes (the kernel fp8q_linear(FP8Q_W8A8, ...) runs for that
+ * shape): every GEMM workgroup casts the rows it reads, and from 17 rows on
  * a whole column of workgroups reads each row, so one separate cast is cheaper.
  *
  *   x_bf16       [m, k] bf16, ld_x >= k, ld_x % 8 == 0, 16-byte aligned
@@ -403,7 +407,7 @@ fp8q_status fp8q_linear_describe(fp8q_mode mode, int64_t m, int64_t n, int64_t k
 
 /*
  * The same for fp8q_linear_w8a8_dynamic (the absmax pass, then the GEMM that
- * casts the activations, or the quantizer and the FP8 MFMA GEMM above 64
+ * casts the activations, or the quantizer and the GEMM on the codes above 16
  * rows).  Host-only; launches nothing.
  */
 fp8q_status fp8q_linear_w8a8_dynamic_describe(int64_t m, int64_t n, int64_t k, char *buf,

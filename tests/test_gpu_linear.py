@@ -164,10 +164,18 @@ def test_w8a8_exact_every_code(fq, orc, m, n, k):
 # N around the 256 x 256 tile, and more than 8 tile-rows
 PREFILL16 = [(65, 300, 640), (256, 256, 64), (513, 257, 200), (300, 520, 1000), (129, 200, 96),
              (777, 64, 2048), (1000, 1000, 1280), (2305, 2048, 640), (100, 96, 4104), (257, 33, 13)]
+# From 65 to 1024 rows a narrow weight on a long enough K runs the decode
+# kernels instead of a GEMM (the GEMM's grid would be one round of a few
+# tiles); these shapes have more than 1024 rows, so the GEMMs take them
+# whatever N is.
+GEMM_ROWS = [(1089, 300, 640), (1324, 520, 1000), (1801, 64, 2048), (1030, 1000, 1280),
+             (1124, 96, 4104)]
+PREFILL16_EXACT = [(1089, 300, 640), (256, 256, 64), (513, 257, 200), (1324, 520, 1000),
+                   (129, 200, 96), (1801, 64, 2048)]
 
 
 @pytest.mark.parametrize("mode", [0, 2])
-@pytest.mark.parametrize("m,n,k", PREFILL16[:6])
+@pytest.mark.parametrize("m,n,k", PREFILL16_EXACT)
 def test_prefill16_exact_every_code(fq, orc, mode, m, n, k):
     """One-hot 16-bit rows through k_w8a16_gemm: every E4M3 code widened
     exactly, the tile layouts and the zero-filled K tail bit for bit."""
@@ -184,7 +192,7 @@ def test_prefill16_exact_every_code(fq, orc, mode, m, n, k):
 
 
 @pytest.mark.parametrize("mode", [0, 2])
-@pytest.mark.parametrize("m,n,k", PREFILL16)
+@pytest.mark.parametrize("m,n,k", PREFILL16 + GEMM_ROWS)
 def test_prefill16_ragged(fq, orc, mode, m, n, k):
     w = workloads.heavy_tail_weight(n, k, m + n + 5)
     wq, ws, _ = orc.quantize_weight(w)
@@ -250,7 +258,7 @@ MANY_TILE_ROWS = [(2305, 2048, 640), (4100, 600, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", RAGGED + [(300, 520, 1000), (256, 256, 4096), (513, 257, 200)] + WHOLE_STAGES
-                         + MANY_TILE_ROWS + PANEL_SHAPES)
+                         + MANY_TILE_ROWS + PANEL_SHAPES + GEMM_ROWS)
 def test_w8a8_ragged(fq, orc, m, n, k):
     w = workloads.heavy_tail_weight(n, k, m + n)
     x = workloads.outlier_act(m, k, k)
@@ -471,3 +479,39 @@ def test_output_stride_guard(fq, orc, mode, m, n, k):
     assert (yb[m:, :] == sentinel).all(), "wrote past row m"
     y = host_bf16_as_f64(ybuf[:m, :n].view(torch.bfloat16))
     assert_gemm_close(y, ref, f"stride guard mode {mode} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_mid_rows_route_by_cost(fq, mode):
+    """65..1024 rows: the decode kernels where the GEMM's grid would be one
+    round of a few tiles (Llama-3-8B q_proj at 128 rows), the GEMMs on a wide
+    weight (gate+up at 512 rows) and past 1024 rows."""
+    assert fq.describe_linear(mode, 128, 4096, 4096).startswith("k_w8a16_tile<")
+    gemm = "k_w8a8 " if mode == 1 else "k_w8a16_gemm<"
+    assert fq.describe_linear(mode, 512, 28672, 4096).startswith(gemm)
+    assert fq.describe_linear(mode, 1025, 4096, 4096).startswith(gemm)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("m", [65, 128, 200, 256])
+def test_mid_rows_q_proj(fq, orc, mode, m):
+    """Llama-3-8B q_proj (N = K = 4096) at 65..256 rows, on the decode kernels
+    in 64-row groups along the grid, against the oracle."""
+    wl = workloads.WORKLOADS["q_proj_decode"]
+    lin = wl.linears[0]
+    wq, ws, _ = orc.quantize_weight(workloads.weight(wl, lin))
+    say("mid rows q_proj", mode, m, fq.describe_linear(mode, m, lin.n, lin.k))
+    assert fq.describe_linear(mode, m, lin.n, lin.k).startswith("k_w8a16_tile<")
+    if mode == 1:
+        xq, xs, _ = orc.quantize_act(workloads.activation(wl, m, lin.k))
+        y = run_w8a8(fq, xq, xs, wq, ws)
+        ref = orc.linear(1, xq, wq, ws, xs)
+    elif mode == 0:
+        x = workloads.activation(wl, m, lin.k)
+        y = run_w8a16(fq, x, wq, ws)
+        ref = orc.linear(0, x, wq, ws)
+    else:
+        x = f16_act(m, lin.k, 77 + m)
+        y = run_w8a16_f16(fq, x, wq, ws)
+        ref = orc.linear(2, x, wq, ws)
+    assert_gemm_close(y, ref, f"mid rows q_proj mode {mode} m={m}")

@@ -55,7 +55,8 @@ SHAPES = [(1, 4096, 4096, "k_w8a16_panel"), (8, 4096, 4096, "k_w8a16_panel"),
           (64, 4096, 4096, "k_act_cast<0> + k_w8a16_panel"), (40, 300, 3000, "k_w8a16_tile"),
           (3, 100, 13, "k_w8a16"), (12, 8192, 8192, "k_w8a16_panel"),
           (2, 28672, 2048, "k_w8a16_panel"), (13, 3000, 2560, "k_w8a16_panel"),
-          (65, 520, 1000, "k_w8a8"), (300, 256, 4096, "k_w8a8")]
+          (65, 520, 1000, "k_act_cast<0> + k_w8a16_tile"), (300, 256, 4096, "k_act_cast<0> + k_w8a16_tile"),
+          (1100, 520, 1000, "k_act_cast<0> + k_w8a8"), (300, 28672, 1024, "k_act_cast<0> + k_w8a8")]
 
 
 @pytest.mark.parametrize("m,n,k,kern", SHAPES)
