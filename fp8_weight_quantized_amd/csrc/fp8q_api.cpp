@@ -483,11 +483,19 @@ bool valid_group(int64_t group)
     return group == 64 || group == 128 || group == 256 || group == 512;
 }
 
+bool mid_rows_decode_cheaper(fp8q_mode mode, int64_t m, int64_t n, int64_t k, double gemm_scale);
+size_t grouped_decode_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t group);
+
 // Grouped fp8_w_fp8_a with more than the decode rows runs the FP8 MFMA GEMM,
-// which folds group scales at its 128-k stages (groups of 128 k or more).
-bool grouped_uses_gemm(fp8q_mode mode, int64_t m, int64_t group)
+// which folds group scales at its 128-k stages (groups of 128 k or more),
+// except where the decode kernels are cheaper (the rule of rows_on_decode
+// below, with the grouped GEMM's cost about 1.25x the per-channel one's).
+bool grouped_uses_gemm(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t group)
 {
-    return mode == FP8Q_W8A8 && m > kW8A8DecodeMaxM && group >= 128;
+    if (mode != FP8Q_W8A8 || m <= kW8A8DecodeMaxM || group < 128)
+        return false;
+    return !(mid_rows_decode_cheaper(mode, m, n, k, 1.25) &&
+             grouped_decode_workspace(mode, m, n, k, group) <= ((size_t)4 << 20));
 }
 
 int act_type(fp8q_mode mode)
@@ -516,18 +524,29 @@ int act_type(fp8q_mode mode)
 constexpr int64_t kMidRowsMax = 1024;
 constexpr size_t kMidRowsMaxWorkspace = (size_t)4 << 20;
 
-bool rows_on_decode(fp8q_mode mode, int64_t m, int64_t n, int64_t k)
+// the estimates above for 65..1024 rows; gemm_scale scales the GEMM's
+bool mid_rows_decode_cheaper(fp8q_mode mode, int64_t m, int64_t n, int64_t k, double gemm_scale)
 {
-    if (m <= kW8A8DecodeMaxM)
-        return true;
-    if (m > kMidRowsMax)
+    if (m <= kW8A8DecodeMaxM || m > kMidRowsMax)
         return false;
     const double tiles = (double)((m + 255) / 256) * (double)((n + 255) / 256);
     const double rounds = (double)(int64_t)((tiles + 255.0) / 256.0);
     const double gemm = mode == FP8Q_W8A8 ? rounds * (double)k / 128.0 * 1.45
                                           : rounds * (double)k / 64.0 * 1.4;
     const double decode = 5.0 + (double)((m + 63) / 64) * (double)n * (double)k / 3.2e6;
-    return decode < gemm &&
+    return decode < gemm * gemm_scale;
+}
+
+size_t grouped_decode_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t group)
+{
+    return fp8q::launch::plan_w8a16_grouped(m, n, k, group, act_type(mode)).workspace;
+}
+
+bool rows_on_decode(fp8q_mode mode, int64_t m, int64_t n, int64_t k)
+{
+    if (m <= kW8A8DecodeMaxM)
+        return true;
+    return mid_rows_decode_cheaper(mode, m, n, k, 1.0) &&
            fp8q::launch::plan_w8a16(m, n, k, act_type(mode)).workspace <= kMidRowsMaxWorkspace;
 }
 
@@ -539,7 +558,7 @@ size_t linear_workspace(fp8q_mode mode, int64_t m, int64_t n, int64_t k, int64_t
     if (group > 0) {
         if (!valid_group(group))
             return 0;
-        if (grouped_uses_gemm(mode, m, group))
+        if (grouped_uses_gemm(mode, m, n, k, group))
             return round_up(fp8q::launch::plan_w8a8(m, n, k).workspace, 256);
         return round_up(fp8q::launch::plan_w8a16_grouped(m, n, k, group, act_type(mode)).workspace,
                         256);
@@ -622,7 +641,7 @@ fp8q_status linear_impl(fp8q_mode mode, const void *x, int64_t m, int64_t k, int
 
     const int act = act_type(mode);
     hipError_t e;
-    if (group > 0 && grouped_uses_gemm(mode, m, group)) {
+    if (group > 0 && grouped_uses_gemm(mode, m, n, k, group)) {
         const auto plan = fp8q::launch::plan_w8a8(m, n, k);
         e = fp8q::launch::w8a8(plan, static_cast<const uint8_t *>(x), m, k, ld_x, x_scale, w_fp8,
                                n, ld_w, w_scale, y_bf16, ld_y, stream, group);
@@ -1018,7 +1037,7 @@ fp8q_status fp8q_linear_grouped_describe(fp8q_mode mode, int64_t m, int64_t n, i
     if (!valid_group(group))
         return fail(FP8Q_ERR_INVALID_ARG, "group must be 64, 128, 256 or 512 (got %lld)",
                     (long long)group);
-    if (grouped_uses_gemm(mode, m, group))
+    if (grouped_uses_gemm(mode, m, n, k, group))
         describe_w8a8(m, n, k, true, buf, len);
     else
         describe_w8a16(fp8q::launch::plan_w8a16_grouped(m, n, k, group, act_type(mode)), buf, len);

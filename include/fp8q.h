@@ -366,7 +366,9 @@ fp8q_status fp8q_linear_w8a8_dynamic(const uint16_t *x_bf16, int64_t m, int64_t 
  * Arguments as fp8q_linear, plus group (64, 128, 256 or 512); w_scale must lie
  * inside one device allocation and hold positive finite scales.
  * FP8Q_W8A8 with more than 64 activation rows and group >= 128 runs the FP8
- * MFMA GEMM: its accumulators are kept in units of the current group's scale,
+ * MFMA GEMM (from 65 to 1024 rows on a narrow weight the decode kernels
+ * instead, by the cost estimate fp8q_linear uses, the GEMM's cost taken as
+ * 1.25 times the per-channel one's): its accumulators are kept in units of the current group's scale,
  * multiplied by s[n][g-1] / s[n][g] (hardware reciprocal) as group g opens, and
  * scaled by the last group's scale at the end.  This needs adjacent group scales
  * of a row within a factor of about 1e28 of each other, which holds for weights

@@ -198,6 +198,13 @@ def test_describe(L):
 
 def test_describe_grouped(L):
     buf = ctypes.create_string_buffer(256)
+    # fp8_w_fp8_a from 65 to 1024 rows: the decode kernels on a narrow weight,
+    # the grouped FP8 GEMM on a wide one or past 1024 rows
+    for m, n, g, want in ((128, 4096, 128, b"k_w8a16_tile<"), (512, 4096, 512, b"k_w8a16_tile<"),
+                          (1024, 4096, 128, b"k_w8a8<true>"), (128, 28672, 128, b"k_w8a8<true>"),
+                          (512, 8192, 128, b"k_w8a8<true>"), (1025, 256, 256, b"k_w8a8<true>")):
+        assert L.fp8q_linear_grouped_describe(1, m, n, 4096, g, buf, 256) == 0
+        assert buf.value.startswith(want), (m, n, g, buf.value)
     # up to 16 rows on a 4096-row weight: the panel kernel with group scales
     assert L.fp8q_linear_grouped_describe(0, 1, 4096, 4096, 128, buf, 256) == 0
     assert buf.value.startswith(b"k_w8a16_panel<1, 1, 2, 4, 4, 2>")
