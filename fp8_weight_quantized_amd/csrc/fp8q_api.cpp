@@ -514,7 +514,7 @@ int act_type(fp8q_mode mode)
 // the cheaper of two cost estimates in microseconds, fitted to measurements
 // on MI355X (K = 4096; N = 4096, 8192, 28672; M = 65..1024; HIP graphs with
 // the weights rotated past the Infinity Cache):
-//   decode kernels   5 + ceil(M / 64) * N * K / 3.2e6
+//   decode kernels   5 + ceil(M / 64) * N * K / 3.5e6
 //   FP8 GEMM         rounds * (K / 128) * 1.45
 //   16-bit GEMM      rounds * (K / 64) * 1.4
 // where rounds = ceil(256 x 256 tiles / 256).  E.g. N = K = 4096 at 128 rows:
@@ -533,7 +533,7 @@ bool mid_rows_decode_cheaper(fp8q_mode mode, int64_t m, int64_t n, int64_t k, do
     const double rounds = (double)(int64_t)((tiles + 255.0) / 256.0);
     const double gemm = mode == FP8Q_W8A8 ? rounds * (double)k / 128.0 * 1.45
                                           : rounds * (double)k / 64.0 * 1.4;
-    const double decode = 5.0 + (double)((m + 63) / 64) * (double)n * (double)k / 3.2e6;
+    const double decode = 5.0 + (double)((m + 63) / 64) * (double)n * (double)k / 3.5e6;
     return decode < gemm * gemm_scale;
 }
 

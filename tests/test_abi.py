@@ -157,8 +157,10 @@ def test_describe(L):
     # 65..1024 rows: the decode kernels where the GEMM's grid would be one
     # round of a few tiles, the GEMMs otherwise
     for mode, m, n, want in ((1, 128, 4096, b"k_w8a16_tile<"), (1, 256, 4096, b"k_w8a16_tile<"),
-                             (1, 512, 4096, b"k_w8a8 "), (1, 65, 28672, b"k_w8a8 "),
-                             (1, 128, 8192, b"k_w8a16_tile<"), (1, 256, 8192, b"k_w8a8 "),
+                             (1, 512, 4096, b"k_w8a16_tile<"), (1, 768, 4096, b"k_w8a8 "),
+                             (1, 65, 28672, b"k_w8a8 "),
+                             (1, 128, 8192, b"k_w8a16_tile<"), (1, 256, 8192, b"k_w8a16_tile<"),
+                             (1, 384, 8192, b"k_w8a8 "),
                              (0, 512, 4096, b"k_w8a16_tile<"), (0, 1024, 4096, b"k_w8a16_tile<"),
                              (0, 1025, 4096, b"k_w8a16_gemm<false>"),
                              (0, 256, 28672, b"k_w8a16_gemm<false>"),
