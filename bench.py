@@ -403,6 +403,39 @@ def main() -> int:
             log(rows["f4_grouped_q_proj_decode"])
             del pool_g, gg
             torch.cuda.empty_cache()
+
+            # 128 and 256 rows on the same weight (batched decode): the decode
+            # kernels in 64-row groups, which the host picks over the prefill
+            # GEMMs for a weight this narrow
+            mid = {}
+            for mode in (0, 1):
+                for m in (128, 256):
+                    xm = up_bf16(workloads.activation(wl, m, K))
+                    xs_m = None
+                    if mode == 1:
+                        xm, xs_m = fq.quantize_act(xm)
+                    ym = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+                    nwm = L.fp8q_linear_workspace_size(mode, m, N, K)
+                    wsm = torch.empty(nwm, dtype=torch.uint8, device=dev) if nwm else None
+
+                    def call_mid(i: int, stream: int, mode=mode, m=m, xm=xm, xs_m=xs_m, ym=ym,
+                                 nwm=nwm, wsm=wsm):
+                        st = L.fp8q_linear(mode, ptr(xm), m, K, K, None if xs_m is None else ptr(xs_m),
+                                           ptr(pool[i % copies_n]), N, K, ptr(w_scale), ptr(ym), N,
+                                           ptr(wsm), nwm, stream)
+                        if st != 0:
+                            raise RuntimeError(_lib.last_error())
+                    usm = time_graph(torch, dev, [lambda h, i=i: call_mid(i, h) for i in range(copies_n)])
+                    bm = N * K + 4 * N + (2 if mode == 0 else 1) * m * K + 2 * m * N
+                    mid[f"{'fp8_w_bf16_a' if mode == 0 else 'fp8_w_fp8_a'} M={m}"] = {
+                        "us": round(usm, 2), "GB/s": round(bm / (usm * 1e-6) / 1e9, 1),
+                        "kernel": fq.describe_linear(mode, m, N, K)}
+            rows["mid_rows_q_proj"] = {
+                "shape": "N=K=4096 (Llama-3-8B q_proj), 128 and 256 rows", "calls": mid,
+                "timing": "HIP graph of calls on weight copies rotated past the Infinity Cache",
+                "note": "beyond the decode configs: 65..1024 rows on a narrow weight run the decode "
+                        "kernels where a cost estimate says they beat the prefill GEMMs"}
+            log(rows["mid_rows_q_proj"])
         cpu = None if args.no_cpu_baseline else {}
         if "tiny" in sections:
             rows.update(tiny_rows(fq, L, up_bf16, ptr, workloads, torch, dev, cpu))
