@@ -1451,7 +1451,7 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act,
                        bool grouped = false)
 {
     const bool f8 = act == kW8A16ActF8, q = act == kW8A16ActQ;
-    if (m < 1 || m > 64 || n < 1 || k % 512 != 0 || k < 2048)
+    if (m < 1 || m > 512 || n < 1 || k % 512 != 0 || k < 2048)
         return false;
     W8A16Plan p = out;
     p.kind = W8A16Plan::kPanel;
@@ -1461,7 +1461,36 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act,
     p.rpw = 0;
     p.kper = k;
     p.kchunk = k / 4;
-    if (m <= 16) {
+    if (m > 64) {
+        // 65..512 rows (a batched decode the host runs here instead of a
+        // prefill GEMM): 64 weight rows x 32 activation rows per workgroup,
+        // the tile that reads the least per CU for these shapes (K x (64 +
+        // 2 x 32) bytes of operands per k for bf16).  Two 128-k chunks in
+        // flight per wave where the grid is one round, else one (64 KB of
+        // rings: two workgroups per CU).  Against the tile kernel, K = 4096,
+        // graphs, weights rotated past the Infinity Cache:
+        //   E4M3, N = 4096: 65..512 rows 10.8 / 11.0 / 16.7 / 23.8 / 34.8 us
+        //     (65, 128, 256, 384, 512) against 16.7 / 18.0 / 21.3 / 40.5 /
+        //     42.5; N = 8192: 19.2 / 19.3 / 27.7 / 40.5 (65..256) against
+        //     23.0 / 22.7 / 41.5 / 44.1
+        //   bf16, N = 4096: 11.9 / 12.1 / 19.4 / 35.8 / 39.7 against 16.3 /
+        //     17.3 / 20.9 / 39.7 / 40.4; a grid of more than one round on a
+        //     wider weight lost (N = 8192 at 128..512 rows 23.0..91.6 against
+        //     21.8..80.2, N = 28672 at 128 rows 98.1 against 86.2) except at
+        //     3 activation groups (65 rows: 20.0 against 21.7 at N = 8192,
+        //     68.9 against 84.5 at N = 28672), so 16-bit activations take
+        //     it only there.
+        if (q || grouped)
+            return false;
+        const int64_t wgs = div_up(n, 64) * div_up(m, 32);
+        if (wgs < 128 || (!f8 && wgs > 256 && n > 4096 && div_up(m, 32) > 3))
+            return false;
+        p.af = 4;
+        p.mb = 2;
+        p.steps = 2;
+        p.depth = wgs <= 256 ? 2 : 1;
+        p.xd = 32;
+    } else if (m <= 16) {
         if (n < 256)
             return false;
         static const int kAf[5] = {1, 2, 3, 4, 7};
@@ -1739,7 +1768,8 @@ static bool launch_panel(const W8A16Plan &p, const void *x, int64_t m, int64_t k
                          const float *w_scale, uint16_t *y, int64_t ld_y, const QuantArgs &qa,
                          hipStream_t stream)
 {
-    constexpr bool kGrouped = AT != kActQ && AF != 7 && !(AT == kActF8 && MB == 2);
+    constexpr bool kGrouped = AT != kActQ && AF != 7 && !(AT == kActF8 && MB == 2) &&
+                              !(AF == 4 && MB == 2);
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.grid_m);
     if (p.group > 0) {
         if constexpr (kGrouped) {
@@ -1790,6 +1820,7 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
             FP8Q_PANEL_CASE(2, 1, 4, 3, 16)
             FP8Q_PANEL_CASE(2, 1, 4, 2, 16)
             FP8Q_PANEL_CASE(2, 2, 4, 2, 32)
+            FP8Q_PANEL_CASE(4, 2, 2, 2, 32) FP8Q_PANEL_CASE(4, 2, 2, 1, 32)
         } else if constexpr (AT == kActQ) {
             // activations cast on the fly: stage (and cast) only the rows that exist
             FP8Q_PANEL_CASE(1, 1, 2, 3, 4) FP8Q_PANEL_CASE(2, 1, 2, 3, 4) FP8Q_PANEL_MB1(4)
@@ -1799,6 +1830,7 @@ static hipError_t dispatch(const W8A16Plan &p, const void *x, int64_t m, int64_t
             FP8Q_PANEL_CASE(1, 1, 2, 4, 16) FP8Q_PANEL_CASE(2, 1, 2, 4, 16) FP8Q_PANEL_MB1(16)
             FP8Q_PANEL_CASE(2, 1, 2, 3, 16)
             FP8Q_PANEL_CASE(2, 2, 2, 2, 32)
+            FP8Q_PANEL_CASE(4, 2, 2, 2, 32) FP8Q_PANEL_CASE(4, 2, 2, 1, 32)
         }
         if constexpr (AT != kActQ) {
             // a small weight: 4 activation rows per workgroup

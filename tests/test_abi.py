@@ -53,11 +53,13 @@ def test_workspace_queries(L):
     # rows W8A8 runs the decode kernels and their K-split scratch
     assert L.fp8q_linear_workspace_size(1, 8192, 28672, 4096) == 0
     assert L.fp8q_linear_workspace_size(1, 65, 28672, 4096) == 0
-    # 65..1024 rows on a narrow weight: the decode kernels in 64-row groups
-    # (N = 4096: 16 tiles of the GEMM against 128 x 2 decode workgroups, K
-    # split in 2), or the 16-bit GEMM past 1024 rows
-    assert L.fp8q_linear_workspace_size(1, 65, 4096, 4096) == 2 * 65 * 4096 * 4
+    # 65..1024 rows on a narrow weight: the decode kernels (the panel kernel
+    # with 64 x 32 tiles up to 512 rows, whole K per workgroup, no scratch;
+    # the tile kernel with K split where the panel does not take the shape),
+    # or the 16-bit GEMM past 1024 rows
+    assert L.fp8q_linear_workspace_size(1, 65, 4096, 4096) == 0
     assert L.fp8q_linear_workspace_size(0, 128, 8192, 4096) == 0
+    assert L.fp8q_linear_workspace_size(0, 128, 1024, 4096) == 4 * 128 * 1024 * 4
     assert L.fp8q_linear_workspace_size(0, 1025, 4096, 4096) == 0
     assert L.fp8q_linear_workspace_size(1, 64, 4096, 4096) == 0         # the panel kernel
     assert L.fp8q_linear_workspace_size(1, 64, 1024, 4096) == 4 * 64 * 1024 * 4
@@ -156,19 +158,26 @@ def test_describe(L):
     assert b"32x112" in buf.value
     # 65..1024 rows: the decode kernels where the GEMM's grid would be one
     # round of a few tiles, the GEMMs otherwise
-    for mode, m, n, want in ((1, 128, 4096, b"k_w8a16_tile<"), (1, 256, 4096, b"k_w8a16_tile<"),
-                             (1, 512, 4096, b"k_w8a16_tile<"), (1, 768, 4096, b"k_w8a8 "),
+    # (the panel kernel with 64 x 32 tiles: two chunks in flight where its
+    # grid is one round, else one; 16-bit activations on a wider weight only
+    # at 3 activation groups)
+    for mode, m, n, want in ((1, 128, 4096, b"k_w8a16_panel<4, 2, 2, 2, 4>"),
+                             (1, 256, 4096, b"k_w8a16_panel<4, 2, 2, 1, 4>"),
+                             (1, 512, 4096, b"k_w8a16_panel<4, 2, 2, 1, 4>"), (1, 768, 4096, b"k_w8a8 "),
                              (1, 65, 28672, b"k_w8a8 "),
-                             (1, 128, 8192, b"k_w8a16_tile<"), (1, 256, 8192, b"k_w8a16_tile<"),
+                             (1, 128, 8192, b"k_w8a16_panel<4, 2, 2, 1, 4>"),
+                             (1, 256, 8192, b"k_w8a16_panel<4, 2, 2, 1, 4>"),
                              (1, 384, 8192, b"k_w8a8 "),
-                             (0, 512, 4096, b"k_w8a16_tile<"), (0, 1024, 4096, b"k_w8a16_tile<"),
+                             (0, 512, 4096, b"k_w8a16_panel<4, 2, 2, 1, 4>"), (0, 1024, 4096, b"k_w8a16_tile<"),
+                             (0, 128, 8192, b"k_w8a16_tile<"), (0, 65, 8192, b"k_w8a16_panel<4, 2, 2, 1, 4>"),
                              (0, 1025, 4096, b"k_w8a16_gemm<false>"),
                              (0, 256, 28672, b"k_w8a16_gemm<false>"),
-                             (2, 128, 28672, b"k_w8a16_tile<"), (2, 256, 28672, b"k_w8a16_gemm<true>")):
+                             (2, 128, 28672, b"k_w8a16_tile<"), (2, 65, 28672, b"k_w8a16_panel<4, 2, 2, 1, 4>"),
+                             (2, 256, 28672, b"k_w8a16_gemm<true>"), (0, 128, 1024, b"k_w8a16_tile<")):
         assert L.fp8q_linear_describe(mode, m, n, 4096, buf, 256) == 0
         assert buf.value.startswith(want), (mode, m, n, buf.value)
     assert L.fp8q_linear_w8a8_dynamic_describe(128, 4096, 4096, buf, 256) == 0
-    assert buf.value.startswith(b"k_act_amax + k_act_cast<0> + k_w8a16_tile<")
+    assert buf.value.startswith(b"k_act_amax + k_act_cast<0> + k_w8a16_panel<4, 2,")
     assert L.fp8q_linear_w8a8_dynamic_describe(128, 28672, 4096, buf, 256) == 0
     assert buf.value.startswith(b"k_act_amax + k_act_cast<0> + k_w8a8 ")
     assert L.fp8q_linear_describe(1, 8, 4096, 4096, buf, 256) == 0

@@ -486,22 +486,23 @@ def test_mid_rows_route_by_cost(fq, mode):
     """65..1024 rows: the decode kernels where the GEMM's grid would be one
     round of a few tiles (Llama-3-8B q_proj at 128 rows), the GEMMs on a wide
     weight (gate+up at 512 rows) and past 1024 rows."""
-    assert fq.describe_linear(mode, 128, 4096, 4096).startswith("k_w8a16_tile<")
+    assert fq.describe_linear(mode, 128, 4096, 4096).startswith("k_w8a16_panel<4, 2,")
     gemm = "k_w8a8 " if mode == 1 else "k_w8a16_gemm<"
     assert fq.describe_linear(mode, 512, 28672, 4096).startswith(gemm)
     assert fq.describe_linear(mode, 1025, 4096, 4096).startswith(gemm)
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
-@pytest.mark.parametrize("m", [65, 128, 200, 256])
+@pytest.mark.parametrize("m", [65, 128, 200, 256, 512])
 def test_mid_rows_q_proj(fq, orc, mode, m):
-    """Llama-3-8B q_proj (N = K = 4096) at 65..256 rows, on the decode kernels
-    in 64-row groups along the grid, against the oracle."""
+    """Llama-3-8B q_proj (N = K = 4096) at 65..256 rows, on the decode panel
+    kernel with 64 weight rows x 32 activation rows per workgroup (two or one
+    chunks in flight per wave), against the oracle."""
     wl = workloads.WORKLOADS["q_proj_decode"]
     lin = wl.linears[0]
     wq, ws, _ = orc.quantize_weight(workloads.weight(wl, lin))
     say("mid rows q_proj", mode, m, fq.describe_linear(mode, m, lin.n, lin.k))
-    assert fq.describe_linear(mode, m, lin.n, lin.k).startswith("k_w8a16_tile<")
+    assert fq.describe_linear(mode, m, lin.n, lin.k).startswith("k_w8a16_panel<4, 2,")
     if mode == 1:
         xq, xs, _ = orc.quantize_act(workloads.activation(wl, m, lin.k))
         y = run_w8a8(fq, xq, xs, wq, ws)
