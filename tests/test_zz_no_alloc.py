@@ -59,7 +59,9 @@ def _call(L, fn, mode, xd, xsd, m, k, wd, n, wsd, y, extra):
 # splits K (so the scratch carries partial tiles between two kernels)
 PAIRS = [[(1, 12, 28672, 8208), (0, 12, 1022, 7000)],
          [(1, 64, 1024, 4096), (1, 24, 1024, 8192)],
-         [(0, 40, 300, 3000), (0, 12, 1000, 6000)]]
+         [(0, 40, 300, 3000), (0, 12, 1000, 6000)],
+         # more than 64 rows on a narrow weight: the decode kernels with K split
+         [(1, 128, 1024, 4096), (0, 100, 700, 4096)]]
 
 
 @pytest.mark.parametrize("pair", PAIRS)
