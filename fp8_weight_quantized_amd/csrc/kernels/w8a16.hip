@@ -1549,8 +1549,20 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act,
         p.depth = m > 32 || (f8 && k < 3 * 4 * 64 * p.steps) ? 2 : 3;
         p.xd = 16 * p.mb;
         const int64_t wgs = div_up(n, 32) * div_up(m, 16 * p.mb);
-        if (wgs < 192 || wgs > 320 || k % (4 * 64 * p.steps) != 0 || k / (4 * 64 * p.steps) < p.depth)
+        if (wgs > 320 && m > 32 && !grouped && div_up(n, 64) * 2 <= 256) {
+            // 33..64 rows on a weight of up to 8192 rows: the 64 x 32 tiles
+            // of the 65..512-row plan, one round of workgroups (bf16, 8192 x
+            // 4096: 48 rows 13.0 us, 64 rows 13.2 us against 16.7 / 18.8 us
+            // for the tile kernel; at 14336 rows and more the panels tie
+            // with the tile kernel or lose)
+            p.af = 4;
+            p.steps = 2;
+            p.depth = 2;
+            p.xd = 32;
+        } else if (wgs < 192 || wgs > 320 || k % (4 * 64 * p.steps) != 0 ||
+                   k / (4 * 64 * p.steps) < p.depth) {
             return false;
+        }
     }
     p.rows = 16 * p.af;
     p.grid_n = div_up(n, 16 * p.af);
