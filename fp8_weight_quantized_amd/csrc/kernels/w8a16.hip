@@ -1549,7 +1549,26 @@ static bool plan_panel(W8A16Plan &out, int64_t m, int64_t n, int64_t k, int act,
         p.depth = m > 32 || (f8 && k < 3 * 4 * 64 * p.steps) ? 2 : 3;
         p.xd = 16 * p.mb;
         const int64_t wgs = div_up(n, 32) * div_up(m, 16 * p.mb);
-        if (wgs > 320 && m > 32 && !grouped && div_up(n, 64) * 2 <= 256) {
+        const int64_t n64 = div_up(n, 64);
+        if (wgs > 320 && m <= 32 && !grouped && n64 * 2 >= 192 && n64 * 2 <= 256) {
+            // 17..32 rows on 6145..8192 weight rows: 64-row panels, two
+            // 16-row activation groups, one round of workgroups (bf16, 8192
+            // x 4096: 24 rows 10.5 us, 32 rows 10.8 us against 14.2 / 14.6
+            // us for the tile kernel)
+            p.af = 4;
+            p.steps = 2;
+            p.depth = 3;
+            p.xd = 16;
+        } else if (wgs > 320 && m <= 32 && !grouped && n64 >= 192 && n64 <= 256) {
+            // 17..32 rows on 12289..16384 weight rows: 64 x 32 tiles, one
+            // round (bf16, 14336 x 4096: 24 rows 14.4 us, 32 rows 15.0 us
+            // against 19.8 / 20.1 us for the tile kernel)
+            p.af = 4;
+            p.mb = 2;
+            p.steps = 2;
+            p.depth = 2;
+            p.xd = 32;
+        } else if (wgs > 320 && m > 32 && !grouped && n64 * 2 <= 256) {
             // 33..64 rows on a weight of up to 8192 rows: the 64 x 32 tiles
             // of the 65..512-row plan, one round of workgroups (bf16, 8192 x
             // 4096: 48 rows 13.0 us, 64 rows 13.2 us against 16.7 / 18.8 us

@@ -516,3 +516,36 @@ def test_mid_rows_q_proj(fq, orc, mode, m):
         y = run_w8a16_f16(fq, x, wq, ws)
         ref = orc.linear(2, x, wq, ws)
     assert_gemm_close(y, ref, f"mid rows q_proj mode {mode} m={m}")
+
+
+# 17..64 rows on weights of 6145..16384 rows: 64-row panels in one round of
+# workgroups (16-row or 32-row activation groups), where the 32-row panels
+# would need more than one round
+WIDE_ONE_ROUND = [(17, 6144, 2048, "k_w8a16_panel<4, 1, 2, 3, 4>"),
+                  (32, 8192, 4096, "k_w8a16_panel<4, 1, 2, 3, 4>"),
+                  (24, 14336, 2048, "k_w8a16_panel<4, 2, 2, 2, 4>"),
+                  (48, 8192, 2048, "k_w8a16_panel<4, 2, 2, 2, 4>"),
+                  (64, 6000, 2560, "k_w8a16_panel<4, 2, 2, 2, 4>")]
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("m,n,k,kernel", WIDE_ONE_ROUND)
+def test_panel_wide_one_round(fq, orc, mode, m, n, k, kernel):
+    plan = fq.describe_linear(mode, m, n, k)
+    assert plan.startswith(kernel), plan
+    w = workloads.heavy_tail_weight(n, k, 60 + m)
+    wq, ws, _ = orc.quantize_weight(w)
+    say("wide one-round panel", mode, m, n, k, plan)
+    if mode == 1:
+        xq, xs, _ = orc.quantize_act(workloads.outlier_act(m, k, 61 + m))
+        y = run_w8a8(fq, xq, xs, wq, ws)
+        ref = orc.linear(1, xq, wq, ws, xs)
+    elif mode == 0:
+        x = workloads.normal_act(m, k, 62 + m)
+        y = run_w8a16(fq, x, wq, ws)
+        ref = orc.linear(0, x, wq, ws)
+    else:
+        x = f16_act(m, k, 63 + m)
+        y = run_w8a16_f16(fq, x, wq, ws)
+        ref = orc.linear(2, x, wq, ws)
+    assert_gemm_close(y, ref, f"wide one-round panel mode {mode} {m}x{n}x{k}")
